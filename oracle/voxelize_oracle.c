@@ -1,0 +1,235 @@
+/*
+ * Sequential CPU oracle for PointPillars-style pillar / voxel binning.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * definition the GPU library is checked against. Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the library itself
+ * never does, and the two share no code, headers or tables.
+ *
+ * Source: "Voxelize" (ethan-howes.github.io/projects/voxelize).
+ *   - Output tensors: the introduction (a [V,32,4] per-pillar point stack,
+ *     [V,3] grid coordinates, [V] per-pillar counts).
+ *   - Binning: section "Binning a point" (NaN/Inf check, z-slab, floorf cell
+ *     index, strict < on the upper grid bound, flattened id cy*grid_x+cx).
+ *   - Coordinates (z, y, x) with z = 0 for pillars, and "keep the first K"
+ *     (points past max_points are dropped): section "Claiming a pillar and
+ *     packing points".
+ *   - Pillar assignment by a dictionary in insertion order, as the page's
+ *     NumPy reference does: section "Results".
+ *
+ * Readings taken where the page is silent (each one fixes a single output):
+ *   - pillars are numbered in order of first occurrence in the input;
+ *   - the first max_voxels pillars are kept; points of later pillars are
+ *     dropped and create no pillar, later points of kept pillars still count;
+ *   - inside a pillar the max_points lowest input indices are kept, in order;
+ *   - counts = min(total points of the pillar, max_points);
+ *   - rows past the count are +0.0f;
+ *   - the NaN/Inf check applies to x, y, z only (intensity is copied as bits);
+ *   - the z-slab is z_min <= z < z_max; in 3D mode (gz > 1) the z cell index
+ *     floorf((z - z_min) / vz) must also lie in [0, gz);
+ *   - x_max and y_max do not enter binning: the grid size bounds the cell;
+ *   - range tests are made on the float floor value before any conversion,
+ *     every operation in IEEE fp32 round-to-nearest, no FMA contraction.
+ *
+ * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    float x_min, y_min, z_min;
+    float vx, vy, vz;
+    int64_t gx, gy, gz;
+} oracle_grid;
+
+static oracle_grid make_grid(const float range[6], const float cell[3], const int32_t grid[3])
+{
+    oracle_grid g;
+    g.x_min = range[0];
+    g.y_min = range[1];
+    g.z_min = range[2];
+    g.vx = cell[0];
+    g.vy = cell[1];
+    g.vz = cell[2];
+    g.gx = grid[0];
+    g.gy = grid[1];
+    g.gz = grid[2];
+    return g;
+}
+
+/*
+ * Bin one point, following "Binning a point": returns 1 and writes the cell
+ * (cx, cy, cz) when the point is kept, 0 when it is rejected.
+ */
+static int bin_point(const float *p, const oracle_grid *g, float z_max,
+                     int64_t *cx, int64_t *cy, int64_t *cz)
+{
+    float x = p[0], y = p[1], z = p[2];
+
+    /* NaN/Inf check on the coordinates. */
+    if (isnan(x) || isinf(x) || isnan(y) || isinf(y) || isnan(z) || isinf(z))
+        return 0;
+
+    /* Drop points outside the z-slab. */
+    if (!(z >= g->z_min && z < z_max))
+        return 0;
+
+    /* Cell index with floorf of ((coordinate - min) / cell size). */
+    float fx = floorf((x - g->x_min) / g->vx);
+    float fy = floorf((y - g->y_min) / g->vy);
+
+    /* Reject anything outside the grid, strict < on the upper bound. */
+    if (!(fx >= 0.0f && fx < (float)g->gx))
+        return 0;
+    if (!(fy >= 0.0f && fy < (float)g->gy))
+        return 0;
+
+    float fz = 0.0f;
+    if (g->gz > 1) {
+        fz = floorf((z - g->z_min) / g->vz);
+        if (!(fz >= 0.0f && fz < (float)g->gz))
+            return 0;
+    }
+
+    *cx = (int64_t)fx;
+    *cy = (int64_t)fy;
+    *cz = (int64_t)fz;
+    return 1;
+}
+
+/* Flattened cell id: cy*grid_x + cx for pillars, (cz*gy + cy)*gx + cx in 3D. */
+static int64_t flat_key(const oracle_grid *g, int64_t cx, int64_t cy, int64_t cz)
+{
+    return (cz * g->gy + cy) * g->gx + cx;
+}
+
+/*
+ * Per-point binning, exported so the tests can compare it with an independent
+ * float32 evaluation: valid[i] = 1/0 and key[i] = flattened id or -1.
+ */
+int oracle_bin(const float *points, int64_t n, const float range[6], const float cell[3],
+               const int32_t grid[3], int8_t *valid, int64_t *key)
+{
+    oracle_grid g = make_grid(range, cell, grid);
+    for (int64_t i = 0; i < n; i++) {
+        int64_t cx, cy, cz;
+        if (bin_point(points + 4 * i, &g, range[5], &cx, &cy, &cz)) {
+            valid[i] = 1;
+            key[i] = flat_key(&g, cx, cy, cz);
+        } else {
+            valid[i] = 0;
+            key[i] = -1;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The dictionary: flattened key -> pillar id, holding only the kept pillars.
+ * A plain open-addressing map; nothing about it is visible in the output.
+ */
+typedef struct {
+    int64_t cap;      /* power of two */
+    int64_t *keys;    /* -1 = empty */
+    int32_t *vals;
+} key_map;
+
+static int map_init(key_map *m, int64_t max_entries)
+{
+    m->cap = 16;
+    while (m->cap < 2 * max_entries + 2)
+        m->cap *= 2;
+    m->keys = (int64_t *)malloc((size_t)m->cap * sizeof(int64_t));
+    m->vals = (int32_t *)malloc((size_t)m->cap * sizeof(int32_t));
+    if (!m->keys || !m->vals)
+        return -1;
+    for (int64_t s = 0; s < m->cap; s++)
+        m->keys[s] = -1;
+    return 0;
+}
+
+static void map_free(key_map *m)
+{
+    free(m->keys);
+    free(m->vals);
+}
+
+/* Returns the slot holding `key`, or the empty slot where it would go. */
+static int64_t map_slot(const key_map *m, int64_t key)
+{
+    uint64_t h = (uint64_t)key * 0x9E3779B97F4A7C15ull;
+    int64_t s = (int64_t)(h >> 20) & (m->cap - 1);
+    while (m->keys[s] != -1 && m->keys[s] != key)
+        s = (s + 1) & (m->cap - 1);
+    return s;
+}
+
+/*
+ * The whole operation, one point at a time in input order.
+ *
+ * voxels is [max_voxels, max_points, 4] float, coords [max_voxels, 3] int32
+ * (z, y, x), num_points [max_voxels] int32; rows [0, V) are written, V goes to
+ * *num_voxels. Returns 0, or -1 if memory for the dictionary is unavailable.
+ */
+int oracle_voxelize(const float *points, int64_t n, const float range[6], const float cell[3],
+                    const int32_t grid[3], int32_t max_points, int32_t max_voxels,
+                    float *voxels, int32_t *coords, int32_t *num_points, int32_t *num_voxels)
+{
+    oracle_grid g = make_grid(range, cell, grid);
+    const int64_t K = max_points;
+    key_map dict;
+    if (map_init(&dict, max_voxels) != 0) {
+        map_free(&dict);
+        return -1;
+    }
+    int64_t *total = (int64_t *)calloc((size_t)max_voxels + 1, sizeof(int64_t));
+    if (!total) {
+        map_free(&dict);
+        return -1;
+    }
+    int64_t V = 0;
+
+    for (int64_t i = 0; i < n; i++) {
+        const float *p = points + 4 * i;
+        int64_t cx, cy, cz;
+        if (!bin_point(p, &g, range[5], &cx, &cy, &cz))
+            continue;
+        int64_t key = flat_key(&g, cx, cy, cz);
+
+        int64_t s = map_slot(&dict, key);
+        int64_t pid;
+        if (dict.keys[s] == key) {
+            pid = dict.vals[s];
+        } else if (V < max_voxels) {
+            /* A new pillar, numbered in order of first occurrence. */
+            pid = V++;
+            dict.keys[s] = key;
+            dict.vals[s] = (int32_t)pid;
+            coords[3 * pid + 0] = (int32_t)cz;  /* z (0 for pillars) */
+            coords[3 * pid + 1] = (int32_t)cy;  /* y */
+            coords[3 * pid + 2] = (int32_t)cx;  /* x */
+        } else {
+            continue;  /* its pillar is past the max_voxels cap: dropped */
+        }
+
+        total[pid] += 1;
+        if (total[pid] <= K) {
+            /* keep the first K points of the pillar, copied bit for bit */
+            memcpy(voxels + (pid * K + (total[pid] - 1)) * 4, p, 4 * sizeof(float));
+        }
+    }
+
+    for (int64_t pid = 0; pid < V; pid++) {
+        int64_t c = total[pid] < K ? total[pid] : K;
+        num_points[pid] = (int32_t)c;
+        for (int64_t j = c; j < K; j++)
+            memset(voxels + (pid * K + j) * 4, 0, 4 * sizeof(float));
+    }
+    *num_voxels = (int32_t)V;
+
+    free(total);
+    map_free(&dict);
+    return 0;
+}

@@ -1,0 +1,104 @@
+"""Independent checks for the oracle (test-only; shares no code with it).
+
+``bin_np`` evaluates the binning rules of the "Voxelize" page ("Binning a
+point") with vectorised numpy float32 operations; ``sort_then_segment`` groups
+points the way the page's "Design Decisions" section describes the naive
+method: sort every point by its cell id, then cut the sorted list into
+segments. Segments are then ordered by their lowest point index, the first
+``max_voxels`` are kept and each keeps its ``max_points`` lowest indices.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+F32 = np.float32
+
+
+def bin_np(points, range_, cell, grid):
+    p = np.asarray(points, dtype=F32)
+    x, y, z = p[:, 0], p[:, 1], p[:, 2]
+    x0, y0, z0, _, _, z1 = (F32(v) for v in range_)
+    vx, vy, vz = (F32(v) for v in cell)
+    gx, gy, gz = (int(v) for v in grid)
+    with np.errstate(all="ignore"):
+        ok = np.isfinite(x) & np.isfinite(y) & np.isfinite(z)
+        ok &= (z >= z0) & (z < z1)
+        fx = np.floor((x - x0) / vx)
+        fy = np.floor((y - y0) / vy)
+        ok &= (fx >= F32(0)) & (fx < F32(gx)) & (fy >= F32(0)) & (fy < F32(gy))
+        if gz > 1:
+            fz = np.floor((z - z0) / vz)
+            ok &= (fz >= F32(0)) & (fz < F32(gz))
+        else:
+            fz = np.zeros_like(fx)
+    cx = np.where(ok, fx, 0).astype(np.int64)
+    cy = np.where(ok, fy, 0).astype(np.int64)
+    cz = np.where(ok, fz, 0).astype(np.int64)
+    key = np.where(ok, (cz * gy + cy) * gx + cx, -1)
+    return ok, key
+
+
+def decode(key, grid):
+    gx, gy, _ = (int(v) for v in grid)
+    key = np.asarray(key, dtype=np.int64)
+    cx = key % gx
+    cy = (key // gx) % gy
+    cz = key // (gx * gy)
+    return np.stack([cz, cy, cx], axis=1).astype(np.int32)
+
+
+def sort_then_segment(points, range_, cell, grid, max_points, max_voxels):
+    """Brute-force voxelization: (voxels [V,K,4], coords [V,3], counts [V])."""
+    p = np.ascontiguousarray(points, dtype=F32)
+    K, M = int(max_points), int(max_voxels)
+    ok, key = bin_np(p, range_, cell, grid)
+    idx = np.flatnonzero(ok)
+    k = key[idx]
+    order = np.argsort(k, kind="stable")          # sort by cell id; ties keep index order
+    ks, js = k[order], idx[order]
+    n = ks.size
+    if n == 0:
+        return (np.zeros((0, K, 4), F32), np.zeros((0, 3), np.int32), np.zeros((0,), np.int32))
+    start_flag = np.r_[True, ks[1:] != ks[:-1]]
+    starts = np.flatnonzero(start_flag)
+    seg_of = np.cumsum(start_flag) - 1
+    seg_len = np.diff(np.r_[starts, n])
+    seg_first = js[starts]                         # lowest index of each segment
+    seg_rank = np.empty(starts.size, dtype=np.int64)
+    seg_rank[np.argsort(seg_first, kind="stable")] = np.arange(starts.size)
+    V = min(starts.size, M)
+    pos = np.arange(n) - starts[seg_of]
+    rank = seg_rank[seg_of]
+    take = (rank < V) & (pos < K)
+    voxels = np.zeros((V, K, 4), dtype=F32)
+    voxels.view(np.uint32)[rank[take], pos[take]] = p.view(np.uint32)[js[take]]
+    kept_seg = np.flatnonzero(seg_rank < V)
+    coords = np.zeros((V, 3), np.int32)
+    counts = np.zeros((V,), np.int32)
+    coords[seg_rank[kept_seg]] = decode(ks[starts[kept_seg]], grid)
+    counts[seg_rank[kept_seg]] = np.minimum(seg_len[kept_seg], K)
+    return voxels, coords, counts
+
+
+# ---- exact IEEE float32 evaluation with rationals (boundary points) --------
+
+def round_f32(q: Fraction) -> F32:
+    """Round a rational to the nearest float32, ties to even (exactly)."""
+    c = F32(float(q))
+    best = None
+    for cand in (np.nextafter(c, F32(-np.inf)), c, np.nextafter(c, F32(np.inf))):
+        if not np.isfinite(cand):
+            continue
+        d = abs(Fraction(float(cand)) - q)
+        if best is None or d < best[0] or (d == best[0] and (int(cand.view(np.uint32)) & 1) == 0):
+            best = (d, cand)
+    return F32(best[1])
+
+
+def exact_cell(v, v0, cell) -> int:
+    """floor(fl32(fl32(v - v0) / cell)) evaluated with exact rationals."""
+    diff = round_f32(Fraction(float(F32(v))) - Fraction(float(F32(v0))))
+    quo = round_f32(Fraction(float(diff)) / Fraction(float(F32(cell))))
+    return int(np.floor(float(quo)))

@@ -1,0 +1,151 @@
+"""The pins must reject a wrong oracle.
+
+Each case copies the oracle's C source, plants one plausible mistake (a
+dropped term, a wrong bound, a swapped index, a different rounding), builds it
+with the same flags, and runs a battery of the independent pins against it.
+The unmodified source must pass the battery and every mutant must fail it.
+All of this runs on the CPU.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from bruteforce import bin_np, exact_cell, sort_then_segment
+from workloads import generate, get_config
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+MUTANTS = {
+    "truncation_instead_of_floor": [("floorf((x - g->x_min) / g->vx)", "truncf((x - g->x_min) / g->vx)")],
+    "non_strict_upper_x": [("fx < (float)g->gx", "fx <= (float)g->gx")],
+    "non_strict_zslab_top": [("z < z_max", "z <= z_max")],
+    "strict_zslab_bottom": [("z >= g->z_min", "z > g->z_min")],
+    "non_strict_upper_z_cell": [("fz < (float)g->gz", "fz <= (float)g->gz")],
+    "keep_one_point_less": [("total[pid] <= K", "total[pid] < K")],
+    "coords_y_gets_x": [("coords[3 * pid + 1] = (int32_t)cy;", "coords[3 * pid + 1] = (int32_t)cx;")],
+    "cap_one_short": [("V < max_voxels", "V < max_voxels - 1")],
+    "rows_reversed": [("(pid * K + (total[pid] - 1))", "(pid * K + (K - total[pid]))")],
+    "key_uses_gx_for_gy": [("(cz * g->gy + cy)", "(cz * g->gx + cy)")],
+    "reciprocal_multiply": [("(x - g->x_min) / g->vx", "(x - g->x_min) * (1.0f / g->vx)")],
+    "y_divided_by_vx": [("(y - g->y_min) / g->vy", "(y - g->y_min) / g->vx")],
+    "no_zero_padding": [("memset(voxels + (pid * K + j) * 4, 0, 4 * sizeof(float));", "(void)0;")],
+    "counts_not_clamped": [("num_points[pid] = (int32_t)c;", "num_points[pid] = (int32_t)total[pid];")],
+    "double_precision_binning": [("floorf((x - g->x_min) / g->vx)",
+                                  "(float)floor(((double)x - (double)g->x_min) / (double)g->vx)")],
+    "keep_last_k": [("if (total[pid] <= K) {", "{"),
+                    ("(pid * K + (total[pid] - 1))", "(pid * K + (total[pid] - 1) % K)")],
+    "x_min_for_y": [("(y - g->y_min) / g->vy", "(y - g->x_min) / g->vy")],
+}
+
+
+def _same(a, b):
+    va, ca, na = a
+    vb, cb, nb = b
+    return (va.shape == vb.shape and np.array_equal(ca, cb) and np.array_equal(na, nb)
+            and np.array_equal(va.view(np.uint32), vb.view(np.uint32)))
+
+
+def _battery(lib):
+    """Names of the pins that fail for this oracle build."""
+    fails = []
+    hand = json.load(open(os.path.join(GOLDEN, "hand_cases.json")))
+    for key, gkey in (("cases", "grid_4x4"), ("cases_3d", "grid_3d")):
+        gs = hand[gkey]
+        for case in hand[key]:
+            pts = (np.array([[float(v) for v in r] for r in case["points"]], F32)
+                   if case["points"] else np.zeros((0, 4), F32))
+            vox, coords, counts = oracle.voxelize(pts, gs["range"], gs["cell"], gs["grid"],
+                                                  case["max_points"], case["max_voxels"], lib=lib)
+            ok = coords.tolist() == case["coords"] and counts.tolist() == case["num_points"]
+            if ok:
+                for p, rows in enumerate(case["rows"]):
+                    for j, src in enumerate(rows):
+                        want = np.zeros(4, F32) if src is None else pts[src]
+                        ok &= bool(np.array_equal(vox[p, j].view(np.uint32), want.view(np.uint32)))
+            if not ok:
+                fails.append("hand:" + case["name"])
+    edge = json.load(open(os.path.join(GOLDEN, "edge_points.json")))
+    pts, info = generate("tiny")
+    gsp = edge["grid"]
+    valid, key = oracle.bin_points(pts, gsp["range"], gsp["cell"], gsp["grid"], lib=lib)
+    for name, exp in edge["points"].items():
+        i = info["edge_index"][name]
+        if bool(valid[i]) != exp["kept"]:
+            fails.append("edge:" + name)
+        elif exp["kept"]:
+            cx = exact_cell(pts[i, 0], gsp["range"][0], gsp["cell"][0])
+            cy = exact_cell(pts[i, 1], gsp["range"][1], gsp["cell"][1])
+            if key[i] != cy * gsp["grid"][0] + cx:
+                fails.append("edge_cell:" + name)
+    # 3D z boundary
+    prm = get_config("voxel3d").params
+    z = np.array([np.nextafter(F32(prm.range_[5]), F32(-np.inf))], F32)
+    p3 = np.array([[10.0, 1.0, z[0], 0.0]], F32)
+    v3, _ = oracle.bin_points(p3, prm.range_, prm.cell, prm.grid, lib=lib)
+    if bool(v3[0]) != (exact_cell(z[0], prm.range_[2], prm.cell[2]) < prm.grid[2]):
+        fails.append("z3d_boundary")
+    # boundary sweep against numpy float32
+    for name in ("tiny", "voxel3d"):
+        prm = get_config(name).params
+        k = np.arange(prm.grid[0] + 1, dtype=np.float64)
+        xs = (F32(prm.range_[0]) + k * float(F32(prm.cell[0]))).astype(F32)
+        xs = np.concatenate([xs, np.nextafter(xs, F32(np.inf)), np.nextafter(xs, F32(-np.inf))])
+        sw = np.zeros((xs.size, 4), F32)
+        sw[:, 0] = xs
+        sw[:, 1] = F32((prm.range_[1] + prm.range_[4]) / 2)
+        sw[:, 2] = F32((prm.range_[2] + prm.range_[5]) / 2)
+        ov, ok_ = oracle.bin_points(sw, prm.range_, prm.cell, prm.grid, lib=lib)
+        nv, nk = bin_np(sw, prm.range_, prm.cell, prm.grid)
+        if not (np.array_equal(ov, nv) and np.array_equal(ok_, nk)):
+            fails.append("sweep:" + name)
+    # sort-then-segment on workloads and on fixed random tiny grids
+    for name, n in (("kitti_frame", None), ("voxel3d", 200000), ("tiny", None)):
+        cfg = get_config(name)
+        pts, _ = generate(name, n=n)
+        p = cfg.params
+        got = oracle.voxelize(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels, lib=lib)
+        if not _same(got, sort_then_segment(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)):
+            fails.append("brute:" + name)
+    rng = np.random.default_rng(7)
+    for t in range(40):
+        gx, gy = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        vx, vy = float(F32(rng.choice([0.16, 0.3, 1.0]))), float(F32(rng.choice([0.1, 0.5, 0.7])))
+        n = int(rng.integers(1, 80))
+        pts = np.zeros((n, 4), F32)
+        pts[:, 0] = ((rng.integers(-1, gx + 1, n) + rng.choice([0.0, 0.5], n)) * vx).astype(F32)
+        pts[:, 1] = ((rng.integers(-1, gy + 1, n) + rng.choice([0.0, 0.5], n)) * vy).astype(F32)
+        pts[:, 2] = rng.uniform(-3.5, 1.5, n).astype(F32)
+        pts[:, 3] = np.arange(n, dtype=F32)
+        r = (0.0, 0.0, -3.0, gx * vx, gy * vy, 1.0)
+        K, M = int(rng.integers(1, 4)), int(rng.integers(1, 8))
+        got = oracle.voxelize(pts, r, (vx, vy, 4.0), (gx, gy, 1), K, M, lib=lib)
+        if not _same(got, sort_then_segment(pts, r, (vx, vy, 4.0), (gx, gy, 1), K, M)):
+            fails.append("brute:random")
+            break
+    return fails
+
+
+def _build(tmp_path, name, edits):
+    src = open(oracle.SOURCE).read()
+    for old, new in edits:
+        assert src.count(old) >= 1, (name, old)
+        src = src.replace(old, new)
+    path = tmp_path / f"{name}.c"
+    path.write_text(src)
+    out = tmp_path / f"lib{name}.so"
+    oracle.build(str(path), str(out))
+    return oracle.load(str(out))
+
+
+def test_unmodified_oracle_passes_battery(tmp_path):
+    assert _battery(_build(tmp_path, "control", [])) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    fails = _battery(_build(tmp_path, name, MUTANTS[name]))
+    assert fails, f"mutant {name} passes every pin"
