@@ -1,0 +1,198 @@
+"""Benchmark: pillar voxelization throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+A step is one complete voxelize call (insert, rank, select, pack) over one
+synthetic cloud already resident in HBM, outputs and workspace pre-allocated.
+W untimed steps, then K steps timed with HIP events on the call's stream,
+bracketed by device synchronisation (the page's protocol: mean over timed
+iterations after warm-up, inputs on the GPU). Prints one JSON line.
+
+* value: Mpoints/s = N / (time per call), N counting every input point.
+* roofline: the dominant kernel (largest mean stage time, measured live with
+  HIP events between the stages) against MI355X's 8 TB/s HBM peak, using the
+  kernel's algorithmic bytes per launch.
+* cpu_baseline: the CPU oracle (one thread) on the same cloud on this host.
+* --all: one extra JSON line per workload (to stderr) for the results table.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "kitti_frame"
+METRIC = "Mpoints/s voxelized + achieved HBM GB/s (fraction of peak) at 122,880-pt frame"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on the oracle's CPU sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--profile-iters", type=int, default=50)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(N, P, V, K, rows):
+    """Compulsory bytes of the whole call and of each kernel.
+
+    whole call: read every point once (16 B) + write the dense output,
+    V * (16 K + 16) bytes (rows incl. zero padding, 12 B coords, 4 B count).
+    insert: its share of the input read, 16 B per prefix point.
+    rank:   4 B per prefix point (the slot index written by insert).
+    select: 16 B per point past the prefix + 4 B per prefix point (slot).
+    pack:   the dense output + 16 B per kept row gathered from the input.
+    """
+    out = V * (16 * K + 16)
+    return dict(call=16 * N + out, insert=16 * P, rank=4 * P, select=16 * (N - P) + 4 * P,
+                pack=out + 16 * rows)
+
+
+def time_calls(vx, x, steps, warmup, torch):
+    for _ in range(warmup):
+        vx.run(x)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        vx.run(x)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def check_parity(vx, pts, prm):
+    import oracle
+    gv, gc, gn = (t.cpu().numpy() for t in vx.outputs())
+    ov, oc, on = oracle.voxelize_params(pts, prm)
+    return bool(gv.shape == ov.shape and np.array_equal(gc, oc) and np.array_equal(gn, on)
+                and np.array_equal(gv.view(np.uint32), ov.view(np.uint32)))
+
+
+def cpu_baseline(pts, prm, seconds):
+    """The oracle as it stands, on one host core, repeated on the full cloud
+    until `seconds` of CPU work are spent (at least 3 repetitions)."""
+    import oracle
+    oracle.load()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.voxelize_params(pts, prm)
+        reps += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and reps >= 3) or reps >= 100000:
+            break
+    per = el / reps
+    return {"value": round(pts.shape[0] / per / 1e6, 3), "unit": "Mpoints/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} repetitions of the full {pts.shape[0]:,}-point cloud "
+                      f"({el:.1f} s, {per * 1e3:.2f} ms each), single-threaded C oracle, "
+                      f"host {platform.processor() or platform.machine()} with "
+                      f"{os.cpu_count()} logical CPUs"}
+
+
+def run_workload(name, steps, warmup, profile_iters, torch, vox):
+    from workloads import generate, get_config
+    cfg = get_config(name)
+    p = cfg.params
+    pts, _ = generate(name)
+    N = pts.shape[0]
+    x = torch.from_numpy(pts).to("cuda:0")
+    vx = vox.Voxelizer(N, p.range_, p.cell, p.grid, p.max_points, p.max_voxels, device="cuda:0")
+    ms = time_calls(vx, x, steps, warmup, torch)
+    vx.run(x)
+    torch.cuda.synchronize()
+    V = int(vx.num_voxels.item())
+    rows = int(vx.num_points[:max(V, 0)].sum().item()) if V > 0 else 0
+    parity = check_parity(vx, pts, p)
+    stage_ms, total_ms = vx.profile(x, profile_iters)
+    S = 8 * p.max_voxels
+    P = min(N, S // 2)
+    alg = algorithmic_bytes(N, P, V, p.max_points, rows)
+    return dict(cfg=cfg, pts=pts, N=N, V=V, rows=rows, ms=ms, parity=parity, stage_ms=stage_ms,
+                total_ms=total_ms, alg=alg, P=P)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Frames are independent, so more GPUs would "
+              f"each run their own frames; no cross-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import sparse_spatial_hashing_amd as vox
+
+    r = run_workload(args.workload, args.steps, args.warmup, args.profile_iters, torch, vox)
+    N, ms = r["N"], r["ms"]
+    value = N / (ms * 1e-3) / 1e6
+    gbs = r["alg"]["call"] / (ms * 1e-3) / 1e9
+    dom = max(r["stage_ms"], key=r["stage_ms"].get)
+    dom_ms = r["stage_ms"][dom]
+    dom_gbs = r["alg"][dom] / (dom_ms * 1e-3) / 1e9
+    p = r["cfg"].params
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "Mpoints/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_points": N, "grid": list(p.grid),
+                   "cell_m": list(p.cell), "max_points": p.max_points,
+                   "max_voxels": p.max_voxels, "pillars": r["V"], "kept_rows": r["rows"]},
+        "achieved_gbs_alg": round(gbs, 1),
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "parity_vs_oracle": r["parity"],
+        "stages_ms": {k: round(v, 5) for k, v in r["stage_ms"].items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "alg_bytes_per_launch": int(r["alg"][dom]),
+                     "launch_ms": round(dom_ms, 5), "traffic": None},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(r["pts"], p, args.cpu_seconds)
+    if args.all:
+        from workloads import config_names
+        for name in config_names():
+            q = run_workload(name, args.steps, args.warmup, args.profile_iters, torch, vox)
+            print(json.dumps({
+                "workload": name, "N": q["N"], "V": q["V"], "kept_rows": q["rows"],
+                "us_per_call": round(q["ms"] * 1e3, 2),
+                "mpoints_s": round(q["N"] / (q["ms"] * 1e-3) / 1e6, 1),
+                "gbs_alg": round(q["alg"]["call"] / (q["ms"] * 1e-3) / 1e9, 1),
+                "frac_hbm": round(q["alg"]["call"] / (q["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "stages_us": {k: round(v * 1e3, 2) for k, v in q["stage_ms"].items()},
+                "parity": q["parity"]}), file=sys.stderr, flush=True)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * voxelize.h -- C ABI of the MI355X (gfx950) pillar / voxel binning library.
+ *
+ * The operation is the one described on the "Voxelize" page
+ * (ethan-howes.github.io/projects/voxelize): an unordered [N, 4] float32
+ * cloud (x, y, z, intensity) is turned into the three tensors PointPillars
+ * consumes (introduction): a [V, K, 4] stack of per-pillar points, [V, 3]
+ * int32 grid coordinates (z, y, x) and [V] int32 per-pillar counts. Points are
+ * grouped through an open-addressing hash table ("A hash table instead of a
+ * sort") sized 8 x max_voxels ("A fixed table, sized 8x the voxel budget").
+ *
+ * Output order and content are deterministic (the page's kernel writes pillars
+ * in hash-slot order and points in arrival order; this library does not):
+ *   - pillars are numbered in order of first occurrence in the input, and the
+ *     first max_voxels of them are kept; points whose pillar is past the cap
+ *     are dropped;
+ *   - each pillar keeps its max_points lowest input indices, in index order
+ *     ("keep the first K", section "Claiming a pillar and packing points");
+ *   - num_points[p] = min(points in pillar p, max_points); rows past it are
+ *     +0.0f; rows are bit copies of the input rows;
+ *   - coords[p] = (z, y, x) cell indices, z = 0 in pillar mode (grid[2] == 1).
+ * Binning follows section "Binning a point": NaN/Inf in x, y or z rejects a
+ * point; the z-slab is z_min <= z < z_max; cell = floorf((v - v_min) / cell)
+ * in IEEE fp32 (correctly rounded divide, no FMA, denormals kept); a cell is
+ * kept when 0 <= cell < grid (strict upper bound). In 3D mode (grid[2] > 1)
+ * the z cell must also lie in [0, grid[2]). x_max and y_max are validated but
+ * do not enter binning: the grid size bounds the cell.
+ *
+ * Conventions for every entry point:
+ *   - Returns VOX_OK (0) or a negative VOX_E* code. Argument checks happen on
+ *     the host before any HIP call; on an argument error nothing is launched.
+ *   - Device pointers belong to the caller and must live on the current HIP
+ *     device. Host pointers are read during the call only.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising, unless the entry point says otherwise. Nothing
+ *     is allocated on the device.
+ *   - The library keeps no mutable global state. Calls on different streams
+ *     with different workspaces may run concurrently; two calls that share a
+ *     workspace must be ordered (same stream, or synchronised).
+ */
+#ifndef VOXELIZE_H
+#define VOXELIZE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes -------------------------------------------------------- */
+#define VOX_OK 0
+#define VOX_EINVAL -1      /* bad argument (null pointer, bad size, range, cell or grid) */
+#define VOX_EWORKSPACE -2  /* workspace smaller than vox_workspace_bytes() or misaligned */
+#define VOX_EHIP -4        /* a HIP call failed; vox_last_hip_error() returns its code */
+
+/* ---- device status written to num_voxels[0] instead of V ----------------- */
+/* The single-pass path inserts the first P = min(N, table_slots/2) points into
+ * the table and decides the max_voxels cap among them. When N > P and those P
+ * points hold fewer than max_voxels distinct cells, the cap cannot be decided
+ * in one pass: num_voxels[0] is set to VOX_STATUS_NEEDS_CHUNKED, the outputs
+ * are not written, the workspace is left clean, and the caller repeats the
+ * call with voxelize_chunked(). */
+#define VOX_STATUS_NEEDS_CHUNKED (-16)
+/* An internal bound was exceeded (a probe sequence longer than the table or a
+ * look-back wait past its spin limit). Not reachable with valid inputs; the
+ * outputs are not written and the workspace must be re-zeroed. */
+#define VOX_STATUS_DEVICE_ERROR (-17)
+
+/* ---- options (tests and tuning; NULL = defaults) ------------------------- */
+typedef struct vox_options {
+    int64_t table_slots;    /* hash table slots S; 0 = 8 * max_voxels (at least 64);
+                               otherwise 2 * max_voxels <= S <= 2^31 - 1 */
+    int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N, S/2);
+                               clamped to [1, S/2] */
+    int32_t hash;           /* 0 = 64-bit mix + multiply-high reduction, 1 = key mod S */
+    int32_t reserved;
+} vox_options;
+
+/*
+ * Workspace size in bytes for a call with n_points points, max_voxels and
+ * max_points (and options, NULL for defaults). The workspace is device memory
+ * the caller owns, 256-byte aligned, that must be all zero before its first
+ * use (hipMemset or torch.zeros). Every call that returns VOX_OK and whose
+ * stream work completes leaves it all zero again, so it can be reused without
+ * clearing. Returns >= 0, or VOX_EINVAL.
+ */
+int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_points,
+                            const vox_options* options);
+
+/*
+ * Pillar / voxel binning of one cloud (the whole operation described above).
+ *
+ *   points      device, [n_points, 4] float32, row-major, 16-byte aligned
+ *   n_points    N >= 0, N <= 2^31 - 1; N = 0 gives V = 0
+ *   range       host, 6 floats: x_min, y_min, z_min, x_max, y_max, z_max
+ *               (finite, min < max)
+ *   cell        host, 3 floats: vx, vy, vz (finite, > 0)
+ *   grid        host, 3 int32: gx, gy, gz (1 <= g <= 2^24; gz == 1 is pillar mode)
+ *   max_points  K >= 1 (rows per pillar)
+ *   max_voxels  M >= 1 (pillar cap)
+ *   voxels      device, [M, K, 4] float32, 16-byte aligned; rows [0, V) written
+ *   coords      device, [M, 3] int32 (z, y, x); rows [0, V) written
+ *   num_points  device, [M] int32; entries [0, V) written
+ *   num_voxels  device, int32[1]: V, or a VOX_STATUS_* code (< 0)
+ *   workspace   device, vox_workspace_bytes(N, M, K, options) bytes, zero on entry
+ *   stream      HIP stream
+ *
+ * Rows >= V of the outputs are not touched. Asynchronous: read num_voxels
+ * after the stream has completed.
+ */
+int voxelize(const float* points, int64_t n_points, const float range[6], const float cell[3],
+             const int32_t grid[3], int32_t max_points, int32_t max_voxels, float* voxels,
+             int32_t* coords, int32_t* num_points, int32_t* num_voxels, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
+/* voxelize() with options (table size, prefix length, hash); same contract. */
+int voxelize_ex(const float* points, int64_t n_points, const float range[6],
+                const float cell[3], const int32_t grid[3], int32_t max_points,
+                int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                int32_t* num_voxels, void* workspace, size_t workspace_bytes,
+                hipStream_t stream, const vox_options* options);
+
+/*
+ * The same operation for any input, including the case voxelize() reports as
+ * VOX_STATUS_NEEDS_CHUNKED: the table is filled chunk by chunk (each chunk at
+ * most table_slots/2 - (cells already in the table) points, so the load never
+ * exceeds one half) until max_voxels cells are in it or every point is in.
+ * SYNCHRONISES `stream` once per chunk to read the number of cells so far.
+ * Same arguments, workspace size and outputs as voxelize_ex().
+ */
+int voxelize_chunked(const float* points, int64_t n_points, const float range[6],
+                     const float cell[3], const int32_t grid[3], int32_t max_points,
+                     int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                     int32_t* num_voxels, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, const vox_options* options);
+
+/*
+ * The per-point binning step alone ("Binning a point"), for parity tests:
+ * valid[i] = 1 if point i is kept, else 0; key[i] = (cz * gy + cy) * gx + cx
+ * as int64 (cz = 0 in pillar mode), or -1. valid and key are device arrays of
+ * n_points entries. Asynchronous.
+ */
+int vox_bin_points(const float* points, int64_t n_points, const float range[6],
+                   const float cell[3], const int32_t grid[3], int8_t* valid, int64_t* key,
+                   hipStream_t stream);
+
+/*
+ * Stage timing for the benchmark: runs voxelize_ex() `iters` times on
+ * `stream` with a HIP event between consecutive kernels and writes the mean
+ * milliseconds of each stage to stage_ms[0..VOX_NUM_STAGES) (insert, rank,
+ * select, pack) and of the whole call to *total_ms. Synchronises `stream`.
+ */
+#define VOX_NUM_STAGES 4
+int vox_profile_stages(const float* points, int64_t n_points, const float range[6],
+                       const float cell[3], const int32_t grid[3], int32_t max_points,
+                       int32_t max_voxels, float* voxels, int32_t* coords,
+                       int32_t* num_points, int32_t* num_voxels, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, const vox_options* options,
+                       int32_t iters, float* stage_ms, float* total_ms);
+
+/* Name of each stage, for reports ("insert", "rank", "select", "pack"). */
+const char* vox_stage_name(int32_t stage);
+
+/* Human-readable text for a return code or a device status. */
+const char* vox_strerror(int32_t code);
+
+/* The hipError_t of the last HIP failure seen by this thread (0 if none). */
+int32_t vox_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VOXELIZE_H */

@@ -1,0 +1,264 @@
+"""MI355X (gfx950) pillar / voxel binning: a thin ctypes binding over libvoxelize.so.
+
+Every step of the operation runs in the library's HIP kernels; this module
+only checks tensor arguments (dtype, device, contiguity), allocates outputs
+and the workspace with torch, passes raw pointers and the current stream, and
+reads the pillar count back (one synchronisation), as the "Voxelize" page's
+Python entry point does ("The PyTorch side"). There is no CPU fallback: if the
+library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch  # imported first: the library binds to the HIP runtime torch has loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libvoxelize.so")
+
+VOX_OK = 0
+VOX_EINVAL = -1
+VOX_EWORKSPACE = -2
+VOX_EHIP = -4
+VOX_STATUS_NEEDS_CHUNKED = -16
+VOX_STATUS_DEVICE_ERROR = -17
+STAGES = ("insert", "rank", "select", "pack")
+
+
+class VoxError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class Options(ctypes.Structure):
+    """Mirror of ``vox_options`` (0 fields mean defaults)."""
+    _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
+                ("hash", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(
+            f"{LIBRARY_PATH} is missing: build it with `python sparse_spatial_hashing_amd/csrc/build.py`"
+            " (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIBRARY_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    op = ctypes.POINTER(Options)
+    lib.vox_workspace_bytes.argtypes = [i64, i32, i32, op]
+    lib.vox_workspace_bytes.restype = i64
+    common = [vp, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.voxelize.argtypes = common
+    lib.voxelize.restype = ctypes.c_int
+    for name in ("voxelize_ex", "voxelize_chunked"):
+        f = getattr(lib, name)
+        f.argtypes = common + [op]
+        f.restype = ctypes.c_int
+    lib.vox_bin_points.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp]
+    lib.vox_bin_points.restype = ctypes.c_int
+    lib.vox_profile_stages.argtypes = common + [op, i32, vp, vp]
+    lib.vox_profile_stages.restype = ctypes.c_int
+    lib.vox_stage_name.argtypes = [i32]
+    lib.vox_stage_name.restype = ctypes.c_char_p
+    lib.vox_strerror.argtypes = [i32]
+    lib.vox_strerror.restype = ctypes.c_char_p
+    lib.vox_last_hip_error.argtypes = []
+    lib.vox_last_hip_error.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return _lib.vox_strerror(int(code)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != VOX_OK:
+        if rc == VOX_EHIP:
+            raise VoxError(rc, f"{what} (hipError {_lib.vox_last_hip_error()})")
+        raise VoxError(rc, what)
+
+
+def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0):
+    if not (table_slots or prefix_points or hash):
+        return None
+    return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), 0))
+
+
+def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
+    n = _lib.vox_workspace_bytes(int(n_points), int(max_voxels), int(max_points), _options(**opts))
+    if n < 0:
+        raise VoxError(int(n), "vox_workspace_bytes")
+    return int(n)
+
+
+class _Workspaces:
+    """Zeroed workspaces reused per (device, stream). Every completed call
+    returns its workspace to all-zero, so reuse needs no clearing."""
+
+    def __init__(self):
+        self._lock = threading.Lock()
+        self._cache: Dict[Tuple[int, int], torch.Tensor] = {}
+
+    def get(self, device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+        key = (device.index, stream)
+        with self._lock:
+            ws = self._cache.get(key)
+            if ws is None or ws.numel() < nbytes:
+                ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+                self._cache[key] = ws
+            return ws
+
+    def drop(self, device: torch.device, stream: int) -> None:
+        with self._lock:
+            self._cache.pop((device.index, stream), None)
+
+
+_workspaces = _Workspaces()
+
+
+def _host_params(range_, cell, grid):
+    r = (ctypes.c_float * 6)(*[float(v) for v in range_])
+    c = (ctypes.c_float * 3)(*[float(v) for v in cell])
+    g = (ctypes.c_int32 * 3)(*[int(v) for v in grid])
+    return r, c, g
+
+
+def _check_points(points: torch.Tensor) -> None:
+    if not isinstance(points, torch.Tensor):
+        raise TypeError("points must be a torch.Tensor")
+    if points.dtype != torch.float32 or points.dim() != 2 or points.shape[1] != 4:
+        raise ValueError("points must be a [N, 4] float32 tensor")
+    if not points.is_cuda:
+        raise ValueError("points must be on a GPU device")
+    if not points.is_contiguous():
+        raise ValueError("points must be contiguous")
+
+
+@torch.no_grad()
+def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
+             grid: Sequence[int], max_points: int, max_voxels: int, *,
+             table_slots: int = 0, prefix_points: int = 0, hash: int = 0,
+             chunked: bool = False, return_device_outputs: bool = False):
+    """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
+
+    Returns ``(voxels[V, K, 4] f32, coords[V, 3] i32 (z, y, x), num_points[V] i32)``
+    as views of freshly allocated outputs. ``chunked=True`` calls the chunked
+    entry point directly; otherwise it is used only when the single-pass call
+    reports that the cap could not be decided.
+    """
+    _check_points(points)
+    dev = points.device
+    N, K, M = points.shape[0], int(max_points), int(max_voxels)
+    opts = _options(table_slots, prefix_points, hash)
+    nbytes = workspace_bytes(N, M, K, table_slots=table_slots, prefix_points=prefix_points,
+                             hash=hash)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        ws = _workspaces.get(dev, stream, nbytes)
+        voxels = torch.empty((M, K, 4), dtype=torch.float32, device=dev)
+        coords = torch.empty((M, 3), dtype=torch.int32, device=dev)
+        counts = torch.empty((M,), dtype=torch.int32, device=dev)
+        nv = torch.empty((1,), dtype=torch.int32, device=dev)
+        r, c, g = _host_params(range_, cell, grid)
+        args = [ctypes.c_void_p(points.data_ptr()), N, r, c, g, K, M,
+                ctypes.c_void_p(voxels.data_ptr()), ctypes.c_void_p(coords.data_ptr()),
+                ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(nv.data_ptr()),
+                ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                ctypes.c_void_p(stream)]
+        if chunked:
+            _check(_lib.voxelize_chunked(*args, opts), "voxelize_chunked")
+        else:
+            _check(_lib.voxelize_ex(*args, opts), "voxelize")
+        V = int(nv.item())
+        if V == VOX_STATUS_NEEDS_CHUNKED and not chunked:
+            _check(_lib.voxelize_chunked(*args, opts), "voxelize_chunked")
+            V = int(nv.item())
+        if V < 0:
+            _workspaces.drop(dev, stream)
+            raise VoxError(V, "voxelize (device status)")
+    if return_device_outputs:
+        return voxels, coords, counts, nv
+    return voxels[:V], coords[:V], counts[:V]
+
+
+@torch.no_grad()
+def bin_points(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
+               grid: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-point binning alone: (valid bool[N], key int64[N], -1 when rejected)."""
+    _check_points(points)
+    dev = points.device
+    N = points.shape[0]
+    with torch.cuda.device(dev):
+        valid = torch.empty((N,), dtype=torch.int8, device=dev)
+        key = torch.empty((N,), dtype=torch.int64, device=dev)
+        r, c, g = _host_params(range_, cell, grid)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _check(_lib.vox_bin_points(ctypes.c_void_p(points.data_ptr()), N, r, c, g,
+                                   ctypes.c_void_p(valid.data_ptr()),
+                                   ctypes.c_void_p(key.data_ptr()), ctypes.c_void_p(stream)),
+               "vox_bin_points")
+    return valid.bool(), key
+
+
+class Voxelizer:
+    """Pre-allocated outputs and workspace for repeated calls with one shape.
+
+    ``run(points)`` enqueues one call on the current stream and returns the
+    device tensor holding V; nothing is allocated or synchronised per call.
+    Used by the benchmark and by callers that keep their own stream timing.
+    """
+
+    def __init__(self, n_points: int, range_, cell, grid, max_points: int, max_voxels: int,
+                 device="cuda", **opts):
+        self.N, self.K, self.M = int(n_points), int(max_points), int(max_voxels)
+        self.device = torch.device(device)
+        self._opts = _options(**opts)
+        self.nbytes = workspace_bytes(self.N, self.M, self.K, **opts)
+        self.workspace = torch.zeros(self.nbytes, dtype=torch.uint8, device=self.device)
+        self.voxels = torch.empty((self.M, self.K, 4), dtype=torch.float32, device=self.device)
+        self.coords = torch.empty((self.M, 3), dtype=torch.int32, device=self.device)
+        self.num_points = torch.empty((self.M,), dtype=torch.int32, device=self.device)
+        self.num_voxels = torch.zeros((1,), dtype=torch.int32, device=self.device)
+        self._r, self._c, self._g = _host_params(range_, cell, grid)
+
+    def _args(self, points: torch.Tensor, stream: int):
+        _check_points(points)
+        if points.shape[0] != self.N:
+            raise ValueError(f"expected {self.N} points, got {points.shape[0]}")
+        return [ctypes.c_void_p(points.data_ptr()), self.N, self._r, self._c, self._g, self.K,
+                self.M, ctypes.c_void_p(self.voxels.data_ptr()),
+                ctypes.c_void_p(self.coords.data_ptr()),
+                ctypes.c_void_p(self.num_points.data_ptr()),
+                ctypes.c_void_p(self.num_voxels.data_ptr()),
+                ctypes.c_void_p(self.workspace.data_ptr()), ctypes.c_size_t(self.nbytes),
+                ctypes.c_void_p(stream)]
+
+    def run(self, points: torch.Tensor) -> torch.Tensor:
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _check(_lib.voxelize_ex(*self._args(points, stream), self._opts), "voxelize")
+        return self.num_voxels
+
+    def profile(self, points: torch.Tensor, iters: int) -> Tuple[Dict[str, float], float]:
+        """Mean milliseconds per stage and per call, from HIP events on the call's stream."""
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        stage = (ctypes.c_float * len(STAGES))()
+        total = ctypes.c_float()
+        _check(_lib.vox_profile_stages(*self._args(points, stream), self._opts, int(iters),
+                                       stage, ctypes.byref(total)), "vox_profile_stages")
+        return {STAGES[k]: float(stage[k]) for k in range(len(STAGES))}, float(total.value)
+
+    def outputs(self):
+        V = int(self.num_voxels.item())
+        if V < 0:
+            raise VoxError(V, "voxelize (device status)")
+        return self.voxels[:V], self.coords[:V], self.num_points[:V]

@@ -1,0 +1,891 @@
+// Pillar / voxel binning for MI355X (gfx950): HIP kernels and the C ABI.
+//
+// The operation is the one of the "Voxelize" page
+// (ethan-howes.github.io/projects/voxelize); the contract (deterministic
+// order, cap, truncation) is stated in include/voxelize.h. The page's own
+// kernel ("Claiming a pillar and packing points", "Compaction") writes each
+// pillar at its hash slot in arrival order and compacts the table with a
+// copy_if; this design instead makes the result a pure function of the input:
+//
+//   insert  points [0, P): bin, find-or-claim the cell in a 64-bit-keyed
+//           linear-probe table (CAS on an empty slot), record the lowest
+//           point index per cell (atomicMax of ~index), remember each point's
+//           slot. P = min(N, S/2) keeps the load at or below one half, so no
+//           probe sequence can run away (the page sizes its table 8x the
+//           pillar budget for the same reason: "A fixed table").
+//   rank    single-pass scan (decoupled look-back) over points [0, P): point
+//           i is a pillar's first occurrence iff the slot's lowest index is
+//           i; its rank among first occurrences is the pillar id. The first
+//           max_voxels ids are kept (written back into the slot).
+//   select  every point of a kept pillar (prefix points through their slot,
+//           the rest by a lookup-only probe) enters its pillar's row of K
+//           lowest indices with an ordered atomicMax cascade; the result is
+//           independent of arrival order.
+//   pack    per kept pillar: gather the selected rows (bit copies, 16-byte
+//           loads), zero padding, coordinates and counts; then return every
+//           workspace word this call touched to zero.
+//
+// No fast-math: binning must be IEEE fp32 (correctly rounded divide, no FMA
+// contraction, denormals kept) to agree bit for bit with any other fp32
+// implementation of "Binning a point".
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "voxelize.h"
+
+namespace {
+
+constexpr int kBlock = 256;                 // 4 wavefronts of 64 lanes
+constexpr int kWave = 64;
+constexpr int kRankTile = 1024;             // points per look-back tile
+constexpr int kRankIters = kRankTile / kBlock;
+constexpr unsigned kSpinLimit = 1u << 24;   // look-back wait bound (never reached in practice)
+constexpr int kPackMaxBlocks = 8192;
+
+// One table slot. key1 = cell key + 1 (0 = empty). first = ~(lowest point
+// index of the cell) while inserting (atomicMax keeps the lowest index), then
+// pid + 1 once the cell is ranked and kept (top bit clear, so the two never
+// collide: indices are < 2^31).
+struct alignas(16) Slot {
+    unsigned long long key1;
+    unsigned int first;
+    unsigned int pad;
+};
+
+// First 256 bytes of the workspace.
+struct alignas(256) Header {
+    unsigned int claims;       // cells inserted (wave-aggregated); read by the chunked path
+    unsigned int rank_ticket;  // look-back tile tickets
+    int status;                // V, or a VOX_STATUS_* code; written by the last rank tile
+    int distinct;              // cells in the table (first occurrences in [0, P))
+    unsigned int error;        // nonzero: an internal bound was exceeded
+    unsigned int pack_done;    // pack blocks finished
+    unsigned int pad[58];
+};
+static_assert(sizeof(Header) == 256, "header is 256 bytes");
+
+struct Grid {
+    float x_min, y_min, z_min, z_max;
+    float vx, vy, vz;
+    int gx, gy, gz;
+};
+
+// ---------------------------------------------------------------- binning --
+
+// "Binning a point": NaN/Inf check on x, y, z; z-slab z_min <= z < z_max;
+// cell = floorf((v - v_min) / cell) tested in float against [0, g) before any
+// conversion. Returns the flattened key (cz * gy + cy) * gx + cx, or -1.
+__device__ __forceinline__ long long bin_key(float4 p, const Grid& g) {
+    // bitwise & on ints: every test is evaluated, no branches
+    int ok = (int)isfinite(p.x) & (int)isfinite(p.y) & (int)isfinite(p.z);
+    ok &= (int)(p.z >= g.z_min) & (int)(p.z < g.z_max);
+    const float fx = floorf((p.x - g.x_min) / g.vx);
+    const float fy = floorf((p.y - g.y_min) / g.vy);
+    ok &= (int)(fx >= 0.0f) & (int)(fx < (float)g.gx) & (int)(fy >= 0.0f) & (int)(fy < (float)g.gy);
+    long long cz = 0;
+    if (g.gz > 1) {
+        const float fz = floorf((p.z - g.z_min) / g.vz);
+        ok &= (int)(fz >= 0.0f) & (int)(fz < (float)g.gz);
+        cz = ok ? (long long)fz : 0;
+    }
+    if (!ok) return -1;
+    return (cz * g.gy + (long long)fy) * g.gx + (long long)fx;
+}
+
+// ------------------------------------------------------------------ table --
+
+__device__ __forceinline__ unsigned long long mix64(unsigned long long k) {
+    // 64-bit finaliser (xor-shift / multiply), spreads neighbouring cells
+    k ^= k >> 33;
+    k *= 0xff51afd7ed558ccdull;
+    k ^= k >> 33;
+    k *= 0xc4ceb9fe1a85ec53ull;
+    k ^= k >> 33;
+    return k;
+}
+
+__device__ __forceinline__ unsigned home_slot(long long key, unsigned S, int hash) {
+    if (hash == 1) return (unsigned)((unsigned long long)key % S);
+    // multiply-high range reduction: no 64-bit modulo
+    return (unsigned)__umul64hi(mix64((unsigned long long)key), (unsigned long long)S);
+}
+
+// Lookup only: slot holding key1, or -1. The table is not modified while this
+// runs (select), so plain loads see final keys.
+__device__ __forceinline__ int find_slot(const Slot* __restrict__ table, unsigned S, int hash,
+                                         long long key, unsigned* err) {
+    const unsigned long long k1 = (unsigned long long)key + 1ull;
+    unsigned s = home_slot(key, S, hash);
+    for (unsigned probe = 0; probe < S; ++probe) {
+        const unsigned long long cur = table[s].key1;
+        if (cur == k1) return (int)s;
+        if (cur == 0ull) return -1;
+        s = (s + 1u == S) ? 0u : s + 1u;
+    }
+    atomicOr(err, 1u);
+    return -1;
+}
+
+// ----------------------------------------------------------------- insert --
+
+__global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pts,
+                                                   long long begin, long long end, Grid g,
+                                                   Slot* __restrict__ table, unsigned S,
+                                                   int hash, int* __restrict__ slot_of,
+                                                   Header* __restrict__ hdr) {
+    const long long i = begin + (long long)blockIdx.x * kBlock + threadIdx.x;
+    bool claimed = false;
+    if (i < end) {
+        int out = -1;
+        const long long key = bin_key(pts[i], g);
+        if (key >= 0) {
+            const unsigned long long k1 = (unsigned long long)key + 1ull;
+            unsigned s = home_slot(key, S, hash);
+            unsigned probe = 0;
+            for (;;) {
+                // A plain read can only be stale as 0 (keys never change once
+                // set within a call); the CAS then returns the real key.
+                unsigned long long cur = table[s].key1;
+                if (cur == 0ull) {
+                    cur = atomicCAS(&table[s].key1, 0ull, k1);
+                    if (cur == 0ull) {
+                        claimed = true;
+                        break;
+                    }
+                }
+                if (cur == k1) break;
+                s = (s + 1u == S) ? 0u : s + 1u;
+                if (++probe >= S) {
+                    atomicOr(&hdr->error, 1u);
+                    s = 0xffffffffu;
+                    break;
+                }
+            }
+            if (s != 0xffffffffu) {
+                const unsigned enc = ~(unsigned)i;
+                // first only grows (atomicMax), so a stale read is never too
+                // large: skipping the atomic when it already holds a lower
+                // index is safe.
+                if (table[s].first < enc) atomicMax(&table[s].first, enc);
+                out = (int)s;
+            }
+        }
+        slot_of[i] = out;
+    }
+    const unsigned long long b = __ballot(claimed);
+    if (__lane_id() == 0 && b != 0ull) atomicAdd(&hdr->claims, (unsigned)__popcll(b));
+}
+
+// ------------------------------------------------------------------- rank --
+
+constexpr unsigned long long kFlagAgg = 1ull << 62;
+constexpr unsigned long long kFlagIncl = 2ull << 62;
+constexpr unsigned long long kValueMask = (1ull << 62) - 1ull;
+
+__global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M,
+                                                 Slot* __restrict__ table,
+                                                 const int* __restrict__ slot_of,
+                                                 unsigned long long* __restrict__ tile_state,
+                                                 long long ntiles, int* __restrict__ occ_slot,
+                                                 long long* __restrict__ kept_key,
+                                                 Header* __restrict__ hdr) {
+    __shared__ unsigned tile_sh;
+    __shared__ unsigned wave_cnt[kRankIters][kBlock / kWave];
+    __shared__ unsigned long long excl_sh;
+
+    const int t = threadIdx.x;
+    const int w = t / kWave;
+    const int lane = __lane_id();
+    if (t == 0) tile_sh = atomicAdd(&hdr->rank_ticket, 1u);  // tiles in dispatch order
+    __syncthreads();
+    const long long tile = tile_sh;
+    const long long base = tile * kRankTile;
+
+    bool is_first[kRankIters];
+    int slot[kRankIters];
+    unsigned long long key1[kRankIters];
+    unsigned before[kRankIters];  // first occurrences before this lane in its wave
+#pragma unroll
+    for (int k = 0; k < kRankIters; ++k) {
+        const long long i = base + (long long)k * kBlock + t;
+        is_first[k] = false;
+        slot[k] = -1;
+        key1[k] = 0;
+        if (i < P) {
+            const int s = slot_of[i];
+            if (s >= 0) {
+                const Slot sl = table[s];
+                slot[k] = s;
+                key1[k] = sl.key1;
+                is_first[k] = (sl.first == ~(unsigned)i);
+            }
+        }
+        const unsigned long long b = __ballot(is_first[k]);
+        before[k] = (unsigned)__popcll(b & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_cnt[k][w] = (unsigned)__popcll(b);
+    }
+    __syncthreads();
+
+    // Tile-local exclusive offset of this lane's points (index order is
+    // k-major, then wave, then lane).
+    unsigned local[kRankIters];
+    unsigned run = 0;
+#pragma unroll
+    for (int k = 0; k < kRankIters; ++k) {
+        unsigned off = run;
+        for (int ww = 0; ww < kBlock / kWave; ++ww) {
+            if (ww < w) off += wave_cnt[k][ww];
+            run += wave_cnt[k][ww];
+        }
+        local[k] = off + before[k];
+    }
+    const unsigned aggregate = run;
+
+    if (t == 0) {
+        unsigned long long excl = 0;
+        if (tile == 0) {
+            __hip_atomic_store(&tile_state[0], kFlagIncl | (unsigned long long)aggregate,
+                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            __hip_atomic_store(&tile_state[tile], kFlagAgg | (unsigned long long)aggregate,
+                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            long long j = tile - 1;
+            unsigned spins = 0;
+            for (;;) {
+                const unsigned long long v = __hip_atomic_load(&tile_state[j], __ATOMIC_ACQUIRE,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+                if ((v & ~kValueMask) == 0ull) {
+                    // predecessor has not published yet; it holds an earlier
+                    // ticket, so it is resident and will
+                    if (++spins > kSpinLimit) {
+                        atomicOr(&hdr->error, 2u);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                excl += v & kValueMask;
+                if ((v & ~kValueMask) == kFlagIncl || j == 0) break;
+                --j;
+            }
+            __hip_atomic_store(&tile_state[tile], kFlagIncl | (excl + aggregate),
+                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        excl_sh = excl;
+        if (tile == ntiles - 1) {
+            // the last tile knows the number of distinct cells in [0, P)
+            const long long distinct = (long long)excl + aggregate;
+            int status = (int)(distinct < M ? distinct : M);
+            if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
+            hdr->distinct = (int)distinct;
+            hdr->status = status;
+        }
+    }
+    __syncthreads();
+    const unsigned long long excl = excl_sh;
+
+#pragma unroll
+    for (int k = 0; k < kRankIters; ++k) {
+        if (!is_first[k]) continue;
+        const long long r = (long long)excl + local[k];
+        if (r >= P) {  // cannot happen: there are at most P first occurrences
+            atomicOr(&hdr->error, 2u);
+            continue;
+        }
+        occ_slot[r] = slot[k];
+        if (r < M) {
+            table[slot[k]].first = (unsigned)r + 1u;  // kept: pillar id + 1
+            kept_key[r] = (long long)(key1[k] - 1ull);
+        }
+    }
+}
+
+// ----------------------------------------------------------------- select --
+
+// Insert encoded index v (= ~i, larger = lower index) into row[0..K) which
+// holds the K largest encoded values seen, in descending order (0 = empty).
+// Values at a position only grow, so a stale read is never larger than the
+// current value: skipping positions whose read value exceeds v, and dropping
+// v when the last position already exceeds it, are both exact.
+template <int KC>
+__device__ __forceinline__ void cascade(unsigned* __restrict__ row, int K, unsigned v) {
+    int j = 0;
+    if constexpr (KC > 0 && KC % 4 == 0) {
+        unsigned r[KC];
+#pragma unroll
+        for (int q = 0; q < KC / 4; ++q) {
+            const uint4 x = reinterpret_cast<const uint4*>(row)[q];
+            r[4 * q + 0] = x.x;
+            r[4 * q + 1] = x.y;
+            r[4 * q + 2] = x.z;
+            r[4 * q + 3] = x.w;
+        }
+        if (r[KC - 1] > v) return;
+        j = KC;
+#pragma unroll
+        for (int q = KC - 1; q >= 0; --q)
+            if (r[q] < v) j = q;
+        K = KC;
+    } else {
+        if (row[K - 1] > v) return;
+        while (j < K && row[j] > v) ++j;
+    }
+    for (; j < K; ++j) {
+        const unsigned old = atomicMax(&row[j], v);
+        if (old == 0u) return;   // took an empty position
+        if (old < v) v = old;    // displaced a higher index: carry it on
+    }
+}
+
+template <int KC>
+__global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pts, long long N,
+                                                   long long P, Grid g,
+                                                   const Slot* __restrict__ table, unsigned S,
+                                                   int hash, int* __restrict__ slot_of,
+                                                   unsigned* __restrict__ sel, int K,
+                                                   Header* __restrict__ hdr) {
+    const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= N) return;
+    const int status = hdr->status;
+    int s = -1;
+    if (i < P) {
+        s = slot_of[i];
+        slot_of[i] = 0;  // last reader: return the word to zero for the next call
+    }
+    if (status <= 0 || hdr->error != 0u) return;  // nothing kept, or cap undecided
+    if (i >= P) {
+        const long long key = bin_key(pts[i], g);
+        s = key < 0 ? -1 : find_slot(table, S, hash, key, &hdr->error);
+    }
+    if (s < 0) return;
+    const unsigned tag = table[s].first;
+    if (tag == 0u || (tag & 0x80000000u)) return;  // cell not among the kept pillars
+    const long long pid = (long long)(tag - 1u);
+    if (pid >= status) {  // cannot happen on a clean workspace
+        atomicOr(&hdr->error, 4u);
+        return;
+    }
+    cascade<KC>(sel + pid * K, K, ~(unsigned)i);
+}
+
+// ------------------------------------------------------------------- pack --
+
+__global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts, long long N,
+                                                 unsigned* __restrict__ sel, int K, int M,
+                                                 long long* __restrict__ kept_key, int gx,
+                                                 int gy, float4* __restrict__ voxels,
+                                                 int* __restrict__ coords,
+                                                 int* __restrict__ num_points,
+                                                 int* __restrict__ num_voxels,
+                                                 int* __restrict__ occ_slot,
+                                                 Slot* __restrict__ table, unsigned S,
+                                                 unsigned long long* __restrict__ tile_state,
+                                                 long long ntiles, Header* __restrict__ hdr) {
+    const int status = hdr->status;
+    const unsigned err = hdr->error;
+    const long long distinct = hdr->distinct;
+    const long long V = (status > 0 && err == 0u) ? status : 0;
+    const int lane = __lane_id();
+    const long long nthreads = (long long)gridDim.x * kBlock;
+    const long long gtid = (long long)blockIdx.x * kBlock + threadIdx.x;
+    const long long nwaves = nthreads / kWave;
+    const long long gwave = gtid / kWave;
+
+    // 1) pillars. A wave owns whole pillars, so it can count a row with a
+    //    ballot and clear it without racing another wave.
+    if (K <= kWave) {
+        const int per = kWave / K;        // pillars per wave pass
+        const int sub = lane / K;         // which of them this lane serves
+        const int j = lane - sub * K;     // row inside the pillar
+        const bool used = sub < per;
+        for (long long p0 = gwave * per; p0 < V; p0 += nwaves * per) {
+            const long long p = p0 + sub;
+            const bool live = used && p < V;
+            unsigned v = 0u;
+            if (live) v = sel[p * K + j];
+            const unsigned long long b = __ballot(v != 0u);
+            if (live) {
+                float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (v != 0u) {
+                    const unsigned src = ~v;
+                    if (src < N) row = pts[src];
+                    else atomicOr(&hdr->error, 8u);
+                    sel[p * K + j] = 0u;
+                }
+                voxels[p * K + j] = row;
+                if (j == 0) {
+                    const unsigned long long mine = (b >> (sub * K)) &
+                        (K == 64 ? ~0ull : ((1ull << K) - 1ull));
+                    num_points[p] = __popcll(mine);
+                    const long long key = kept_key[p];
+                    kept_key[p] = 0;
+                    const long long plane = (long long)gx * gy;
+                    coords[3 * p + 0] = (int)(key / plane);
+                    coords[3 * p + 1] = (int)((key % plane) / gx);
+                    coords[3 * p + 2] = (int)(key % gx);
+                }
+            }
+        }
+    } else {
+        for (long long p = gwave; p < V; p += nwaves) {
+            int count = 0;
+            for (int j0 = 0; j0 < K; j0 += kWave) {
+                const int j = j0 + lane;
+                unsigned v = 0u;
+                if (j < K) v = sel[p * K + j];
+                count += __popcll(__ballot(v != 0u));
+                if (j < K) {
+                    float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (v != 0u) {
+                        const unsigned src = ~v;
+                        if (src < N) row = pts[src];
+                        else atomicOr(&hdr->error, 8u);
+                        sel[p * K + j] = 0u;
+                    }
+                    voxels[p * K + j] = row;
+                }
+            }
+            if (lane == 0) {
+                num_points[p] = count;
+                const long long key = kept_key[p];
+                kept_key[p] = 0;
+                const long long plane = (long long)gx * gy;
+                coords[3 * p + 0] = (int)(key / plane);
+                coords[3 * p + 1] = (int)((key % plane) / gx);
+                coords[3 * p + 2] = (int)(key % gx);
+            }
+        }
+    }
+
+    // 2) clear every table slot this call claimed, the slot list itself, the
+    //    kept keys the pillar pass did not consume, and the look-back tiles
+    const Slot zero = {0ull, 0u, 0u};
+    const long long kept_written = distinct < M ? distinct : M;
+    for (long long r = gtid; r < distinct; r += nthreads) {
+        const int s = occ_slot[r];
+        occ_slot[r] = 0;
+        if (s >= 0 && (unsigned)s < S) table[s] = zero;
+        else atomicOr(&hdr->error, 16u);
+        if (r >= V && r < kept_written) kept_key[r] = 0;
+    }
+    for (long long r = gtid; r < ntiles; r += nthreads) tile_state[r] = 0ull;
+
+    // 3) the last block to finish publishes the result and clears the header
+    __shared__ bool last_sh;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) last_sh = (atomicAdd(&hdr->pack_done, 1u) == gridDim.x - 1u);
+    __syncthreads();
+    if (last_sh && threadIdx.x == 0) {
+        __threadfence();
+        int out = status;
+        if (err != 0u || hdr->error != 0u) out = VOX_STATUS_DEVICE_ERROR;
+        num_voxels[0] = out;
+        hdr->claims = 0u;
+        hdr->rank_ticket = 0u;
+        hdr->status = 0;
+        hdr->distinct = 0;
+        hdr->error = 0u;
+        hdr->pack_done = 0u;
+    }
+}
+
+// -------------------------------------------------------------- bin only --
+
+__global__ __launch_bounds__(kBlock) void k_bin(const float4* __restrict__ pts, long long N,
+                                                Grid g, int8_t* __restrict__ valid,
+                                                long long* __restrict__ key) {
+    const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= N) return;
+    const long long k = bin_key(pts[i], g);
+    valid[i] = k >= 0 ? 1 : 0;
+    key[i] = k;
+}
+
+// =================================================================== host ==
+
+thread_local int32_t g_last_hip_error = 0;
+
+inline int hip_fail(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return VOX_EHIP;
+}
+
+inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+    long long N, P, S;
+    int K, M, hash;
+    long long ntiles;
+    // byte offsets into the workspace
+    size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_sel, bytes;
+};
+
+inline bool finite_f(float v) { return isfinite(v); }
+
+int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
+    if (N < 0 || N > 2147483647ll) return VOX_EINVAL;
+    if (M < 1 || K < 1) return VOX_EINVAL;
+    if ((long long)M > (1ll << 27)) return VOX_EINVAL;
+    if ((long long)M * (long long)K > (1ll << 40)) return VOX_EINVAL;
+    long long S = 8ll * M;
+    if (S < 64) S = 64;
+    int hash = 0;
+    long long P = 0;
+    if (opt) {
+        if (opt->table_slots < 0 || opt->prefix_points < 0) return VOX_EINVAL;
+        if (opt->table_slots > 0) S = opt->table_slots;
+        if (opt->hash < 0 || opt->hash > 1) return VOX_EINVAL;
+        hash = opt->hash;
+        P = opt->prefix_points;
+    }
+    // S >= 2M: while fewer than M cells are in the table, a chunk of
+    // S/2 - cells >= 1 points always fits at load <= 1/2
+    if (S < 2ll * M || S > 2147483647ll) return VOX_EINVAL;
+    if (P == 0) P = S / 2;
+    if (P > S / 2) P = S / 2;
+    if (P > N) P = N;
+    pl->N = N;
+    pl->P = P;
+    pl->S = S;
+    pl->K = K;
+    pl->M = M;
+    pl->hash = hash;
+    // arrays indexed by point go to N: the chunked path can insert every point
+    const long long Nw = N > 0 ? N : 1;
+    pl->ntiles = cdiv(Nw, kRankTile);
+    size_t off = sizeof(Header);
+    pl->off_table = off;
+    off = align256(off + (size_t)S * sizeof(Slot));
+    pl->off_slot = off;
+    off = align256(off + (size_t)Nw * sizeof(int));
+    pl->off_tiles = off;
+    off = align256(off + (size_t)pl->ntiles * sizeof(unsigned long long));
+    pl->off_occ = off;
+    off = align256(off + (size_t)Nw * sizeof(int));
+    pl->off_kept = off;
+    off = align256(off + (size_t)M * sizeof(long long));
+    pl->off_sel = off;
+    off = align256(off + (size_t)M * (size_t)K * sizeof(unsigned));
+    pl->bytes = off;
+    return VOX_OK;
+}
+
+int check_grid(const float range[6], const float cell[3], const int32_t grid[3], Grid* g) {
+    if (!range || !cell || !grid) return VOX_EINVAL;
+    for (int a = 0; a < 3; ++a) {
+        if (!finite_f(range[a]) || !finite_f(range[a + 3]) || !(range[a] < range[a + 3]))
+            return VOX_EINVAL;
+        if (!finite_f(cell[a]) || !(cell[a] > 0.0f)) return VOX_EINVAL;
+        if (grid[a] < 1 || grid[a] > (1 << 24)) return VOX_EINVAL;
+    }
+    g->x_min = range[0];
+    g->y_min = range[1];
+    g->z_min = range[2];
+    g->z_max = range[5];
+    g->vx = cell[0];
+    g->vy = cell[1];
+    g->vz = cell[2];
+    g->gx = grid[0];
+    g->gy = grid[1];
+    g->gz = grid[2];
+    return VOX_OK;
+}
+
+int check_args(const float* points, long long N, const float range[6], const float cell[3],
+               const int32_t grid[3], float* voxels, int32_t* coords, int32_t* num_points,
+               int32_t* num_voxels, void* ws, Grid* g) {
+    if (!voxels || !coords || !num_points || !num_voxels || !ws) return VOX_EINVAL;
+    if (N > 0 && !points) return VOX_EINVAL;
+    if (points && ((uintptr_t)points & 15u)) return VOX_EINVAL;
+    if (((uintptr_t)voxels & 15u) || ((uintptr_t)coords & 3u) || ((uintptr_t)num_points & 3u) ||
+        ((uintptr_t)num_voxels & 3u))
+        return VOX_EINVAL;
+    return check_grid(range, cell, grid, g);
+}
+
+struct Buffers {
+    Header* hdr;
+    Slot* table;
+    int* slot_of;
+    unsigned long long* tiles;
+    int* occ;
+    long long* kept;
+    unsigned* sel;
+};
+
+Buffers carve(void* ws, const Plan& pl) {
+    char* b = static_cast<char*>(ws);
+    Buffers x;
+    x.hdr = reinterpret_cast<Header*>(b);
+    x.table = reinterpret_cast<Slot*>(b + pl.off_table);
+    x.slot_of = reinterpret_cast<int*>(b + pl.off_slot);
+    x.tiles = reinterpret_cast<unsigned long long*>(b + pl.off_tiles);
+    x.occ = reinterpret_cast<int*>(b + pl.off_occ);
+    x.kept = reinterpret_cast<long long*>(b + pl.off_kept);
+    x.sel = reinterpret_cast<unsigned*>(b + pl.off_sel);
+    return x;
+}
+
+int launch_insert(const float* points, long long begin, long long end, const Grid& g,
+                  const Plan& pl, const Buffers& bf, hipStream_t st) {
+    const long long n = end - begin;
+    const unsigned blocks = (unsigned)(n > 0 ? cdiv(n, kBlock) : 1);
+    hipLaunchKernelGGL(k_insert, dim3(blocks), dim3(kBlock), 0, st,
+                       reinterpret_cast<const float4*>(points), begin, end, g, bf.table,
+                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : hip_fail(e);
+}
+
+int launch_rank(long long P, const Plan& pl, const Buffers& bf, hipStream_t st) {
+    const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
+    hipLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, P, pl.N, pl.M,
+                       bf.table, bf.slot_of, bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : hip_fail(e);
+}
+
+int launch_select(const float* points, long long P, const Grid& g, const Plan& pl,
+                  const Buffers& bf, hipStream_t st) {
+    const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
+    const float4* p4 = reinterpret_cast<const float4*>(points);
+    if (pl.K == 32) {
+        hipLaunchKernelGGL(k_select<32>, dim3(blocks), dim3(kBlock), 0, st, p4, pl.N, P, g,
+                           bf.table, (unsigned)pl.S, pl.hash, bf.slot_of, bf.sel, pl.K, bf.hdr);
+    } else {
+        hipLaunchKernelGGL(k_select<0>, dim3(blocks), dim3(kBlock), 0, st, p4, pl.N, P, g,
+                           bf.table, (unsigned)pl.S, pl.hash, bf.slot_of, bf.sel, pl.K, bf.hdr);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : hip_fail(e);
+}
+
+int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
+                const Buffers& bf, float* voxels, int32_t* coords, int32_t* num_points,
+                int32_t* num_voxels, hipStream_t st) {
+    const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
+    long long work = (long long)pl.M * pl.K;
+    if (P > work) work = P;
+    long long blocks = cdiv(work, kBlock);
+    if (blocks < 1) blocks = 1;
+    if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                       reinterpret_cast<const float4*>(points), pl.N, bf.sel, pl.K, pl.M,
+                       bf.kept, g.gx, g.gy, reinterpret_cast<float4*>(voxels), coords,
+                       num_points, num_voxels, bf.occ, bf.table, (unsigned)pl.S, bf.tiles,
+                       ntiles, bf.hdr);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : hip_fail(e);
+}
+
+int prepare(const float* points, int64_t n_points, const float range[6], const float cell[3],
+            const int32_t grid[3], int32_t max_points, int32_t max_voxels, float* voxels,
+            int32_t* coords, int32_t* num_points, int32_t* num_voxels, void* workspace,
+            size_t workspace_bytes, const vox_options* options, Grid* g, Plan* pl) {
+    int rc = check_args(points, n_points, range, cell, grid, voxels, coords, num_points,
+                        num_voxels, workspace, g);
+    if (rc != VOX_OK) return rc;
+    rc = make_plan(n_points, max_voxels, max_points, options, pl);
+    if (rc != VOX_OK) return rc;
+    if (((uintptr_t)workspace & 255u) || workspace_bytes < pl->bytes) return VOX_EWORKSPACE;
+    return VOX_OK;
+}
+
+// The four stages of one call; events (if given) are recorded between them.
+int run_pipeline(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
+                 float* voxels, int32_t* coords, int32_t* num_points, int32_t* num_voxels,
+                 hipStream_t st, hipEvent_t* ev) {
+    int rc;
+    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hip_fail(hipGetLastError());
+    if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st)) != VOX_OK) return rc;
+    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hip_fail(hipGetLastError());
+    if ((rc = launch_rank(pl.P, pl, bf, st)) != VOX_OK) return rc;
+    if (ev && hipEventRecord(ev[2], st) != hipSuccess) return hip_fail(hipGetLastError());
+    if ((rc = launch_select(points, pl.P, g, pl, bf, st)) != VOX_OK) return rc;
+    if (ev && hipEventRecord(ev[3], st) != hipSuccess) return hip_fail(hipGetLastError());
+    if ((rc = launch_pack(points, pl.P, g, pl, bf, voxels, coords, num_points, num_voxels, st)) !=
+        VOX_OK)
+        return rc;
+    if (ev && hipEventRecord(ev[4], st) != hipSuccess) return hip_fail(hipGetLastError());
+    return VOX_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI ==
+
+extern "C" {
+
+int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_points,
+                            const vox_options* options) {
+    Plan pl;
+    const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
+    if (rc != VOX_OK) return rc;
+    return (int64_t)pl.bytes;
+}
+
+int voxelize_ex(const float* points, int64_t n_points, const float range[6],
+                const float cell[3], const int32_t grid[3], int32_t max_points,
+                int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                int32_t* num_voxels, void* workspace, size_t workspace_bytes,
+                hipStream_t stream, const vox_options* options) {
+    Grid g;
+    Plan pl;
+    const int rc = prepare(points, n_points, range, cell, grid, max_points, max_voxels, voxels,
+                           coords, num_points, num_voxels, workspace, workspace_bytes, options,
+                           &g, &pl);
+    if (rc != VOX_OK) return rc;
+    const Buffers bf = carve(workspace, pl);
+    return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, stream,
+                        nullptr);
+}
+
+int voxelize(const float* points, int64_t n_points, const float range[6], const float cell[3],
+             const int32_t grid[3], int32_t max_points, int32_t max_voxels, float* voxels,
+             int32_t* coords, int32_t* num_points, int32_t* num_voxels, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+    return voxelize_ex(points, n_points, range, cell, grid, max_points, max_voxels, voxels,
+                       coords, num_points, num_voxels, workspace, workspace_bytes, stream,
+                       nullptr);
+}
+
+int voxelize_chunked(const float* points, int64_t n_points, const float range[6],
+                     const float cell[3], const int32_t grid[3], int32_t max_points,
+                     int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                     int32_t* num_voxels, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, const vox_options* options) {
+    Grid g;
+    Plan pl;
+    int rc = prepare(points, n_points, range, cell, grid, max_points, max_voxels, voxels,
+                     coords, num_points, num_voxels, workspace, workspace_bytes, options, &g,
+                     &pl);
+    if (rc != VOX_OK) return rc;
+    const Buffers bf = carve(workspace, pl);
+    // Fill the table chunk by chunk while fewer than M cells are in it. Before
+    // each chunk `have` < M cells are present, so a chunk of S/2 - have points
+    // keeps the load at or below one half.
+    long long done = 0;
+    long long have = 0;
+    const long long half = pl.S / 2;
+    while (done < pl.N && have < pl.M) {
+        long long chunk = half - have;
+        if (chunk > pl.N - done) chunk = pl.N - done;
+        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream)) != VOX_OK)
+            return rc;
+        done += chunk;
+        unsigned claims = 0;
+        hipError_t e = hipMemcpyAsync(&claims, &bf.hdr->claims, sizeof(claims),
+                                      hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+        have = claims;
+    }
+    Plan p2 = pl;
+    p2.P = done;
+    if ((rc = launch_rank(done, p2, bf, stream)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, done, g, p2, bf, stream)) != VOX_OK) return rc;
+    return launch_pack(points, done, g, p2, bf, voxels, coords, num_points, num_voxels, stream);
+}
+
+int vox_bin_points(const float* points, int64_t n_points, const float range[6],
+                   const float cell[3], const int32_t grid[3], int8_t* valid, int64_t* key,
+                   hipStream_t stream) {
+    if (!range || !cell || !grid || n_points < 0 || n_points > 2147483647ll) return VOX_EINVAL;
+    if (n_points > 0 && (!points || !valid || !key)) return VOX_EINVAL;
+    if (points && ((uintptr_t)points & 15u)) return VOX_EINVAL;
+    if (key && ((uintptr_t)key & 7u)) return VOX_EINVAL;
+    Grid g;
+    const int rc = check_grid(range, cell, grid, &g);
+    if (rc != VOX_OK) return rc;
+    if (n_points == 0) return VOX_OK;
+    hipLaunchKernelGGL(k_bin, dim3((unsigned)cdiv(n_points, kBlock)), dim3(kBlock), 0, stream,
+                       reinterpret_cast<const float4*>(points), (long long)n_points, g, valid,
+                       reinterpret_cast<long long*>(key));
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : hip_fail(e);
+}
+
+int vox_profile_stages(const float* points, int64_t n_points, const float range[6],
+                       const float cell[3], const int32_t grid[3], int32_t max_points,
+                       int32_t max_voxels, float* voxels, int32_t* coords,
+                       int32_t* num_points, int32_t* num_voxels, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, const vox_options* options,
+                       int32_t iters, float* stage_ms, float* total_ms) {
+    if (iters < 1 || !stage_ms || !total_ms) return VOX_EINVAL;
+    Grid g;
+    Plan pl;
+    int rc = prepare(points, n_points, range, cell, grid, max_points, max_voxels, voxels,
+                     coords, num_points, num_voxels, workspace, workspace_bytes, options, &g,
+                     &pl);
+    if (rc != VOX_OK) return rc;
+    const Buffers bf = carve(workspace, pl);
+    const int nev = VOX_NUM_STAGES + 1;
+    hipEvent_t* ev = new hipEvent_t[(size_t)iters * nev];
+    int created = 0;
+    for (; created < iters * nev; ++created) {
+        const hipError_t e = hipEventCreate(&ev[created]);
+        if (e != hipSuccess) {
+            rc = hip_fail(e);
+            break;
+        }
+    }
+    for (int it = 0; rc == VOX_OK && it < iters; ++it)
+        rc = run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, stream,
+                          ev + (size_t)it * nev);
+    if (rc == VOX_OK) {
+        const hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) rc = hip_fail(e);
+    }
+    if (rc == VOX_OK) {
+        double acc[VOX_NUM_STAGES] = {0};
+        double tot = 0;
+        for (int it = 0; it < iters && rc == VOX_OK; ++it) {
+            hipEvent_t* e = ev + (size_t)it * nev;
+            for (int s = 0; s < VOX_NUM_STAGES; ++s) {
+                float ms = 0;
+                const hipError_t he = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+                if (he != hipSuccess) {
+                    rc = hip_fail(he);
+                    break;
+                }
+                acc[s] += ms;
+            }
+            float ms = 0;
+            if (hipEventElapsedTime(&ms, e[0], e[VOX_NUM_STAGES]) == hipSuccess) tot += ms;
+        }
+        for (int s = 0; s < VOX_NUM_STAGES; ++s) stage_ms[s] = (float)(acc[s] / iters);
+        *total_ms = (float)(tot / iters);
+    }
+    for (int k = 0; k < created; ++k) (void)hipEventDestroy(ev[k]);
+    delete[] ev;
+    return rc;
+}
+
+const char* vox_stage_name(int32_t stage) {
+    static const char* names[VOX_NUM_STAGES] = {"insert", "rank", "select", "pack"};
+    if (stage < 0 || stage >= VOX_NUM_STAGES) return "unknown";
+    return names[stage];
+}
+
+const char* vox_strerror(int32_t code) {
+    switch (code) {
+        case VOX_OK: return "ok";
+        case VOX_EINVAL: return "invalid argument";
+        case VOX_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+        case VOX_EHIP: return "HIP runtime error (see vox_last_hip_error)";
+        case VOX_STATUS_NEEDS_CHUNKED:
+            return "cap not decidable in one pass: repeat with voxelize_chunked";
+        case VOX_STATUS_DEVICE_ERROR: return "internal device bound exceeded";
+        default: return "unknown error";
+    }
+}
+
+int32_t vox_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

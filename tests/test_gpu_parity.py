@@ -1,0 +1,317 @@
+"""GPU parity: the HIP library against the CPU oracle, bit for bit.
+
+Every comparison is exact (integer and bit-copy work): the three output
+tensors must equal the oracle's bitwise, and per-point binning must equal the
+oracle's (valid, key) pairs. Inputs come from the seeded generators only.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import sparse_spatial_hashing_amd as vox  # noqa: E402
+from workloads import config_names, generate, get_config  # noqa: E402
+
+DEV = torch.device("cuda:0")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_vox(pts, prm, **kw):
+    say(f"  gpu voxelize N={pts.shape[0]} K={prm[3]} M={prm[4]} {kw}")
+    out = vox.voxelize(torch.from_numpy(np.ascontiguousarray(pts)).to(DEV), *prm, **kw)
+    torch.cuda.synchronize()
+    return tuple(t.cpu().numpy() for t in out)
+
+
+def params_of(cfg):
+    p = cfg.params
+    return (p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+
+
+def assert_bitwise(got, want, what=""):
+    gv, gc, gn = got
+    ov, oc, on = want
+    assert gv.shape == ov.shape, (what, gv.shape, ov.shape)
+    assert np.array_equal(gc, oc), f"{what}: coords differ"
+    assert np.array_equal(gn, on), f"{what}: num_points differ"
+    bad = np.flatnonzero(np.any(gv.view(np.uint32) != ov.view(np.uint32), axis=(1, 2)))
+    assert bad.size == 0, f"{what}: voxels differ in {bad.size} pillars, first {bad[:5]}"
+
+
+# ------------------------------------------------------ workspace hygiene ---
+
+def test_workspace_all_zero_after_calls_of_different_shapes():
+    """Each call returns every workspace word it wrote to zero, so one cached
+    workspace can serve calls whose layouts differ (N, M, K)."""
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    seq = [("tiny", None), ("kitti_frame", 40000), ("voxel3d", 60000), ("uniform_25k", None),
+           ("kitti_frame", 9000), ("voxel3d", 3000)]
+    for name, n in seq:
+        cfg = get_config(name)
+        pts, _ = generate(name, n=n) if n else generate(name)
+        say(f"hygiene {name} N={pts.shape[0]}")
+        got = gpu_vox(pts, params_of(cfg))
+        ws = vox._workspaces._cache[(DEV.index, stream)]
+        assert int(torch.count_nonzero(ws).item()) == 0, f"workspace dirty after {name}"
+        assert_bitwise(got, oracle.voxelize_params(pts, cfg.params), name)
+
+
+# ------------------------------------------------------------ K1 binning ----
+
+@pytest.mark.parametrize("name", config_names())
+def test_bin_parity(name):
+    cfg = get_config(name)
+    p = cfg.params
+    pts, _ = generate(name)
+    say(f"bin parity {name} N={pts.shape[0]}")
+    valid, key = vox.bin_points(torch.from_numpy(pts).to(DEV), p.range_, p.cell, p.grid)
+    ov, ok = oracle.bin_points(pts, p.range_, p.cell, p.grid)
+    assert np.array_equal(valid.cpu().numpy(), ov)
+    assert np.array_equal(key.cpu().numpy(), ok)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dense_multisweep", "voxel3d"])
+def test_bin_parity_boundary_sweep(name):
+    """Points at every cell boundary k*v + min and 1-3 floats either side."""
+    p = get_config(name).params
+    r, c, g = p.range_, p.cell, p.grid
+    cols = []
+    for axis, (lo, v, n) in enumerate(((r[0], c[0], g[0]), (r[1], c[1], g[1]),
+                                       (r[2], c[2], max(g[2], 2)))):
+        base = (F32(lo) + np.arange(-1, n + 2) * float(F32(v))).astype(F32)
+        vals = [base]
+        up, dn = base, base
+        for _ in range(3):
+            up = np.nextafter(up, F32(np.inf))
+            dn = np.nextafter(dn, F32(-np.inf))
+            vals += [up, dn]
+        vals = np.concatenate(vals)
+        blk = np.zeros((vals.size, 4), F32)
+        blk[:, 0] = F32((r[0] + r[3]) / 2)
+        blk[:, 1] = F32((r[1] + r[4]) / 2)
+        blk[:, 2] = F32((r[2] + r[5]) / 2)
+        blk[:, axis] = vals
+        cols.append(blk)
+    pts = np.concatenate(cols)
+    say(f"bin sweep {name} N={pts.shape[0]}")
+    valid, key = vox.bin_points(torch.from_numpy(pts).to(DEV), r, c, g)
+    ov, ok = oracle.bin_points(pts, r, c, g)
+    assert np.array_equal(valid.cpu().numpy(), ov)
+    assert np.array_equal(key.cpu().numpy(), ok)
+
+
+# ------------------------------------------------------- end to end ---------
+
+@pytest.mark.parametrize("name", config_names())
+def test_voxelize_parity(name):
+    cfg = get_config(name)
+    pts, _ = generate(name)
+    say(f"voxelize parity {name}")
+    got = gpu_vox(pts, params_of(cfg))
+    assert_bitwise(got, oracle.voxelize_params(pts, cfg.params), name)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("name", ["kitti_frame", "uniform_130k"])
+def test_voxelize_parity_other_seeds(name, seed):
+    cfg = get_config(name)
+    pts, _ = generate(name, seed=seed)
+    say(f"voxelize parity {name} seed={seed}")
+    assert_bitwise(gpu_vox(pts, params_of(cfg)), oracle.voxelize_params(pts, cfg.params), name)
+
+
+def _golden_cases():
+    data = json.load(open(os.path.join(GOLDEN, "hand_cases.json")))
+    out = [(c, data["grid_4x4"]) for c in data["cases"]]
+    out += [(c, data["grid_3d"]) for c in data["cases_3d"]]
+    return out
+
+
+@pytest.mark.parametrize("case,gs", _golden_cases(), ids=lambda x: x.get("name", "grid"))
+def test_hand_cases_on_gpu(case, gs):
+    pts = (np.array([[float(v) for v in r] for r in case["points"]], F32)
+           if case["points"] else np.zeros((0, 4), F32))
+    say(f"hand case {case['name']}")
+    vv, cc, nn = gpu_vox(pts, (gs["range"], gs["cell"], gs["grid"], case["max_points"],
+                               case["max_voxels"]))
+    assert cc.tolist() == case["coords"]
+    assert nn.tolist() == case["num_points"]
+    for p, rows in enumerate(case["rows"]):
+        for j, src in enumerate(rows):
+            want = np.zeros(4, F32) if src is None else pts[src]
+            assert np.array_equal(vv[p, j].view(np.uint32), want.view(np.uint32))
+
+
+def _random_problem(rng):
+    gx, gy = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+    gz = int(rng.choice([1, 1, 2, 5]))
+    vx = float(F32(rng.choice([0.1, 0.16, 0.25, 1.0, 0.3])))
+    vy = float(F32(rng.choice([0.1, 0.16, 0.2, 0.5, 0.7])))
+    vz = float(F32(rng.choice([0.1, 0.5, 1.0])))
+    x0, y0, z0 = (float(F32(v)) for v in (rng.uniform(-5, 5), rng.uniform(-40, 5), -3.0))
+    z1 = z0 + (gz * vz if gz > 1 else 4.0)
+    n = int(rng.choice([1, 7, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 5000, 20000]))
+    hot = rng.integers(0, 4)  # how concentrated the points are
+    spread = [1.0, 0.3, 0.05, 0.01][hot]
+    fx = (rng.random(n) * spread * gx * 1.2 - 0.1 * gx)
+    fy = (rng.random(n) * spread * gy * 1.2 - 0.1 * gy)
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = (x0 + fx * vx).astype(F32)
+    pts[:, 1] = (y0 + fy * vy).astype(F32)
+    pts[:, 2] = (z0 + rng.uniform(-0.1, 1.1, n) * (z1 - z0)).astype(F32)
+    pts[:, 3] = rng.random(n).astype(F32)
+    on_edge = rng.random(n) < 0.1
+    pts[on_edge, 0] = (x0 + np.floor(fx[on_edge]) * vx).astype(F32)
+    nan = rng.random(n) < 0.02
+    pts[nan, int(rng.integers(0, 3))] = np.nan
+    K = int(rng.choice([1, 2, 3, 5, 8, 32, 33, 64, 70]))
+    M = int(rng.choice([1, 2, 10, 100, 1000, 100000]))
+    rr = (x0, y0, z0, x0 + gx * vx, y0 + gy * vy, z1)
+    return pts, (rr, (vx, vy, vz), (gx, gy, gz), K, M)
+
+
+def test_seeded_fuzz_small_problems():
+    rng = np.random.default_rng(2024)
+    for t in range(120):
+        pts, prm = _random_problem(rng)
+        say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]}")
+        assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), f"fuzz {t}")
+
+
+# ------------------------------------------------- invariance / options -----
+
+@pytest.mark.parametrize("name", ["kitti_frame", "voxel3d", "dense_multisweep"])
+def test_result_independent_of_table_and_hash(name):
+    cfg = get_config(name)
+    pts, _ = generate(name)
+    want = oracle.voxelize_params(pts, cfg.params)
+    M = cfg.params.max_voxels
+    for kw in (dict(hash=1), dict(table_slots=12 * M + 7), dict(table_slots=12 * M + 7, hash=1),
+               dict(table_slots=3 * M), dict(table_slots=32 * M)):
+        say(f"invariance {name} {kw}")
+        assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
+
+
+@pytest.mark.parametrize("name", ["kitti_frame", "tiny", "voxel3d"])
+def test_small_prefix_and_chunked_path(name):
+    """A short prefix cannot decide the cap: the library reports it and the
+    chunked entry point gives the same tensors."""
+    cfg = get_config(name)
+    pts, _ = generate(name)
+    want = oracle.voxelize_params(pts, cfg.params)
+    for kw in (dict(prefix_points=4096), dict(prefix_points=1), dict(chunked=True),
+               dict(chunked=True, table_slots=2 * cfg.params.max_voxels)):
+        say(f"prefix/chunked {name} {kw}")
+        assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
+
+
+def test_needs_chunked_status_is_reported_and_workspace_stays_clean():
+    cfg = get_config("kitti_frame")
+    p = cfg.params
+    pts, _ = generate("kitti_frame")
+    say("needs-chunked status")
+    v = vox.Voxelizer(pts.shape[0], p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                      device=DEV, prefix_points=1000)
+    x = torch.from_numpy(pts).to(DEV)
+    nv = v.run(x)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == vox.VOX_STATUS_NEEDS_CHUNKED
+    assert int(torch.count_nonzero(v.workspace).item()) == 0
+
+
+def test_repeated_calls_identical_and_workspace_zero():
+    cfg = get_config("dense_multisweep")
+    p = cfg.params
+    pts, _ = generate("dense_multisweep")
+    say("repeat x10 dense")
+    v = vox.Voxelizer(pts.shape[0], p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                      device=DEV)
+    x = torch.from_numpy(pts).to(DEV)
+    want = oracle.voxelize_params(pts, p)
+    for it in range(10):
+        v.run(x)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(v.workspace).item()) == 0, f"workspace dirty after {it}"
+        got = tuple(t.cpu().numpy() for t in v.outputs())
+        assert_bitwise(got, want, f"repeat {it}")
+
+
+def test_outputs_past_V_untouched():
+    cfg = get_config("tiny")
+    p = cfg.params
+    pts, _ = generate("tiny")
+    say("rows past V untouched")
+    v = vox.Voxelizer(pts.shape[0], p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                      device=DEV)
+    v.voxels.fill_(7.0)
+    v.coords.fill_(-9)
+    v.num_points.fill_(-9)
+    v.run(torch.from_numpy(pts).to(DEV))
+    torch.cuda.synchronize()
+    V = int(v.num_voxels.item())
+    assert 0 < V < p.max_voxels
+    assert bool((v.voxels[V:] == 7.0).all()) and bool((v.coords[V:] == -9).all())
+    assert bool((v.num_points[V:] == -9).all())
+
+
+# ------------------------------------------------------------ edge cases ----
+
+def test_empty_and_all_rejected():
+    prm = ((0, 0, -1, 4, 4, 1), (1, 1, 2), (4, 4, 1), 4, 8)
+    say("empty input")
+    vv, cc, nn = gpu_vox(np.zeros((0, 4), F32), prm)
+    assert vv.shape == (0, 4, 4) and cc.shape == (0, 3) and nn.shape == (0,)
+    bad = np.array([[np.nan, 0, 0, 0], [0, np.inf, 0, 0], [0.5, 0.5, 1.0, 0], [4.0, 0.5, 0, 0],
+                    [-1e-30, 0.5, 0, 0]], F32)
+    say("all rejected")
+    vv, cc, nn = gpu_vox(bad, prm)
+    assert vv.shape[0] == 0
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 31, 32, 33, 64, 65, 100])
+def test_max_points_variants(K):
+    cfg = get_config("kitti_frame")
+    p = cfg.params
+    pts, _ = generate("kitti_frame", n=30000)
+    say(f"K={K}")
+    prm = (p.range_, p.cell, p.grid, K, 3000)
+    assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), f"K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 7, 50000])
+def test_max_voxels_variants(M):
+    cfg = get_config("kitti_frame")
+    p = cfg.params
+    pts, _ = generate("kitti_frame", n=20000)
+    say(f"M={M}")
+    prm = (p.range_, p.cell, p.grid, p.max_points, M)
+    assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), f"M={M}")
+
+
+def test_single_cell_heavy_pillar():
+    """Every point in one cell: one pillar keeps the 32 lowest of 100,000."""
+    rng = np.random.default_rng(5)
+    n = 100000
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = rng.uniform(10.01, 10.15, n).astype(F32)
+    pts[:, 1] = rng.uniform(0.01, 0.15, n).astype(F32)
+    pts[:, 2] = F32(-1.0)
+    pts[:, 3] = np.arange(n, dtype=F32)
+    prm = ((0.0, -39.68, -3.0, 69.12, 39.68, 1.0), (0.16, 0.16, 4.0), (432, 496, 1), 32, 12000)
+    say("single heavy cell")
+    assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), "heavy cell")
