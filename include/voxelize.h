@@ -76,16 +76,19 @@ typedef struct vox_options {
     int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N, S/2);
                                clamped to [1, S/2] */
     int32_t hash;           /* 0 = 64-bit mix + multiply-high reduction, 1 = key mod S */
-    int32_t reserved;
+    int32_t bucket_cap;     /* per-pillar arrival slots before the overflow row; 0 = 16 * K
+                               rounded up to a multiple of 64 (K <= 64); at most 2^20 */
 } vox_options;
 
 /*
  * Workspace size in bytes for a call with n_points points, max_voxels and
  * max_points (and options, NULL for defaults). The workspace is device memory
  * the caller owns, 256-byte aligned, that must be all zero before its first
- * use (hipMemset or torch.zeros). Every call that returns VOX_OK and whose
- * stream work completes leaves it all zero again, so it can be reused without
- * clearing. Returns >= 0, or VOX_EINVAL.
+ * use (hipMemset or torch.zeros). A completed call whose num_voxels is not
+ * VOX_STATUS_DEVICE_ERROR leaves it ready for the next call of any shape:
+ * every byte past the first 256 is zero again, and the first 256 hold only
+ * two result words that the next call overwrites. After a device error the
+ * workspace must be zeroed again. Returns >= 0, or VOX_EINVAL.
  */
 int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_points,
                             const vox_options* options);

@@ -26,6 +26,17 @@ VOX_EHIP = -4
 VOX_STATUS_NEEDS_CHUNKED = -16
 VOX_STATUS_DEVICE_ERROR = -17
 STAGES = ("insert", "rank", "select", "pack")
+HEADER_BYTES = 256          # the workspace's first 256 bytes hold the result words
+
+
+def workspace_is_clean(ws: "torch.Tensor") -> bool:
+    """True when a workspace is ready for reuse: everything past the header is
+    zero and so are the header's counters (only the two result words, bytes
+    8..16, may be nonzero)."""
+    head = ws[:HEADER_BYTES].view(torch.int32)
+    rest_zero = int(torch.count_nonzero(ws[HEADER_BYTES:]).item()) == 0
+    counters = torch.cat([head[0:2], head[4:]])
+    return rest_zero and int(torch.count_nonzero(counters).item()) == 0
 
 
 class VoxError(RuntimeError):
@@ -37,7 +48,7 @@ class VoxError(RuntimeError):
 class Options(ctypes.Structure):
     """Mirror of ``vox_options`` (0 fields mean defaults)."""
     _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
-                ("hash", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -88,10 +99,10 @@ def _check(rc: int, what: str) -> None:
         raise VoxError(rc, what)
 
 
-def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0):
-    if not (table_slots or prefix_points or hash):
+def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0):
+    if not (table_slots or prefix_points or hash or bucket_cap):
         return None
-    return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), 0))
+    return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), int(bucket_cap)))
 
 
 def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
@@ -103,7 +114,8 @@ def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> 
 
 class _Workspaces:
     """Zeroed workspaces reused per (device, stream). Every completed call
-    returns its workspace to all-zero, so reuse needs no clearing."""
+    leaves its workspace ready for the next call of any shape, so reuse needs
+    no clearing; a workspace that saw a device error is dropped."""
 
     def __init__(self):
         self._lock = threading.Lock()
@@ -147,7 +159,7 @@ def _check_points(points: torch.Tensor) -> None:
 @torch.no_grad()
 def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
              grid: Sequence[int], max_points: int, max_voxels: int, *,
-             table_slots: int = 0, prefix_points: int = 0, hash: int = 0,
+             table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
              chunked: bool = False, return_device_outputs: bool = False):
     """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
 
@@ -159,9 +171,9 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     _check_points(points)
     dev = points.device
     N, K, M = points.shape[0], int(max_points), int(max_voxels)
-    opts = _options(table_slots, prefix_points, hash)
+    opts = _options(table_slots, prefix_points, hash, bucket_cap)
     nbytes = workspace_bytes(N, M, K, table_slots=table_slots, prefix_points=prefix_points,
-                             hash=hash)
+                             hash=hash, bucket_cap=bucket_cap)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         ws = _workspaces.get(dev, stream, nbytes)

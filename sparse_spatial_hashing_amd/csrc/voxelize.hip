@@ -5,7 +5,7 @@
 // order, cap, truncation) is stated in include/voxelize.h. The page's own
 // kernel ("Claiming a pillar and packing points", "Compaction") writes each
 // pillar at its hash slot in arrival order and compacts the table with a
-// copy_if; this design instead makes the result a pure function of the input:
+// copy_if; this design makes the result a pure function of the input:
 //
 //   insert  points [0, P): bin, find-or-claim the cell in a 64-bit-keyed
 //           linear-probe table (CAS on an empty slot), record the lowest
@@ -13,17 +13,29 @@
 //           slot. P = min(N, S/2) keeps the load at or below one half, so no
 //           probe sequence can run away (the page sizes its table 8x the
 //           pillar budget for the same reason: "A fixed table").
-//   rank    single-pass scan (decoupled look-back) over points [0, P): point
-//           i is a pillar's first occurrence iff the slot's lowest index is
-//           i; its rank among first occurrences is the pillar id. The first
-//           max_voxels ids are kept (written back into the slot).
+//   rank    single-pass scan with decoupled look-back over points [0, P):
+//           point i is a pillar's first occurrence iff its slot's lowest
+//           index is i; its rank among first occurrences is the pillar id.
+//           The first max_voxels ids are kept (written back into the slot).
 //   select  every point of a kept pillar (prefix points through their slot,
-//           the rest by a lookup-only probe) enters its pillar's row of K
-//           lowest indices with an ordered atomicMax cascade; the result is
-//           independent of arrival order.
-//   pack    per kept pillar: gather the selected rows (bit copies, 16-byte
-//           loads), zero padding, coordinates and counts; then return every
-//           workspace word this call touched to zero.
+//           the others by a lookup-only probe) takes one arrival ticket from
+//           its pillar's counter and parks its index in the pillar's bucket;
+//           arrivals past the bucket go through an ordered atomicMax cascade
+//           that keeps their K lowest indices.
+//   pack    one wavefront per kept pillar sorts the bucket (bitonic network
+//           across the 64 lanes), merges the overflow row, keeps the K lowest
+//           indices, gathers those rows (bit copies, 16-byte loads), writes
+//           zero padding, coordinates and counts, and returns every
+//           workspace word the call wrote to zero.
+//
+// gfx950 notes that shape the code. Blocks are dealt round-robin to the 8
+// XCDs, each with its own L2. Device-scope read-modify-write atomics are
+// executed beyond the L2 at a fixed rate whatever the footprint, so each
+// stage issues at most one returning atomic per point, and no counter is hit
+// by every block. An agent-scope acquire or release (and __threadfence) costs
+// an L2 invalidate or write-back on this part, so no kernel uses one: the
+// look-back publishes its value inside the atomic word with relaxed loads
+// and stores, and everything else crosses kernel boundaries.
 //
 // No fast-math: binning must be IEEE fp32 (correctly rounded divide, no FMA
 // contraction, denormals kept) to agree bit for bit with any other fp32
@@ -41,10 +53,12 @@ namespace {
 
 constexpr int kBlock = 256;                 // 4 wavefronts of 64 lanes
 constexpr int kWave = 64;
+constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kRankTile = 1024;             // points per look-back tile
 constexpr int kRankIters = kRankTile / kBlock;
-constexpr unsigned kSpinLimit = 1u << 24;   // look-back wait bound (never reached in practice)
-constexpr int kPackMaxBlocks = 8192;
+constexpr unsigned kSpinLimit = 1u << 22;   // look-back poll bound (never reached in practice)
+constexpr int kPackMaxBlocks = 4096;
+constexpr int kSortLanes = 64;              // pillars with K <= 64 use the bucket + bitonic path
 
 // One table slot. key1 = cell key + 1 (0 = empty). first = ~(lowest point
 // index of the cell) while inserting (atomicMax keeps the lowest index), then
@@ -56,15 +70,15 @@ struct alignas(16) Slot {
     unsigned int pad;
 };
 
-// First 256 bytes of the workspace.
+// First 256 bytes of the workspace. status and distinct are result words
+// assigned by every call; the other words are zero between calls.
 struct alignas(256) Header {
-    unsigned int claims;       // cells inserted (wave-aggregated); read by the chunked path
-    unsigned int rank_ticket;  // look-back tile tickets
+    unsigned int claims;       // cells inserted (chunked path only); cleared by rank
+    unsigned int rank_ticket;  // look-back tile tickets; cleared by select
     int status;                // V, or a VOX_STATUS_* code; written by the last rank tile
     int distinct;              // cells in the table (first occurrences in [0, P))
-    unsigned int error;        // nonzero: an internal bound was exceeded
-    unsigned int pack_done;    // pack blocks finished
-    unsigned int pad[58];
+    unsigned int error;        // nonzero: an internal bound was exceeded (sticky)
+    unsigned int pad[59];
 };
 static_assert(sizeof(Header) == 256, "header is 256 bytes");
 
@@ -130,13 +144,18 @@ __device__ __forceinline__ int find_slot(const Slot* __restrict__ table, unsigne
     return -1;
 }
 
+__device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsigned bit) {
+    atomicOr(&hdr->error, bit);
+    num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+}
+
 // ----------------------------------------------------------------- insert --
 
 __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pts,
                                                    long long begin, long long end, Grid g,
                                                    Slot* __restrict__ table, unsigned S,
                                                    int hash, int* __restrict__ slot_of,
-                                                   Header* __restrict__ hdr) {
+                                                   Header* __restrict__ hdr, int count_claims) {
     const long long i = begin + (long long)blockIdx.x * kBlock + threadIdx.x;
     bool claimed = false;
     if (i < end) {
@@ -169,15 +188,18 @@ __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pt
                 const unsigned enc = ~(unsigned)i;
                 // first only grows (atomicMax), so a stale read is never too
                 // large: skipping the atomic when it already holds a lower
-                // index is safe.
+                // index is exact.
                 if (table[s].first < enc) atomicMax(&table[s].first, enc);
                 out = (int)s;
             }
         }
         slot_of[i] = out;
     }
-    const unsigned long long b = __ballot(claimed);
-    if (__lane_id() == 0 && b != 0ull) atomicAdd(&hdr->claims, (unsigned)__popcll(b));
+    if (count_claims) {
+        // only the chunked path reads the number of cells; one atomic per wave
+        const unsigned long long b = __ballot(claimed);
+        if (__lane_id() == 0 && b != 0ull) atomicAdd(&hdr->claims, (unsigned)__popcll(b));
+    }
 }
 
 // ------------------------------------------------------------------- rank --
@@ -186,21 +208,73 @@ constexpr unsigned long long kFlagAgg = 1ull << 62;
 constexpr unsigned long long kFlagIncl = 2ull << 62;
 constexpr unsigned long long kValueMask = (1ull << 62) - 1ull;
 
+__device__ __forceinline__ unsigned long long load_relaxed(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Exclusive prefix of this tile from its predecessors' published words, read
+// 64 tiles per poll by the whole wavefront (lane l looks at tile - 1 - l).
+// Every published word carries its own value, so relaxed accesses suffice.
+// All 64 lanes must call this together.
+__device__ unsigned long long look_back(unsigned long long* tile_state, long long tile,
+                                        unsigned* err, bool* failed) {
+    const int lane = __lane_id();
+    unsigned long long excl = 0;
+    long long hi = tile - 1;
+    unsigned polls = 0;
+    while (true) {
+        const long long j = hi - lane;
+        const unsigned long long v = j >= 0 ? load_relaxed(&tile_state[j]) : kFlagIncl;
+        const unsigned long long flag = v & ~kValueMask;
+        const unsigned long long incl = __ballot(flag == kFlagIncl);
+        const unsigned long long waiting = __ballot(flag == 0ull);
+        const int stop = incl ? __builtin_ctzll(incl) : kWave - 1;   // nearest inclusive
+        const unsigned long long need = (stop == kWave - 1) ? ~0ull : ((2ull << stop) - 1ull);
+        if (waiting & need) {
+            if (++polls > kSpinLimit) {
+                if (lane == 0) atomicOr(err, 2u);
+                *failed = true;
+                return 0;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        excl += wave_sum64(lane <= stop ? (v & kValueMask) : 0ull);
+        if (incl) return excl;
+        hi -= kWave;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M,
                                                  Slot* __restrict__ table,
                                                  const int* __restrict__ slot_of,
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, int* __restrict__ occ_slot,
                                                  long long* __restrict__ kept_key,
-                                                 Header* __restrict__ hdr) {
+                                                 Header* __restrict__ hdr,
+                                                 int* __restrict__ num_voxels) {
     __shared__ unsigned tile_sh;
-    __shared__ unsigned wave_cnt[kRankIters][kBlock / kWave];
+    __shared__ unsigned wave_cnt[kRankIters][kWavesPerBlock];
     __shared__ unsigned long long excl_sh;
+    __shared__ int failed_sh;
 
     const int t = threadIdx.x;
     const int w = t / kWave;
     const int lane = __lane_id();
-    if (t == 0) tile_sh = atomicAdd(&hdr->rank_ticket, 1u);  // tiles in dispatch order
+    if (t == 0) {
+        tile_sh = atomicAdd(&hdr->rank_ticket, 1u);  // tiles in dispatch order
+        failed_sh = 0;
+        if (blockIdx.x == 0) hdr->claims = 0u;       // read by the host between inserts only
+    }
     __syncthreads();
     const long long tile = tile_sh;
     const long long base = tile * kRankTile;
@@ -237,7 +311,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
 #pragma unroll
     for (int k = 0; k < kRankIters; ++k) {
         unsigned off = run;
-        for (int ww = 0; ww < kBlock / kWave; ++ww) {
+        for (int ww = 0; ww < kWavesPerBlock; ++ww) {
             if (ww < w) off += wave_cnt[k][ww];
             run += wave_cnt[k][ww];
         }
@@ -245,47 +319,39 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
     }
     const unsigned aggregate = run;
 
-    if (t == 0) {
+    if (w == 0) {
         unsigned long long excl = 0;
+        bool failed = false;
         if (tile == 0) {
-            __hip_atomic_store(&tile_state[0], kFlagIncl | (unsigned long long)aggregate,
-                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) store_relaxed(&tile_state[0], kFlagIncl | (unsigned long long)aggregate);
         } else {
-            __hip_atomic_store(&tile_state[tile], kFlagAgg | (unsigned long long)aggregate,
-                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            long long j = tile - 1;
-            unsigned spins = 0;
-            for (;;) {
-                const unsigned long long v = __hip_atomic_load(&tile_state[j], __ATOMIC_ACQUIRE,
-                                                               __HIP_MEMORY_SCOPE_AGENT);
-                if ((v & ~kValueMask) == 0ull) {
-                    // predecessor has not published yet; it holds an earlier
-                    // ticket, so it is resident and will
-                    if (++spins > kSpinLimit) {
-                        atomicOr(&hdr->error, 2u);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                excl += v & kValueMask;
-                if ((v & ~kValueMask) == kFlagIncl || j == 0) break;
-                --j;
-            }
-            __hip_atomic_store(&tile_state[tile], kFlagIncl | (excl + aggregate),
-                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) store_relaxed(&tile_state[tile], kFlagAgg | (unsigned long long)aggregate);
+            excl = look_back(tile_state, tile, &hdr->error, &failed);
+            if (lane == 0 && !failed)
+                store_relaxed(&tile_state[tile], kFlagIncl | (excl + aggregate));
         }
-        excl_sh = excl;
-        if (tile == ntiles - 1) {
-            // the last tile knows the number of distinct cells in [0, P)
-            const long long distinct = (long long)excl + aggregate;
-            int status = (int)(distinct < M ? distinct : M);
-            if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
-            hdr->distinct = (int)distinct;
-            hdr->status = status;
+        if (lane == 0) {
+            excl_sh = excl;
+            failed_sh = failed ? 1 : 0;
+            if (tile == ntiles - 1) {
+                // the last tile knows the number of distinct cells in [0, P)
+                const long long distinct = (long long)excl + aggregate;
+                int status = (int)(distinct < M ? distinct : M);
+                if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
+                if (failed || __hip_atomic_load(&hdr->error, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                    status = VOX_STATUS_DEVICE_ERROR;
+                hdr->distinct = (int)distinct;
+                hdr->status = status;
+                num_voxels[0] = status;
+            }
         }
     }
     __syncthreads();
+    if (failed_sh) {
+        if (t == 0) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+        return;
+    }
     const unsigned long long excl = excl_sh;
 
 #pragma unroll
@@ -293,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
         if (!is_first[k]) continue;
         const long long r = (long long)excl + local[k];
         if (r >= P) {  // cannot happen: there are at most P first occurrences
-            atomicOr(&hdr->error, 2u);
+            report_error(hdr, num_voxels, 2u);
             continue;
         }
         occ_slot[r] = slot[k];
@@ -311,29 +377,10 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
 // Values at a position only grow, so a stale read is never larger than the
 // current value: skipping positions whose read value exceeds v, and dropping
 // v when the last position already exceeds it, are both exact.
-template <int KC>
 __device__ __forceinline__ void cascade(unsigned* __restrict__ row, int K, unsigned v) {
+    if (row[K - 1] > v) return;
     int j = 0;
-    if constexpr (KC > 0 && KC % 4 == 0) {
-        unsigned r[KC];
-#pragma unroll
-        for (int q = 0; q < KC / 4; ++q) {
-            const uint4 x = reinterpret_cast<const uint4*>(row)[q];
-            r[4 * q + 0] = x.x;
-            r[4 * q + 1] = x.y;
-            r[4 * q + 2] = x.z;
-            r[4 * q + 3] = x.w;
-        }
-        if (r[KC - 1] > v) return;
-        j = KC;
-#pragma unroll
-        for (int q = KC - 1; q >= 0; --q)
-            if (r[q] < v) j = q;
-        K = KC;
-    } else {
-        if (row[K - 1] > v) return;
-        while (j < K && row[j] > v) ++j;
-    }
+    while (j < K && row[j] > v) ++j;
     for (; j < K; ++j) {
         const unsigned old = atomicMax(&row[j], v);
         if (old == 0u) return;   // took an empty position
@@ -341,14 +388,20 @@ __device__ __forceinline__ void cascade(unsigned* __restrict__ row, int K, unsig
     }
 }
 
-template <int KC>
 __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pts, long long N,
                                                    long long P, Grid g,
                                                    const Slot* __restrict__ table, unsigned S,
                                                    int hash, int* __restrict__ slot_of,
-                                                   unsigned* __restrict__ sel, int K,
-                                                   Header* __restrict__ hdr) {
+                                                   unsigned* __restrict__ cnt,
+                                                   unsigned* __restrict__ bucket, int cap,
+                                                   unsigned* __restrict__ ovf, int K,
+                                                   Header* __restrict__ hdr,
+                                                   int* __restrict__ num_voxels) {
     const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr->rank_ticket = 0u;  // rank is done with it
+        if (hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    }
     if (i >= N) return;
     const int status = hdr->status;
     int s = -1;
@@ -356,7 +409,7 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
         s = slot_of[i];
         slot_of[i] = 0;  // last reader: return the word to zero for the next call
     }
-    if (status <= 0 || hdr->error != 0u) return;  // nothing kept, or cap undecided
+    if (status <= 0) return;  // nothing kept, cap undecided, or an error
     if (i >= P) {
         const long long key = bin_key(pts[i], g);
         s = key < 0 ? -1 : find_slot(table, S, hash, key, &hdr->error);
@@ -364,18 +417,62 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
     if (s < 0) return;
     const unsigned tag = table[s].first;
     if (tag == 0u || (tag & 0x80000000u)) return;  // cell not among the kept pillars
-    const long long pid = (long long)(tag - 1u);
-    if (pid >= status) {  // cannot happen on a clean workspace
-        atomicOr(&hdr->error, 4u);
+    const unsigned pid = tag - 1u;
+    if (pid >= (unsigned)status) {  // cannot happen on a clean workspace
+        report_error(hdr, num_voxels, 4u);
         return;
     }
-    cascade<KC>(sel + pid * K, K, ~(unsigned)i);
+    if (cap > 0) {
+        const unsigned a = atomicAdd(&cnt[pid], 1u);  // one returning atomic per point
+        if (a < (unsigned)cap) {
+            bucket[(size_t)pid * cap + a] = (unsigned)i;
+            return;
+        }
+    }
+    cascade(ovf + (size_t)pid * K, K, ~(unsigned)i);
 }
 
 // ------------------------------------------------------------------- pack --
 
+// Ascending bitonic sort of one value per lane across the 64-lane wavefront.
+__device__ __forceinline__ unsigned sort64(unsigned v, int lane) {
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const unsigned o = (unsigned)__shfl_xor((int)v, j);
+            const bool keep_min = ((lane & j) == 0) == ((lane & k) == 0);
+            v = keep_min ? (v < o ? v : o) : (v > o ? v : o);
+        }
+    }
+    return v;
+}
+
+// a and b ascending across the wavefront: returns the 64 smallest of both,
+// ascending (elementwise min against the reversed b is bitonic; then merge).
+__device__ __forceinline__ unsigned merge64(unsigned a, unsigned b, int lane) {
+    const unsigned rb = (unsigned)__shfl((int)b, kWave - 1 - lane);
+    unsigned v = a < rb ? a : rb;
+#pragma unroll
+    for (int j = kWave >> 1; j > 0; j >>= 1) {
+        const unsigned o = (unsigned)__shfl_xor((int)v, j);
+        v = ((lane & j) == 0) ? (v < o ? v : o) : (v > o ? v : o);
+    }
+    return v;
+}
+
+__device__ __forceinline__ void write_coords(int* __restrict__ coords, long long p, long long key,
+                                             int gx, int gy) {
+    const long long plane = (long long)gx * gy;
+    coords[3 * p + 0] = (int)(key / plane);
+    coords[3 * p + 1] = (int)((key % plane) / gx);
+    coords[3 * p + 2] = (int)(key % gx);
+}
+
 __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts, long long N,
-                                                 unsigned* __restrict__ sel, int K, int M,
+                                                 unsigned* __restrict__ cnt,
+                                                 unsigned* __restrict__ bucket, int cap,
+                                                 unsigned* __restrict__ ovf, int K, int M,
                                                  long long* __restrict__ kept_key, int gx,
                                                  int gy, float4* __restrict__ voxels,
                                                  int* __restrict__ coords,
@@ -386,78 +483,83 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, Header* __restrict__ hdr) {
     const int status = hdr->status;
-    const unsigned err = hdr->error;
     const long long distinct = hdr->distinct;
-    const long long V = (status > 0 && err == 0u) ? status : 0;
+    const long long V = status > 0 ? status : 0;
     const int lane = __lane_id();
     const long long nthreads = (long long)gridDim.x * kBlock;
     const long long gtid = (long long)blockIdx.x * kBlock + threadIdx.x;
     const long long nwaves = nthreads / kWave;
     const long long gwave = gtid / kWave;
+    if (gtid == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
 
-    // 1) pillars. A wave owns whole pillars, so it can count a row with a
-    //    ballot and clear it without racing another wave.
-    if (K <= kWave) {
-        const int per = kWave / K;        // pillars per wave pass
-        const int sub = lane / K;         // which of them this lane serves
-        const int j = lane - sub * K;     // row inside the pillar
-        const bool used = sub < per;
-        for (long long p0 = gwave * per; p0 < V; p0 += nwaves * per) {
-            const long long p = p0 + sub;
-            const bool live = used && p < V;
-            unsigned v = 0u;
-            if (live) v = sel[p * K + j];
-            const unsigned long long b = __ballot(v != 0u);
-            if (live) {
-                float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (v != 0u) {
-                    const unsigned src = ~v;
-                    if (src < N) row = pts[src];
-                    else atomicOr(&hdr->error, 8u);
-                    sel[p * K + j] = 0u;
+    // 1) pillars, one wavefront each: nothing else touches a pillar's
+    //    counter, bucket or overflow row, so they are read and cleared here.
+    for (long long p = gwave; p < V; p += nwaves) {
+        if (cap > 0) {
+            // K <= 64: sort the bucket, merge the overflow row, keep K lowest
+            const unsigned total = cnt[p];
+            const unsigned b = total < (unsigned)cap ? total : (unsigned)cap;
+            unsigned best = 0xffffffffu;  // lane j: j-th lowest index so far
+            unsigned* bk = bucket + (size_t)p * cap;
+            for (unsigned c0 = 0; c0 < b; c0 += kWave) {
+                const unsigned c = c0 + lane;
+                unsigned v = 0xffffffffu;
+                if (c < b) {
+                    v = bk[c];
+                    bk[c] = 0u;
                 }
-                voxels[p * K + j] = row;
-                if (j == 0) {
-                    const unsigned long long mine = (b >> (sub * K)) &
-                        (K == 64 ? ~0ull : ((1ull << K) - 1ull));
-                    num_points[p] = __popcll(mine);
-                    const long long key = kept_key[p];
-                    kept_key[p] = 0;
-                    const long long plane = (long long)gx * gy;
-                    coords[3 * p + 0] = (int)(key / plane);
-                    coords[3 * p + 1] = (int)((key % plane) / gx);
-                    coords[3 * p + 2] = (int)(key % gx);
-                }
+                v = sort64(v, lane);
+                best = c0 == 0 ? v : merge64(best, v, lane);
             }
-        }
-    } else {
-        for (long long p = gwave; p < V; p += nwaves) {
+            if (total > (unsigned)cap) {
+                // arrivals past the bucket: their K lowest, already ascending
+                unsigned o = 0xffffffffu;
+                if (lane < K) {
+                    const unsigned e = ovf[(size_t)p * K + lane];
+                    if (e != 0u) {
+                        o = ~e;
+                        ovf[(size_t)p * K + lane] = 0u;
+                    }
+                }
+                best = merge64(best, o, lane);
+            }
+            const unsigned count = total < (unsigned)K ? total : (unsigned)K;
+            if (lane < K) {
+                float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+                if ((unsigned)lane < count) {
+                    if (best < N) row = pts[best];
+                    else report_error(hdr, num_voxels, 8u);
+                }
+                voxels[p * K + lane] = row;
+            }
+            if (lane == 0) {
+                num_points[p] = (int)count;
+                cnt[p] = 0u;
+            }
+        } else {
+            // K > 64: the overflow row is the whole selection, in order
             int count = 0;
             for (int j0 = 0; j0 < K; j0 += kWave) {
                 const int j = j0 + lane;
                 unsigned v = 0u;
-                if (j < K) v = sel[p * K + j];
+                if (j < K) v = ovf[(size_t)p * K + j];
                 count += __popcll(__ballot(v != 0u));
                 if (j < K) {
                     float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
                     if (v != 0u) {
                         const unsigned src = ~v;
                         if (src < N) row = pts[src];
-                        else atomicOr(&hdr->error, 8u);
-                        sel[p * K + j] = 0u;
+                        else report_error(hdr, num_voxels, 8u);
+                        ovf[(size_t)p * K + j] = 0u;
                     }
                     voxels[p * K + j] = row;
                 }
             }
-            if (lane == 0) {
-                num_points[p] = count;
-                const long long key = kept_key[p];
-                kept_key[p] = 0;
-                const long long plane = (long long)gx * gy;
-                coords[3 * p + 0] = (int)(key / plane);
-                coords[3 * p + 1] = (int)((key % plane) / gx);
-                coords[3 * p + 2] = (int)(key % gx);
-            }
+            if (lane == 0) num_points[p] = count;
+        }
+        if (lane == 0) {
+            write_coords(coords, p, kept_key[p], gx, gy);
+            kept_key[p] = 0;
         }
     }
 
@@ -469,29 +571,10 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
         const int s = occ_slot[r];
         occ_slot[r] = 0;
         if (s >= 0 && (unsigned)s < S) table[s] = zero;
-        else atomicOr(&hdr->error, 16u);
+        else report_error(hdr, num_voxels, 16u);
         if (r >= V && r < kept_written) kept_key[r] = 0;
     }
     for (long long r = gtid; r < ntiles; r += nthreads) tile_state[r] = 0ull;
-
-    // 3) the last block to finish publishes the result and clears the header
-    __shared__ bool last_sh;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last_sh = (atomicAdd(&hdr->pack_done, 1u) == gridDim.x - 1u);
-    __syncthreads();
-    if (last_sh && threadIdx.x == 0) {
-        __threadfence();
-        int out = status;
-        if (err != 0u || hdr->error != 0u) out = VOX_STATUS_DEVICE_ERROR;
-        num_voxels[0] = out;
-        hdr->claims = 0u;
-        hdr->rank_ticket = 0u;
-        hdr->status = 0;
-        hdr->distinct = 0;
-        hdr->error = 0u;
-        hdr->pack_done = 0u;
-    }
 }
 
 // -------------------------------------------------------------- bin only --
@@ -520,13 +603,19 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
     long long N, P, S;
-    int K, M, hash;
+    int K, M, hash, cap;
     long long ntiles;
     // byte offsets into the workspace
-    size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_sel, bytes;
+    size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf, bytes;
 };
 
 inline bool finite_f(float v) { return isfinite(v); }
+
+// Default bucket capacity: 16 K rounded up to a whole number of wavefronts.
+inline int default_cap(int K) {
+    if (K > kSortLanes) return 0;
+    return (int)cdiv(16ll * K, kWave) * kWave;
+}
 
 int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     if (N < 0 || N > 2147483647ll) return VOX_EINVAL;
@@ -537,12 +626,18 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     if (S < 64) S = 64;
     int hash = 0;
     long long P = 0;
+    int cap = default_cap(K);
     if (opt) {
-        if (opt->table_slots < 0 || opt->prefix_points < 0) return VOX_EINVAL;
+        if (opt->table_slots < 0 || opt->prefix_points < 0 || opt->bucket_cap < 0)
+            return VOX_EINVAL;
         if (opt->table_slots > 0) S = opt->table_slots;
         if (opt->hash < 0 || opt->hash > 1) return VOX_EINVAL;
         hash = opt->hash;
         P = opt->prefix_points;
+        if (opt->bucket_cap > 0 && K <= kSortLanes) {
+            if (opt->bucket_cap > (1 << 20)) return VOX_EINVAL;
+            cap = opt->bucket_cap;
+        }
     }
     // S >= 2M: while fewer than M cells are in the table, a chunk of
     // S/2 - cells >= 1 points always fits at load <= 1/2
@@ -556,6 +651,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->K = K;
     pl->M = M;
     pl->hash = hash;
+    pl->cap = cap;
     // arrays indexed by point go to N: the chunked path can insert every point
     const long long Nw = N > 0 ? N : 1;
     pl->ntiles = cdiv(Nw, kRankTile);
@@ -570,7 +666,11 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     off = align256(off + (size_t)Nw * sizeof(int));
     pl->off_kept = off;
     off = align256(off + (size_t)M * sizeof(long long));
-    pl->off_sel = off;
+    pl->off_cnt = off;
+    off = align256(off + (size_t)M * sizeof(unsigned));
+    pl->off_bucket = off;
+    off = align256(off + (size_t)M * (size_t)cap * sizeof(unsigned));
+    pl->off_ovf = off;
     off = align256(off + (size_t)M * (size_t)K * sizeof(unsigned));
     pl->bytes = off;
     return VOX_OK;
@@ -616,7 +716,9 @@ struct Buffers {
     unsigned long long* tiles;
     int* occ;
     long long* kept;
-    unsigned* sel;
+    unsigned* cnt;
+    unsigned* bucket;
+    unsigned* ovf;
 };
 
 Buffers carve(void* ws, const Plan& pl) {
@@ -628,60 +730,63 @@ Buffers carve(void* ws, const Plan& pl) {
     x.tiles = reinterpret_cast<unsigned long long*>(b + pl.off_tiles);
     x.occ = reinterpret_cast<int*>(b + pl.off_occ);
     x.kept = reinterpret_cast<long long*>(b + pl.off_kept);
-    x.sel = reinterpret_cast<unsigned*>(b + pl.off_sel);
+    x.cnt = reinterpret_cast<unsigned*>(b + pl.off_cnt);
+    x.bucket = reinterpret_cast<unsigned*>(b + pl.off_bucket);
+    x.ovf = reinterpret_cast<unsigned*>(b + pl.off_ovf);
     return x;
 }
 
+int last_launch() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : hip_fail(e);
+}
+
 int launch_insert(const float* points, long long begin, long long end, const Grid& g,
-                  const Plan& pl, const Buffers& bf, hipStream_t st) {
+                  const Plan& pl, const Buffers& bf, hipStream_t st, int count_claims) {
     const long long n = end - begin;
     const unsigned blocks = (unsigned)(n > 0 ? cdiv(n, kBlock) : 1);
     hipLaunchKernelGGL(k_insert, dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const float4*>(points), begin, end, g, bf.table,
-                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? VOX_OK : hip_fail(e);
+                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr, count_claims);
+    return last_launch();
 }
 
-int launch_rank(long long P, const Plan& pl, const Buffers& bf, hipStream_t st) {
+int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_voxels,
+                hipStream_t st) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
     hipLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, P, pl.N, pl.M,
-                       bf.table, bf.slot_of, bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? VOX_OK : hip_fail(e);
+                       bf.table, bf.slot_of, bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr,
+                       num_voxels);
+    return last_launch();
 }
 
 int launch_select(const float* points, long long P, const Grid& g, const Plan& pl,
-                  const Buffers& bf, hipStream_t st) {
+                  const Buffers& bf, int32_t* num_voxels, hipStream_t st) {
     const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
-    const float4* p4 = reinterpret_cast<const float4*>(points);
-    if (pl.K == 32) {
-        hipLaunchKernelGGL(k_select<32>, dim3(blocks), dim3(kBlock), 0, st, p4, pl.N, P, g,
-                           bf.table, (unsigned)pl.S, pl.hash, bf.slot_of, bf.sel, pl.K, bf.hdr);
-    } else {
-        hipLaunchKernelGGL(k_select<0>, dim3(blocks), dim3(kBlock), 0, st, p4, pl.N, P, g,
-                           bf.table, (unsigned)pl.S, pl.hash, bf.slot_of, bf.sel, pl.K, bf.hdr);
-    }
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? VOX_OK : hip_fail(e);
+    hipLaunchKernelGGL(k_select, dim3(blocks), dim3(kBlock), 0, st,
+                       reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
+                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.cnt, bf.bucket, pl.cap, bf.ovf,
+                       pl.K, bf.hdr, num_voxels);
+    return last_launch();
 }
 
 int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                 const Buffers& bf, float* voxels, int32_t* coords, int32_t* num_points,
                 int32_t* num_voxels, hipStream_t st) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
-    long long work = (long long)pl.M * pl.K;
-    if (P > work) work = P;
-    long long blocks = cdiv(work, kBlock);
+    // one wavefront per kept pillar (at most M), and enough threads for the
+    // cleanup of at most P table slots
+    long long blocks = cdiv((long long)pl.M, kWavesPerBlock);
+    const long long clean_blocks = cdiv(P > 0 ? P : 1, kBlock);
+    if (clean_blocks > blocks) blocks = clean_blocks;
     if (blocks < 1) blocks = 1;
     if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
     hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(kBlock), 0, st,
-                       reinterpret_cast<const float4*>(points), pl.N, bf.sel, pl.K, pl.M,
-                       bf.kept, g.gx, g.gy, reinterpret_cast<float4*>(voxels), coords,
-                       num_points, num_voxels, bf.occ, bf.table, (unsigned)pl.S, bf.tiles,
-                       ntiles, bf.hdr);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? VOX_OK : hip_fail(e);
+                       reinterpret_cast<const float4*>(points), pl.N, bf.cnt, bf.bucket, pl.cap,
+                       bf.ovf, pl.K, pl.M, bf.kept, g.gx, g.gy,
+                       reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
+                       bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
+    return last_launch();
 }
 
 int prepare(const float* points, int64_t n_points, const float range[6], const float cell[3],
@@ -703,11 +808,11 @@ int run_pipeline(const float* points, const Grid& g, const Plan& pl, const Buffe
                  hipStream_t st, hipEvent_t* ev) {
     int rc;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st)) != VOX_OK) return rc;
+    if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st, 0)) != VOX_OK) return rc;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_rank(pl.P, pl, bf, st)) != VOX_OK) return rc;
+    if ((rc = launch_rank(pl.P, pl, bf, num_voxels, st)) != VOX_OK) return rc;
     if (ev && hipEventRecord(ev[2], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_select(points, pl.P, g, pl, bf, st)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, pl.P, g, pl, bf, num_voxels, st)) != VOX_OK) return rc;
     if (ev && hipEventRecord(ev[3], st) != hipSuccess) return hip_fail(hipGetLastError());
     if ((rc = launch_pack(points, pl.P, g, pl, bf, voxels, coords, num_points, num_voxels, st)) !=
         VOX_OK)
@@ -776,7 +881,7 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
     while (done < pl.N && have < pl.M) {
         long long chunk = half - have;
         if (chunk > pl.N - done) chunk = pl.N - done;
-        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream)) != VOX_OK)
+        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream, 1)) != VOX_OK)
             return rc;
         done += chunk;
         unsigned claims = 0;
@@ -788,8 +893,8 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
     }
     Plan p2 = pl;
     p2.P = done;
-    if ((rc = launch_rank(done, p2, bf, stream)) != VOX_OK) return rc;
-    if ((rc = launch_select(points, done, g, p2, bf, stream)) != VOX_OK) return rc;
+    if ((rc = launch_rank(done, p2, bf, num_voxels, stream)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, done, g, p2, bf, num_voxels, stream)) != VOX_OK) return rc;
     return launch_pack(points, done, g, p2, bf, voxels, coords, num_points, num_voxels, stream);
 }
 
@@ -807,8 +912,7 @@ int vox_bin_points(const float* points, int64_t n_points, const float range[6],
     hipLaunchKernelGGL(k_bin, dim3((unsigned)cdiv(n_points, kBlock)), dim3(kBlock), 0, stream,
                        reinterpret_cast<const float4*>(points), (long long)n_points, g, valid,
                        reinterpret_cast<long long*>(key));
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? VOX_OK : hip_fail(e);
+    return last_launch();
 }
 
 int vox_profile_stages(const float* points, int64_t n_points, const float range[6],

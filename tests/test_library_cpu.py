@@ -56,6 +56,17 @@ def test_workspace_bytes_rejects_bad_sizes(args):
         vox.workspace_bytes(*args)
 
 
+def test_workspace_bytes_bucket_cap_option():
+    base = vox.workspace_bytes(1000, 100, 32)
+    small = vox.workspace_bytes(1000, 100, 32, bucket_cap=64)
+    assert small < base          # default bucket is 16 K = 512 slots per pillar
+    assert vox.workspace_bytes(1000, 100, 100) > 0   # K > 64 has no bucket
+    with pytest.raises(vox.VoxError):
+        vox.workspace_bytes(1000, 100, 32, bucket_cap=-1)
+    with pytest.raises(vox.VoxError):
+        vox.workspace_bytes(1000, 100, 32, bucket_cap=(1 << 20) + 1)
+
+
 def test_workspace_bytes_rejects_small_table():
     with pytest.raises(vox.VoxError):
         vox.workspace_bytes(1000, 100, 4, table_slots=150)   # needs >= 2 * max_voxels
