@@ -123,8 +123,7 @@ def run_workload(name, steps, warmup, profile_iters, torch, vox):
     rows = int(vx.num_points[:max(V, 0)].sum().item()) if V > 0 else 0
     parity = check_parity(vx, pts, p)
     stage_ms, total_ms = vx.profile(x, profile_iters)
-    S = 8 * p.max_voxels
-    P = min(N, S // 2)
+    P = vox.plan(N, p.max_voxels, p.max_points)["prefix_points"]
     alg = algorithmic_bytes(N, P, V, p.max_points, rows)
     return dict(cfg=cfg, pts=pts, N=N, V=V, rows=rows, ms=ms, parity=parity, stage_ms=stage_ms,
                 total_ms=total_ms, alg=alg, P=P)

@@ -7,7 +7,8 @@
  * consumes (introduction): a [V, K, 4] stack of per-pillar points, [V, 3]
  * int32 grid coordinates (z, y, x) and [V] int32 per-pillar counts. Points are
  * grouped through an open-addressing hash table ("A hash table instead of a
- * sort") sized 8 x max_voxels ("A fixed table, sized 8x the voxel budget").
+ * sort") sized from the pillar budget, as the page's is ("A fixed table, sized
+ * 8x the voxel budget"); here 16 slots per pillar, see vox_options.
  *
  * Output order and content are deterministic (the page's kernel writes pillars
  * in hash-slot order and points in arrival order; this library does not):
@@ -57,7 +58,7 @@ extern "C" {
 #define VOX_EHIP -4        /* a HIP call failed; vox_last_hip_error() returns its code */
 
 /* ---- device status written to num_voxels[0] instead of V ----------------- */
-/* The single-pass path inserts the first P = min(N, table_slots/2) points into
+/* The single-pass path inserts the first P = min(N, table_slots/4) points into
  * the table and decides the max_voxels cap among them. When N > P and those P
  * points hold fewer than max_voxels distinct cells, the cap cannot be decided
  * in one pass: num_voxels[0] is set to VOX_STATUS_NEEDS_CHUNKED, the outputs
@@ -71,10 +72,11 @@ extern "C" {
 
 /* ---- options (tests and tuning; NULL = defaults) ------------------------- */
 typedef struct vox_options {
-    int64_t table_slots;    /* hash table slots S; 0 = 8 * max_voxels (at least 64);
-                               otherwise 2 * max_voxels <= S <= 2^31 - 1 */
-    int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N, S/2);
-                               clamped to [1, S/2] */
+    int64_t table_slots;    /* hash table slots S; 0 = 16 * max_voxels (at least 64);
+                               otherwise 2 * max_voxels <= S <= 2^31 - 16; rounded up to
+                               a multiple of 16 (one 128-byte line) */
+    int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N, S/4);
+                               at most S/2 (and N) */
     int32_t hash;           /* 0 = 64-bit mix + multiply-high reduction, 1 = key mod S */
     int32_t bucket_cap;     /* per-pillar arrival slots before the overflow row; 0 = 16 * K
                                rounded up to a multiple of 64 (K <= 64); at most 2^20 */
@@ -97,11 +99,12 @@ int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_po
  * Pillar / voxel binning of one cloud (the whole operation described above).
  *
  *   points      device, [n_points, 4] float32, row-major, 16-byte aligned
- *   n_points    N >= 0, N <= 2^31 - 1; N = 0 gives V = 0
+ *   n_points    N >= 0, N <= 2^30 - 1; N = 0 gives V = 0
  *   range       host, 6 floats: x_min, y_min, z_min, x_max, y_max, z_max
  *               (finite, min < max)
  *   cell        host, 3 floats: vx, vy, vz (finite, > 0)
- *   grid        host, 3 int32: gx, gy, gz (1 <= g <= 2^24; gz == 1 is pillar mode)
+ *   grid        host, 3 int32: gx, gy, gz (1 <= g <= 2^24, gx * gy * gz <= 2^33 - 2;
+ *               gz == 1 is pillar mode)
  *   max_points  K >= 1 (rows per pillar)
  *   max_voxels  M >= 1 (pillar cap)
  *   voxels      device, [M, K, 4] float32, 16-byte aligned; rows [0, V) written
@@ -139,6 +142,15 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
                      int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
                      int32_t* num_voxels, void* workspace, size_t workspace_bytes,
                      hipStream_t stream, const vox_options* options);
+
+/*
+ * The sizes a call would use (for reports and tests): table slots S, prefix
+ * length P and bucket slots per pillar (0 when max_points > 64). Any output
+ * pointer may be NULL. Returns VOX_OK or VOX_EINVAL.
+ */
+int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,
+             const vox_options* options, int64_t* table_slots, int64_t* prefix_points,
+             int32_t* bucket_cap);
 
 /*
  * The per-point binning step alone ("Binning a point"), for parity tests:

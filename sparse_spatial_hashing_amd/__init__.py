@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = common + [op]
         f.restype = ctypes.c_int
+    lib.vox_plan.argtypes = [i64, i32, i32, op, vp, vp, vp]
+    lib.vox_plan.restype = ctypes.c_int
     lib.vox_bin_points.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp]
     lib.vox_bin_points.restype = ctypes.c_int
     lib.vox_profile_stages.argtypes = common + [op, i32, vp, vp]
@@ -110,6 +112,14 @@ def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> 
     if n < 0:
         raise VoxError(int(n), "vox_workspace_bytes")
     return int(n)
+
+
+def plan(n_points: int, max_voxels: int, max_points: int, **opts) -> Dict[str, int]:
+    """Table slots, prefix length and bucket slots a call with these sizes uses."""
+    S, P, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(_lib.vox_plan(int(n_points), int(max_voxels), int(max_points), _options(**opts),
+                         ctypes.byref(S), ctypes.byref(P), ctypes.byref(cap)), "vox_plan")
+    return {"table_slots": S.value, "prefix_points": P.value, "bucket_cap": cap.value}
 
 
 class _Workspaces:

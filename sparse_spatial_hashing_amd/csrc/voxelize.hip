@@ -7,26 +7,29 @@
 // pillar at its hash slot in arrival order and compacts the table with a
 // copy_if; this design makes the result a pure function of the input:
 //
-//   insert  points [0, P): bin, find-or-claim the cell in a 64-bit-keyed
-//           linear-probe table (CAS on an empty slot), record the lowest
-//           point index per cell (atomicMax of ~index), remember each point's
-//           slot. P = min(N, S/2) keeps the load at or below one half, so no
-//           probe sequence can run away (the page sizes its table 8x the
-//           pillar budget for the same reason: "A fixed table").
+//   insert  points [0, P): bin, find-or-claim the cell in a linear-probe
+//           table of 64-bit words (key and lowest index of the cell: one CAS
+//           claims an empty slot, one 64-bit atomicMax lowers the index),
+//           remember each point's slot. The table has 16 slots per kept
+//           pillar and P = min(N, 4 max_voxels), so inserts see a load of at
+//           most 1/4 and probe chains stay short (the page sizes its table
+//           8x the pillar budget for the same reason: "A fixed table").
 //   rank    single-pass scan with decoupled look-back over points [0, P):
 //           point i is a pillar's first occurrence iff its slot's lowest
 //           index is i; its rank among first occurrences is the pillar id.
-//           The first max_voxels ids are kept (written back into the slot).
+//           The first max_voxels ids are kept (written into the slot word).
 //   select  every point of a kept pillar (prefix points through their slot,
 //           the others by a lookup-only probe) takes one arrival ticket from
 //           its pillar's counter and parks its index in the pillar's bucket;
 //           arrivals past the bucket go through an ordered atomicMax cascade
 //           that keeps their K lowest indices.
-//   pack    one wavefront per kept pillar sorts the bucket (bitonic network
-//           across the 64 lanes), merges the overflow row, keeps the K lowest
-//           indices, gathers those rows (bit copies, 16-byte loads), writes
-//           zero padding, coordinates and counts, and returns every
-//           workspace word the call wrote to zero.
+//   pack    a lane segment per kept pillar (several pillars per wavefront)
+//           orders the pillar's candidates by rank (scalar broadcasts); a
+//           pillar with more candidates than its segment takes the whole
+//           wavefront, a bitonic network and the overflow row. The K lowest
+//           indices become rows (bit copies, 16-byte loads) with zero padding,
+//           coordinates and counts; then every workspace word the call wrote
+//           is returned to zero.
 //
 // gfx950 notes that shape the code. Blocks are dealt round-robin to the 8
 // XCDs, each with its own L2. Device-scope read-modify-write atomics are
@@ -60,15 +63,26 @@ constexpr unsigned kSpinLimit = 1u << 22;   // look-back poll bound (never reach
 constexpr int kPackMaxBlocks = 4096;
 constexpr int kSortLanes = 64;              // pillars with K <= 64 use the bucket + bitonic path
 
-// One table slot. key1 = cell key + 1 (0 = empty). first = ~(lowest point
-// index of the cell) while inserting (atomicMax keeps the lowest index), then
-// pid + 1 once the cell is ranked and kept (top bit clear, so the two never
-// collide: indices are < 2^31).
-struct alignas(16) Slot {
-    unsigned long long key1;
-    unsigned int first;
-    unsigned int pad;
-};
+// One table slot is a single 64-bit word, 0 = empty:
+//   bits 63..31  cell key + 1 (so grids hold at most 2^33 - 2 cells)
+//   bit  30      kept flag, set by rank once the cell is among the kept pillars
+//   bits 29..0   ~(lowest point index) while inserting, the pillar id once kept
+// A cell is claimed with one CAS; later points of the cell lower its index
+// with one 64-bit atomicMax (the key bits are equal and the flag is clear, so
+// the maximum is taken on ~index). Point indices are < 2^30.
+constexpr int kKeyShift = 31;
+constexpr unsigned long long kKeptFlag = 1ull << 30;
+constexpr unsigned long long kIdxMask = (1ull << 30) - 1ull;
+constexpr unsigned long long kMaxCells = (1ull << 33) - 2ull;
+constexpr long long kMaxPoints = (1ll << 30) - 1;
+
+__host__ __device__ __forceinline__ unsigned long long slot_key1(unsigned long long w) {
+    return w >> kKeyShift;
+}
+__host__ __device__ __forceinline__ unsigned long long slot_word(unsigned long long key1,
+                                                                 unsigned i) {
+    return (key1 << kKeyShift) | ((unsigned long long)(~i) & kIdxMask);
+}
 
 // First 256 bytes of the workspace. status and distinct are result words
 // assigned by every call; the other words are zero between calls.
@@ -128,20 +142,48 @@ __device__ __forceinline__ unsigned home_slot(long long key, unsigned S, int has
     return (unsigned)__umul64hi(mix64((unsigned long long)key), (unsigned long long)S);
 }
 
-// Lookup only: slot holding key1, or -1. The table is not modified while this
-// runs (select), so plain loads see final keys.
-__device__ __forceinline__ int find_slot(const Slot* __restrict__ table, unsigned S, int hash,
-                                         long long key, unsigned* err) {
+// Lookups probe the table a cache line at a time: the 16 slots (128 bytes) of
+// the line holding the probe position come in with eight independent 16-byte
+// loads, so a probe sequence costs one memory round trip per line instead of
+// one per slot. (Inserts probe slot by slot with CAS: a line snapshot sends
+// every lane that hashes into the line to the same empty slot.) S is a
+// multiple of 16.
+constexpr unsigned kLineSlots = 16;
+
+__device__ __forceinline__ void load_line(const unsigned long long* __restrict__ table,
+                                          unsigned line_base, unsigned long long w[kLineSlots]) {
+    const uint4* q = reinterpret_cast<const uint4*>(table + line_base);
+#pragma unroll
+    for (int k = 0; k < (int)kLineSlots / 2; ++k) {
+        const uint4 v = q[k];
+        w[2 * k] = ((unsigned long long)v.y << 32) | v.x;
+        w[2 * k + 1] = ((unsigned long long)v.w << 32) | v.z;
+    }
+}
+
+// Lookup only: the word of the slot holding the key, or 0. The table is not
+// modified while this runs (select), so plain loads see final words.
+__device__ __forceinline__ unsigned long long find_word(const unsigned long long* __restrict__ table,
+                                                        unsigned S, int hash, long long key,
+                                                        unsigned* err) {
     const unsigned long long k1 = (unsigned long long)key + 1ull;
-    unsigned s = home_slot(key, S, hash);
-    for (unsigned probe = 0; probe < S; ++probe) {
-        const unsigned long long cur = table[s].key1;
-        if (cur == k1) return (int)s;
-        if (cur == 0ull) return -1;
-        s = (s + 1u == S) ? 0u : s + 1u;
+    const unsigned h = home_slot(key, S, hash);
+    unsigned base = h & ~(kLineSlots - 1u);
+    unsigned off = h - base;
+    for (unsigned probe = 0; probe < S; probe += kLineSlots) {
+        unsigned long long w[kLineSlots];
+        load_line(table, base, w);
+#pragma unroll
+        for (unsigned k = 0; k < kLineSlots; ++k) {
+            if (k < off) continue;
+            if (slot_key1(w[k]) == k1) return w[k];
+            if (w[k] == 0ull) return 0ull;
+        }
+        off = 0;
+        base = (base + kLineSlots == S) ? 0u : base + kLineSlots;
     }
     atomicOr(err, 1u);
-    return -1;
+    return 0ull;
 }
 
 __device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsigned bit) {
@@ -153,8 +195,9 @@ __device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsig
 
 __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pts,
                                                    long long begin, long long end, Grid g,
-                                                   Slot* __restrict__ table, unsigned S,
-                                                   int hash, int* __restrict__ slot_of,
+                                                   unsigned long long* __restrict__ table,
+                                                   unsigned S, int hash,
+                                                   int* __restrict__ slot_of,
                                                    Header* __restrict__ hdr, int count_claims) {
     const long long i = begin + (long long)blockIdx.x * kBlock + threadIdx.x;
     bool claimed = false;
@@ -163,34 +206,29 @@ __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pt
         const long long key = bin_key(pts[i], g);
         if (key >= 0) {
             const unsigned long long k1 = (unsigned long long)key + 1ull;
+            const unsigned long long mine = slot_word(k1, (unsigned)i);
             unsigned s = home_slot(key, S, hash);
             unsigned probe = 0;
+            // CAS first: the returned word says whether the slot was empty
+            // (now ours), holds this cell, or holds another cell (probe on).
+            // Every step reads fresh state, so lanes that collide spread out.
             for (;;) {
-                // A plain read can only be stale as 0 (keys never change once
-                // set within a call); the CAS then returns the real key.
-                unsigned long long cur = table[s].key1;
+                const unsigned long long cur = atomicCAS(&table[s], 0ull, mine);
                 if (cur == 0ull) {
-                    cur = atomicCAS(&table[s].key1, 0ull, k1);
-                    if (cur == 0ull) {
-                        claimed = true;
-                        break;
-                    }
+                    claimed = true;
+                    out = (int)s;
+                    break;
                 }
-                if (cur == k1) break;
+                if (slot_key1(cur) == k1) {
+                    if (cur < mine) atomicMax(&table[s], mine);  // lower index wins
+                    out = (int)s;
+                    break;
+                }
                 s = (s + 1u == S) ? 0u : s + 1u;
                 if (++probe >= S) {
                     atomicOr(&hdr->error, 1u);
-                    s = 0xffffffffu;
                     break;
                 }
-            }
-            if (s != 0xffffffffu) {
-                const unsigned enc = ~(unsigned)i;
-                // first only grows (atomicMax), so a stale read is never too
-                // large: skipping the atomic when it already holds a lower
-                // index is exact.
-                if (table[s].first < enc) atomicMax(&table[s].first, enc);
-                out = (int)s;
             }
         }
         slot_of[i] = out;
@@ -255,7 +293,7 @@ __device__ unsigned long long look_back(unsigned long long* tile_state, long lon
 }
 
 __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M,
-                                                 Slot* __restrict__ table,
+                                                 unsigned long long* __restrict__ table,
                                                  const int* __restrict__ slot_of,
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, int* __restrict__ occ_slot,
@@ -292,10 +330,13 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
         if (i < P) {
             const int s = slot_of[i];
             if (s >= 0) {
-                const Slot sl = table[s];
+                const unsigned long long wd = table[s];
                 slot[k] = s;
-                key1[k] = sl.key1;
-                is_first[k] = (sl.first == ~(unsigned)i);
+                key1[k] = slot_key1(wd);
+                // a kept word was tagged by the tile of its own first point,
+                // so a flagged word never marks a first occurrence here
+                is_first[k] = (wd & (kKeptFlag | kIdxMask)) ==
+                              ((unsigned long long)(~(unsigned)i) & kIdxMask);
             }
         }
         const unsigned long long b = __ballot(is_first[k]);
@@ -364,7 +405,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
         }
         occ_slot[r] = slot[k];
         if (r < M) {
-            table[slot[k]].first = (unsigned)r + 1u;  // kept: pillar id + 1
+            table[slot[k]] = (key1[k] << kKeyShift) | kKeptFlag | (unsigned long long)r;
             kept_key[r] = (long long)(key1[k] - 1ull);
         }
     }
@@ -390,8 +431,9 @@ __device__ __forceinline__ void cascade(unsigned* __restrict__ row, int K, unsig
 
 __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pts, long long N,
                                                    long long P, Grid g,
-                                                   const Slot* __restrict__ table, unsigned S,
-                                                   int hash, int* __restrict__ slot_of,
+                                                   const unsigned long long* __restrict__ table,
+                                                   unsigned S, int hash,
+                                                   int* __restrict__ slot_of,
                                                    unsigned* __restrict__ cnt,
                                                    unsigned* __restrict__ bucket, int cap,
                                                    unsigned* __restrict__ ovf, int K,
@@ -410,14 +452,15 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
         slot_of[i] = 0;  // last reader: return the word to zero for the next call
     }
     if (status <= 0) return;  // nothing kept, cap undecided, or an error
-    if (i >= P) {
+    unsigned long long wd = 0ull;
+    if (i < P) {
+        if (s >= 0) wd = table[s];
+    } else {
         const long long key = bin_key(pts[i], g);
-        s = key < 0 ? -1 : find_slot(table, S, hash, key, &hdr->error);
+        if (key >= 0) wd = find_word(table, S, hash, key, &hdr->error);
     }
-    if (s < 0) return;
-    const unsigned tag = table[s].first;
-    if (tag == 0u || (tag & 0x80000000u)) return;  // cell not among the kept pillars
-    const unsigned pid = tag - 1u;
+    if (!(wd & kKeptFlag)) return;  // no cell, or not among the kept pillars
+    const unsigned pid = (unsigned)(wd & kIdxMask);
     if (pid >= (unsigned)status) {  // cannot happen on a clean workspace
         report_error(hdr, num_voxels, 4u);
         return;
@@ -425,7 +468,7 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
     if (cap > 0) {
         const unsigned a = atomicAdd(&cnt[pid], 1u);  // one returning atomic per point
         if (a < (unsigned)cap) {
-            bucket[(size_t)pid * cap + a] = (unsigned)i;
+            bucket[(size_t)pid * cap + a] = (unsigned)i + 1u;  // 0 = empty slot
             return;
         }
     }
@@ -469,17 +512,67 @@ __device__ __forceinline__ void write_coords(int* __restrict__ coords, long long
     coords[3 * p + 2] = (int)(key % gx);
 }
 
+// One kept pillar with the whole wavefront (K <= 64): bucket of any size,
+// overflow row, bitonic ordering. Used when a pillar has more candidates than
+// its lane segment holds.
+__device__ void pack_pillar_wave(long long p, const float4* __restrict__ pts, long long N,
+                                 unsigned* __restrict__ cnt, unsigned* __restrict__ bucket,
+                                 int cap, unsigned* __restrict__ ovf, int K,
+                                 float4* __restrict__ voxels, int* __restrict__ num_points,
+                                 int* __restrict__ num_voxels, Header* __restrict__ hdr,
+                                 int lane) {
+    unsigned* bk = bucket + (size_t)p * cap;
+    const unsigned total = cnt[p];
+    const unsigned b = total < (unsigned)cap ? total : (unsigned)cap;
+    const unsigned count = total < (unsigned)K ? total : (unsigned)K;
+    unsigned best = 0xffffffffu;  // lane j: j-th lowest index so far
+    for (unsigned c0 = 0; c0 < b; c0 += kWave) {
+        const unsigned c = c0 + lane;
+        unsigned v = 0xffffffffu;
+        if (c < b) {
+            v = bk[c] - 1u;  // entries hold index + 1
+            bk[c] = 0u;
+        }
+        v = sort64(v, lane);
+        best = c0 == 0 ? v : merge64(best, v, lane);
+    }
+    if (total > (unsigned)cap) {
+        // arrivals past the bucket: their K lowest, already ascending
+        unsigned o = 0xffffffffu;
+        if (lane < K) {
+            const unsigned e = ovf[(size_t)p * K + lane];
+            if (e != 0u) {
+                o = ~e;
+                ovf[(size_t)p * K + lane] = 0u;
+            }
+        }
+        best = merge64(best, o, lane);
+    }
+    if (lane < K) {
+        float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+        if ((unsigned)lane < count) {
+            if (best < N) row = pts[best];
+            else report_error(hdr, num_voxels, 8u);
+        }
+        voxels[p * K + lane] = row;
+    }
+    if (lane == 0) {
+        num_points[p] = (int)count;
+        cnt[p] = 0u;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts, long long N,
                                                  unsigned* __restrict__ cnt,
                                                  unsigned* __restrict__ bucket, int cap,
                                                  unsigned* __restrict__ ovf, int K, int M,
-                                                 long long* __restrict__ kept_key, int gx,
-                                                 int gy, float4* __restrict__ voxels,
+                                                 int seg, long long* __restrict__ kept_key,
+                                                 int gx, int gy, float4* __restrict__ voxels,
                                                  int* __restrict__ coords,
                                                  int* __restrict__ num_points,
                                                  int* __restrict__ num_voxels,
                                                  int* __restrict__ occ_slot,
-                                                 Slot* __restrict__ table, unsigned S,
+                                                 unsigned long long* __restrict__ table, unsigned S,
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, Header* __restrict__ hdr) {
     const int status = hdr->status;
@@ -492,52 +585,79 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
     const long long gwave = gtid / kWave;
     if (gtid == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
 
-    // 1) pillars, one wavefront each: nothing else touches a pillar's
-    //    counter, bucket or overflow row, so they are read and cleared here.
-    for (long long p = gwave; p < V; p += nwaves) {
-        if (cap > 0) {
-            // K <= 64: sort the bucket, merge the overflow row, keep K lowest
-            const unsigned total = cnt[p];
-            const unsigned b = total < (unsigned)cap ? total : (unsigned)cap;
-            unsigned best = 0xffffffffu;  // lane j: j-th lowest index so far
-            unsigned* bk = bucket + (size_t)p * cap;
-            for (unsigned c0 = 0; c0 < b; c0 += kWave) {
-                const unsigned c = c0 + lane;
-                unsigned v = 0xffffffffu;
-                if (c < b) {
-                    v = bk[c];
-                    bk[c] = 0u;
-                }
-                v = sort64(v, lane);
-                best = c0 == 0 ? v : merge64(best, v, lane);
+    // 1) pillars. Nothing else touches a pillar's counter, bucket or overflow
+    //    row, so they are read and cleared here.
+    if (cap > 0) {
+        // K <= 64: a wavefront serves W = 64 / seg pillars at once, seg lanes
+        // each (seg = next power of two >= max(K, 8)). Bucket entries hold
+        // index + 1 (0 = empty), so a segment reads its first seg entries
+        // together with the counter instead of after it.
+        const int W = kWave / seg;
+        const int sidx = lane / seg;          // this lane's pillar within the pass
+        const int l = lane - sidx * seg;      // lane within the segment
+        const unsigned fit = (unsigned)(cap < seg ? cap : seg);
+        for (long long g0 = gwave * W; g0 < V; g0 += nwaves * W) {
+            const long long p = g0 + sidx;
+            const bool live = p < V;
+            unsigned raw = 0u, total = 0u;
+            if (live) {
+                if ((unsigned)l < fit) raw = bucket[(size_t)p * cap + l];
+                total = cnt[p];
             }
-            if (total > (unsigned)cap) {
-                // arrivals past the bucket: their K lowest, already ascending
-                unsigned o = 0xffffffffu;
-                if (lane < K) {
-                    const unsigned e = ovf[(size_t)p * K + lane];
-                    if (e != 0u) {
-                        o = ~e;
-                        ovf[(size_t)p * K + lane] = 0u;
+            if (__ballot(live && total > fit) == 0ull) {
+                // every pillar of the pass has at most `fit` candidates and
+                // no overflow: a lane's rank is the number of smaller
+                // candidates in its segment (indices are distinct)
+                const unsigned b = total;
+                unsigned bmax = 0;
+                for (int q = 0; q < W; ++q) {
+                    const unsigned bq = (unsigned)__builtin_amdgcn_readlane((int)b, q * seg);
+                    bmax = bq > bmax ? bq : bmax;
+                }
+                const unsigned v = raw - 1u;  // empty lanes become 0xffffffff
+                if (raw != 0u) bucket[(size_t)p * cap + l] = 0u;
+                unsigned rank = 0;
+                for (unsigned t = 0; t < bmax; ++t) {
+                    unsigned u = 0xffffffffu;
+                    for (int q = 0; q < W; ++q) {
+                        const unsigned x =
+                            (unsigned)__builtin_amdgcn_readlane((int)v, q * seg + (int)t);
+                        if (q == sidx) u = x;
+                    }
+                    rank += (t < b && u < v) ? 1u : 0u;
+                }
+                if (live) {
+                    const unsigned count = total < (unsigned)K ? total : (unsigned)K;
+                    if ((unsigned)l < b && rank < (unsigned)K) {
+                        float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (v < N) row = pts[v];
+                        else report_error(hdr, num_voxels, 8u);
+                        voxels[p * K + rank] = row;
+                    }
+                    if ((unsigned)l >= count && l < K)
+                        voxels[p * K + l] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (l == 0) {
+                        num_points[p] = (int)count;
+                        cnt[p] = 0u;
                     }
                 }
-                best = merge64(best, o, lane);
-            }
-            const unsigned count = total < (unsigned)K ? total : (unsigned)K;
-            if (lane < K) {
-                float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
-                if ((unsigned)lane < count) {
-                    if (best < N) row = pts[best];
-                    else report_error(hdr, num_voxels, 8u);
+            } else {
+                // a pillar of this pass is heavy: take them one at a time
+                for (int q = 0; q < W; ++q) {
+                    const long long pq = g0 + q;
+                    if (pq < V)
+                        pack_pillar_wave(pq, pts, N, cnt, bucket, cap, ovf, K, voxels,
+                                         num_points, num_voxels, hdr, lane);
                 }
-                voxels[p * K + lane] = row;
             }
-            if (lane == 0) {
-                num_points[p] = (int)count;
-                cnt[p] = 0u;
+            if (live && l == 0) {
+                write_coords(coords, p, kept_key[p], gx, gy);
+                kept_key[p] = 0;
             }
-        } else {
-            // K > 64: the overflow row is the whole selection, in order
+        }
+    } else {
+        // K > 64: the overflow row is the whole selection, in order
+        for (long long p = gwave; p < V; p += nwaves) {
             int count = 0;
             for (int j0 = 0; j0 < K; j0 += kWave) {
                 const int j = j0 + lane;
@@ -555,23 +675,25 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
                     voxels[p * K + j] = row;
                 }
             }
-            if (lane == 0) num_points[p] = count;
-        }
-        if (lane == 0) {
-            write_coords(coords, p, kept_key[p], gx, gy);
-            kept_key[p] = 0;
+            if (lane == 0) {
+                num_points[p] = count;
+                write_coords(coords, p, kept_key[p], gx, gy);
+                kept_key[p] = 0;
+            }
         }
     }
 
     // 2) clear every table slot this call claimed, the slot list itself, the
     //    kept keys the pillar pass did not consume, and the look-back tiles
-    const Slot zero = {0ull, 0u, 0u};
     const long long kept_written = distinct < M ? distinct : M;
     for (long long r = gtid; r < distinct; r += nthreads) {
         const int s = occ_slot[r];
         occ_slot[r] = 0;
-        if (s >= 0 && (unsigned)s < S) table[s] = zero;
-        else report_error(hdr, num_voxels, 16u);
+        if (s >= 0 && (unsigned)s < S) {
+            table[s] = 0ull;
+        } else {
+            report_error(hdr, num_voxels, 16u);
+        }
         if (r >= V && r < kept_written) kept_key[r] = 0;
     }
     for (long long r = gtid; r < ntiles; r += nthreads) tile_state[r] = 0ull;
@@ -618,11 +740,14 @@ inline int default_cap(int K) {
 }
 
 int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
-    if (N < 0 || N > 2147483647ll) return VOX_EINVAL;
+    if (N < 0 || N > kMaxPoints) return VOX_EINVAL;
     if (M < 1 || K < 1) return VOX_EINVAL;
     if ((long long)M > (1ll << 27)) return VOX_EINVAL;
     if ((long long)M * (long long)K > (1ll << 40)) return VOX_EINVAL;
-    long long S = 8ll * M;
+    // 16 slots per kept pillar and a prefix of S/4 points: inserts see a load
+    // of at most 1/4, which keeps probe chains (one atomic round trip per
+    // step) short. Only occupied slots are ever cleared, so the size is free.
+    long long S = 16ll * M;
     if (S < 64) S = 64;
     int hash = 0;
     long long P = 0;
@@ -640,9 +765,11 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         }
     }
     // S >= 2M: while fewer than M cells are in the table, a chunk of
-    // S/2 - cells >= 1 points always fits at load <= 1/2
-    if (S < 2ll * M || S > 2147483647ll) return VOX_EINVAL;
-    if (P == 0) P = S / 2;
+    // S/2 - cells >= 1 points always fits at load <= 1/2. Probing works a
+    // cache line (16 slots) at a time, so S is rounded up to a multiple of 16.
+    if (S < 2ll * M || S > 2147483647ll - 15) return VOX_EINVAL;
+    S = (S + (long long)kLineSlots - 1) / (long long)kLineSlots * (long long)kLineSlots;
+    if (P == 0) P = S / 4;
     if (P > S / 2) P = S / 2;
     if (P > N) P = N;
     pl->N = N;
@@ -657,7 +784,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->ntiles = cdiv(Nw, kRankTile);
     size_t off = sizeof(Header);
     pl->off_table = off;
-    off = align256(off + (size_t)S * sizeof(Slot));
+    off = align256(off + (size_t)S * sizeof(unsigned long long));
     pl->off_slot = off;
     off = align256(off + (size_t)Nw * sizeof(int));
     pl->off_tiles = off;
@@ -684,6 +811,9 @@ int check_grid(const float range[6], const float cell[3], const int32_t grid[3],
         if (!finite_f(cell[a]) || !(cell[a] > 0.0f)) return VOX_EINVAL;
         if (grid[a] < 1 || grid[a] > (1 << 24)) return VOX_EINVAL;
     }
+    if ((unsigned long long)grid[0] * (unsigned long long)grid[1] * (unsigned long long)grid[2] >
+        kMaxCells)
+        return VOX_EINVAL;
     g->x_min = range[0];
     g->y_min = range[1];
     g->z_min = range[2];
@@ -711,7 +841,7 @@ int check_args(const float* points, long long N, const float range[6], const flo
 
 struct Buffers {
     Header* hdr;
-    Slot* table;
+    unsigned long long* table;
     int* slot_of;
     unsigned long long* tiles;
     int* occ;
@@ -725,7 +855,7 @@ Buffers carve(void* ws, const Plan& pl) {
     char* b = static_cast<char*>(ws);
     Buffers x;
     x.hdr = reinterpret_cast<Header*>(b);
-    x.table = reinterpret_cast<Slot*>(b + pl.off_table);
+    x.table = reinterpret_cast<unsigned long long*>(b + pl.off_table);
     x.slot_of = reinterpret_cast<int*>(b + pl.off_slot);
     x.tiles = reinterpret_cast<unsigned long long*>(b + pl.off_tiles);
     x.occ = reinterpret_cast<int*>(b + pl.off_occ);
@@ -774,16 +904,20 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                 const Buffers& bf, float* voxels, int32_t* coords, int32_t* num_points,
                 int32_t* num_voxels, hipStream_t st) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
-    // one wavefront per kept pillar (at most M), and enough threads for the
-    // cleanup of at most P table slots
-    long long blocks = cdiv((long long)pl.M, kWavesPerBlock);
+    // lanes per pillar: next power of two >= max(K, 8) (a whole wave if K > 64)
+    int seg = 8;
+    while (seg < pl.K && seg < kWave) seg *= 2;
+    const long long per_wave = kWave / seg;
+    // enough wavefronts for at most M pillars, and threads for the cleanup of
+    // at most P table slots
+    long long blocks = cdiv(cdiv((long long)pl.M, per_wave), kWavesPerBlock);
     const long long clean_blocks = cdiv(P > 0 ? P : 1, kBlock);
     if (clean_blocks > blocks) blocks = clean_blocks;
     if (blocks < 1) blocks = 1;
     if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
     hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const float4*>(points), pl.N, bf.cnt, bf.bucket, pl.cap,
-                       bf.ovf, pl.K, pl.M, bf.kept, g.gx, g.gy,
+                       bf.ovf, pl.K, pl.M, seg, bf.kept, g.gx, g.gy,
                        reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
                        bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
     return last_launch();
@@ -833,6 +967,18 @@ int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_po
     const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
     if (rc != VOX_OK) return rc;
     return (int64_t)pl.bytes;
+}
+
+int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,
+             const vox_options* options, int64_t* table_slots, int64_t* prefix_points,
+             int32_t* bucket_cap) {
+    Plan pl;
+    const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
+    if (rc != VOX_OK) return rc;
+    if (table_slots) *table_slots = pl.S;
+    if (prefix_points) *prefix_points = pl.P;
+    if (bucket_cap) *bucket_cap = pl.cap;
+    return VOX_OK;
 }
 
 int voxelize_ex(const float* points, int64_t n_points, const float range[6],

@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("voxelize", "voxelize_ex", "voxelize_chunked", "vox_workspace_bytes",
               "vox_bin_points", "vox_profile_stages", "vox_strerror", "vox_last_hip_error",
-              "vox_stage_name"):
+              "vox_stage_name", "vox_plan"):
         assert n in names, n
 
 
@@ -50,7 +50,7 @@ def test_workspace_bytes_defaults_and_scaling():
     assert vox.workspace_bytes(0, 1, 1) > 0
 
 
-@pytest.mark.parametrize("args", [(-1, 10, 4), (10, 0, 4), (10, 4, 0), (2**31, 10, 4)])
+@pytest.mark.parametrize("args", [(-1, 10, 4), (10, 0, 4), (10, 4, 0), (2**30, 10, 4)])
 def test_workspace_bytes_rejects_bad_sizes(args):
     with pytest.raises(vox.VoxError):
         vox.workspace_bytes(*args)
@@ -88,6 +88,7 @@ def _call(lib, points=0x1000, n=10, rng=(0, -1, -3, 1, 1, 1), cell=(0.1, 0.1, 4)
     dict(points=0), dict(points=0x1004), dict(n=-1), dict(rng=(0, -1, -3, 0, 1, 1)),
     dict(rng=(float("nan"), -1, -3, 1, 1, 1)), dict(cell=(0.0, 0.1, 4)),
     dict(cell=(0.1, float("inf"), 4)), dict(grid=(0, 20, 1)), dict(grid=(10, 1 << 25, 1)),
+    dict(grid=(1 << 12, 1 << 12, 1 << 9)),
     dict(K=0), dict(M=0), dict(voxels=0), dict(voxels=0x2004), dict(coords=0), dict(counts=0),
     dict(nv=0), dict(ws=0),
 ])
