@@ -46,11 +46,64 @@ def parse():
                     help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
     ap.add_argument("--profile-iters", type=int, default=50)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run 10 plain device copies of this many MiB (counter calibration)")
+    ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
+                    help="only summarise rocprofv3 CSV output found under DIR (no GPU)")
     return ap.parse_args()
 
 
+def copy_probe(mib):
+    """Plain device-to-device copies of a known size: what FETCH_SIZE and
+    WRITE_SIZE read for them calibrates the counters (bytes per counted KiB)."""
+    import torch
+    n = (mib << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 10}), flush=True)
+
+
+def rocprof_summary(root):
+    """Per-kernel mean duration (kernel-trace stats) and, when present, mean
+    per-dispatch counter values, for the library's kernels and plain copies."""
+    import csv
+    import glob
+    import re
+    out = []
+    for f in sorted(glob.glob(os.path.join(root, "**", "*kernel_stats.csv"), recursive=True)):
+        out.append(f"# {os.path.relpath(f, root)}")
+        out.append(f"{'kernel':28s} {'calls':>7s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+        for r in csv.DictReader(open(f)):
+            m = re.search(r"k_(\w+?)\(", r["Name"])
+            name = "k_" + m.group(1) if m else r["Name"][:28]
+            out.append(f"{name:28s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
+                       f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
+    for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+        acc = {}
+        for r in csv.DictReader(open(f)):
+            m = re.search(r"k_(\w+?)\(", r["Kernel_Name"])
+            if m:
+                name = "k_" + m.group(1)
+            elif "copy" in r["Kernel_Name"].lower():
+                name = "copy(" + r["Grid_Size"] + ")"
+            else:
+                continue
+            key = (name, r["Counter_Name"])
+            d = acc.setdefault(key, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if acc:
+            out.append(f"# {os.path.relpath(f, root)} (mean per dispatch, summed over instances)")
+            for (name, cn), d in sorted(acc.items()):
+                vals = list(d.values())
+                out.append(f"{name:28s} {cn:24s} {sum(vals) / len(vals):14.1f}  (dispatches {len(vals)})")
+    print("\n".join(out))
+
+
 def algorithmic_bytes(N, P, V, K, rows):
-    """Compulsory bytes of the whole call and of each kernel (see DESIGN.md).
+    """Compulsory bytes of the whole call and of each kernel.
 
     whole call: read every point once (16 B) + write the dense output,
     V * (16 K + 16) bytes (rows incl. zero padding, 12 B coords, 4 B count).
@@ -62,6 +115,25 @@ def algorithmic_bytes(N, P, V, K, rows):
     out = V * (16 * K + 16)
     return dict(call=16 * N + out, insert=16 * P, rank=4 * P, select=16 * (N - P) + 4 * P,
                 pack=out + 16 * rows)
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/<workload>_traffic.txt), or None when it is missing or was taken
+    on a different library source than the one built now."""
+    import hashlib
+    src = os.path.join(ROOT, "sparse_spatial_hashing_amd", "csrc", "voxelize.hip")
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    recorded, found = None, None
+    for line in open(path):
+        if line.startswith("source_sha256:"):
+            recorded = line.split(":", 1)[1].strip()
+        if line.startswith(f"traffic k_{kernel} "):
+            found = int(line.rsplit("bytes=", 1)[1])
+    return found if recorded == sha else None
 
 
 def time_calls(vx, x, steps, warmup, torch):
@@ -131,6 +203,12 @@ def run_workload(name, steps, warmup, profile_iters, torch, vox):
 
 def main():
     args = parse()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
+    if args.copy_probe_mb:
+        copy_probe(args.copy_probe_mb)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Frames are independent, so more GPUs would "
@@ -174,7 +252,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "alg_bytes_per_launch": int(r["alg"][dom]),
-                     "launch_ms": round(dom_ms, 5), "traffic": None},
+                     "launch_ms": round(dom_ms, 5),
+                     "traffic": recorded_traffic(args.workload, dom)},
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["pts"], p, args.cpu_seconds)
