@@ -80,6 +80,10 @@ typedef struct vox_options {
     int32_t hash;           /* 0 = 64-bit mix + multiply-high reduction, 1 = key mod S */
     int32_t bucket_cap;     /* per-pillar arrival slots before the overflow row; 0 = 16 * K
                                rounded up to a multiple of 64 (K <= 64); at most 2^20 */
+    int32_t compact_table;  /* 1 = lookups past the prefix probe a small table of the
+                               kept cells (4 slots per pillar) built by rank; 0 = they
+                               probe the main table (default) */
+    int32_t reserved;
 } vox_options;
 
 /*

@@ -48,7 +48,8 @@ class VoxError(RuntimeError):
 class Options(ctypes.Structure):
     """Mirror of ``vox_options`` (0 fields mean defaults)."""
     _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
-                ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32)]
+                ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32),
+                ("compact_table", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -101,10 +102,12 @@ def _check(rc: int, what: str) -> None:
         raise VoxError(rc, what)
 
 
-def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0):
-    if not (table_slots or prefix_points or hash or bucket_cap):
+def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
+             compact_table: int = 0):
+    if not (table_slots or prefix_points or hash or bucket_cap or compact_table):
         return None
-    return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), int(bucket_cap)))
+    return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), int(bucket_cap),
+                                  int(compact_table), 0))
 
 
 def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
@@ -170,7 +173,8 @@ def _check_points(points: torch.Tensor) -> None:
 def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
              grid: Sequence[int], max_points: int, max_voxels: int, *,
              table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             chunked: bool = False, return_device_outputs: bool = False):
+             compact_table: int = 0, chunked: bool = False,
+             return_device_outputs: bool = False):
     """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
 
     Returns ``(voxels[V, K, 4] f32, coords[V, 3] i32 (z, y, x), num_points[V] i32)``
@@ -181,9 +185,9 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     _check_points(points)
     dev = points.device
     N, K, M = points.shape[0], int(max_points), int(max_voxels)
-    opts = _options(table_slots, prefix_points, hash, bucket_cap)
+    opts = _options(table_slots, prefix_points, hash, bucket_cap, compact_table)
     nbytes = workspace_bytes(N, M, K, table_slots=table_slots, prefix_points=prefix_points,
-                             hash=hash, bucket_cap=bucket_cap)
+                             hash=hash, bucket_cap=bucket_cap, compact_table=compact_table)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         ws = _workspaces.get(dev, stream, nbytes)

@@ -170,7 +170,9 @@ __device__ __forceinline__ unsigned long long find_word(const unsigned long long
     const unsigned h = home_slot(key, S, hash);
     unsigned base = h & ~(kLineSlots - 1u);
     unsigned off = h - base;
-    for (unsigned probe = 0; probe < S; probe += kLineSlots) {
+    // The first line examines slots [off, 16); after wrapping all the way
+    // round, the home line is read again whole, so its [0, off) part is seen.
+    for (unsigned seen = 0; seen < S;) {
         unsigned long long w[kLineSlots];
         load_line(table, base, w);
 #pragma unroll
@@ -179,6 +181,7 @@ __device__ __forceinline__ unsigned long long find_word(const unsigned long long
             if (slot_key1(w[k]) == k1) return w[k];
             if (w[k] == 0ull) return 0ull;
         }
+        seen += kLineSlots - off;
         off = 0;
         base = (base + kLineSlots == S) ? 0u : base + kLineSlots;
     }
@@ -294,6 +297,9 @@ __device__ unsigned long long look_back(unsigned long long* tile_state, long lon
 
 __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M,
                                                  unsigned long long* __restrict__ table,
+                                                 unsigned long long* __restrict__ compact,
+                                                 unsigned C, int hash,
+                                                 int* __restrict__ kept_cslot,
                                                  const int* __restrict__ slot_of,
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, int* __restrict__ occ_slot,
@@ -407,6 +413,22 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
         if (r < M) {
             table[slot[k]] = (key1[k] << kKeyShift) | kKeptFlag | (unsigned long long)r;
             kept_key[r] = (long long)(key1[k] - 1ull);
+            if (C > 0) {
+                // the kept cells also go into a small table that lookups past
+                // the prefix probe instead of the big one (it stays in L2)
+                const unsigned long long wd = (key1[k] << kKeyShift) | (unsigned long long)r;
+                unsigned cs = home_slot((long long)(key1[k] - 1ull), C, hash);
+                unsigned probe = 0;
+                while (atomicCAS(&compact[cs], 0ull, wd) != 0ull) {
+                    cs = (cs + 1u == C) ? 0u : cs + 1u;
+                    if (++probe >= C) {
+                        report_error(hdr, num_voxels, 32u);
+                        cs = 0xffffffffu;
+                        break;
+                    }
+                }
+                kept_cslot[r] = (int)cs;
+            }
         }
     }
 }
@@ -432,7 +454,9 @@ __device__ __forceinline__ void cascade(unsigned* __restrict__ row, int K, unsig
 __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pts, long long N,
                                                    long long P, Grid g,
                                                    const unsigned long long* __restrict__ table,
-                                                   unsigned S, int hash,
+                                                   unsigned S,
+                                                   const unsigned long long* __restrict__ compact,
+                                                   unsigned C, int hash,
                                                    int* __restrict__ slot_of,
                                                    unsigned* __restrict__ cnt,
                                                    unsigned* __restrict__ bucket, int cap,
@@ -457,7 +481,15 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
         if (s >= 0) wd = table[s];
     } else {
         const long long key = bin_key(pts[i], g);
-        if (key >= 0) wd = find_word(table, S, hash, key, &hdr->error);
+        if (key >= 0) {
+            if (C > 0) {
+                // the compact table holds only kept cells: found means kept
+                wd = find_word(compact, C, hash, key, &hdr->error);
+                if (wd != 0ull) wd |= kKeptFlag;
+            } else {
+                wd = find_word(table, S, hash, key, &hdr->error);
+            }
+        }
     }
     if (!(wd & kKeptFlag)) return;  // no cell, or not among the kept pillars
     const unsigned pid = (unsigned)(wd & kIdxMask);
@@ -562,11 +594,23 @@ __device__ void pack_pillar_wave(long long p, const float4* __restrict__ pts, lo
     }
 }
 
+// Return kept pillar r's compact-table slot and its record to zero.
+__device__ __forceinline__ void clear_compact(unsigned long long* __restrict__ compact, unsigned C,
+                                              int* __restrict__ kept_cslot, long long r,
+                                              Header* __restrict__ hdr, int* __restrict__ num_voxels) {
+    const int cs = kept_cslot[r];
+    kept_cslot[r] = 0;
+    if (cs >= 0 && (unsigned)cs < C) compact[cs] = 0ull;
+    else report_error(hdr, num_voxels, 16u);
+}
+
 __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts, long long N,
                                                  unsigned* __restrict__ cnt,
                                                  unsigned* __restrict__ bucket, int cap,
                                                  unsigned* __restrict__ ovf, int K, int M,
                                                  int seg, long long* __restrict__ kept_key,
+                                                 unsigned long long* __restrict__ compact,
+                                                 unsigned C, int* __restrict__ kept_cslot,
                                                  int gx, int gy, float4* __restrict__ voxels,
                                                  int* __restrict__ coords,
                                                  int* __restrict__ num_points,
@@ -653,6 +697,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
             if (live && l == 0) {
                 write_coords(coords, p, kept_key[p], gx, gy);
                 kept_key[p] = 0;
+                if (C > 0) clear_compact(compact, C, kept_cslot, p, hdr, num_voxels);
             }
         }
     } else {
@@ -679,6 +724,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
                 num_points[p] = count;
                 write_coords(coords, p, kept_key[p], gx, gy);
                 kept_key[p] = 0;
+                if (C > 0) clear_compact(compact, C, kept_cslot, p, hdr, num_voxels);
             }
         }
     }
@@ -694,7 +740,10 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
         } else {
             report_error(hdr, num_voxels, 16u);
         }
-        if (r >= V && r < kept_written) kept_key[r] = 0;
+        if (r >= V && r < kept_written) {
+            kept_key[r] = 0;
+            if (C > 0) clear_compact(compact, C, kept_cslot, r, hdr, num_voxels);
+        }
     }
     for (long long r = gtid; r < ntiles; r += nthreads) tile_state[r] = 0ull;
 }
@@ -724,11 +773,12 @@ inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-    long long N, P, S;
+    long long N, P, S, C;  // C: compact kept-cell table slots (0 = not used)
     int K, M, hash, cap;
     long long ntiles;
     // byte offsets into the workspace
-    size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf, bytes;
+    size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf,
+        off_compact, off_kcs, bytes;
 };
 
 inline bool finite_f(float v) { return isfinite(v); }
@@ -757,6 +807,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
             return VOX_EINVAL;
         if (opt->table_slots > 0) S = opt->table_slots;
         if (opt->hash < 0 || opt->hash > 1) return VOX_EINVAL;
+        if (opt->compact_table < 0 || opt->compact_table > 1) return VOX_EINVAL;
         hash = opt->hash;
         P = opt->prefix_points;
         if (opt->bucket_cap > 0 && K <= kSortLanes) {
@@ -779,6 +830,12 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->M = M;
     pl->hash = hash;
     pl->cap = cap;
+    // On request, rank also copies the kept cells into a table of 4 slots per
+    // pillar that lookups past the prefix probe instead of the big one (it
+    // stays in L2). Off by default: on the measured workloads the extra CAS
+    // chain in rank costs more than the lookups save.
+    pl->C = (opt && opt->compact_table == 1)
+                ? (4ll * M + kLineSlots - 1) / kLineSlots * kLineSlots : 0;
     // arrays indexed by point go to N: the chunked path can insert every point
     const long long Nw = N > 0 ? N : 1;
     pl->ntiles = cdiv(Nw, kRankTile);
@@ -799,6 +856,10 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     off = align256(off + (size_t)M * (size_t)cap * sizeof(unsigned));
     pl->off_ovf = off;
     off = align256(off + (size_t)M * (size_t)K * sizeof(unsigned));
+    pl->off_compact = off;
+    off = align256(off + (size_t)pl->C * sizeof(unsigned long long));
+    pl->off_kcs = off;
+    off = align256(off + (pl->C > 0 ? (size_t)M * sizeof(int) : 0));
     pl->bytes = off;
     return VOX_OK;
 }
@@ -849,6 +910,8 @@ struct Buffers {
     unsigned* cnt;
     unsigned* bucket;
     unsigned* ovf;
+    unsigned long long* compact;
+    int* kcs;
 };
 
 Buffers carve(void* ws, const Plan& pl) {
@@ -863,6 +926,8 @@ Buffers carve(void* ws, const Plan& pl) {
     x.cnt = reinterpret_cast<unsigned*>(b + pl.off_cnt);
     x.bucket = reinterpret_cast<unsigned*>(b + pl.off_bucket);
     x.ovf = reinterpret_cast<unsigned*>(b + pl.off_ovf);
+    x.compact = reinterpret_cast<unsigned long long*>(b + pl.off_compact);
+    x.kcs = reinterpret_cast<int*>(b + pl.off_kcs);
     return x;
 }
 
@@ -885,8 +950,8 @@ int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_vox
                 hipStream_t st) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
     hipLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, P, pl.N, pl.M,
-                       bf.table, bf.slot_of, bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr,
-                       num_voxels);
+                       bf.table, bf.compact, (unsigned)pl.C, pl.hash, bf.kcs, bf.slot_of,
+                       bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr, num_voxels);
     return last_launch();
 }
 
@@ -895,8 +960,8 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
     const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
     hipLaunchKernelGGL(k_select, dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
-                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.cnt, bf.bucket, pl.cap, bf.ovf,
-                       pl.K, bf.hdr, num_voxels);
+                       (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of, bf.cnt,
+                       bf.bucket, pl.cap, bf.ovf, pl.K, bf.hdr, num_voxels);
     return last_launch();
 }
 
@@ -917,7 +982,8 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
     if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
     hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const float4*>(points), pl.N, bf.cnt, bf.bucket, pl.cap,
-                       bf.ovf, pl.K, pl.M, seg, bf.kept, g.gx, g.gy,
+                       bf.ovf, pl.K, pl.M, seg, bf.kept, bf.compact, (unsigned)pl.C, bf.kcs,
+                       g.gx, g.gy,
                        reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
                        bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
     return last_launch();

@@ -203,7 +203,9 @@ def test_result_independent_of_table_and_hash(name):
     M = cfg.params.max_voxels
     for kw in (dict(hash=1), dict(table_slots=12 * M + 7), dict(table_slots=12 * M + 7, hash=1),
                dict(table_slots=3 * M), dict(table_slots=32 * M), dict(bucket_cap=1),
-               dict(bucket_cap=33), dict(bucket_cap=64), dict(bucket_cap=100)):
+               dict(bucket_cap=33), dict(bucket_cap=64), dict(bucket_cap=100),
+               dict(compact_table=1), dict(compact_table=1, hash=1),
+               dict(compact_table=1, bucket_cap=1)):
         say(f"invariance {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
 
@@ -216,7 +218,8 @@ def test_small_prefix_and_chunked_path(name):
     pts, _ = generate(name)
     want = oracle.voxelize_params(pts, cfg.params)
     for kw in (dict(prefix_points=4096), dict(prefix_points=1), dict(chunked=True),
-               dict(chunked=True, table_slots=2 * cfg.params.max_voxels)):
+               dict(chunked=True, table_slots=2 * cfg.params.max_voxels),
+               dict(prefix_points=4096, compact_table=1), dict(chunked=True, compact_table=1)):
         say(f"prefix/chunked {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
 
@@ -298,14 +301,17 @@ def test_max_points_variants(K):
         assert_bitwise(gpu_vox(pts, prm, bucket_cap=K), want, f"K={K} bucket_cap={K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 7, 50000])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 50000])
 def test_max_voxels_variants(M):
     cfg = get_config("kitti_frame")
     p = cfg.params
     pts, _ = generate("kitti_frame", n=20000)
     say(f"M={M}")
     prm = (p.range_, p.cell, p.grid, p.max_points, M)
-    assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), f"M={M}")
+    want = oracle.voxelize(pts, *prm)
+    assert_bitwise(gpu_vox(pts, prm), want, f"M={M}")
+    # a kept-cell table of one 16-slot line: lookups must wrap around it
+    assert_bitwise(gpu_vox(pts, prm, compact_table=1), want, f"M={M} compact")
 
 
 def test_single_cell_heavy_pillar():

@@ -67,6 +67,13 @@ def test_workspace_bytes_bucket_cap_option():
         vox.workspace_bytes(1000, 100, 32, bucket_cap=(1 << 20) + 1)
 
 
+def test_compact_table_option():
+    assert vox.workspace_bytes(1000, 100, 32, compact_table=1) > vox.workspace_bytes(1000, 100, 32)
+    assert vox.plan(1000, 100, 32)["prefix_points"] == 400   # min(N, 4 * max_voxels)
+    with pytest.raises(vox.VoxError):
+        vox.workspace_bytes(1000, 100, 32, compact_table=2)
+
+
 def test_workspace_bytes_rejects_small_table():
     with pytest.raises(vox.VoxError):
         vox.workspace_bytes(1000, 100, 4, table_slots=150)   # needs >= 2 * max_voxels
