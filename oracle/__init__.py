@@ -48,6 +48,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.oracle_voxelize.argtypes = [vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32,
                                     ctypes.c_int32, vp, vp, vp, vp]
     lib.oracle_voxelize.restype = ctypes.c_int
+    lib.oracle_voxelize_map.argtypes = [vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32,
+                                        ctypes.c_int32, vp, vp, vp, vp, vp]
+    lib.oracle_voxelize_map.restype = ctypes.c_int
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -107,6 +110,30 @@ def voxelize(points: np.ndarray, range_: Sequence[float], cell: Sequence[float],
         raise MemoryError("oracle_voxelize could not allocate its dictionary")
     V = int(nv[0])
     return voxels[:V].copy(), coords[:V].copy(), counts[:V].copy()
+
+
+def voxelize_map(points: np.ndarray, range_: Sequence[float], cell: Sequence[float],
+                 grid: Sequence[int], max_points: int, max_voxels: int,
+                 lib: Optional[ctypes.CDLL] = None):
+    """``voxelize`` plus the inverse map ``point_pillar [N] i32`` (pillar id of
+    each point's cell when that pillar is kept, else -1)."""
+    lib = lib or load()
+    p = _points(points)
+    r, c, g = _param_arrays(range_, cell, grid)
+    K, M = int(max_points), int(max_voxels)
+    if K <= 0 or M <= 0:
+        raise ValueError("max_points and max_voxels must be positive")
+    voxels = np.full((M, K, 4), 0xFFFFFFFF, dtype=np.uint32).view(np.float32)
+    coords = np.full((M, 3), -1, dtype=np.int32)
+    counts = np.full((M,), -1, dtype=np.int32)
+    pmap = np.full((p.shape[0],), -2, dtype=np.int32)
+    nv = np.zeros(1, dtype=np.int32)
+    rc = lib.oracle_voxelize_map(_ptr(p), p.shape[0], _ptr(r), _ptr(c), _ptr(g), K, M,
+                                 _ptr(voxels), _ptr(coords), _ptr(counts), _ptr(nv), _ptr(pmap))
+    if rc != 0:
+        raise MemoryError("oracle_voxelize_map could not allocate its dictionary")
+    V = int(nv[0])
+    return voxels[:V].copy(), coords[:V].copy(), counts[:V].copy(), pmap
 
 
 def voxelize_params(points: np.ndarray, params, lib: Optional[ctypes.CDLL] = None):

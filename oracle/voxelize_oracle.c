@@ -173,9 +173,30 @@ static int64_t map_slot(const key_map *m, int64_t key)
  * (z, y, x), num_points [max_voxels] int32; rows [0, V) are written, V goes to
  * *num_voxels. Returns 0, or -1 if memory for the dictionary is unavailable.
  */
+int oracle_voxelize_map(const float *points, int64_t n, const float range[6],
+                        const float cell[3], const int32_t grid[3], int32_t max_points,
+                        int32_t max_voxels, float *voxels, int32_t *coords,
+                        int32_t *num_points, int32_t *num_voxels, int32_t *point_pillar);
+
 int oracle_voxelize(const float *points, int64_t n, const float range[6], const float cell[3],
                     const int32_t grid[3], int32_t max_points, int32_t max_voxels,
                     float *voxels, int32_t *coords, int32_t *num_points, int32_t *num_voxels)
+{
+    return oracle_voxelize_map(points, n, range, cell, grid, max_points, max_voxels, voxels,
+                               coords, num_points, num_voxels, NULL);
+}
+
+/*
+ * The same operation, also writing the inverse map when point_pillar is not
+ * NULL: point_pillar[i] = the pillar id of point i's cell when that pillar is
+ * kept (whether or not the point is among the pillar's first max_points), -1
+ * for a rejected point or a point whose pillar is past the cap. The map is
+ * what a consumer needs to scatter per-point results back through the pillars.
+ */
+int oracle_voxelize_map(const float *points, int64_t n, const float range[6],
+                        const float cell[3], const int32_t grid[3], int32_t max_points,
+                        int32_t max_voxels, float *voxels, int32_t *coords,
+                        int32_t *num_points, int32_t *num_voxels, int32_t *point_pillar)
 {
     oracle_grid g = make_grid(range, cell, grid);
     const int64_t K = max_points;
@@ -194,6 +215,8 @@ int oracle_voxelize(const float *points, int64_t n, const float range[6], const 
     for (int64_t i = 0; i < n; i++) {
         const float *p = points + 4 * i;
         int64_t cx, cy, cz;
+        if (point_pillar)
+            point_pillar[i] = -1;
         if (!bin_point(p, &g, range[5], &cx, &cy, &cz))
             continue;
         int64_t key = flat_key(&g, cx, cy, cz);
@@ -214,6 +237,8 @@ int oracle_voxelize(const float *points, int64_t n, const float range[6], const 
             continue;  /* its pillar is past the max_voxels cap: dropped */
         }
 
+        if (point_pillar)
+            point_pillar[i] = (int32_t)pid;
         total[pid] += 1;
         if (total[pid] <= K) {
             /* keep the first K points of the pillar, copied bit for bit */

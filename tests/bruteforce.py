@@ -49,8 +49,9 @@ def decode(key, grid):
     return np.stack([cz, cy, cx], axis=1).astype(np.int32)
 
 
-def sort_then_segment(points, range_, cell, grid, max_points, max_voxels):
-    """Brute-force voxelization: (voxels [V,K,4], coords [V,3], counts [V])."""
+def sort_then_segment(points, range_, cell, grid, max_points, max_voxels, point_map=False):
+    """Brute-force voxelization: (voxels [V,K,4], coords [V,3], counts [V]), and
+    with point_map=True also the per-point pillar id of kept pillars (else -1)."""
     p = np.ascontiguousarray(points, dtype=F32)
     K, M = int(max_points), int(max_voxels)
     ok, key = bin_np(p, range_, cell, grid)
@@ -60,7 +61,8 @@ def sort_then_segment(points, range_, cell, grid, max_points, max_voxels):
     ks, js = k[order], idx[order]
     n = ks.size
     if n == 0:
-        return (np.zeros((0, K, 4), F32), np.zeros((0, 3), np.int32), np.zeros((0,), np.int32))
+        out = (np.zeros((0, K, 4), F32), np.zeros((0, 3), np.int32), np.zeros((0,), np.int32))
+        return out + (np.full(p.shape[0], -1, np.int32),) if point_map else out
     start_flag = np.r_[True, ks[1:] != ks[:-1]]
     starts = np.flatnonzero(start_flag)
     seg_of = np.cumsum(start_flag) - 1
@@ -79,6 +81,10 @@ def sort_then_segment(points, range_, cell, grid, max_points, max_voxels):
     counts = np.zeros((V,), np.int32)
     coords[seg_rank[kept_seg]] = decode(ks[starts[kept_seg]], grid)
     counts[seg_rank[kept_seg]] = np.minimum(seg_len[kept_seg], K)
+    if point_map:
+        pmap = np.full(p.shape[0], -1, np.int32)
+        pmap[js] = np.where(rank < V, rank, -1)
+        return voxels, coords, counts, pmap
     return voxels, coords, counts
 
 

@@ -39,6 +39,9 @@ MUTANTS = {
     "keep_last_k": [("if (total[pid] <= K) {", "{"),
                     ("(pid * K + (total[pid] - 1))", "(pid * K + (total[pid] - 1) % K)")],
     "x_min_for_y": [("(y - g->y_min) / g->vy", "(y - g->x_min) / g->vy")],
+    "map_zero_for_dropped": [("point_pillar[i] = -1;", "point_pillar[i] = 0;")],
+    "map_only_kept_rows": [("        if (point_pillar)\n            point_pillar[i] = (int32_t)pid;\n        total[pid] += 1;\n        if (total[pid] <= K) {",
+                            "        total[pid] += 1;\n        if (total[pid] <= K) {\n            if (point_pillar)\n                point_pillar[i] = (int32_t)pid;")],
 }
 
 
@@ -58,9 +61,11 @@ def _battery(lib):
         for case in hand[key]:
             pts = (np.array([[float(v) for v in r] for r in case["points"]], F32)
                    if case["points"] else np.zeros((0, 4), F32))
-            vox, coords, counts = oracle.voxelize(pts, gs["range"], gs["cell"], gs["grid"],
-                                                  case["max_points"], case["max_voxels"], lib=lib)
-            ok = coords.tolist() == case["coords"] and counts.tolist() == case["num_points"]
+            vox, coords, counts, pmap = oracle.voxelize_map(pts, gs["range"], gs["cell"],
+                                                            gs["grid"], case["max_points"],
+                                                            case["max_voxels"], lib=lib)
+            ok = (coords.tolist() == case["coords"] and counts.tolist() == case["num_points"]
+                  and pmap.tolist() == case["point_pillar"])
             if ok:
                 for p, rows in enumerate(case["rows"]):
                     for j, src in enumerate(rows):
@@ -107,8 +112,11 @@ def _battery(lib):
         cfg = get_config(name)
         pts, _ = generate(name, n=n)
         p = cfg.params
-        got = oracle.voxelize(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels, lib=lib)
-        if not _same(got, sort_then_segment(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)):
+        got = oracle.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                                  lib=lib)
+        want = sort_then_segment(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                                 point_map=True)
+        if not (_same(got[:3], want[:3]) and np.array_equal(got[3], want[3])):
             fails.append("brute:" + name)
     rng = np.random.default_rng(7)
     for t in range(40):

@@ -104,9 +104,10 @@ def test_tiny_cluster_truncated_to_lowest_indices():
 
 def _run_hand_case(case, grid_spec):
     pts = _as_points(case["points"])
-    out = oracle.voxelize(pts, grid_spec["range"], grid_spec["cell"], grid_spec["grid"],
-                          case["max_points"], case["max_voxels"])
-    vox, coords, counts = out
+    out = oracle.voxelize_map(pts, grid_spec["range"], grid_spec["cell"], grid_spec["grid"],
+                              case["max_points"], case["max_voxels"])
+    vox, coords, counts, pmap = out
+    assert pmap.tolist() == case["point_pillar"], case["name"]
     K = case["max_points"]
     V = len(case["coords"])
     assert vox.shape == (V, K, 4), case["name"]
@@ -202,9 +203,13 @@ def test_oracle_matches_sort_then_segment(name):
     cfg = get_config(name)
     pts, _ = generate(name)
     p = cfg.params
-    got = oracle.voxelize_params(pts, p)
-    want = sort_then_segment(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
-    assert_same(got, want)
+    got = oracle.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+    want = sort_then_segment(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                             point_map=True)
+    assert_same(got[:3], want[:3])
+    assert np.array_equal(got[3], want[3])
+    # the map agrees with the tensors: every listed row belongs to its pillar
+    assert got[3].max() < got[1].shape[0] and (got[3] >= -1).all()
 
 
 @st.composite
@@ -244,7 +249,10 @@ def tiny_problem(draw):
 @given(tiny_problem())
 def test_oracle_matches_sort_then_segment_fuzzed(prob):
     pts, r, c, g, K, M = prob
-    assert_same(oracle.voxelize(pts, r, c, g, K, M), sort_then_segment(pts, r, c, g, K, M))
+    got = oracle.voxelize_map(pts, r, c, g, K, M)
+    want = sort_then_segment(pts, r, c, g, K, M, point_map=True)
+    assert_same(got[:3], want[:3])
+    assert np.array_equal(got[3], want[3])
 
 
 # ---------------------------------------------------------- np.unique --------
