@@ -148,6 +148,25 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
                      hipStream_t stream, const vox_options* options);
 
 /*
+ * voxelize_ex() that also returns the inverse map, and can run the chunked
+ * path itself:
+ *   point_pillar  device int32[n_points] (4-byte aligned), or NULL: for each
+ *                 input point, the pillar id of its cell when that pillar is
+ *                 kept (whether or not the point is among the pillar's first
+ *                 max_points), else -1 (rejected point, or pillar past the cap).
+ *                 Written unless num_voxels reports a VOX_STATUS_* code.
+ *   chunked       0: single pass, asynchronous (as voxelize_ex());
+ *                 1: the chunked path (as voxelize_chunked(), synchronising).
+ * This is what a consumer needs to send per-pillar results back to points.
+ */
+int voxelize_map(const float* points, int64_t n_points, const float range[6],
+                 const float cell[3], const int32_t grid[3], int32_t max_points,
+                 int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                 int32_t* num_voxels, int32_t* point_pillar, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream, const vox_options* options,
+                 int32_t chunked);
+
+/*
  * The sizes a call would use (for reports and tests): table slots S, prefix
  * length P and bucket slots per pillar (0 when max_points > 64). Any output
  * pointer may be NULL. Returns VOX_OK or VOX_EINVAL.

@@ -69,6 +69,9 @@ def _load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = common + [op]
         f.restype = ctypes.c_int
+    lib.voxelize_map.argtypes = [vp, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp,
+                                 op, i32]
+    lib.voxelize_map.restype = ctypes.c_int
     lib.vox_plan.argtypes = [i64, i32, i32, op, vp, vp, vp]
     lib.vox_plan.restype = ctypes.c_int
     lib.vox_bin_points.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp]
@@ -173,14 +176,15 @@ def _check_points(points: torch.Tensor) -> None:
 def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
              grid: Sequence[int], max_points: int, max_voxels: int, *,
              table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             compact_table: int = 0, chunked: bool = False,
+             compact_table: int = 0, chunked: bool = False, point_map: bool = False,
              return_device_outputs: bool = False):
     """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
 
     Returns ``(voxels[V, K, 4] f32, coords[V, 3] i32 (z, y, x), num_points[V] i32)``
-    as views of freshly allocated outputs. ``chunked=True`` calls the chunked
-    entry point directly; otherwise it is used only when the single-pass call
-    reports that the cap could not be decided.
+    as views of freshly allocated outputs, and with ``point_map=True`` also
+    ``point_pillar[N] i32`` (pillar id of each point's cell when kept, else -1).
+    ``chunked=True`` calls the chunked path directly; otherwise it is used only
+    when the single-pass call reports that the cap could not be decided.
     """
     _check_points(points)
     dev = points.device
@@ -195,25 +199,26 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
         coords = torch.empty((M, 3), dtype=torch.int32, device=dev)
         counts = torch.empty((M,), dtype=torch.int32, device=dev)
         nv = torch.empty((1,), dtype=torch.int32, device=dev)
+        pmap = torch.empty((N,), dtype=torch.int32, device=dev) if point_map else None
         r, c, g = _host_params(range_, cell, grid)
         args = [ctypes.c_void_p(points.data_ptr()), N, r, c, g, K, M,
                 ctypes.c_void_p(voxels.data_ptr()), ctypes.c_void_p(coords.data_ptr()),
                 ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(nv.data_ptr()),
+                ctypes.c_void_p(pmap.data_ptr() if pmap is not None else 0),
                 ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
-                ctypes.c_void_p(stream)]
-        if chunked:
-            _check(_lib.voxelize_chunked(*args, opts), "voxelize_chunked")
-        else:
-            _check(_lib.voxelize_ex(*args, opts), "voxelize")
+                ctypes.c_void_p(stream), opts]
+        _check(_lib.voxelize_map(*args, 1 if chunked else 0), "voxelize")
         V = int(nv.item())
         if V == VOX_STATUS_NEEDS_CHUNKED and not chunked:
-            _check(_lib.voxelize_chunked(*args, opts), "voxelize_chunked")
+            _check(_lib.voxelize_map(*args, 1), "voxelize (chunked)")
             V = int(nv.item())
         if V < 0:
             _workspaces.drop(dev, stream)
             raise VoxError(V, "voxelize (device status)")
     if return_device_outputs:
         return voxels, coords, counts, nv
+    if point_map:
+        return voxels[:V], coords[:V], counts[:V], pmap
     return voxels[:V], coords[:V], counts[:V]
 
 

@@ -462,7 +462,8 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
                                                    unsigned* __restrict__ bucket, int cap,
                                                    unsigned* __restrict__ ovf, int K,
                                                    Header* __restrict__ hdr,
-                                                   int* __restrict__ num_voxels) {
+                                                   int* __restrict__ num_voxels,
+                                                   int* __restrict__ point_pillar) {
     const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         hdr->rank_ticket = 0u;  // rank is done with it
@@ -475,7 +476,10 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
         s = slot_of[i];
         slot_of[i] = 0;  // last reader: return the word to zero for the next call
     }
-    if (status <= 0) return;  // nothing kept, cap undecided, or an error
+    if (status <= 0) {  // nothing kept, cap undecided, or an error
+        if (status == 0 && point_pillar) point_pillar[i] = -1;
+        return;
+    }
     unsigned long long wd = 0ull;
     if (i < P) {
         if (s >= 0) wd = table[s];
@@ -491,12 +495,16 @@ __global__ __launch_bounds__(kBlock) void k_select(const float4* __restrict__ pt
             }
         }
     }
-    if (!(wd & kKeptFlag)) return;  // no cell, or not among the kept pillars
+    if (!(wd & kKeptFlag)) {  // no cell, or not among the kept pillars
+        if (point_pillar) point_pillar[i] = -1;
+        return;
+    }
     const unsigned pid = (unsigned)(wd & kIdxMask);
     if (pid >= (unsigned)status) {  // cannot happen on a clean workspace
         report_error(hdr, num_voxels, 4u);
         return;
     }
+    if (point_pillar) point_pillar[i] = (int)pid;  // the inverse map, when asked for
     if (cap > 0) {
         const unsigned a = atomicAdd(&cnt[pid], 1u);  // one returning atomic per point
         if (a < (unsigned)cap) {
@@ -956,12 +964,13 @@ int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_vox
 }
 
 int launch_select(const float* points, long long P, const Grid& g, const Plan& pl,
-                  const Buffers& bf, int32_t* num_voxels, hipStream_t st) {
+                  const Buffers& bf, int32_t* num_voxels, int32_t* point_pillar,
+                  hipStream_t st) {
     const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
     hipLaunchKernelGGL(k_select, dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
                        (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of, bf.cnt,
-                       bf.bucket, pl.cap, bf.ovf, pl.K, bf.hdr, num_voxels);
+                       bf.bucket, pl.cap, bf.ovf, pl.K, bf.hdr, num_voxels, point_pillar);
     return last_launch();
 }
 
@@ -1005,14 +1014,15 @@ int prepare(const float* points, int64_t n_points, const float range[6], const f
 // The four stages of one call; events (if given) are recorded between them.
 int run_pipeline(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
                  float* voxels, int32_t* coords, int32_t* num_points, int32_t* num_voxels,
-                 hipStream_t st, hipEvent_t* ev) {
+                 int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
     int rc;
     if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hip_fail(hipGetLastError());
     if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st, 0)) != VOX_OK) return rc;
     if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hip_fail(hipGetLastError());
     if ((rc = launch_rank(pl.P, pl, bf, num_voxels, st)) != VOX_OK) return rc;
     if (ev && hipEventRecord(ev[2], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_select(points, pl.P, g, pl, bf, num_voxels, st)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, pl.P, g, pl, bf, num_voxels, point_pillar, st)) != VOX_OK)
+        return rc;
     if (ev && hipEventRecord(ev[3], st) != hipSuccess) return hip_fail(hipGetLastError());
     if ((rc = launch_pack(points, pl.P, g, pl, bf, voxels, coords, num_points, num_voxels, st)) !=
         VOX_OK)
@@ -1059,8 +1069,8 @@ int voxelize_ex(const float* points, int64_t n_points, const float range[6],
                            &g, &pl);
     if (rc != VOX_OK) return rc;
     const Buffers bf = carve(workspace, pl);
-    return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, stream,
-                        nullptr);
+    return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, nullptr,
+                        stream, nullptr);
 }
 
 int voxelize(const float* points, int64_t n_points, const float range[6], const float cell[3],
@@ -1077,13 +1087,28 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
                      int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
                      int32_t* num_voxels, void* workspace, size_t workspace_bytes,
                      hipStream_t stream, const vox_options* options) {
+    return voxelize_map(points, n_points, range, cell, grid, max_points, max_voxels, voxels,
+                        coords, num_points, num_voxels, nullptr, workspace, workspace_bytes,
+                        stream, options, 1);
+}
+
+int voxelize_map(const float* points, int64_t n_points, const float range[6],
+                 const float cell[3], const int32_t grid[3], int32_t max_points,
+                 int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                 int32_t* num_voxels, int32_t* point_pillar, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream, const vox_options* options,
+                 int32_t chunked) {
     Grid g;
     Plan pl;
     int rc = prepare(points, n_points, range, cell, grid, max_points, max_voxels, voxels,
                      coords, num_points, num_voxels, workspace, workspace_bytes, options, &g,
                      &pl);
     if (rc != VOX_OK) return rc;
+    if (n_points > 0 && point_pillar && ((uintptr_t)point_pillar & 3u)) return VOX_EINVAL;
     const Buffers bf = carve(workspace, pl);
+    if (!chunked)
+        return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels,
+                            point_pillar, stream, nullptr);
     // Fill the table chunk by chunk while fewer than M cells are in it. Before
     // each chunk `have` < M cells are present, so a chunk of S/2 - have points
     // keeps the load at or below one half.
@@ -1106,7 +1131,8 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
     Plan p2 = pl;
     p2.P = done;
     if ((rc = launch_rank(done, p2, bf, num_voxels, stream)) != VOX_OK) return rc;
-    if ((rc = launch_select(points, done, g, p2, bf, num_voxels, stream)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, done, g, p2, bf, num_voxels, point_pillar, stream)) != VOX_OK)
+        return rc;
     return launch_pack(points, done, g, p2, bf, voxels, coords, num_points, num_voxels, stream);
 }
 
@@ -1152,8 +1178,8 @@ int vox_profile_stages(const float* points, int64_t n_points, const float range[
         }
     }
     for (int it = 0; rc == VOX_OK && it < iters; ++it)
-        rc = run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, stream,
-                          ev + (size_t)it * nev);
+        rc = run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, nullptr,
+                          stream, ev + (size_t)it * nev);
     if (rc == VOX_OK) {
         const hipError_t e = hipStreamSynchronize(stream);
         if (e != hipSuccess) rc = hip_fail(e);

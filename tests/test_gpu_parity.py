@@ -190,7 +190,23 @@ def test_seeded_fuzz_small_problems():
     for t in range(120):
         pts, prm = _random_problem(rng)
         say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]}")
-        assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), f"fuzz {t}")
+        got = gpu_vox(pts, prm, point_map=True)
+        want = oracle.voxelize_map(pts, *prm)
+        assert_bitwise(got[:3], want[:3], f"fuzz {t}")
+        assert np.array_equal(got[3], want[3]), f"fuzz {t}: point map differs"
+
+
+@pytest.mark.parametrize("name", config_names())
+def test_point_map_parity(name):
+    """The inverse map: each point's kept pillar id, or -1."""
+    cfg = get_config(name)
+    pts, _ = generate(name)
+    say(f"point map {name}")
+    got = gpu_vox(pts, params_of(cfg), point_map=True)
+    p = cfg.params
+    want = oracle.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+    assert_bitwise(got[:3], want[:3], name)
+    assert np.array_equal(got[3], want[3]), f"{name}: point map differs"
 
 
 # ------------------------------------------------- invariance / options -----
@@ -222,6 +238,13 @@ def test_small_prefix_and_chunked_path(name):
                dict(prefix_points=4096, compact_table=1), dict(chunked=True, compact_table=1)):
         say(f"prefix/chunked {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
+    p = cfg.params
+    want_map = oracle.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)[3]
+    for kw in (dict(prefix_points=1000, point_map=True), dict(chunked=True, point_map=True)):
+        say(f"prefix/chunked map {name} {kw}")
+        got = gpu_vox(pts, params_of(cfg), **kw)
+        assert_bitwise(got[:3], want, f"{name} {kw}")
+        assert np.array_equal(got[3], want_map), f"{name} {kw}: point map differs"
 
 
 def test_needs_chunked_status_is_reported_and_workspace_stays_clean():

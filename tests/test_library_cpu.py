@@ -25,7 +25,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("voxelize", "voxelize_ex", "voxelize_chunked", "vox_workspace_bytes",
               "vox_bin_points", "vox_profile_stages", "vox_strerror", "vox_last_hip_error",
-              "vox_stage_name", "vox_plan"):
+              "vox_stage_name", "vox_plan", "voxelize_map"):
         assert n in names, n
 
 
