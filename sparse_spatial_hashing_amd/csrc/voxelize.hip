@@ -142,10 +142,10 @@ __device__ __forceinline__ unsigned home_slot(long long key, unsigned S, int has
     return (unsigned)__umul64hi(mix64((unsigned long long)key), (unsigned long long)S);
 }
 
-// Lookups probe the table a cache line at a time: the 16 slots (128 bytes) of
-// the line holding the probe position come in with eight independent 16-byte
-// loads, so a probe sequence costs one memory round trip per line instead of
-// one per slot. (Inserts probe slot by slot with CAS: a line snapshot sends
+// Lookups read the aligned slot pair holding the home slot first (16 bytes);
+// when that does not settle it, they probe a cache line at a time: the 16
+// slots (128 bytes) of the line come in with eight independent 16-byte loads,
+// so a probe sequence costs one memory round trip per line, not per slot. (Inserts probe slot by slot with CAS: a line snapshot sends
 // every lane that hashes into the line to the same empty slot.) S is a
 // multiple of 16.
 constexpr unsigned kLineSlots = 16;
@@ -168,6 +168,22 @@ __device__ __forceinline__ unsigned long long find_word(const unsigned long long
                                                         unsigned* err) {
     const unsigned long long k1 = (unsigned long long)key + 1ull;
     const unsigned h = home_slot(key, S, hash);
+    {
+        // At the insert load (at most 1/4) the aligned pair holding the home
+        // slot nearly always settles the lookup: one 16-byte load
+        const uint4 q = *reinterpret_cast<const uint4*>(table + (h & ~1u));
+        const unsigned long long w0 = ((unsigned long long)q.y << 32) | q.x;
+        const unsigned long long w1 = ((unsigned long long)q.w << 32) | q.z;
+        if (h & 1u) {
+            if (slot_key1(w1) == k1) return w1;
+            if (w1 == 0ull) return 0ull;
+        } else {
+            if (slot_key1(w0) == k1) return w0;
+            if (w0 == 0ull) return 0ull;
+            if (slot_key1(w1) == k1) return w1;
+            if (w1 == 0ull) return 0ull;
+        }
+    }
     unsigned base = h & ~(kLineSlots - 1u);
     unsigned off = h - base;
     // The first line examines slots [off, 16); after wrapping all the way
