@@ -77,13 +77,19 @@ typedef struct vox_options {
                                a multiple of 16 (one 128-byte line) */
     int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N, S/4);
                                at most S/2 (and N) */
-    int32_t hash;           /* 0 = 64-bit mix + multiply-high reduction, 1 = key mod S */
+    int32_t hash;           /* home slot: 0 = key folded to 32 bits times 0x9E3779B1, then a
+                               multiply-high reduction to [0, S); 1 = key mod S; 2 = a
+                               64-bit mixer, then the same reduction */
     int32_t bucket_cap;     /* per-pillar arrival slots before the overflow row; 0 = 16 * K
                                rounded up to a multiple of 64 (K <= 64); at most 2^20 */
     int32_t compact_table;  /* 1 = lookups past the prefix probe a small table of the
                                kept cells (4 slots per pillar) built by rank; 0 = they
                                probe the main table (default) */
-    int32_t reserved;
+    int32_t select_path;    /* route from lookups to rows: 0 = automatic (partitioned when
+                               K <= 64 and max_voxels <= 524288, buckets otherwise),
+                               1 = per-pillar buckets filled by one device atomic per
+                               point, 2 = partitioned by pillar-id bins in LDS (EINVAL
+                               outside those limits). The output is the same. */
 } vox_options;
 
 /*
@@ -168,7 +174,8 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
 
 /*
  * The sizes a call would use (for reports and tests): table slots S, prefix
- * length P and bucket slots per pillar (0 when max_points > 64). Any output
+ * length P and bucket slots per pillar (0 when max_points > 64 or when the
+ * partitioned select path is taken, which has no buckets). Any output
  * pointer may be NULL. Returns VOX_OK or VOX_EINVAL.
  */
 int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,

@@ -49,7 +49,7 @@ class Options(ctypes.Structure):
     """Mirror of ``vox_options`` (0 fields mean defaults)."""
     _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
                 ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32),
-                ("compact_table", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("compact_table", ctypes.c_int32), ("select_path", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -106,11 +106,11 @@ def _check(rc: int, what: str) -> None:
 
 
 def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             compact_table: int = 0):
-    if not (table_slots or prefix_points or hash or bucket_cap or compact_table):
+             compact_table: int = 0, select_path: int = 0):
+    if not (table_slots or prefix_points or hash or bucket_cap or compact_table or select_path):
         return None
     return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), int(bucket_cap),
-                                  int(compact_table), 0))
+                                  int(compact_table), int(select_path)))
 
 
 def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
@@ -176,8 +176,8 @@ def _check_points(points: torch.Tensor) -> None:
 def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
              grid: Sequence[int], max_points: int, max_voxels: int, *,
              table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             compact_table: int = 0, chunked: bool = False, point_map: bool = False,
-             return_device_outputs: bool = False):
+             compact_table: int = 0, select_path: int = 0, chunked: bool = False,
+             point_map: bool = False, return_device_outputs: bool = False):
     """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
 
     Returns ``(voxels[V, K, 4] f32, coords[V, 3] i32 (z, y, x), num_points[V] i32)``
@@ -189,9 +189,10 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     _check_points(points)
     dev = points.device
     N, K, M = points.shape[0], int(max_points), int(max_voxels)
-    opts = _options(table_slots, prefix_points, hash, bucket_cap, compact_table)
-    nbytes = workspace_bytes(N, M, K, table_slots=table_slots, prefix_points=prefix_points,
-                             hash=hash, bucket_cap=bucket_cap, compact_table=compact_table)
+    kw = dict(table_slots=table_slots, prefix_points=prefix_points, hash=hash,
+              bucket_cap=bucket_cap, compact_table=compact_table, select_path=select_path)
+    opts = _options(**kw)
+    nbytes = workspace_bytes(N, M, K, **kw)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         ws = _workspaces.get(dev, stream, nbytes)

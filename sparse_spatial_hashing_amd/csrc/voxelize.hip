@@ -136,10 +136,17 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long k) {
     return k;
 }
 
+// hash 0: multiplicative (Fibonacci) hashing of the key folded to 32 bits,
+//         then a multiply-high range reduction (a few instructions; grid keys
+//         of neighbouring cells land far apart);
+// hash 1: key mod S;
+// hash 2: a 64-bit mixer, then the same reduction.
 __device__ __forceinline__ unsigned home_slot(long long key, unsigned S, int hash) {
     if (hash == 1) return (unsigned)((unsigned long long)key % S);
-    // multiply-high range reduction: no 64-bit modulo
-    return (unsigned)__umul64hi(mix64((unsigned long long)key), (unsigned long long)S);
+    if (hash == 2)
+        return (unsigned)__umul64hi(mix64((unsigned long long)key), (unsigned long long)S);
+    const unsigned h = ((unsigned)key ^ (unsigned)((unsigned long long)key >> 32)) * 0x9E3779B1u;
+    return __umulhi(h, S);
 }
 
 // Lookups read the aligned slot pair holding the home slot first (16 bytes);
@@ -161,29 +168,33 @@ __device__ __forceinline__ void load_line(const unsigned long long* __restrict__
     }
 }
 
-// Lookup only: the word of the slot holding the key, or 0. The table is not
-// modified while this runs (select), so plain loads see final words.
-__device__ __forceinline__ unsigned long long find_word(const unsigned long long* __restrict__ table,
-                                                        unsigned S, int hash, long long key,
-                                                        unsigned* err) {
-    const unsigned long long k1 = (unsigned long long)key + 1ull;
-    const unsigned h = home_slot(key, S, hash);
-    {
-        // At the insert load (at most 1/4) the aligned pair holding the home
-        // slot nearly always settles the lookup: one 16-byte load
-        const uint4 q = *reinterpret_cast<const uint4*>(table + (h & ~1u));
-        const unsigned long long w0 = ((unsigned long long)q.y << 32) | q.x;
-        const unsigned long long w1 = ((unsigned long long)q.w << 32) | q.z;
-        if (h & 1u) {
-            if (slot_key1(w1) == k1) return w1;
-            if (w1 == 0ull) return 0ull;
-        } else {
-            if (slot_key1(w0) == k1) return w0;
-            if (w0 == 0ull) return 0ull;
-            if (slot_key1(w1) == k1) return w1;
-            if (w1 == 0ull) return 0ull;
-        }
+// The aligned pair holding the home slot h, as one 16-byte load. At the
+// insert load (at most 1/4) it nearly always settles a lookup.
+__device__ __forceinline__ uint4 load_pair(const unsigned long long* __restrict__ table,
+                                           unsigned h) {
+    return *reinterpret_cast<const uint4*>(table + (h & ~1u));
+}
+
+// True when the pair settles the lookup of k1 (= key + 1): *out is then the
+// word holding the key, or 0 when an empty slot ends the probe first.
+__device__ __forceinline__ bool pair_settles(uint4 q, unsigned h, unsigned long long k1,
+                                             unsigned long long* out) {
+    const unsigned long long w0 = ((unsigned long long)q.y << 32) | q.x;
+    const unsigned long long w1 = ((unsigned long long)q.w << 32) | q.z;
+    if (!(h & 1u)) {
+        if (slot_key1(w0) == k1) { *out = w0; return true; }
+        if (w0 == 0ull) { *out = 0ull; return true; }
     }
+    if (slot_key1(w1) == k1) { *out = w1; return true; }
+    if (w1 == 0ull) { *out = 0ull; return true; }
+    return false;
+}
+
+// Lookup only, probing line by line from the home slot h. The table is not
+// modified while lookups run, so plain loads see final words.
+__device__ __forceinline__ unsigned long long find_word_lines(
+    const unsigned long long* __restrict__ table, unsigned S, unsigned h, unsigned long long k1,
+    unsigned* err) {
     unsigned base = h & ~(kLineSlots - 1u);
     unsigned off = h - base;
     // The first line examines slots [off, 16); after wrapping all the way
@@ -203,6 +214,17 @@ __device__ __forceinline__ unsigned long long find_word(const unsigned long long
     }
     atomicOr(err, 1u);
     return 0ull;
+}
+
+// Lookup only: the word of the slot holding the key, or 0.
+__device__ __forceinline__ unsigned long long find_word(const unsigned long long* __restrict__ table,
+                                                        unsigned S, int hash, long long key,
+                                                        unsigned* err) {
+    const unsigned long long k1 = (unsigned long long)key + 1ull;
+    const unsigned h = home_slot(key, S, hash);
+    unsigned long long wd;
+    if (pair_settles(load_pair(table, h), h, k1, &wd)) return wd;
+    return find_word_lines(table, S, h, k1, err);
 }
 
 __device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsigned bit) {
@@ -628,6 +650,36 @@ __device__ __forceinline__ void clear_compact(unsigned long long* __restrict__ c
     else report_error(hdr, num_voxels, 16u);
 }
 
+// Clears every table slot the call claimed (through the list rank wrote),
+// the list itself, the kept keys of ids past V that no pillar pass consumed,
+// and the look-back tiles: grid-stride over the calling kernel's threads.
+__device__ __forceinline__ void release_workspace(long long gtid, long long nthreads,
+                                                  long long distinct, long long V, int M,
+                                                  int* __restrict__ occ_slot,
+                                                  unsigned long long* __restrict__ table,
+                                                  unsigned S, long long* __restrict__ kept_key,
+                                                  unsigned long long* __restrict__ compact,
+                                                  unsigned C, int* __restrict__ kept_cslot,
+                                                  unsigned long long* __restrict__ tile_state,
+                                                  long long ntiles, Header* __restrict__ hdr,
+                                                  int* __restrict__ num_voxels) {
+    const long long kept_written = distinct < M ? distinct : M;
+    for (long long r = gtid; r < distinct; r += nthreads) {
+        const int s = occ_slot[r];
+        occ_slot[r] = 0;
+        if (s >= 0 && (unsigned)s < S) {
+            table[s] = 0ull;
+        } else {
+            report_error(hdr, num_voxels, 16u);
+        }
+        if (r >= V && r < kept_written) {
+            kept_key[r] = 0;
+            if (C > 0) clear_compact(compact, C, kept_cslot, r, hdr, num_voxels);
+        }
+    }
+    for (long long r = gtid; r < ntiles; r += nthreads) tile_state[r] = 0ull;
+}
+
 __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts, long long N,
                                                  unsigned* __restrict__ cnt,
                                                  unsigned* __restrict__ bucket, int cap,
@@ -753,23 +805,452 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
         }
     }
 
-    // 2) clear every table slot this call claimed, the slot list itself, the
-    //    kept keys the pillar pass did not consume, and the look-back tiles
-    const long long kept_written = distinct < M ? distinct : M;
-    for (long long r = gtid; r < distinct; r += nthreads) {
-        const int s = occ_slot[r];
-        occ_slot[r] = 0;
-        if (s >= 0 && (unsigned)s < S) {
-            table[s] = 0ull;
-        } else {
-            report_error(hdr, num_voxels, 16u);
+    // 2) return the rest of the workspace to zero
+    release_workspace(gtid, nthreads, distinct, V, M, occ_slot, table, S, kept_key, compact, C,
+                      kept_cslot, tile_state, ntiles, hdr, num_voxels);
+}
+
+// ------------------------------------------------- partitioned select/pack --
+//
+// For K <= 64 and up to kMaxBins * 128 pillars, select and pack avoid the
+// per-point counter atomic (device atomics run at a fixed rate beyond the
+// L2) and any sorting. Pillar ids are dealt to nbins bins round-robin (bin =
+// id mod nbins), at most G = 2^gshift per bin: ids follow first occurrence,
+// so the dense cells that come first spread over all bins.
+//   k_part  one block per tile of 256-4096 points finds each point's pillar
+//           (as select does) and writes the tile's kept points to its stretch
+//           of a staging array, bin after bin, as one 32-bit word each (id
+//           within the bin << 16 | index within the tile). Inside a bin's run
+//           the words are in index order: each wavefront owns a contiguous
+//           stretch of the tile, ranks its lanes among equal bins with
+//           ballots, and the wavefronts take the LDS bin counters in turn.
+//           The start and length of every bin's run in the tile go to a
+//           [bins x tiles] count table.
+//   k_bins  one block per bin reads the bin's runs tile after tile, so each
+//           pillar's points arrive in index order: a point's rank in its
+//           pillar is the number of earlier arrivals with the same id
+//           (ballots within the wavefront, a per-wavefront prefix in LDS and
+//           a running count per pillar), and ranks below K are the rows.
+//           Each staging word and count entry is zeroed by its reader.
+// The rows are those of the bucket path bit for bit; only the route differs.
+
+constexpr int kPartMaxPer = 16;                // points per k_part thread, at most
+constexpr int kPartBatch = 8;                  // lookups in flight per thread
+constexpr int kMaxBins = 4096;                 // bins per call (LDS histogram)
+constexpr int kBinsPerThread = kMaxBins / kBlock;
+constexpr int kBinBlock = 1024;                // k_bins threads (16 wavefronts)
+constexpr int kBinWaves = kBinBlock / kWave;
+constexpr unsigned kNoPid = 0xffffffffu;
+
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const unsigned o = (unsigned)__shfl_up((int)v, d);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the block (NW wavefronts); *total gets the sum.
+// wsum is an LDS array of NW words. Contains two barriers.
+template <int NW>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, unsigned* total) {
+    const int lane = __lane_id();
+    const int w = threadIdx.x / kWave;
+    const unsigned incl = wave_incl_scan(v, lane);
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    unsigned off = 0, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+        const unsigned x = wsum[ww];
+        if (ww < w) off += x;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + incl - v;
+}
+
+// Block bid of a grid of n blocks -> tile: XCD x = bid % 8 takes the
+// contiguous tiles [x q + min(x, r), ...) with q = n / 8, r = n % 8 (a
+// bijection onto [0, n)).
+__device__ __forceinline__ long long xcd_tile(long long bid, long long n) {
+    const long long q = n / 8, r = n % 8;
+    const long long x = bid % 8, y = bid / 8;
+    return x * q + (x < r ? x : r) + y;
+}
+
+// Lanes of the wavefront whose value v (nbits low bits) equals this lane's,
+// among the lanes with `valid` set: one ballot per bit. Every lane calls it.
+__device__ __forceinline__ unsigned long long match_mask(unsigned v, bool valid, int nbits) {
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = ((v >> b) & 1u) != 0u;
+        const unsigned long long bb = __ballot(valid && bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+__device__ __forceinline__ unsigned long long lanes_below(int lane) {
+    return (1ull << lane) - 1ull;
+}
+__device__ __forceinline__ unsigned long long lanes_above(int lane) {
+    return ~((2ull << lane) - 1ull);  // lane 63: 2 << 63 wraps to 0, mask 0
+}
+
+// PER points per thread: wavefront w of the block takes the contiguous
+// points [base + 64 PER w, base + 64 PER (w + 1)), 64 at a time. Lookups go
+// PER_B at a time: within a batch every load is issued before any result is
+// used, and only block-uniform branches guard them.
+template <int PER>
+__global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts, long long N,
+                                                 long long P, Grid g,
+                                                 const unsigned long long* __restrict__ table,
+                                                 unsigned S,
+                                                 const unsigned long long* __restrict__ compact,
+                                                 unsigned C, int hash, int* __restrict__ slot_of,
+                                                 int nbits, long long ptiles,
+                                                 unsigned* __restrict__ cm,
+                                                 unsigned* __restrict__ staging,
+                                                 Header* __restrict__ hdr,
+                                                 int* __restrict__ num_voxels,
+                                                 int* __restrict__ point_pillar) {
+    constexpr int TILE = kBlock * PER;
+    constexpr int PER_B = PER < kPartBatch ? PER : kPartBatch;
+    __shared__ unsigned hist[kMaxBins];
+    __shared__ unsigned wsum[kWavesPerBlock];
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = t / kWave;
+    // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+    // range of tiles, so that neighbouring count-table words (one row per
+    // bin, one word per tile) are written through the same L2.
+    const long long tile = xcd_tile(blockIdx.x, ptiles);
+    const long long base = tile * TILE;
+    const long long wbase = base + (long long)w * (kWave * PER);
+    if (blockIdx.x == 0 && t == 0) {
+        hdr->rank_ticket = 0u;  // rank is done with it
+        if (hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    }
+    const int status = hdr->status;
+    const int nbins = 1 << nbits;
+    const unsigned bmask = (unsigned)nbins - 1u;
+    const int nb = status > 0 ? nbins : 0;
+    for (int b = t; b < nb; b += kBlock) hist[b] = 0u;
+    __syncthreads();
+
+    // lookups go to the kept-cell table when there is one (found = kept)
+    const unsigned long long* __restrict__ look = C > 0 ? compact : table;
+    const unsigned LS = C > 0 ? C : S;
+    const bool any_prefix = base < P;                              // block-uniform
+    const bool any_rest = status > 0 && base + TILE > P && base < N;
+    unsigned pid[PER];
+#pragma unroll
+    for (int k0 = 0; k0 < PER; k0 += PER_B) {
+        unsigned long long wd[PER_B];
+        long long ii[PER_B];
+#pragma unroll
+        for (int k = 0; k < PER_B; ++k) {
+            ii[k] = wbase + (long long)(k0 + k) * kWave + lane;
+            wd[k] = 0ull;
         }
-        if (r >= V && r < kept_written) {
-            kept_key[r] = 0;
-            if (C > 0) clear_compact(compact, C, kept_cslot, r, hdr, num_voxels);
+        if (any_prefix) {
+            // prefix points: the slot insert recorded, then its word
+            int sl[PER_B];
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) sl[k] = slot_of[ii[k] < P ? ii[k] : P - 1];
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k)
+                if (ii[k] < P) slot_of[ii[k]] = 0;  // last reader: back to zero
+            if (status > 0) {
+                unsigned long long w[PER_B];
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k) {
+                    const bool ok = ii[k] < P && sl[k] >= 0 && (unsigned)sl[k] < S;
+                    w[k] = table[ok ? sl[k] : 0];
+                    if (!ok) w[k] = 0ull;
+                }
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    if (ii[k] < P) wd[k] = w[k];
+            }
+        }
+        if (any_rest) {
+            // later points: bin, then probe the home pair, then (rarely) lines
+            float4 pt[PER_B];
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) pt[k] = pts[ii[k] < N ? ii[k] : N - 1];
+            long long key[PER_B];
+            unsigned h[PER_B];
+            uint4 q[PER_B];
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) {
+                key[k] = (ii[k] >= P && ii[k] < N) ? bin_key(pt[k], g) : -1;
+                h[k] = home_slot(key[k] >= 0 ? key[k] : 0, LS, hash);
+                q[k] = load_pair(look, h[k]);
+            }
+            // Lookups the home pair does not settle go on pair by pair; all
+            // of the batch's pending probes are issued together each round.
+            bool pend[PER_B];
+            unsigned cur[PER_B], seen[PER_B];
+            unsigned long long w[PER_B];
+            bool any = false;
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) {
+                w[k] = 0ull;
+                pend[k] = false;
+                cur[k] = 0u;
+                seen[k] = 0u;
+                if (key[k] >= 0) {
+                    const unsigned long long k1 = (unsigned long long)key[k] + 1ull;
+                    if (!pair_settles(q[k], h[k], k1, &w[k])) {
+                        pend[k] = true;
+                        any = true;
+                        const unsigned nx = (h[k] | 1u) + 1u;  // next aligned pair
+                        cur[k] = nx == LS ? 0u : nx;
+                        seen[k] = 2u - (h[k] & 1u);
+                    }
+                }
+            }
+            while (__ballot(any) != 0ull) {
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    if (pend[k]) q[k] = load_pair(look, cur[k]);
+                any = false;
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k) {
+                    if (!pend[k]) continue;
+                    const unsigned long long k1 = (unsigned long long)key[k] + 1ull;
+                    // cur is even: the pair's slots are checked in probe order
+                    if (pair_settles(q[k], cur[k], k1, &w[k])) {
+                        pend[k] = false;
+                        continue;
+                    }
+                    seen[k] += 2u;
+                    if (seen[k] >= LS) {  // every slot seen: cannot happen
+                        atomicOr(&hdr->error, 1u);
+                        w[k] = 0ull;
+                        pend[k] = false;
+                        continue;
+                    }
+                    cur[k] = cur[k] + 2u == LS ? 0u : cur[k] + 2u;
+                    any = true;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) {
+                if (key[k] >= 0) {
+                    if (C > 0 && w[k] != 0ull) w[k] |= kKeptFlag;
+                    wd[k] = w[k];
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PER_B; ++k) {
+            const long long i = ii[k];
+            unsigned p = kNoPid;
+            if (wd[k] & kKeptFlag) {
+                const unsigned v = (unsigned)(wd[k] & kIdxMask);
+                if (v < (unsigned)status) p = v;
+                else report_error(hdr, num_voxels, 4u);  // not on a clean workspace
+            }
+            if (point_pillar && i < N && status >= 0) point_pillar[i] = p == kNoPid ? -1 : (int)p;
+            pid[k0 + k] = p;
         }
     }
-    for (long long r = gtid; r < ntiles; r += nthreads) tile_state[r] = 0ull;
+
+    // Rank among equal bins: within the wavefront by ballots, then the
+    // wavefronts take the LDS counters in turn (points are in index order
+    // along (wavefront, k, lane)).
+    unsigned pos[PER], grp[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const bool valid = pid[k] != kNoPid;
+        const unsigned bin = valid ? pid[k] & bmask : 0u;
+        const unsigned long long m = match_mask(bin, valid, nbits);
+        pos[k] = (unsigned)__popcll(m & lanes_below(lane));
+        grp[k] = (valid && (m & lanes_above(lane)) == 0ull) ? (unsigned)__popcll(m) : 0u;
+    }
+    for (int ww = 0; ww < kWavesPerBlock; ++ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                if (pid[k] == kNoPid) continue;
+                const unsigned bin = pid[k] & bmask;
+                const unsigned before = hist[bin];  // the whole group reads first,
+                pos[k] += before;
+                if (grp[k] != 0u) hist[bin] = before + grp[k];  // then its last lane adds
+            }
+        }
+        __syncthreads();
+    }
+
+    // bin starts within the tile; each thread owns kBinsPerThread bins
+    unsigned c[kBinsPerThread];
+    unsigned mine = 0;
+#pragma unroll
+    for (int q = 0; q < kBinsPerThread; ++q) {
+        const int b = t * kBinsPerThread + q;
+        c[q] = b < nb ? hist[b] : 0u;
+        mine += c[q];
+    }
+    unsigned total;
+    unsigned run = block_excl_scan<kWavesPerBlock>(mine, wsum, &total);
+#pragma unroll
+    for (int q = 0; q < kBinsPerThread; ++q) {
+        const int b = t * kBinsPerThread + q;
+        if (b < nb) {
+            cm[(size_t)b * ptiles + tile] = run | (c[q] << 16);
+            hist[b] = run;
+        }
+        run += c[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (pid[k] == kNoPid) continue;
+        const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);  // in the tile
+        const unsigned bin = pid[k] & bmask;
+        const unsigned id = pid[k] >> nbits;  // id within the bin
+        staging[base + hist[bin] + pos[k]] = (id << 16) | local;
+    }
+}
+
+__global__ __launch_bounds__(kBinBlock) void k_bins(
+    const float4* __restrict__ pts, long long N, unsigned* __restrict__ cm,
+    unsigned* __restrict__ staging, long long ptiles, int ptile, int gshift, int nbits, int K,
+    int M, long long* __restrict__ kept_key, unsigned long long* __restrict__ compact, unsigned C,
+    int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ voxels,
+    int* __restrict__ coords, int* __restrict__ num_points, int* __restrict__ num_voxels,
+    int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
+    unsigned long long* __restrict__ tile_state, long long ntiles, Header* __restrict__ hdr) {
+    extern __shared__ unsigned lds[];
+    const int G = 1 << gshift;
+    unsigned* running = lds;                     // [G] arrivals so far per pillar
+    unsigned* wcnt = running + G;                // [kBinWaves * G] per-wavefront counts
+    unsigned* roff = wcnt + kBinWaves * G;       // [kBinBlock + 1] run offsets in the group
+    unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock] run start within its tile
+    unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
+    unsigned* best = wsum + kBinWaves;           // [G * K] the K lowest indices, in order
+
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = t / kWave;
+    const int status = hdr->status;
+    const long long V = status > 0 ? status : 0;
+    const long long distinct = hdr->distinct;
+    const long long b = blockIdx.x;
+    if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+
+    // bin b holds the ids b, b + nbins, b + 2 nbins, ... below V
+    const long long nbins = 1ll << nbits;
+    if (status > 0) {
+        const int Gb = b < V ? (int)((V - b + nbins - 1) >> nbits) : 0;
+        for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
+        for (int x = t; x < kBinWaves * G; x += kBinBlock) wcnt[x] = 0u;
+        for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
+            // this group's runs: tile tg + t holds one of length e >> 16
+            const long long tt = tg + t;
+            unsigned e = 0u;
+            if (tt < ptiles) {
+                e = cm[(size_t)b * ptiles + tt];
+                cm[(size_t)b * ptiles + tt] = 0u;  // last reader
+            }
+            unsigned ng;
+            const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
+            roff[t] = ro;
+            rsrc[t] = e & 0xffffu;
+            const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+            __syncthreads();
+            // arrivals in order, kBinBlock at a time: arrival x of the group
+            // lies in the last run whose offset is <= x
+            for (unsigned x0 = 0; x0 < ng; x0 += kBinBlock) {
+                const unsigned x = x0 + (unsigned)t;
+                bool valid = x < ng;
+                unsigned pl = 0u, idx = 0u;
+                if (valid) {
+                    int lo = 0, hi = nruns;
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (roff[mid] <= x) lo = mid;
+                        else hi = mid;
+                    }
+                    const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
+                    const unsigned v = staging[src];
+                    staging[src] = 0u;  // last reader
+                    pl = v >> 16;
+                    idx = (unsigned)((tg + lo) * ptile) + (v & 0xffffu);
+                    if (pl >= (unsigned)Gb) {  // not on a clean workspace
+                        report_error(hdr, num_voxels, 4u);
+                        valid = false;
+                        pl = 0u;
+                    }
+                }
+                const unsigned long long m = match_mask(pl, valid, gshift);
+                const unsigned rank = (unsigned)__popcll(m & lanes_below(lane));
+                if (valid && (m & lanes_above(lane)) == 0ull) wcnt[w * G + pl] = (unsigned)__popcll(m);
+                __syncthreads();
+                if (t < G) {
+                    // exclusive prefix over the wavefronts, on top of the
+                    // arrivals of earlier rounds
+                    unsigned acc = running[t];
+                    for (int ww = 0; ww < kBinWaves; ++ww) {
+                        const unsigned cw = wcnt[ww * G + t];
+                        wcnt[ww * G + t] = acc;
+                        acc += cw;
+                    }
+                    running[t] = acc;
+                }
+                __syncthreads();
+                if (valid) {
+                    const unsigned r = wcnt[w * G + pl] + rank;
+                    if (r < (unsigned)K) best[pl * K + r] = idx;
+                }
+                __syncthreads();
+                for (int y = t; y < kBinWaves * G; y += kBinBlock) wcnt[y] = 0u;
+                __syncthreads();
+            }
+        }
+        // rows: the selection in index order, then zero padding; a pillar's K
+        // rows are contiguous
+        const int rows = Gb * K;
+        for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
+            float4 row[4];
+            int xx[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                xx[u] = x0 + u * kBinBlock + t;
+                row[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (xx[u] < rows) {
+                    const int p = xx[u] / K;
+                    const int r = xx[u] - p * K;
+                    if ((unsigned)r < running[p]) {
+                        const unsigned v = best[p * K + r];
+                        if (v < N) row[u] = pts[v];
+                        else report_error(hdr, num_voxels, 8u);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (xx[u] >= rows) continue;
+                const int p = xx[u] / K;
+                voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)] = row[u];
+            }
+        }
+        for (int p = t; p < Gb; p += kBinBlock) {
+            const long long pp = b + ((long long)p << nbits);
+            num_points[pp] = (int)(running[p] < (unsigned)K ? running[p] : (unsigned)K);
+            write_coords(coords, pp, kept_key[pp], gx, gy);
+            kept_key[pp] = 0;
+            if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
+        }
+    }
+    const long long nthreads = (long long)gridDim.x * kBinBlock;
+    release_workspace(b * kBinBlock + t, nthreads, distinct, V, M, occ_slot, table, S, kept_key,
+                      compact, C, kept_cslot, tile_state, ntiles, hdr, num_voxels);
 }
 
 // -------------------------------------------------------------- bin only --
@@ -800,10 +1281,21 @@ struct Plan {
     long long N, P, S, C;  // C: compact kept-cell table slots (0 = not used)
     int K, M, hash, cap;
     long long ntiles;
+    // partitioned select/pack (part = 1): bins of 2^gshift pillar ids, ptiles
+    // k_part tiles of 256 pper points, nbits = bits of a bin number, lds bytes
+    // of a k_bins block
+    int part, gshift, nbins, nbits, pper;
+    long long ptiles;
+    size_t lds;
     // byte offsets into the workspace
     size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf,
-        off_compact, off_kcs, bytes;
+        off_compact, off_kcs, off_cm, off_stage, bytes;
 };
+
+// LDS of one k_bins block for bins of G pillars
+inline size_t bins_lds_bytes(int G, int K) {
+    return 4u * (size_t)(G + kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + G * K);
+}
 
 inline bool finite_f(float v) { return isfinite(v); }
 
@@ -830,8 +1322,9 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         if (opt->table_slots < 0 || opt->prefix_points < 0 || opt->bucket_cap < 0)
             return VOX_EINVAL;
         if (opt->table_slots > 0) S = opt->table_slots;
-        if (opt->hash < 0 || opt->hash > 1) return VOX_EINVAL;
+        if (opt->hash < 0 || opt->hash > 2) return VOX_EINVAL;
         if (opt->compact_table < 0 || opt->compact_table > 1) return VOX_EINVAL;
+        if (opt->select_path < 0 || opt->select_path > 2) return VOX_EINVAL;
         hash = opt->hash;
         P = opt->prefix_points;
         if (opt->bucket_cap > 0 && K <= kSortLanes) {
@@ -853,7 +1346,6 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->K = K;
     pl->M = M;
     pl->hash = hash;
-    pl->cap = cap;
     // On request, rank also copies the kept cells into a table of 4 slots per
     // pillar that lookups past the prefix probe instead of the big one (it
     // stays in L2). Off by default: on the measured workloads the extra CAS
@@ -863,6 +1355,36 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     // arrays indexed by point go to N: the chunked path can insert every point
     const long long Nw = N > 0 ? N : 1;
     pl->ntiles = cdiv(Nw, kRankTile);
+    // Select/pack route: per-bin partition (no per-point device atomic) when
+    // K <= 64 and the ids fit kMaxBins bins of at most 128; buckets otherwise.
+    const int path = opt ? opt->select_path : 0;
+    const bool part_ok = K <= kSortLanes && cdiv(M, 128) <= kMaxBins;
+    if (path == 2 && !part_ok) return VOX_EINVAL;
+    pl->part = (path == 2 || (path == 0 && part_ok)) ? 1 : 0;
+    pl->gshift = 0;
+    pl->nbins = 0;
+    pl->nbits = 0;
+    pl->pper = 0;
+    pl->ptiles = 0;
+    pl->lds = 0;
+    if (pl->part) {
+        // a power-of-two number of bins, about M / 64 (M / 128 past 32768
+        // pillars), and G = 2^gshift >= the ids one bin can hold
+        const long long want = cdiv(M, M > 32768 ? 128 : 64);
+        while ((1ll << pl->nbits) < want) ++pl->nbits;
+        pl->nbins = 1 << pl->nbits;
+        const long long per_bin = cdiv(M, pl->nbins);
+        while ((1ll << pl->gshift) < per_bin) ++pl->gshift;
+        pl->lds = bins_lds_bytes(1 << pl->gshift, K);  // at most 50 KB (G = 128, K = 64)
+        // points per k_part thread: the largest power of two up to 16 that
+        // still gives about 1024 tiles (small clouds spread over every CU)
+        int per = 1;
+        while (per < kPartMaxPer && Nw >= (long long)per * 2 * kBlock * 1024) per *= 2;
+        pl->pper = per;
+        pl->ptiles = cdiv(Nw, (long long)kBlock * per);
+        cap = 0;  // no buckets
+    }
+    pl->cap = cap;
     size_t off = sizeof(Header);
     pl->off_table = off;
     off = align256(off + (size_t)S * sizeof(unsigned long long));
@@ -875,15 +1397,19 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->off_kept = off;
     off = align256(off + (size_t)M * sizeof(long long));
     pl->off_cnt = off;
-    off = align256(off + (size_t)M * sizeof(unsigned));
+    off = align256(off + (pl->part ? 0 : (size_t)M * sizeof(unsigned)));
     pl->off_bucket = off;
     off = align256(off + (size_t)M * (size_t)cap * sizeof(unsigned));
     pl->off_ovf = off;
-    off = align256(off + (size_t)M * (size_t)K * sizeof(unsigned));
+    off = align256(off + (pl->part ? 0 : (size_t)M * (size_t)K * sizeof(unsigned)));
     pl->off_compact = off;
     off = align256(off + (size_t)pl->C * sizeof(unsigned long long));
     pl->off_kcs = off;
     off = align256(off + (pl->C > 0 ? (size_t)M * sizeof(int) : 0));
+    pl->off_cm = off;
+    off = align256(off + (size_t)pl->nbins * (size_t)pl->ptiles * sizeof(unsigned));
+    pl->off_stage = off;
+    off = align256(off + (size_t)pl->ptiles * (size_t)(kBlock * pl->pper) * sizeof(unsigned));
     pl->bytes = off;
     return VOX_OK;
 }
@@ -936,6 +1462,8 @@ struct Buffers {
     unsigned* ovf;
     unsigned long long* compact;
     int* kcs;
+    unsigned* cm;
+    unsigned* stage;
 };
 
 Buffers carve(void* ws, const Plan& pl) {
@@ -952,6 +1480,8 @@ Buffers carve(void* ws, const Plan& pl) {
     x.ovf = reinterpret_cast<unsigned*>(b + pl.off_ovf);
     x.compact = reinterpret_cast<unsigned long long*>(b + pl.off_compact);
     x.kcs = reinterpret_cast<int*>(b + pl.off_kcs);
+    x.cm = reinterpret_cast<unsigned*>(b + pl.off_cm);
+    x.stage = reinterpret_cast<unsigned*>(b + pl.off_stage);
     return x;
 }
 
@@ -982,6 +1512,22 @@ int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_vox
 int launch_select(const float* points, long long P, const Grid& g, const Plan& pl,
                   const Buffers& bf, int32_t* num_voxels, int32_t* point_pillar,
                   hipStream_t st) {
+    if (pl.part) {
+        decltype(&k_part<1>) kern = &k_part<1>;
+        switch (pl.pper) {
+            case 2: kern = &k_part<2>; break;
+            case 4: kern = &k_part<4>; break;
+            case 8: kern = &k_part<8>; break;
+            case 16: kern = &k_part<16>; break;
+            default: break;
+        }
+        hipLaunchKernelGGL(kern, dim3((unsigned)pl.ptiles), dim3(kBlock), 0, st,
+                           reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
+                           (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of,
+                           pl.nbits, pl.ptiles, bf.cm, bf.stage, bf.hdr, num_voxels,
+                           point_pillar);
+        return last_launch();
+    }
     const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
     hipLaunchKernelGGL(k_select, dim3(blocks), dim3(kBlock), 0, st,
                        reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
@@ -994,6 +1540,17 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                 const Buffers& bf, float* voxels, int32_t* coords, int32_t* num_points,
                 int32_t* num_voxels, hipStream_t st) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
+    if (pl.part) {
+        // one block per bin; all blocks share the workspace release
+        hipLaunchKernelGGL(k_bins, dim3((unsigned)pl.nbins), dim3(kBinBlock), pl.lds, st,
+                           reinterpret_cast<const float4*>(points), pl.N, bf.cm, bf.stage,
+                           pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.K, pl.M,
+                           bf.kept, bf.compact,
+                           (unsigned)pl.C, bf.kcs, g.gx, g.gy,
+                           reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
+                           bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
+        return last_launch();
+    }
     // lanes per pillar: next power of two >= max(K, 8) (a whole wave if K > 64)
     int seg = 8;
     while (seg < pl.K && seg < kWave) seg *= 2;

@@ -189,8 +189,10 @@ def test_seeded_fuzz_small_problems():
     rng = np.random.default_rng(2024)
     for t in range(120):
         pts, prm = _random_problem(rng)
-        say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]}")
-        got = gpu_vox(pts, prm, point_map=True)
+        # both select routes: every third case takes the bucket route
+        path = 1 if t % 3 == 1 else 0
+        say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]} path={path}")
+        got = gpu_vox(pts, prm, point_map=True, select_path=path)
         want = oracle.voxelize_map(pts, *prm)
         assert_bitwise(got[:3], want[:3], f"fuzz {t}")
         assert np.array_equal(got[3], want[3]), f"fuzz {t}: point map differs"
@@ -217,11 +219,15 @@ def test_result_independent_of_table_and_hash(name):
     pts, _ = generate(name)
     want = oracle.voxelize_params(pts, cfg.params)
     M = cfg.params.max_voxels
-    for kw in (dict(hash=1), dict(table_slots=12 * M + 7), dict(table_slots=12 * M + 7, hash=1),
-               dict(table_slots=3 * M), dict(table_slots=32 * M), dict(bucket_cap=1),
-               dict(bucket_cap=33), dict(bucket_cap=64), dict(bucket_cap=100),
+    for kw in (dict(hash=1), dict(hash=2), dict(table_slots=12 * M + 7),
+               dict(table_slots=12 * M + 7, hash=1), dict(table_slots=12 * M + 7, hash=2),
+               dict(table_slots=3 * M), dict(table_slots=32 * M), dict(select_path=1),
+               dict(select_path=1, bucket_cap=1), dict(select_path=1, bucket_cap=33),
+               dict(select_path=1, bucket_cap=64), dict(select_path=1, bucket_cap=100),
                dict(compact_table=1), dict(compact_table=1, hash=1),
-               dict(compact_table=1, bucket_cap=1)):
+               dict(select_path=1, compact_table=1, bucket_cap=1),
+               dict(select_path=2, table_slots=3 * M, hash=1),
+               dict(select_path=1, table_slots=3 * M, hash=2)):
         say(f"invariance {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
 
@@ -235,12 +241,14 @@ def test_small_prefix_and_chunked_path(name):
     want = oracle.voxelize_params(pts, cfg.params)
     for kw in (dict(prefix_points=4096), dict(prefix_points=1), dict(chunked=True),
                dict(chunked=True, table_slots=2 * cfg.params.max_voxels),
-               dict(prefix_points=4096, compact_table=1), dict(chunked=True, compact_table=1)):
+               dict(prefix_points=4096, compact_table=1), dict(chunked=True, compact_table=1),
+               dict(chunked=True, select_path=1)):
         say(f"prefix/chunked {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
     p = cfg.params
     want_map = oracle.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)[3]
-    for kw in (dict(prefix_points=1000, point_map=True), dict(chunked=True, point_map=True)):
+    for kw in (dict(prefix_points=1000, point_map=True), dict(chunked=True, point_map=True),
+               dict(chunked=True, point_map=True, select_path=1)):
         say(f"prefix/chunked map {name} {kw}")
         got = gpu_vox(pts, params_of(cfg), **kw)
         assert_bitwise(got[:3], want, f"{name} {kw}")
@@ -320,8 +328,10 @@ def test_max_points_variants(K):
     want = oracle.voxelize(pts, *prm)
     assert_bitwise(gpu_vox(pts, prm), want, f"K={K}")
     if K <= 64:
+        assert_bitwise(gpu_vox(pts, prm, select_path=1), want, f"K={K} buckets")
         # a small bucket sends most arrivals of the heavy pillars to the overflow row
-        assert_bitwise(gpu_vox(pts, prm, bucket_cap=K), want, f"K={K} bucket_cap={K}")
+        assert_bitwise(gpu_vox(pts, prm, select_path=1, bucket_cap=K), want,
+                       f"K={K} bucket_cap={K}")
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 50000])
@@ -333,6 +343,7 @@ def test_max_voxels_variants(M):
     prm = (p.range_, p.cell, p.grid, p.max_points, M)
     want = oracle.voxelize(pts, *prm)
     assert_bitwise(gpu_vox(pts, prm), want, f"M={M}")
+    assert_bitwise(gpu_vox(pts, prm, select_path=1), want, f"M={M} buckets")
     # a kept-cell table of one 16-slot line: lookups must wrap around it
     assert_bitwise(gpu_vox(pts, prm, compact_table=1), want, f"M={M} compact")
 
@@ -348,4 +359,26 @@ def test_single_cell_heavy_pillar():
     pts[:, 3] = np.arange(n, dtype=F32)
     prm = ((0.0, -39.68, -3.0, 69.12, 39.68, 1.0), (0.16, 0.16, 4.0), (432, 496, 1), 32, 12000)
     say("single heavy cell")
-    assert_bitwise(gpu_vox(pts, prm), oracle.voxelize(pts, *prm), "heavy cell")
+    want = oracle.voxelize(pts, *prm)
+    assert_bitwise(gpu_vox(pts, prm), want, "heavy cell")
+    assert_bitwise(gpu_vox(pts, prm, select_path=1), want, "heavy cell, buckets")
+
+
+@pytest.mark.parametrize("per_cell,K", [(70, 64), (200, 32), (40, 5)])
+def test_bin_spanning_several_chunks(per_cell, K):
+    """64 cells that share one pillar-id bin, with more candidates than one
+    LDS chunk holds: later chunks merge into the selection of earlier ones."""
+    rng = np.random.default_rng(per_cell)
+    cells = np.arange(64)
+    n = 64 * per_cell
+    cid = rng.permutation(np.repeat(cells, per_cell))
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = ((cid % 8) * 1.0 + rng.uniform(0.05, 0.95, n)).astype(F32)
+    pts[:, 1] = ((cid // 8) * 1.0 + rng.uniform(0.05, 0.95, n)).astype(F32)
+    pts[:, 2] = F32(0.5)
+    pts[:, 3] = np.arange(n, dtype=F32)
+    prm = ((0.0, 0.0, 0.0, 8.0, 8.0, 1.0), (1.0, 1.0, 1.0), (8, 8, 1), K, 64)
+    say(f"multi-chunk bin per_cell={per_cell} K={K}")
+    want = oracle.voxelize(pts, *prm)
+    assert_bitwise(gpu_vox(pts, prm, select_path=2), want, "multi-chunk bin")
+    assert_bitwise(gpu_vox(pts, prm, select_path=1), want, "multi-chunk bin, buckets")

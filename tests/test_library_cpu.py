@@ -57,8 +57,8 @@ def test_workspace_bytes_rejects_bad_sizes(args):
 
 
 def test_workspace_bytes_bucket_cap_option():
-    base = vox.workspace_bytes(1000, 100, 32)
-    small = vox.workspace_bytes(1000, 100, 32, bucket_cap=64)
+    base = vox.workspace_bytes(1000, 100, 32, select_path=1)
+    small = vox.workspace_bytes(1000, 100, 32, select_path=1, bucket_cap=64)
     assert small < base          # default bucket is 16 K = 512 slots per pillar
     assert vox.workspace_bytes(1000, 100, 100) > 0   # K > 64 has no bucket
     with pytest.raises(vox.VoxError):
@@ -121,3 +121,30 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         vox.voxelize(torch.zeros((4, 4)), (0, 0, 0, 1, 1, 1), (0.1, 0.1, 1), (10, 10, 1), 4, 8)
+
+
+def test_select_path_option_limits():
+    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 524288)."""
+    auto = vox.workspace_bytes(100000, 60000, 32)
+    assert auto == vox.workspace_bytes(100000, 60000, 32, select_path=2)
+    assert auto != vox.workspace_bytes(100000, 60000, 32, select_path=1)
+    assert vox.plan(100000, 60000, 32)["bucket_cap"] == 0          # no buckets
+    assert vox.plan(100000, 60000, 32, select_path=1)["bucket_cap"] == 512
+    assert vox.workspace_bytes(1000, 524288, 32, select_path=2) > 0
+    # K > 64 or more than 524288 pillars: only the bucket route exists
+    assert vox.plan(1000, 100, 65)["bucket_cap"] == 0
+    for bad in (dict(select_path=-1), dict(select_path=3)):
+        with pytest.raises(vox.VoxError):
+            vox.workspace_bytes(1000, 100, 32, **bad)
+    for args in ((1000, 100, 65), (1000, 524289, 32)):
+        assert vox.workspace_bytes(*args) > 0
+        with pytest.raises(vox.VoxError):
+            vox.workspace_bytes(*args, select_path=2)
+
+
+def test_hash_option_range():
+    for h in (0, 1, 2):
+        assert vox.workspace_bytes(1000, 100, 32, hash=h) > 0
+    for h in (-1, 3):
+        with pytest.raises(vox.VoxError):
+            vox.workspace_bytes(1000, 100, 32, hash=h)
