@@ -77,14 +77,14 @@ def rocprof_summary(root):
         out.append(f"# {os.path.relpath(f, root)}")
         out.append(f"{'kernel':28s} {'calls':>7s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s}")
         for r in csv.DictReader(open(f)):
-            m = re.search(r"k_(\w+?)\(", r["Name"])
+            m = re.search(r"k_(\w+?(?:<\d+>)?)\(", r["Name"])
             name = "k_" + m.group(1) if m else r["Name"][:28]
             out.append(f"{name:28s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
                        f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
     for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
         acc = {}
         for r in csv.DictReader(open(f)):
-            m = re.search(r"k_(\w+?)\(", r["Kernel_Name"])
+            m = re.search(r"k_(\w+?(?:<\d+>)?)\(", r["Kernel_Name"])
             if m:
                 name = "k_" + m.group(1)
             elif "copy" in r["Kernel_Name"].lower():
@@ -102,25 +102,30 @@ def rocprof_summary(root):
     print("\n".join(out))
 
 
-def algorithmic_bytes(N, P, V, K, rows):
+def algorithmic_bytes(N, P, V, K, rows, kept, partitioned):
     """Compulsory bytes of the whole call and of each kernel.
 
     whole call: read every point once (16 B) + write the dense output,
     V * (16 K + 16) bytes (rows incl. zero padding, 12 B coords, 4 B count).
     insert: its share of the input read, 16 B per prefix point.
     rank:   4 B per prefix point (the slot index written by insert).
-    select: 16 B per point past the prefix + 4 B per prefix point (slot).
-    pack:   the dense output + 16 B per kept row gathered from the input.
+    select: 16 B per point past the prefix + 4 B per prefix point (slot);
+            the partitioned route also writes one 4-byte staging word per
+            point of a kept pillar (`kept` of them).
+    pack:   the dense output + 16 B per kept row gathered from the input;
+            the partitioned route also reads the staging words back.
     """
     out = V * (16 * K + 16)
-    return dict(call=16 * N + out, insert=16 * P, rank=4 * P, select=16 * (N - P) + 4 * P,
-                pack=out + 16 * rows)
+    stage = 4 * kept if partitioned else 0
+    return dict(call=16 * N + out, insert=16 * P, rank=4 * P,
+                select=16 * (N - P) + 4 * P + stage, pack=out + 16 * rows + stage)
 
 
-def recorded_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/<workload>_traffic.txt), or None when it is missing or was taken
-    on a different library source than the one built now."""
+def recorded_traffic(workload, stage):
+    """HBM bytes per launch of the kernel running `stage` from the committed
+    counter summary (profiles/<workload>_traffic.txt), or None when it is
+    missing or was taken on a different library source than the one built
+    now."""
     import hashlib
     src = os.path.join(ROOT, "sparse_spatial_hashing_amd", "csrc", "voxelize.hip")
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
@@ -131,7 +136,7 @@ def recorded_traffic(workload, kernel):
     for line in open(path):
         if line.startswith("source_sha256:"):
             recorded = line.split(":", 1)[1].strip()
-        if line.startswith(f"traffic k_{kernel} "):
+        if line.startswith(f"traffic {stage} "):
             found = int(line.rsplit("bytes=", 1)[1])
     return found if recorded == sha else None
 
@@ -195,10 +200,18 @@ def run_workload(name, steps, warmup, profile_iters, torch, vox):
     rows = int(vx.num_points[:max(V, 0)].sum().item()) if V > 0 else 0
     parity = check_parity(vx, pts, p)
     stage_ms, total_ms = vx.profile(x, profile_iters)
-    P = vox.plan(N, p.max_voxels, p.max_points)["prefix_points"]
-    alg = algorithmic_bytes(N, P, V, p.max_points, rows)
+    pl = vox.plan(N, p.max_voxels, p.max_points)
+    P = pl["prefix_points"]
+    partitioned = p.max_points <= 64 and pl["bucket_cap"] == 0
+    pmap = vox.voxelize(x, p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                        point_map=True)[3]
+    kept = int((pmap >= 0).sum().item())
+    alg = algorithmic_bytes(N, P, V, p.max_points, rows, kept, partitioned)
+    kernels = dict(insert="k_insert", rank="k_rank",
+                   select="k_part" if partitioned else "k_select",
+                   pack="k_bins" if partitioned else "k_pack")
     return dict(cfg=cfg, pts=pts, N=N, V=V, rows=rows, ms=ms, parity=parity, stage_ms=stage_ms,
-                total_ms=total_ms, alg=alg, P=P)
+                total_ms=total_ms, alg=alg, P=P, kept=kept, kernels=kernels)
 
 
 def main():
@@ -248,7 +261,8 @@ def main():
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "parity_vs_oracle": r["parity"],
         "stages_ms": {k: round(v, 5) for k, v in r["stage_ms"].items()},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": r["kernels"][dom], "stage": dom,
+                     "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "alg_bytes_per_launch": int(r["alg"][dom]),

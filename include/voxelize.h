@@ -86,7 +86,8 @@ typedef struct vox_options {
                                kept cells (4 slots per pillar) built by rank; 0 = they
                                probe the main table (default) */
     int32_t select_path;    /* route from lookups to rows: 0 = automatic (partitioned when
-                               K <= 64 and max_voxels <= 524288, buckets otherwise),
+                               K <= 64 and max_voxels <= 262144, or <= 131072 when
+                               K > 32; buckets otherwise),
                                1 = per-pillar buckets filled by one device atomic per
                                point, 2 = partitioned by pillar-id bins in LDS (EINVAL
                                outside those limits). The output is the same. */
@@ -194,9 +195,11 @@ int vox_bin_points(const float* points, int64_t n_points, const float range[6],
 
 /*
  * Stage timing for the benchmark: runs voxelize_ex() `iters` times on
- * `stream` with a HIP event between consecutive kernels and writes the mean
- * milliseconds of each stage to stage_ms[0..VOX_NUM_STAGES) (insert, rank,
- * select, pack) and of the whole call to *total_ms. Synchronises `stream`.
+ * `stream`, each kernel launched with a start and a stop event that the HIP
+ * runtime stamps at the kernel's own start and end (hipExtLaunchKernel), and
+ * writes the mean milliseconds of each stage's kernel to
+ * stage_ms[0..VOX_NUM_STAGES) (insert, rank, select, pack) and from the first
+ * kernel's start to the last one's end to *total_ms. Synchronises `stream`.
  */
 #define VOX_NUM_STAGES 4
 int vox_profile_stages(const float* points, int64_t n_points, const float range[6],

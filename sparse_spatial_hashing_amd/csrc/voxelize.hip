@@ -45,6 +45,7 @@
 // implementation of "Binning a point".
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <math.h>
 #include <stdint.h>
@@ -812,9 +813,9 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 
 // ------------------------------------------------- partitioned select/pack --
 //
-// For K <= 64 and up to kMaxBins * 128 pillars, select and pack avoid the
-// per-point counter atomic (device atomics run at a fixed rate beyond the
-// L2) and any sorting. Pillar ids are dealt to nbins bins round-robin (bin =
+// For K <= 64 and up to kMaxBins * 128 pillars (kMaxBins * 64 when K > 32),
+// select and pack avoid the per-point counter atomic (device atomics run at
+// a fixed rate beyond the L2) and any sorting. Pillar ids are dealt to nbins bins round-robin (bin =
 // id mod nbins), at most G = 2^gshift per bin: ids follow first occurrence,
 // so the dense cells that come first spread over all bins.
 //   k_part  one block per tile of 256-4096 points finds each point's pillar
@@ -823,7 +824,8 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 //           within the bin << 16 | index within the tile). Inside a bin's run
 //           the words are in index order: each wavefront owns a contiguous
 //           stretch of the tile, ranks its lanes among equal bins with
-//           ballots, and the wavefronts take the LDS bin counters in turn.
+//           ballots and its own LDS histogram, and the per-bin scan places
+//           the wavefronts' stretches one after another.
 //           The start and length of every bin's run in the tile go to a
 //           [bins x tiles] count table.
 //   k_bins  one block per bin reads the bin's runs tile after tile, so each
@@ -835,8 +837,8 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 // The rows are those of the bucket path bit for bit; only the route differs.
 
 constexpr int kPartMaxPer = 16;                // points per k_part thread, at most
-constexpr int kPartBatch = 8;                  // lookups in flight per thread
-constexpr int kMaxBins = 4096;                 // bins per call (LDS histogram)
+constexpr int kPartBatch = 4;                  // lookups in flight per thread
+constexpr int kMaxBins = 2048;                 // bins per call (k_part: one LDS histogram per wavefront)
 constexpr int kBinsPerThread = kMaxBins / kBlock;
 constexpr int kBinBlock = 1024;                // k_bins threads (16 wavefronts)
 constexpr int kBinWaves = kBinBlock / kWave;
@@ -919,7 +921,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                                                  int* __restrict__ point_pillar) {
     constexpr int TILE = kBlock * PER;
     constexpr int PER_B = PER < kPartBatch ? PER : kPartBatch;
-    __shared__ unsigned hist[kMaxBins];
+    __shared__ unsigned hist[kWavesPerBlock][kMaxBins];  // one histogram per wavefront
     __shared__ unsigned wsum[kWavesPerBlock];
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -938,7 +940,10 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
     const int nbins = 1 << nbits;
     const unsigned bmask = (unsigned)nbins - 1u;
     const int nb = status > 0 ? nbins : 0;
-    for (int b = t; b < nb; b += kBlock) hist[b] = 0u;
+    for (int b = t; b < nb; b += kBlock) {
+#pragma unroll
+        for (int ww = 0; ww < kWavesPerBlock; ++ww) hist[ww][b] = 0u;
+    }
     __syncthreads();
 
     // lookups go to the kept-cell table when there is one (found = kept)
@@ -1061,39 +1066,37 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         }
     }
 
-    // Rank among equal bins: within the wavefront by ballots, then the
-    // wavefronts take the LDS counters in turn (points are in index order
-    // along (wavefront, k, lane)).
-    unsigned pos[PER], grp[PER];
+    // Rank among equal bins inside this wavefront's stretch, in index order
+    // (k, then lane): ballots within the step, the wavefront's own LDS
+    // histogram across steps.
+    unsigned pos[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const bool valid = pid[k] != kNoPid;
         const unsigned bin = valid ? pid[k] & bmask : 0u;
         const unsigned long long m = match_mask(bin, valid, nbits);
-        pos[k] = (unsigned)__popcll(m & lanes_below(lane));
-        grp[k] = (valid && (m & lanes_above(lane)) == 0ull) ? (unsigned)__popcll(m) : 0u;
-    }
-    for (int ww = 0; ww < kWavesPerBlock; ++ww) {
-        if (w == ww) {
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                if (pid[k] == kNoPid) continue;
-                const unsigned bin = pid[k] & bmask;
-                const unsigned before = hist[bin];  // the whole group reads first,
-                pos[k] += before;
-                if (grp[k] != 0u) hist[bin] = before + grp[k];  // then its last lane adds
-            }
+        pos[k] = 0u;
+        if (valid) {
+            const unsigned before = hist[w][bin];  // the whole group reads first,
+            pos[k] = before + (unsigned)__popcll(m & lanes_below(lane));
+            if ((m & lanes_above(lane)) == 0ull)    // then its last lane adds
+                hist[w][bin] = before + (unsigned)__popcll(m);
         }
-        __syncthreads();
     }
+    __syncthreads();
 
-    // bin starts within the tile; each thread owns kBinsPerThread bins
+    // bin starts within the tile, then each wavefront's start within its bin;
+    // each thread owns kBinsPerThread bins
     unsigned c[kBinsPerThread];
     unsigned mine = 0;
 #pragma unroll
     for (int q = 0; q < kBinsPerThread; ++q) {
         const int b = t * kBinsPerThread + q;
-        c[q] = b < nb ? hist[b] : 0u;
+        c[q] = 0u;
+        if (b < nb) {
+#pragma unroll
+            for (int ww = 0; ww < kWavesPerBlock; ++ww) c[q] += hist[ww][b];
+        }
         mine += c[q];
     }
     unsigned total;
@@ -1103,7 +1106,13 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         const int b = t * kBinsPerThread + q;
         if (b < nb) {
             cm[(size_t)b * ptiles + tile] = run | (c[q] << 16);
-            hist[b] = run;
+            unsigned at = run;
+#pragma unroll
+            for (int ww = 0; ww < kWavesPerBlock; ++ww) {
+                const unsigned cw = hist[ww][b];
+                hist[ww][b] = at;
+                at += cw;
+            }
         }
         run += c[q];
     }
@@ -1114,11 +1123,13 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);  // in the tile
         const unsigned bin = pid[k] & bmask;
         const unsigned id = pid[k] >> nbits;  // id within the bin
-        staging[base + hist[bin] + pos[k]] = (id << 16) | local;
+        staging[base + hist[w][bin] + pos[k]] = (id << 16) | local;
     }
 }
 
-__global__ __launch_bounds__(kBinBlock) void k_bins(
+// At most 64 VGPRs: two 1024-thread blocks per CU.
+__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8)))
+void k_bins(
     const float4* __restrict__ pts, long long N, unsigned* __restrict__ cm,
     unsigned* __restrict__ staging, long long ptiles, int ptile, int gshift, int nbits, int K,
     int M, long long* __restrict__ kept_key, unsigned long long* __restrict__ compact, unsigned C,
@@ -1129,8 +1140,8 @@ __global__ __launch_bounds__(kBinBlock) void k_bins(
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
     unsigned* running = lds;                     // [G] arrivals so far per pillar
-    unsigned* wcnt = running + G;                // [kBinWaves * G] per-wavefront counts
-    unsigned* roff = wcnt + kBinWaves * G;       // [kBinBlock + 1] run offsets in the group
+    unsigned* wbuf = running + G;                // [3][kBinWaves * G] per-wavefront counts
+    unsigned* roff = wbuf + 3 * kBinWaves * G;   // [kBinBlock + 1] run offsets in the group
     unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock] run start within its tile
     unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
     unsigned* best = wsum + kBinWaves;           // [G * K] the K lowest indices, in order
@@ -1138,39 +1149,52 @@ __global__ __launch_bounds__(kBinBlock) void k_bins(
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int w = t / kWave;
+    const long long b = blockIdx.x;
+    // the first group's count entries do not depend on the header: load them
+    // together with it
+    unsigned e = 0u;
+    if ((long long)t < ptiles) e = cm[(size_t)b * ptiles + t];
     const int status = hdr->status;
     const long long V = status > 0 ? status : 0;
     const long long distinct = hdr->distinct;
-    const long long b = blockIdx.x;
     if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    // the release touches nothing below; its memory traffic overlaps the bins
+    release_workspace(b * kBinBlock + t, (long long)gridDim.x * kBinBlock, distinct, V, M,
+                      occ_slot, table, S, kept_key, compact, C, kept_cslot, tile_state, ntiles,
+                      hdr, num_voxels);
+    if (status <= 0) return;  // nothing was staged
 
     // bin b holds the ids b, b + nbins, b + 2 nbins, ... below V
     const long long nbins = 1ll << nbits;
-    if (status > 0) {
-        const int Gb = b < V ? (int)((V - b + nbins - 1) >> nbits) : 0;
-        for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
-        for (int x = t; x < kBinWaves * G; x += kBinBlock) wcnt[x] = 0u;
-        for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
-            // this group's runs: tile tg + t holds one of length e >> 16
-            const long long tt = tg + t;
-            unsigned e = 0u;
-            if (tt < ptiles) {
-                e = cm[(size_t)b * ptiles + tt];
-                cm[(size_t)b * ptiles + tt] = 0u;  // last reader
-            }
-            unsigned ng;
-            const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
-            roff[t] = ro;
-            rsrc[t] = e & 0xffffu;
-            const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
-            __syncthreads();
-            // arrivals in order, kBinBlock at a time: arrival x of the group
-            // lies in the last run whose offset is <= x
-            for (unsigned x0 = 0; x0 < ng; x0 += kBinBlock) {
-                const unsigned x = x0 + (unsigned)t;
-                bool valid = x < ng;
-                unsigned pl = 0u, idx = 0u;
-                if (valid) {
+    const int Gb = b < V ? (int)((V - b + nbins - 1) >> nbits) : 0;
+    for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
+    for (int x = t; x < 3 * kBinWaves * G; x += kBinBlock) wbuf[x] = 0u;
+    unsigned round = 0;
+    for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
+        // this group's runs: tile tg + t holds one of length e >> 16
+        const long long tt = tg + t;
+        if (tg > 0) {
+            e = 0u;
+            if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
+        }
+        if (tt < ptiles) cm[(size_t)b * ptiles + tt] = 0u;  // last reader
+        unsigned ng;
+        const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
+        roff[t] = ro;
+        rsrc[t] = e & 0xffffu;
+        const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+        __syncthreads();
+        // arrivals in order, kBinBlock per round and up to four rounds read
+        // ahead: arrival x of the group lies in the last run whose offset is
+        // <= x
+        for (unsigned x0 = 0; x0 < ng; x0 += 4u * kBinBlock) {
+            unsigned v[4], idx4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const unsigned x = x0 + (unsigned)(u * kBinBlock + t);
+                v[u] = 0u;
+                idx4[u] = 0u;
+                if (x < ng) {
                     int lo = 0, hi = nruns;
                     while (hi - lo > 1) {
                         const int mid = (lo + hi) >> 1;
@@ -1178,79 +1202,93 @@ __global__ __launch_bounds__(kBinBlock) void k_bins(
                         else hi = mid;
                     }
                     const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
-                    const unsigned v = staging[src];
+                    v[u] = staging[src];
                     staging[src] = 0u;  // last reader
-                    pl = v >> 16;
-                    idx = (unsigned)((tg + lo) * ptile) + (v & 0xffffu);
-                    if (pl >= (unsigned)Gb) {  // not on a clean workspace
-                        report_error(hdr, num_voxels, 4u);
-                        valid = false;
-                        pl = 0u;
-                    }
+                    idx4[u] = (unsigned)((tg + lo) * ptile);  // + index within the tile
                 }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const unsigned xr = x0 + (unsigned)(u * kBinBlock);
+                if (xr >= ng) break;  // block-uniform
+                bool valid = xr + (unsigned)t < ng;
+                unsigned pl = v[u] >> 16;
+                const unsigned idx = idx4[u] + (v[u] & 0xffffu);
+                if (valid && pl >= (unsigned)Gb) {  // not on a clean workspace
+                    report_error(hdr, num_voxels, 4u);
+                    valid = false;
+                }
+                if (!valid) pl = 0u;
+                // counts of three rounds rotate: round r writes buffer r % 3
+                // and clears (r + 1) % 3, last read two rounds ago
+                unsigned* cur = wbuf + (round % 3u) * (kBinWaves * G);
+                unsigned* nxt = wbuf + ((round + 1u) % 3u) * (kBinWaves * G);
+                for (int y = t; y < kBinWaves * G; y += kBinBlock) nxt[y] = 0u;
                 const unsigned long long m = match_mask(pl, valid, gshift);
                 const unsigned rank = (unsigned)__popcll(m & lanes_below(lane));
-                if (valid && (m & lanes_above(lane)) == 0ull) wcnt[w * G + pl] = (unsigned)__popcll(m);
+                if (valid && (m & lanes_above(lane)) == 0ull) cur[w * G + pl] = (unsigned)__popcll(m);
                 __syncthreads();
                 if (t < G) {
                     // exclusive prefix over the wavefronts, on top of the
                     // arrivals of earlier rounds
                     unsigned acc = running[t];
-                    for (int ww = 0; ww < kBinWaves; ++ww) {
-                        const unsigned cw = wcnt[ww * G + t];
-                        wcnt[ww * G + t] = acc;
-                        acc += cw;
+#pragma unroll
+                    for (int h0 = 0; h0 < kBinWaves; h0 += 8) {
+                        unsigned cw[8];  // eight reads in flight, then eight writes
+#pragma unroll
+                        for (int ww = 0; ww < 8; ++ww) cw[ww] = cur[(h0 + ww) * G + t];
+#pragma unroll
+                        for (int ww = 0; ww < 8; ++ww) {
+                            cur[(h0 + ww) * G + t] = acc;
+                            acc += cw[ww];
+                        }
                     }
                     running[t] = acc;
                 }
                 __syncthreads();
                 if (valid) {
-                    const unsigned r = wcnt[w * G + pl] + rank;
+                    const unsigned r = cur[w * G + pl] + rank;
                     if (r < (unsigned)K) best[pl * K + r] = idx;
                 }
-                __syncthreads();
-                for (int y = t; y < kBinWaves * G; y += kBinBlock) wcnt[y] = 0u;
-                __syncthreads();
+                ++round;
             }
-        }
-        // rows: the selection in index order, then zero padding; a pillar's K
-        // rows are contiguous
-        const int rows = Gb * K;
-        for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
-            float4 row[4];
-            int xx[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                xx[u] = x0 + u * kBinBlock + t;
-                row[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (xx[u] < rows) {
-                    const int p = xx[u] / K;
-                    const int r = xx[u] - p * K;
-                    if ((unsigned)r < running[p]) {
-                        const unsigned v = best[p * K + r];
-                        if (v < N) row[u] = pts[v];
-                        else report_error(hdr, num_voxels, 8u);
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (xx[u] >= rows) continue;
-                const int p = xx[u] / K;
-                voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)] = row[u];
-            }
-        }
-        for (int p = t; p < Gb; p += kBinBlock) {
-            const long long pp = b + ((long long)p << nbits);
-            num_points[pp] = (int)(running[p] < (unsigned)K ? running[p] : (unsigned)K);
-            write_coords(coords, pp, kept_key[pp], gx, gy);
-            kept_key[pp] = 0;
-            if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
         }
     }
-    const long long nthreads = (long long)gridDim.x * kBinBlock;
-    release_workspace(b * kBinBlock + t, nthreads, distinct, V, M, occ_slot, table, S, kept_key,
-                      compact, C, kept_cslot, tile_state, ntiles, hdr, num_voxels);
+    __syncthreads();
+    // rows: the selection in index order, then zero padding; a pillar's K
+    // rows are contiguous. Gathers and key loads are issued together.
+    const int rows = Gb * K;
+    for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
+        float4 row[4];
+        int xx[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            xx[u] = x0 + u * kBinBlock + t;
+            row[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (xx[u] < rows) {
+                const int p = xx[u] / K;
+                const int r = xx[u] - p * K;
+                if ((unsigned)r < running[p]) {
+                    const unsigned vv = best[p * K + r];
+                    if (vv < N) row[u] = pts[vv];
+                    else report_error(hdr, num_voxels, 8u);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (xx[u] >= rows) continue;
+            const int p = xx[u] / K;
+            voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)] = row[u];
+        }
+    }
+    for (int p = t; p < Gb; p += kBinBlock) {
+        const long long pp = b + ((long long)p << nbits);
+        num_points[pp] = (int)(running[p] < (unsigned)K ? running[p] : (unsigned)K);
+        write_coords(coords, pp, kept_key[pp], gx, gy);
+        kept_key[pp] = 0;
+        if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
+    }
 }
 
 // -------------------------------------------------------------- bin only --
@@ -1294,7 +1332,7 @@ struct Plan {
 
 // LDS of one k_bins block for bins of G pillars
 inline size_t bins_lds_bytes(int G, int K) {
-    return 4u * (size_t)(G + kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + G * K);
+    return 4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + G * K);
 }
 
 inline bool finite_f(float v) { return isfinite(v); }
@@ -1358,7 +1396,9 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     // Select/pack route: per-bin partition (no per-point device atomic) when
     // K <= 64 and the ids fit kMaxBins bins of at most 128; buckets otherwise.
     const int path = opt ? opt->select_path : 0;
-    const bool part_ok = K <= kSortLanes && cdiv(M, 128) <= kMaxBins;
+    // bins of at most 128 ids (64 when K > 32, to keep k_bins within 64 KB of LDS)
+    const int max_per_bin = K > 32 ? 64 : 128;
+    const bool part_ok = K <= kSortLanes && cdiv(M, max_per_bin) <= kMaxBins;
     if (path == 2 && !part_ok) return VOX_EINVAL;
     pl->part = (path == 2 || (path == 0 && part_ok)) ? 1 : 0;
     pl->gshift = 0;
@@ -1370,12 +1410,12 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     if (pl->part) {
         // a power-of-two number of bins, about M / 64 (M / 128 past 32768
         // pillars), and G = 2^gshift >= the ids one bin can hold
-        const long long want = cdiv(M, M > 32768 ? 128 : 64);
+        const long long want = cdiv(M, M > 32768 ? max_per_bin : 64);
         while ((1ll << pl->nbits) < want) ++pl->nbits;
         pl->nbins = 1 << pl->nbits;
         const long long per_bin = cdiv(M, pl->nbins);
         while ((1ll << pl->gshift) < per_bin) ++pl->gshift;
-        pl->lds = bins_lds_bytes(1 << pl->gshift, K);  // at most 50 KB (G = 128, K = 64)
+        pl->lds = bins_lds_bytes(1 << pl->gshift, K);  // at most 50 KB (G 128 / K 32, G 64 / K 64)
         // points per k_part thread: the largest power of two up to 16 that
         // still gives about 1024 tiles (small clouds spread over every CU)
         int per = 1;
@@ -1490,20 +1530,28 @@ int last_launch() {
     return e == hipSuccess ? VOX_OK : hip_fail(e);
 }
 
+// Every launch goes through hipExtLaunchKernelGGL: with a pair of events the
+// runtime stamps them at the kernel's own start and end (stage profiling);
+// without, it is a plain launch.
+inline hipEvent_t ev_start(hipEvent_t* ev) { return ev ? ev[0] : nullptr; }
+inline hipEvent_t ev_stop(hipEvent_t* ev) { return ev ? ev[1] : nullptr; }
+
 int launch_insert(const float* points, long long begin, long long end, const Grid& g,
-                  const Plan& pl, const Buffers& bf, hipStream_t st, int count_claims) {
+                  const Plan& pl, const Buffers& bf, hipStream_t st, int count_claims,
+                  hipEvent_t* ev) {
     const long long n = end - begin;
     const unsigned blocks = (unsigned)(n > 0 ? cdiv(n, kBlock) : 1);
-    hipLaunchKernelGGL(k_insert, dim3(blocks), dim3(kBlock), 0, st,
+    hipExtLaunchKernelGGL(k_insert, dim3(blocks), dim3(kBlock), 0, st, ev_start(ev), ev_stop(ev), 0,
                        reinterpret_cast<const float4*>(points), begin, end, g, bf.table,
                        (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr, count_claims);
     return last_launch();
 }
 
 int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_voxels,
-                hipStream_t st) {
+                hipStream_t st, hipEvent_t* ev) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
-    hipLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, P, pl.N, pl.M,
+    hipExtLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, ev_start(ev),
+                          ev_stop(ev), 0, P, pl.N, pl.M,
                        bf.table, bf.compact, (unsigned)pl.C, pl.hash, bf.kcs, bf.slot_of,
                        bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr, num_voxels);
     return last_launch();
@@ -1511,7 +1559,7 @@ int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_vox
 
 int launch_select(const float* points, long long P, const Grid& g, const Plan& pl,
                   const Buffers& bf, int32_t* num_voxels, int32_t* point_pillar,
-                  hipStream_t st) {
+                  hipStream_t st, hipEvent_t* ev) {
     if (pl.part) {
         decltype(&k_part<1>) kern = &k_part<1>;
         switch (pl.pper) {
@@ -1521,7 +1569,8 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
             case 16: kern = &k_part<16>; break;
             default: break;
         }
-        hipLaunchKernelGGL(kern, dim3((unsigned)pl.ptiles), dim3(kBlock), 0, st,
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)pl.ptiles), dim3(kBlock), 0, st, ev_start(ev),
+                              ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
                            (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of,
                            pl.nbits, pl.ptiles, bf.cm, bf.stage, bf.hdr, num_voxels,
@@ -1529,7 +1578,7 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
         return last_launch();
     }
     const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
-    hipLaunchKernelGGL(k_select, dim3(blocks), dim3(kBlock), 0, st,
+    hipExtLaunchKernelGGL(k_select, dim3(blocks), dim3(kBlock), 0, st, ev_start(ev), ev_stop(ev), 0,
                        reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
                        (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of, bf.cnt,
                        bf.bucket, pl.cap, bf.ovf, pl.K, bf.hdr, num_voxels, point_pillar);
@@ -1538,11 +1587,12 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
 
 int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                 const Buffers& bf, float* voxels, int32_t* coords, int32_t* num_points,
-                int32_t* num_voxels, hipStream_t st) {
+                int32_t* num_voxels, hipStream_t st, hipEvent_t* ev) {
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
     if (pl.part) {
         // one block per bin; all blocks share the workspace release
-        hipLaunchKernelGGL(k_bins, dim3((unsigned)pl.nbins), dim3(kBinBlock), pl.lds, st,
+        hipExtLaunchKernelGGL(k_bins, dim3((unsigned)pl.nbins), dim3(kBinBlock), (unsigned)pl.lds, st,
+                              ev_start(ev), ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, bf.cm, bf.stage,
                            pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.K, pl.M,
                            bf.kept, bf.compact,
@@ -1562,7 +1612,8 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
     if (clean_blocks > blocks) blocks = clean_blocks;
     if (blocks < 1) blocks = 1;
     if (blocks > kPackMaxBlocks) blocks = kPackMaxBlocks;
-    hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+    hipExtLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(kBlock), 0, st, ev_start(ev),
+                          ev_stop(ev), 0,
                        reinterpret_cast<const float4*>(points), pl.N, bf.cnt, bf.bucket, pl.cap,
                        bf.ovf, pl.K, pl.M, seg, bf.kept, bf.compact, (unsigned)pl.C, bf.kcs,
                        g.gx, g.gy,
@@ -1584,24 +1635,21 @@ int prepare(const float* points, int64_t n_points, const float range[6], const f
     return VOX_OK;
 }
 
-// The four stages of one call; events (if given) are recorded between them.
+// The four stages of one call; with ev (2 events per stage), each kernel's
+// own start and end are stamped.
 int run_pipeline(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
                  float* voxels, int32_t* coords, int32_t* num_points, int32_t* num_voxels,
                  int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
     int rc;
-    if (ev && hipEventRecord(ev[0], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st, 0)) != VOX_OK) return rc;
-    if (ev && hipEventRecord(ev[1], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_rank(pl.P, pl, bf, num_voxels, st)) != VOX_OK) return rc;
-    if (ev && hipEventRecord(ev[2], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_select(points, pl.P, g, pl, bf, num_voxels, point_pillar, st)) != VOX_OK)
+    if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st, 0, ev ? ev : nullptr)) != VOX_OK)
         return rc;
-    if (ev && hipEventRecord(ev[3], st) != hipSuccess) return hip_fail(hipGetLastError());
-    if ((rc = launch_pack(points, pl.P, g, pl, bf, voxels, coords, num_points, num_voxels, st)) !=
-        VOX_OK)
+    if ((rc = launch_rank(pl.P, pl, bf, num_voxels, st, ev ? ev + 2 : nullptr)) != VOX_OK)
         return rc;
-    if (ev && hipEventRecord(ev[4], st) != hipSuccess) return hip_fail(hipGetLastError());
-    return VOX_OK;
+    if ((rc = launch_select(points, pl.P, g, pl, bf, num_voxels, point_pillar, st,
+                            ev ? ev + 4 : nullptr)) != VOX_OK)
+        return rc;
+    return launch_pack(points, pl.P, g, pl, bf, voxels, coords, num_points, num_voxels, st,
+                       ev ? ev + 6 : nullptr);
 }
 
 }  // namespace
@@ -1691,7 +1739,8 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
     while (done < pl.N && have < pl.M) {
         long long chunk = half - have;
         if (chunk > pl.N - done) chunk = pl.N - done;
-        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream, 1)) != VOX_OK)
+        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream, 1, nullptr)) !=
+            VOX_OK)
             return rc;
         done += chunk;
         unsigned claims = 0;
@@ -1703,10 +1752,12 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
     }
     Plan p2 = pl;
     p2.P = done;
-    if ((rc = launch_rank(done, p2, bf, num_voxels, stream)) != VOX_OK) return rc;
-    if ((rc = launch_select(points, done, g, p2, bf, num_voxels, point_pillar, stream)) != VOX_OK)
+    if ((rc = launch_rank(done, p2, bf, num_voxels, stream, nullptr)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, done, g, p2, bf, num_voxels, point_pillar, stream,
+                            nullptr)) != VOX_OK)
         return rc;
-    return launch_pack(points, done, g, p2, bf, voxels, coords, num_points, num_voxels, stream);
+    return launch_pack(points, done, g, p2, bf, voxels, coords, num_points, num_voxels, stream,
+                       nullptr);
 }
 
 int vox_bin_points(const float* points, int64_t n_points, const float range[6],
@@ -1740,7 +1791,7 @@ int vox_profile_stages(const float* points, int64_t n_points, const float range[
                      &pl);
     if (rc != VOX_OK) return rc;
     const Buffers bf = carve(workspace, pl);
-    const int nev = VOX_NUM_STAGES + 1;
+    const int nev = 2 * VOX_NUM_STAGES;  // a start and a stop per kernel
     hipEvent_t* ev = new hipEvent_t[(size_t)iters * nev];
     int created = 0;
     for (; created < iters * nev; ++created) {
@@ -1764,7 +1815,7 @@ int vox_profile_stages(const float* points, int64_t n_points, const float range[
             hipEvent_t* e = ev + (size_t)it * nev;
             for (int s = 0; s < VOX_NUM_STAGES; ++s) {
                 float ms = 0;
-                const hipError_t he = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+                const hipError_t he = hipEventElapsedTime(&ms, e[2 * s], e[2 * s + 1]);
                 if (he != hipSuccess) {
                     rc = hip_fail(he);
                     break;
@@ -1772,7 +1823,7 @@ int vox_profile_stages(const float* points, int64_t n_points, const float range[
                 acc[s] += ms;
             }
             float ms = 0;
-            if (hipEventElapsedTime(&ms, e[0], e[VOX_NUM_STAGES]) == hipSuccess) tot += ms;
+            if (hipEventElapsedTime(&ms, e[0], e[nev - 1]) == hipSuccess) tot += ms;
         }
         for (int s = 0; s < VOX_NUM_STAGES; ++s) stage_ms[s] = (float)(acc[s] / iters);
         *total_ms = (float)(tot / iters);

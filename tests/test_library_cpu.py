@@ -124,19 +124,21 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_select_path_option_limits():
-    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 524288)."""
+    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 262144, or
+    <= 131072 when K > 32)."""
     auto = vox.workspace_bytes(100000, 60000, 32)
     assert auto == vox.workspace_bytes(100000, 60000, 32, select_path=2)
     assert auto != vox.workspace_bytes(100000, 60000, 32, select_path=1)
     assert vox.plan(100000, 60000, 32)["bucket_cap"] == 0          # no buckets
     assert vox.plan(100000, 60000, 32, select_path=1)["bucket_cap"] == 512
-    assert vox.workspace_bytes(1000, 524288, 32, select_path=2) > 0
-    # K > 64 or more than 524288 pillars: only the bucket route exists
+    assert vox.workspace_bytes(1000, 262144, 32, select_path=2) > 0
+    # K > 64 or more than 262144 pillars: only the bucket route exists
     assert vox.plan(1000, 100, 65)["bucket_cap"] == 0
     for bad in (dict(select_path=-1), dict(select_path=3)):
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(1000, 100, 32, **bad)
-    for args in ((1000, 100, 65), (1000, 524289, 32)):
+    assert vox.workspace_bytes(1000, 131072, 64, select_path=2) > 0
+    for args in ((1000, 100, 65), (1000, 262145, 32), (1000, 131073, 33)):
         assert vox.workspace_bytes(*args) > 0
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(*args, select_path=2)
