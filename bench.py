@@ -102,7 +102,7 @@ def rocprof_summary(root):
     print("\n".join(out))
 
 
-def algorithmic_bytes(N, P, V, K, rows, kept, partitioned):
+def algorithmic_bytes(N, P, V, K, rows, kept, route):
     """Compulsory bytes of the whole call and of each kernel.
 
     whole call: read every point once (16 B) + write the dense output,
@@ -110,15 +110,18 @@ def algorithmic_bytes(N, P, V, K, rows, kept, partitioned):
     insert: its share of the input read, 16 B per prefix point.
     rank:   4 B per prefix point (the slot index written by insert).
     select: 16 B per point past the prefix + 4 B per prefix point (slot);
-            the partitioned route also writes one 4-byte staging word per
-            point of a kept pillar (`kept` of them).
-    pack:   the dense output + 16 B per kept row gathered from the input;
-            the partitioned route also reads the staging words back.
+            the partitioned routes (2, 3) also write one 4-byte staging word
+            per point of a kept pillar (`kept` of them), route 3 its 16-byte
+            row as well.
+    pack:   the dense output + 16 B per kept row (gathered from the input, or
+            on route 3 copied from the staged rows); the partitioned routes
+            also read the staging words back.
     """
     out = V * (16 * K + 16)
-    stage = 4 * kept if partitioned else 0
+    stage = 4 * kept if route >= 2 else 0
+    carried = 16 * kept if route == 3 else 0
     return dict(call=16 * N + out, insert=16 * P, rank=4 * P,
-                select=16 * (N - P) + 4 * P + stage, pack=out + 16 * rows + stage)
+                select=16 * (N - P) + 4 * P + stage + carried, pack=out + 16 * rows + stage)
 
 
 def recorded_traffic(workload, stage):
@@ -202,14 +205,14 @@ def run_workload(name, steps, warmup, profile_iters, torch, vox):
     stage_ms, total_ms = vx.profile(x, profile_iters)
     pl = vox.plan(N, p.max_voxels, p.max_points)
     P = pl["prefix_points"]
-    partitioned = p.max_points <= 64 and pl["bucket_cap"] == 0
+    route = vox.select_route(N, p.max_voxels, p.max_points)
     pmap = vox.voxelize(x, p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
                         point_map=True)[3]
     kept = int((pmap >= 0).sum().item())
-    alg = algorithmic_bytes(N, P, V, p.max_points, rows, kept, partitioned)
+    alg = algorithmic_bytes(N, P, V, p.max_points, rows, kept, route)
     kernels = dict(insert="k_insert", rank="k_rank",
-                   select="k_part" if partitioned else "k_select",
-                   pack="k_bins" if partitioned else "k_pack")
+                   select="k_part" if route >= 2 else "k_select",
+                   pack="k_bins" if route >= 2 else "k_pack")
     return dict(cfg=cfg, pts=pts, N=N, V=V, rows=rows, ms=ms, parity=parity, stage_ms=stage_ms,
                 total_ms=total_ms, alg=alg, P=P, kept=kept, kernels=kernels)
 

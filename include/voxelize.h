@@ -85,26 +85,39 @@ typedef struct vox_options {
     int32_t compact_table;  /* 1 = lookups past the prefix probe a small table of the
                                kept cells (4 slots per pillar) built by rank; 0 = they
                                probe the main table (default) */
-    int32_t select_path;    /* route from lookups to rows: 0 = automatic (partitioned when
-                               K <= 64 and max_voxels <= 262144, or <= 131072 when
-                               K > 32; buckets otherwise),
+    int32_t select_path;    /* route from lookups to rows (the output is the same):
                                1 = per-pillar buckets filled by one device atomic per
-                               point, 2 = partitioned by pillar-id bins in LDS (EINVAL
-                               outside those limits). The output is the same. */
+                               point; 2 = partitioned by pillar-id bins in LDS, rows
+                               gathered from the cloud; 3 = partitioned, rows carried
+                               through the workspace's scratch; 0 = automatic: 3 from
+                               2^19 points up, else 2, when K <= 64 and max_voxels <=
+                               262144 (<= 131072 when K > 32), else 1. 2 and 3 outside
+                               those limits: VOX_EINVAL. */
 } vox_options;
 
 /*
  * Workspace size in bytes for a call with n_points points, max_voxels and
  * max_points (and options, NULL for defaults). The workspace is device memory
- * the caller owns, 256-byte aligned, that must be all zero before its first
- * use (hipMemset or torch.zeros). A completed call whose num_voxels is not
- * VOX_STATUS_DEVICE_ERROR leaves it ready for the next call of any shape:
- * every byte past the first 256 is zero again, and the first 256 hold only
- * two result words that the next call overwrites. After a device error the
- * workspace must be zeroed again. Returns >= 0, or VOX_EINVAL.
+ * the caller owns, 256-byte aligned. It has two parts:
+ *   [0, Z)      Z = vox_workspace_zero_bytes(same arguments): must be all zero
+ *               before a call (hipMemset or torch.zeros). A completed call
+ *               whose num_voxels is not VOX_STATUS_DEVICE_ERROR leaves it
+ *               ready again: every byte of [256, Z) is zero, and the first 256
+ *               hold only two result words that the next call overwrites.
+ *   [Z, bytes)  scratch (the partitioned select route's staging): written
+ *               before it is read in every call, left as it is afterwards.
+ * A workspace can serve calls of other shapes as long as the new call's
+ * [0, Z') is zero: bytes a previous call used as scratch must be zeroed
+ * first when Z' reaches into them. After a device error the workspace must
+ * be zeroed again. Returns >= 0, or VOX_EINVAL.
  */
 int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_points,
                             const vox_options* options);
+
+/* Z above: the size of the workspace's zero part (<= vox_workspace_bytes). */
+
+int64_t vox_workspace_zero_bytes(int64_t n_points, int32_t max_voxels, int32_t max_points,
+                                 const vox_options* options);
 
 /*
  * Pillar / voxel binning of one cloud (the whole operation described above).
@@ -172,6 +185,11 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
                  int32_t* num_voxels, int32_t* point_pillar, void* workspace,
                  size_t workspace_bytes, hipStream_t stream, const vox_options* options,
                  int32_t chunked);
+
+/* The select route a call would take (1, 2 or 3, as select_path above), or
+ * VOX_EINVAL. */
+int32_t vox_select_route(int64_t n_points, int32_t max_voxels, int32_t max_points,
+                         const vox_options* options);
 
 /*
  * The sizes a call would use (for reports and tests): table slots S, prefix

@@ -29,12 +29,14 @@ STAGES = ("insert", "rank", "select", "pack")
 HEADER_BYTES = 256          # the workspace's first 256 bytes hold the result words
 
 
-def workspace_is_clean(ws: "torch.Tensor") -> bool:
-    """True when a workspace is ready for reuse: everything past the header is
-    zero and so are the header's counters (only the two result words, bytes
-    8..16, may be nonzero)."""
+def workspace_is_clean(ws: "torch.Tensor", zero_bytes: Optional[int] = None) -> bool:
+    """True when a workspace is ready for reuse by a call whose zero part is
+    `zero_bytes` long (default: the whole workspace): the zero part past the
+    header is zero and so are the header's counters (only the two result
+    words, bytes 8..16, may be nonzero)."""
+    end = ws.numel() if zero_bytes is None else int(zero_bytes)
     head = ws[:HEADER_BYTES].view(torch.int32)
-    rest_zero = int(torch.count_nonzero(ws[HEADER_BYTES:]).item()) == 0
+    rest_zero = int(torch.count_nonzero(ws[HEADER_BYTES:end]).item()) == 0
     counters = torch.cat([head[0:2], head[4:]])
     return rest_zero and int(torch.count_nonzero(counters).item()) == 0
 
@@ -62,6 +64,10 @@ def _load() -> ctypes.CDLL:
     op = ctypes.POINTER(Options)
     lib.vox_workspace_bytes.argtypes = [i64, i32, i32, op]
     lib.vox_workspace_bytes.restype = i64
+    lib.vox_workspace_zero_bytes.argtypes = [i64, i32, i32, op]
+    lib.vox_workspace_zero_bytes.restype = i64
+    lib.vox_select_route.argtypes = [i64, i32, i32, op]
+    lib.vox_select_route.restype = i32
     common = [vp, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.voxelize.argtypes = common
     lib.voxelize.restype = ctypes.c_int
@@ -120,6 +126,25 @@ def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> 
     return int(n)
 
 
+def select_route(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
+    """The route a call takes: 1 buckets, 2 partitioned (rows gathered from the
+    cloud), 3 partitioned (rows carried through scratch)."""
+    r = _lib.vox_select_route(int(n_points), int(max_voxels), int(max_points), _options(**opts))
+    if r < 0:
+        raise VoxError(int(r), "vox_select_route")
+    return int(r)
+
+
+def workspace_zero_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
+    """Bytes at the start of the workspace that must be zero before a call
+    (and are zero again after it); the rest is scratch."""
+    n = _lib.vox_workspace_zero_bytes(int(n_points), int(max_voxels), int(max_points),
+                                      _options(**opts))
+    if n < 0:
+        raise VoxError(int(n), "vox_workspace_zero_bytes")
+    return int(n)
+
+
 def plan(n_points: int, max_voxels: int, max_points: int, **opts) -> Dict[str, int]:
     """Table slots, prefix length and bucket slots a call with these sizes uses."""
     S, P, cap = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
@@ -129,26 +154,37 @@ def plan(n_points: int, max_voxels: int, max_points: int, **opts) -> Dict[str, i
 
 
 class _Workspaces:
-    """Zeroed workspaces reused per (device, stream). Every completed call
-    leaves its workspace ready for the next call of any shape, so reuse needs
-    no clearing; a workspace that saw a device error is dropped."""
+    """Workspaces reused per (device, stream). A completed call leaves the
+    zero part of its own layout zero and may leave scratch after it; the cache
+    remembers how long the zero prefix is and clears, on the call's stream,
+    only what a larger zero part of the next call adds. A workspace that saw
+    a device error is dropped."""
 
     def __init__(self):
         self._lock = threading.Lock()
         self._cache: Dict[Tuple[int, int], torch.Tensor] = {}
+        self._clean: Dict[Tuple[int, int], int] = {}
 
-    def get(self, device: torch.device, stream: int, nbytes: int) -> torch.Tensor:
+    def get(self, device: torch.device, stream: int, nbytes: int,
+            zero_bytes: int) -> torch.Tensor:
         key = (device.index, stream)
         with self._lock:
             ws = self._cache.get(key)
             if ws is None or ws.numel() < nbytes:
                 ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
                 self._cache[key] = ws
+                self._clean[key] = ws.numel()
+            clean = self._clean[key]
+            if clean < zero_bytes:
+                ws[clean:zero_bytes].zero_()  # scratch of an earlier, smaller layout
+            # the call will leave [0, zero_bytes) zero and use the rest as scratch
+            self._clean[key] = zero_bytes
             return ws
 
     def drop(self, device: torch.device, stream: int) -> None:
         with self._lock:
             self._cache.pop((device.index, stream), None)
+            self._clean.pop((device.index, stream), None)
 
 
 _workspaces = _Workspaces()
@@ -193,9 +229,10 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
               bucket_cap=bucket_cap, compact_table=compact_table, select_path=select_path)
     opts = _options(**kw)
     nbytes = workspace_bytes(N, M, K, **kw)
+    zbytes = workspace_zero_bytes(N, M, K, **kw)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        ws = _workspaces.get(dev, stream, nbytes)
+        ws = _workspaces.get(dev, stream, nbytes, zbytes)
         voxels = torch.empty((M, K, 4), dtype=torch.float32, device=dev)
         coords = torch.empty((M, 3), dtype=torch.int32, device=dev)
         counts = torch.empty((M,), dtype=torch.int32, device=dev)
@@ -256,6 +293,7 @@ class Voxelizer:
         self.device = torch.device(device)
         self._opts = _options(**opts)
         self.nbytes = workspace_bytes(self.N, self.M, self.K, **opts)
+        self.zero_bytes = workspace_zero_bytes(self.N, self.M, self.K, **opts)
         self.workspace = torch.zeros(self.nbytes, dtype=torch.uint8, device=self.device)
         self.voxels = torch.empty((self.M, self.K, 4), dtype=torch.float32, device=self.device)
         self.coords = torch.empty((self.M, 3), dtype=torch.int32, device=self.device)

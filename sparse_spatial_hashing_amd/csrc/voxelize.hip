@@ -832,8 +832,10 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 //           pillar's points arrive in index order: a point's rank in its
 //           pillar is the number of earlier arrivals with the same id
 //           (ballots within the wavefront, a per-wavefront prefix in LDS and
-//           a running count per pillar), and ranks below K are the rows.
-//           Each staging word and count entry is zeroed by its reader.
+//           a running count per pillar); a rank below K is a row, copied from
+//           the row k_part staged next to the word (no gather from the cloud).
+// Staging and the count table are scratch: every call writes each entry it
+// reads, so they are left as they are (the rest of the workspace is zeroed).
 // The rows are those of the bucket path bit for bit; only the route differs.
 
 constexpr int kPartMaxPer = 16;                // points per k_part thread, at most
@@ -902,11 +904,14 @@ __device__ __forceinline__ unsigned long long lanes_above(int lane) {
     return ~((2ull << lane) - 1ull);  // lane 63: 2 << 63 wraps to 0, mask 0
 }
 
+// CARRY: also copy each kept point's row into a scratch array next to its
+// staging word, so that k_bins copies rows from there instead of gathering
+// them from the cloud (pays off for large clouds).
 // PER points per thread: wavefront w of the block takes the contiguous
 // points [base + 64 PER w, base + 64 PER (w + 1)), 64 at a time. Lookups go
 // PER_B at a time: within a batch every load is issued before any result is
 // used, and only block-uniform branches guard them.
-template <int PER>
+template <int PER, bool CARRY>
 __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts, long long N,
                                                  long long P, Grid g,
                                                  const unsigned long long* __restrict__ table,
@@ -916,6 +921,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                                                  int nbits, long long ptiles,
                                                  unsigned* __restrict__ cm,
                                                  unsigned* __restrict__ staging,
+                                                 float4* __restrict__ stage_pt,
                                                  Header* __restrict__ hdr,
                                                  int* __restrict__ num_voxels,
                                                  int* __restrict__ point_pillar) {
@@ -952,6 +958,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
     const bool any_prefix = base < P;                              // block-uniform
     const bool any_rest = status > 0 && base + TILE > P && base < N;
     unsigned pid[PER];
+    float4 row[PER];  // each point's row (kept to the end when CARRY)
 #pragma unroll
     for (int k0 = 0; k0 < PER; k0 += PER_B) {
         unsigned long long wd[PER_B];
@@ -960,6 +967,8 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         for (int k = 0; k < PER_B; ++k) {
             ii[k] = wbase + (long long)(k0 + k) * kWave + lane;
             wd[k] = 0ull;
+            row[k0 + k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (base < N && (CARRY || any_rest)) row[k0 + k] = pts[ii[k] < N ? ii[k] : N - 1];
         }
         if (any_prefix) {
             // prefix points: the slot insert recorded, then its word
@@ -984,15 +993,12 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         }
         if (any_rest) {
             // later points: bin, then probe the home pair, then (rarely) lines
-            float4 pt[PER_B];
-#pragma unroll
-            for (int k = 0; k < PER_B; ++k) pt[k] = pts[ii[k] < N ? ii[k] : N - 1];
             long long key[PER_B];
             unsigned h[PER_B];
             uint4 q[PER_B];
 #pragma unroll
             for (int k = 0; k < PER_B; ++k) {
-                key[k] = (ii[k] >= P && ii[k] < N) ? bin_key(pt[k], g) : -1;
+                key[k] = (ii[k] >= P && ii[k] < N) ? bin_key(row[k0 + k], g) : -1;
                 h[k] = home_slot(key[k] >= 0 ? key[k] : 0, LS, hash);
                 q[k] = load_pair(look, h[k]);
             }
@@ -1123,15 +1129,21 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);  // in the tile
         const unsigned bin = pid[k] & bmask;
         const unsigned id = pid[k] >> nbits;  // id within the bin
-        staging[base + hist[w][bin] + pos[k]] = (id << 16) | local;
+        const long long at = base + hist[w][bin] + pos[k];
+        staging[at] = (id << 16) | local;
+        if (CARRY) stage_pt[at] = row[k];  // the row itself, bit for bit
     }
 }
 
-// At most 64 VGPRs: two 1024-thread blocks per CU.
+// At most 64 VGPRs: two 1024-thread blocks per CU. CARRY: rows come from
+// the copies k_part staged; otherwise the K lowest indices are kept in LDS
+// and the rows gathered from the cloud at the end.
+template <bool CARRY>
 __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8)))
 void k_bins(
-    const float4* __restrict__ pts, long long N, unsigned* __restrict__ cm,
-    unsigned* __restrict__ staging, long long ptiles, int ptile, int gshift, int nbits, int K,
+    const float4* __restrict__ pts, long long N, const unsigned* __restrict__ cm,
+    const unsigned* __restrict__ staging, const float4* __restrict__ stage_pt, long long ptiles,
+    int ptile, int gshift, int nbits, int K,
     int M, long long* __restrict__ kept_key, unsigned long long* __restrict__ compact, unsigned C,
     int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ voxels,
     int* __restrict__ coords, int* __restrict__ num_points, int* __restrict__ num_voxels,
@@ -1144,7 +1156,7 @@ void k_bins(
     unsigned* roff = wbuf + 3 * kBinWaves * G;   // [kBinBlock + 1] run offsets in the group
     unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock] run start within its tile
     unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
-    unsigned* best = wsum + kBinWaves;           // [G * K] the K lowest indices, in order
+    unsigned* best = wsum + kBinWaves;           // [G * K] without CARRY: the K lowest, in order
 
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -1170,6 +1182,9 @@ void k_bins(
     for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
     for (int x = t; x < 3 * kBinWaves * G; x += kBinBlock) wbuf[x] = 0u;
     unsigned round = 0;
+    bool has_row = false;
+    float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+    long long row_at = 0;
     for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
         // this group's runs: tile tg + t holds one of length e >> 16
         const long long tt = tg + t;
@@ -1177,7 +1192,6 @@ void k_bins(
             e = 0u;
             if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
         }
-        if (tt < ptiles) cm[(size_t)b * ptiles + tt] = 0u;  // last reader
         unsigned ng;
         const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
         roff[t] = ro;
@@ -1188,12 +1202,12 @@ void k_bins(
         // ahead: arrival x of the group lies in the last run whose offset is
         // <= x
         for (unsigned x0 = 0; x0 < ng; x0 += 4u * kBinBlock) {
-            unsigned v[4], idx4[4];
+            unsigned v[4], src4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const unsigned x = x0 + (unsigned)(u * kBinBlock + t);
                 v[u] = 0u;
-                idx4[u] = 0u;
+                src4[u] = 0u;
                 if (x < ng) {
                     int lo = 0, hi = nruns;
                     while (hi - lo > 1) {
@@ -1203,8 +1217,8 @@ void k_bins(
                     }
                     const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
                     v[u] = staging[src];
-                    staging[src] = 0u;  // last reader
-                    idx4[u] = (unsigned)((tg + lo) * ptile);  // + index within the tile
+                    // CARRY: where the row is; otherwise the tile's first index
+                    src4[u] = CARRY ? (unsigned)src : (unsigned)((tg + lo) * ptile);
                 }
             }
 #pragma unroll
@@ -1213,7 +1227,6 @@ void k_bins(
                 if (xr >= ng) break;  // block-uniform
                 bool valid = xr + (unsigned)t < ng;
                 unsigned pl = v[u] >> 16;
-                const unsigned idx = idx4[u] + (v[u] & 0xffffu);
                 if (valid && pl >= (unsigned)Gb) {  // not on a clean workspace
                     report_error(hdr, num_voxels, 4u);
                     valid = false;
@@ -1246,40 +1259,62 @@ void k_bins(
                     running[t] = acc;
                 }
                 __syncthreads();
+                // a rank below K is a row: load it now, store it one round
+                // later (the load stays in flight across the barriers)
+                if (CARRY && has_row) voxels[row_at] = row;
+                has_row = false;
                 if (valid) {
                     const unsigned r = cur[w * G + pl] + rank;
-                    if (r < (unsigned)K) best[pl * K + r] = idx;
+                    if (r < (unsigned)K) {
+                        if (CARRY) {
+                            row = stage_pt[src4[u]];
+                            row_at = (b + ((long long)pl << nbits)) * K + r;
+                            has_row = true;
+                        } else {
+                            best[pl * K + r] = src4[u] + (v[u] & 0xffffu);  // point index
+                        }
+                    }
                 }
                 ++round;
             }
         }
     }
+    if (CARRY && has_row) voxels[row_at] = row;  // the last round's rows
     __syncthreads();
-    // rows: the selection in index order, then zero padding; a pillar's K
-    // rows are contiguous. Gathers and key loads are issued together.
     const int rows = Gb * K;
-    for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
-        float4 row[4];
-        int xx[4];
+    if (CARRY) {
+        // zero padding: rows at or past each pillar's count
+        for (int x = t; x < rows; x += kBinBlock) {
+            const int p = x / K;
+            const int r = x - p * K;
+            if ((unsigned)r >= running[p])
+                voxels[(b + ((long long)p << nbits)) * K + r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        // rows gathered by index (four in flight per thread), then zero padding
+        for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
+            float4 rw[4];
+            int xx[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            xx[u] = x0 + u * kBinBlock + t;
-            row[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (xx[u] < rows) {
-                const int p = xx[u] / K;
-                const int r = xx[u] - p * K;
-                if ((unsigned)r < running[p]) {
-                    const unsigned vv = best[p * K + r];
-                    if (vv < N) row[u] = pts[vv];
-                    else report_error(hdr, num_voxels, 8u);
+            for (int u = 0; u < 4; ++u) {
+                xx[u] = x0 + u * kBinBlock + t;
+                rw[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (xx[u] < rows) {
+                    const int p = xx[u] / K;
+                    const int r = xx[u] - p * K;
+                    if ((unsigned)r < running[p]) {
+                        const unsigned vv = best[p * K + r];
+                        if (vv < N) rw[u] = pts[vv];
+                        else report_error(hdr, num_voxels, 8u);
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (xx[u] >= rows) continue;
-            const int p = xx[u] / K;
-            voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)] = row[u];
+            for (int u = 0; u < 4; ++u) {
+                if (xx[u] >= rows) continue;
+                const int p = xx[u] / K;
+                voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)] = rw[u];
+            }
         }
     }
     for (int p = t; p < Gb; p += kBinBlock) {
@@ -1322,18 +1357,23 @@ struct Plan {
     // partitioned select/pack (part = 1): bins of 2^gshift pillar ids, ptiles
     // k_part tiles of 256 pper points, nbits = bits of a bin number, lds bytes
     // of a k_bins block
-    int part, gshift, nbins, nbits, pper;
+    int part, carry, gshift, nbins, nbits, pper;
     long long ptiles;
     size_t lds;
-    // byte offsets into the workspace
+    // byte offsets into the workspace; [0, zero_bytes) is zero between calls,
+    // [zero_bytes, bytes) is scratch every call writes before reading
     size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf,
-        off_compact, off_kcs, off_cm, off_stage, bytes;
+        off_compact, off_kcs, off_cm, off_stage, off_stage_pt, zero_bytes, bytes;
 };
 
-// LDS of one k_bins block for bins of G pillars
-inline size_t bins_lds_bytes(int G, int K) {
-    return 4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + G * K);
+// LDS of one k_bins block for bins of G pillars (plus the selection when rows
+// are gathered rather than carried)
+inline size_t bins_lds_bytes(int G, int K, bool carry) {
+    return 4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves +
+                         (carry ? 0 : G * K));
 }
+// Clouds of at least this many points carry rows through staging by default.
+constexpr long long kCarryMinPoints = 1ll << 19;
 
 inline bool finite_f(float v) { return isfinite(v); }
 
@@ -1362,7 +1402,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         if (opt->table_slots > 0) S = opt->table_slots;
         if (opt->hash < 0 || opt->hash > 2) return VOX_EINVAL;
         if (opt->compact_table < 0 || opt->compact_table > 1) return VOX_EINVAL;
-        if (opt->select_path < 0 || opt->select_path > 2) return VOX_EINVAL;
+        if (opt->select_path < 0 || opt->select_path > 3) return VOX_EINVAL;
         hash = opt->hash;
         P = opt->prefix_points;
         if (opt->bucket_cap > 0 && K <= kSortLanes) {
@@ -1399,8 +1439,9 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     // bins of at most 128 ids (64 when K > 32, to keep k_bins within 64 KB of LDS)
     const int max_per_bin = K > 32 ? 64 : 128;
     const bool part_ok = K <= kSortLanes && cdiv(M, max_per_bin) <= kMaxBins;
-    if (path == 2 && !part_ok) return VOX_EINVAL;
-    pl->part = (path == 2 || (path == 0 && part_ok)) ? 1 : 0;
+    if (path >= 2 && !part_ok) return VOX_EINVAL;
+    pl->part = (path >= 2 || (path == 0 && part_ok)) ? 1 : 0;
+    pl->carry = pl->part && (path == 3 || (path == 0 && N >= kCarryMinPoints)) ? 1 : 0;
     pl->gshift = 0;
     pl->nbins = 0;
     pl->nbits = 0;
@@ -1415,7 +1456,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         pl->nbins = 1 << pl->nbits;
         const long long per_bin = cdiv(M, pl->nbins);
         while ((1ll << pl->gshift) < per_bin) ++pl->gshift;
-        pl->lds = bins_lds_bytes(1 << pl->gshift, K);  // at most 50 KB (G 128 / K 32, G 64 / K 64)
+        pl->lds = bins_lds_bytes(1 << pl->gshift, K, pl->carry);  // <= 50 KB
         // points per k_part thread: the largest power of two up to 16 that
         // still gives about 1024 tiles (small clouds spread over every CU)
         int per = 1;
@@ -1446,10 +1487,15 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     off = align256(off + (size_t)pl->C * sizeof(unsigned long long));
     pl->off_kcs = off;
     off = align256(off + (pl->C > 0 ? (size_t)M * sizeof(int) : 0));
+    pl->zero_bytes = off;  // the scratch tail starts here
     pl->off_cm = off;
     off = align256(off + (size_t)pl->nbins * (size_t)pl->ptiles * sizeof(unsigned));
     pl->off_stage = off;
     off = align256(off + (size_t)pl->ptiles * (size_t)(kBlock * pl->pper) * sizeof(unsigned));
+    pl->off_stage_pt = off;
+    off = align256(off + (pl->carry ? (size_t)pl->ptiles * (size_t)(kBlock * pl->pper) *
+                                          sizeof(float4)
+                                    : 0));
     pl->bytes = off;
     return VOX_OK;
 }
@@ -1504,6 +1550,7 @@ struct Buffers {
     int* kcs;
     unsigned* cm;
     unsigned* stage;
+    float4* stage_pt;
 };
 
 Buffers carve(void* ws, const Plan& pl) {
@@ -1522,6 +1569,7 @@ Buffers carve(void* ws, const Plan& pl) {
     x.kcs = reinterpret_cast<int*>(b + pl.off_kcs);
     x.cm = reinterpret_cast<unsigned*>(b + pl.off_cm);
     x.stage = reinterpret_cast<unsigned*>(b + pl.off_stage);
+    x.stage_pt = reinterpret_cast<float4*>(b + pl.off_stage_pt);
     return x;
 }
 
@@ -1561,19 +1609,19 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
                   const Buffers& bf, int32_t* num_voxels, int32_t* point_pillar,
                   hipStream_t st, hipEvent_t* ev) {
     if (pl.part) {
-        decltype(&k_part<1>) kern = &k_part<1>;
+        decltype(&k_part<1, false>) kern = pl.carry ? &k_part<1, true> : &k_part<1, false>;
         switch (pl.pper) {
-            case 2: kern = &k_part<2>; break;
-            case 4: kern = &k_part<4>; break;
-            case 8: kern = &k_part<8>; break;
-            case 16: kern = &k_part<16>; break;
+            case 2: kern = pl.carry ? &k_part<2, true> : &k_part<2, false>; break;
+            case 4: kern = pl.carry ? &k_part<4, true> : &k_part<4, false>; break;
+            case 8: kern = pl.carry ? &k_part<8, true> : &k_part<8, false>; break;
+            case 16: kern = pl.carry ? &k_part<16, true> : &k_part<16, false>; break;
             default: break;
         }
         hipExtLaunchKernelGGL(kern, dim3((unsigned)pl.ptiles), dim3(kBlock), 0, st, ev_start(ev),
                               ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
                            (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of,
-                           pl.nbits, pl.ptiles, bf.cm, bf.stage, bf.hdr, num_voxels,
+                           pl.nbits, pl.ptiles, bf.cm, bf.stage, bf.stage_pt, bf.hdr, num_voxels,
                            point_pillar);
         return last_launch();
     }
@@ -1591,10 +1639,12 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
     const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
     if (pl.part) {
         // one block per bin; all blocks share the workspace release
-        hipExtLaunchKernelGGL(k_bins, dim3((unsigned)pl.nbins), dim3(kBinBlock), (unsigned)pl.lds, st,
+        hipExtLaunchKernelGGL(pl.carry ? k_bins<true> : k_bins<false>, dim3((unsigned)pl.nbins),
+                              dim3(kBinBlock), (unsigned)pl.lds, st,
                               ev_start(ev), ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, bf.cm, bf.stage,
-                           pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.K, pl.M,
+                           bf.stage_pt, pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.K,
+                           pl.M,
                            bf.kept, bf.compact,
                            (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                            reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
@@ -1664,6 +1714,22 @@ int64_t vox_workspace_bytes(int64_t n_points, int32_t max_voxels, int32_t max_po
     const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
     if (rc != VOX_OK) return rc;
     return (int64_t)pl.bytes;
+}
+
+int64_t vox_workspace_zero_bytes(int64_t n_points, int32_t max_voxels, int32_t max_points,
+                                 const vox_options* options) {
+    Plan pl;
+    const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
+    if (rc != VOX_OK) return rc;
+    return (int64_t)pl.zero_bytes;
+}
+
+int32_t vox_select_route(int64_t n_points, int32_t max_voxels, int32_t max_points,
+                         const vox_options* options) {
+    Plan pl;
+    const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
+    if (rc != VOX_OK) return rc;
+    return pl.part ? (pl.carry ? 3 : 2) : 1;
 }
 
 int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,

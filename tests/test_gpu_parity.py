@@ -56,19 +56,25 @@ def assert_bitwise(got, want, what=""):
 # ------------------------------------------------------ workspace hygiene ---
 
 def test_workspace_all_zero_after_calls_of_different_shapes():
-    """Each call returns every workspace word it wrote to zero, so one cached
-    workspace can serve calls whose layouts differ (N, M, K)."""
+    """Each call returns every word of its workspace's zero part to zero, and
+    the cached workspace serves calls whose layouts differ (N, M, K, route):
+    a later call whose zero part reaches into an earlier call's scratch gets
+    that stretch cleared first."""
     stream = torch.cuda.current_stream(DEV).cuda_stream
-    seq = [("tiny", None), ("kitti_frame", 40000), ("voxel3d", 60000), ("uniform_25k", None),
-           ("kitti_frame", 9000), ("voxel3d", 3000)]
-    for name, n in seq:
+    seq = [("tiny", None, {}), ("kitti_frame", 40000, {}), ("voxel3d", 60000, {}),
+           ("kitti_frame", 40000, dict(select_path=1)), ("uniform_25k", None, {}),
+           ("kitti_frame", 9000, {}), ("voxel3d", 3000, dict(select_path=1)),
+           ("voxel3d", 3000, {})]
+    for name, n, kw in seq:
         cfg = get_config(name)
+        p = cfg.params
         pts, _ = generate(name, n=n) if n else generate(name)
-        say(f"hygiene {name} N={pts.shape[0]}")
-        got = gpu_vox(pts, params_of(cfg))
+        say(f"hygiene {name} N={pts.shape[0]} {kw}")
+        got = gpu_vox(pts, params_of(cfg), **kw)
         ws = vox._workspaces._cache[(DEV.index, stream)]
-        assert vox.workspace_is_clean(ws), f"workspace dirty after {name}"
-        assert_bitwise(got, oracle.voxelize_params(pts, cfg.params), name)
+        zb = vox.workspace_zero_bytes(pts.shape[0], p.max_voxels, p.max_points, **kw)
+        assert vox.workspace_is_clean(ws, zb), f"workspace zero part dirty after {name}"
+        assert_bitwise(got, oracle.voxelize_params(pts, cfg.params), f"{name} {kw}")
 
 
 # ------------------------------------------------------------ K1 binning ----
@@ -189,8 +195,11 @@ def test_seeded_fuzz_small_problems():
     rng = np.random.default_rng(2024)
     for t in range(120):
         pts, prm = _random_problem(rng)
-        # both select routes: every third case takes the bucket route
-        path = 1 if t % 3 == 1 else 0
+        # every select route: automatic (2 here), buckets, gathered, carried
+        # (the partitioned ones exist for K <= 64)
+        path = (0, 1, 2, 3)[t % 4]
+        if prm[3] > 64 and path >= 2:
+            path = 1
         say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]} path={path}")
         got = gpu_vox(pts, prm, point_map=True, select_path=path)
         want = oracle.voxelize_map(pts, *prm)
@@ -227,7 +236,8 @@ def test_result_independent_of_table_and_hash(name):
                dict(compact_table=1), dict(compact_table=1, hash=1),
                dict(select_path=1, compact_table=1, bucket_cap=1),
                dict(select_path=2, table_slots=3 * M, hash=1),
-               dict(select_path=1, table_slots=3 * M, hash=2)):
+               dict(select_path=1, table_slots=3 * M, hash=2), dict(select_path=2),
+               dict(select_path=3), dict(select_path=3, compact_table=1)):
         say(f"invariance {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
 
@@ -242,7 +252,7 @@ def test_small_prefix_and_chunked_path(name):
     for kw in (dict(prefix_points=4096), dict(prefix_points=1), dict(chunked=True),
                dict(chunked=True, table_slots=2 * cfg.params.max_voxels),
                dict(prefix_points=4096, compact_table=1), dict(chunked=True, compact_table=1),
-               dict(chunked=True, select_path=1)):
+               dict(chunked=True, select_path=1), dict(chunked=True, select_path=3)):
         say(f"prefix/chunked {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
     p = cfg.params
@@ -266,7 +276,7 @@ def test_needs_chunked_status_is_reported_and_workspace_stays_clean():
     nv = v.run(x)
     torch.cuda.synchronize()
     assert int(nv.item()) == vox.VOX_STATUS_NEEDS_CHUNKED
-    assert vox.workspace_is_clean(v.workspace)
+    assert vox.workspace_is_clean(v.workspace, v.zero_bytes)
 
 
 def test_repeated_calls_identical_and_workspace_zero():
@@ -281,7 +291,7 @@ def test_repeated_calls_identical_and_workspace_zero():
     for it in range(10):
         v.run(x)
         torch.cuda.synchronize()
-        assert vox.workspace_is_clean(v.workspace), f"workspace dirty after {it}"
+        assert vox.workspace_is_clean(v.workspace, v.zero_bytes), f"workspace dirty after {it}"
         got = tuple(t.cpu().numpy() for t in v.outputs())
         assert_bitwise(got, want, f"repeat {it}")
 
@@ -328,6 +338,7 @@ def test_max_points_variants(K):
     want = oracle.voxelize(pts, *prm)
     assert_bitwise(gpu_vox(pts, prm), want, f"K={K}")
     if K <= 64:
+        assert_bitwise(gpu_vox(pts, prm, select_path=3), want, f"K={K} carried")
         assert_bitwise(gpu_vox(pts, prm, select_path=1), want, f"K={K} buckets")
         # a small bucket sends most arrivals of the heavy pillars to the overflow row
         assert_bitwise(gpu_vox(pts, prm, select_path=1, bucket_cap=K), want,
@@ -362,6 +373,7 @@ def test_single_cell_heavy_pillar():
     want = oracle.voxelize(pts, *prm)
     assert_bitwise(gpu_vox(pts, prm), want, "heavy cell")
     assert_bitwise(gpu_vox(pts, prm, select_path=1), want, "heavy cell, buckets")
+    assert_bitwise(gpu_vox(pts, prm, select_path=3), want, "heavy cell, carried rows")
 
 
 @pytest.mark.parametrize("per_cell,K", [(70, 64), (200, 32), (40, 5)])
@@ -381,4 +393,5 @@ def test_bin_spanning_several_chunks(per_cell, K):
     say(f"multi-chunk bin per_cell={per_cell} K={K}")
     want = oracle.voxelize(pts, *prm)
     assert_bitwise(gpu_vox(pts, prm, select_path=2), want, "multi-chunk bin")
+    assert_bitwise(gpu_vox(pts, prm, select_path=3), want, "multi-chunk bin, carried rows")
     assert_bitwise(gpu_vox(pts, prm, select_path=1), want, "multi-chunk bin, buckets")

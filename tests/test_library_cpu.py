@@ -134,7 +134,7 @@ def test_select_path_option_limits():
     assert vox.workspace_bytes(1000, 262144, 32, select_path=2) > 0
     # K > 64 or more than 262144 pillars: only the bucket route exists
     assert vox.plan(1000, 100, 65)["bucket_cap"] == 0
-    for bad in (dict(select_path=-1), dict(select_path=3)):
+    for bad in (dict(select_path=-1), dict(select_path=4)):
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(1000, 100, 32, **bad)
     assert vox.workspace_bytes(1000, 131072, 64, select_path=2) > 0
@@ -142,6 +142,8 @@ def test_select_path_option_limits():
         assert vox.workspace_bytes(*args) > 0
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(*args, select_path=2)
+        with pytest.raises(vox.VoxError):
+            vox.workspace_bytes(*args, select_path=3)
 
 
 def test_hash_option_range():
@@ -150,3 +152,32 @@ def test_hash_option_range():
     for h in (-1, 3):
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(1000, 100, 32, hash=h)
+
+
+def test_workspace_zero_part():
+    """The zero part precedes the scratch tail; the bucket route has none."""
+    for args in ((122880, 12000, 32), (2097152, 60000, 32), (1048576, 40000, 5), (0, 1, 1)):
+        total = vox.workspace_bytes(*args)
+        zero = vox.workspace_zero_bytes(*args)
+        assert 256 <= zero <= total and zero % 256 == 0
+        assert vox.workspace_zero_bytes(*args, select_path=1) == \
+            vox.workspace_bytes(*args, select_path=1)
+    assert vox.workspace_zero_bytes(122880, 12000, 32) < vox.workspace_bytes(122880, 12000, 32)
+    with pytest.raises(vox.VoxError):
+        vox.workspace_zero_bytes(-1, 12000, 32)
+
+
+def test_select_route_rules():
+    """Automatic route: partitioned with carried rows from 2^19 points up,
+    partitioned with gathered rows below, buckets for K > 64."""
+    assert vox.select_route(122880, 12000, 32) == 2
+    assert vox.select_route(1 << 19, 12000, 32) == 3
+    assert vox.select_route(2097152, 60000, 32) == 3
+    assert vox.select_route(1000, 100, 65) == 1
+    for p in (1, 2, 3):
+        assert vox.select_route(122880, 12000, 32, select_path=p) == p
+    # carried rows need room for them in the scratch tail
+    assert vox.workspace_bytes(122880, 12000, 32, select_path=3) > \
+        vox.workspace_bytes(122880, 12000, 32, select_path=2)
+    assert vox.workspace_zero_bytes(122880, 12000, 32, select_path=3) == \
+        vox.workspace_zero_bytes(122880, 12000, 32, select_path=2)
