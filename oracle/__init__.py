@@ -4,9 +4,10 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg use this package. The GPU library never imports, links or calls it, and it
 imports nothing from the GPU library.
 
-``voxelize`` and ``bin_points`` wrap the sequential C definition in
-``voxelize_oracle.c`` (see its header for the passages of the "Voxelize" page
-each step follows and the readings taken where the page is silent).
+``voxelize``, ``voxelize_map``, ``downsample`` and ``bin_points`` wrap the
+sequential C definitions in ``voxelize_oracle.c`` (see its comments for the
+passages each step follows and the readings taken where the pages are
+silent).
 """
 from __future__ import annotations
 
@@ -51,6 +52,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.oracle_voxelize_map.argtypes = [vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32,
                                         ctypes.c_int32, vp, vp, vp, vp, vp]
     lib.oracle_voxelize_map.restype = ctypes.c_int
+    lib.oracle_downsample.argtypes = [vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
+                                      vp]
+    lib.oracle_downsample.restype = ctypes.c_int
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -134,6 +138,29 @@ def voxelize_map(points: np.ndarray, range_: Sequence[float], cell: Sequence[flo
         raise MemoryError("oracle_voxelize_map could not allocate its dictionary")
     V = int(nv[0])
     return voxels[:V].copy(), coords[:V].copy(), counts[:V].copy(), pmap
+
+
+def downsample(points: np.ndarray, range_: Sequence[float], cell: Sequence[float],
+               grid: Sequence[int], max_voxels: int, lib: Optional[ctypes.CDLL] = None
+               ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Voxel-grid downsampling: (centroids [V,4] f32 (x, y, z, intensity means),
+    coords [V,3] i32 (z,y,x), counts [V] i32 (all points of the voxel))."""
+    lib = lib or load()
+    p = _points(points)
+    r, c, g = _param_arrays(range_, cell, grid)
+    M = int(max_voxels)
+    if M <= 0:
+        raise ValueError("max_voxels must be positive")
+    cen = np.full((M, 4), 0xFFFFFFFF, dtype=np.uint32).view(np.float32)
+    coords = np.full((M, 3), -1, dtype=np.int32)
+    counts = np.full((M,), -1, dtype=np.int32)
+    nv = np.zeros(1, dtype=np.int32)
+    rc = lib.oracle_downsample(_ptr(p), p.shape[0], _ptr(r), _ptr(c), _ptr(g), M, _ptr(cen),
+                               _ptr(coords), _ptr(counts), _ptr(nv))
+    if rc != 0:
+        raise MemoryError("oracle_downsample could not allocate")
+    V = int(nv[0])
+    return cen[:V].copy(), coords[:V].copy(), counts[:V].copy()
 
 
 def voxelize_params(points: np.ndarray, params, lib: Optional[ctypes.CDLL] = None):

@@ -31,6 +31,9 @@
  *   - range tests are made on the float floor value before any conversion,
  *     every operation in IEEE fp32 round-to-nearest, no FMA contraction.
  *
+ * oracle_downsample (end of file) adds voxel-grid downsampling, one mean
+ * point per kept voxel, from a second page (see its comment).
+ *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared
  */
 #include <math.h>
@@ -254,6 +257,77 @@ int oracle_voxelize_map(const float *points, int64_t n, const float range[6],
     }
     *num_voxels = (int32_t)V;
 
+    free(total);
+    map_free(&dict);
+    return 0;
+}
+
+/*
+ * Voxel-grid downsampling: one output point per kept voxel, the mean of the
+ * points in it. Source: the GPU K-D tree ICP page ("operation 1" of its
+ * section 4.4, a voxel_downsample kernel), whose kernel truncates the cell
+ * index and accumulates with float atomics, so its result depends on thread
+ * order. Readings taken:
+ *   - binning, numbering in first-occurrence order and the max_voxels cap are
+ *     those of oracle_voxelize_map above (floorf cell index, not truncation);
+ *   - each of x, y, z and intensity is summed over the voxel's points in
+ *     input order in double precision, the sum divided by the count in double
+ *     precision, and the quotient rounded once to float (round to nearest);
+ *   - counts[p] = every point of the voxel (there is no max_points here).
+ * centroids is [max_voxels, 4] float, coords [max_voxels, 3] int32 (z, y, x),
+ * counts [max_voxels] int32; rows [0, V) are written and V goes to
+ * *num_voxels. Returns 0, or -1 if memory is unavailable.
+ */
+int oracle_downsample(const float *points, int64_t n, const float range[6], const float cell[3],
+                      const int32_t grid[3], int32_t max_voxels, float *centroids,
+                      int32_t *coords, int32_t *counts, int32_t *num_voxels)
+{
+    oracle_grid g = make_grid(range, cell, grid);
+    key_map dict;
+    if (map_init(&dict, max_voxels) != 0) {
+        map_free(&dict);
+        return -1;
+    }
+    double *sum = (double *)calloc((size_t)max_voxels * 4 + 4, sizeof(double));
+    int64_t *total = (int64_t *)calloc((size_t)max_voxels + 1, sizeof(int64_t));
+    if (!sum || !total) {
+        free(sum);
+        free(total);
+        map_free(&dict);
+        return -1;
+    }
+    int64_t V = 0;
+    for (int64_t i = 0; i < n; i++) {
+        const float *p = points + 4 * i;
+        int64_t cx, cy, cz;
+        if (!bin_point(p, &g, range[5], &cx, &cy, &cz))
+            continue;
+        int64_t key = flat_key(&g, cx, cy, cz);
+        int64_t s = map_slot(&dict, key);
+        int64_t pid;
+        if (dict.keys[s] == key) {
+            pid = dict.vals[s];
+        } else if (V < max_voxels) {
+            pid = V++;
+            dict.keys[s] = key;
+            dict.vals[s] = (int32_t)pid;
+            coords[3 * pid + 0] = (int32_t)cz;
+            coords[3 * pid + 1] = (int32_t)cy;
+            coords[3 * pid + 2] = (int32_t)cx;
+        } else {
+            continue;  /* its voxel is past the cap */
+        }
+        for (int c = 0; c < 4; c++)
+            sum[4 * pid + c] += (double)p[c];  /* input order, double precision */
+        total[pid] += 1;
+    }
+    for (int64_t pid = 0; pid < V; pid++) {
+        for (int c = 0; c < 4; c++)
+            centroids[4 * pid + c] = (float)(sum[4 * pid + c] / (double)total[pid]);
+        counts[pid] = (int32_t)total[pid];
+    }
+    *num_voxels = (int32_t)V;
+    free(sum);
     free(total);
     map_free(&dict);
     return 0;

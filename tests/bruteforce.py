@@ -108,3 +108,45 @@ def exact_cell(v, v0, cell) -> int:
     diff = round_f32(Fraction(float(F32(v))) - Fraction(float(F32(v0))))
     quo = round_f32(Fraction(float(diff)) / Fraction(float(F32(cell))))
     return int(np.floor(float(quo)))
+
+
+# ---- voxel-grid downsampling by grouping (numpy) ---------------------------
+
+def downsample_np(points, range_, cell, grid, max_voxels):
+    """Per-voxel means by numpy grouping: binning by ``bin_np``, voxels
+    numbered by first occurrence (``np.unique``) and capped at max_voxels,
+    x/y/z/intensity summed in float64 with ``np.add.at`` (unbuffered, one
+    index after the other, i.e. in input order), divided by the counts in
+    float64 and rounded once to float32."""
+    p = np.ascontiguousarray(points, dtype=F32)
+    valid, key = bin_np(p, range_, cell, grid)
+    idx = np.flatnonzero(valid)
+    if idx.size == 0:
+        return np.zeros((0, 4), F32), np.zeros((0, 3), np.int32), np.zeros((0,), np.int32)
+    k = key[idx]
+    uk, first, inv = np.unique(k, return_index=True, return_inverse=True)
+    order = np.argsort(first, kind="stable")        # voxels by first occurrence
+    rank = np.empty_like(order)
+    rank[order] = np.arange(order.size)
+    pid = rank[inv.reshape(-1)]
+    V = min(uk.size, int(max_voxels))
+    keep = pid < V
+    sums = np.zeros((V, 4), np.float64)
+    with np.errstate(invalid="ignore"):  # inf + -inf intensity sums are NaN
+        np.add.at(sums, pid[keep], p[idx[keep]].astype(np.float64))
+    counts = np.bincount(pid[keep], minlength=V)
+    with np.errstate(invalid="ignore"):
+        cen = (sums / counts[:, None].astype(np.float64)).astype(F32)
+    coords = decode(uk[order[:V]], grid)
+    return cen, coords, counts.astype(np.int32)
+
+
+def same_f32(a, b) -> bool:
+    """Bitwise equality of float32 arrays, except that any NaN equals any NaN."""
+    a = np.asarray(a, F32)
+    b = np.asarray(b, F32)
+    if a.shape != b.shape:
+        return False
+    na, nb = np.isnan(a), np.isnan(b)
+    return bool(np.array_equal(na, nb) and
+                np.array_equal(a.view(np.uint32)[~na], b.view(np.uint32)[~nb]))

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from bruteforce import bin_np, exact_cell, sort_then_segment
+from bruteforce import bin_np, downsample_np, exact_cell, same_f32, sort_then_segment
 from workloads import generate, get_config
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -40,6 +40,17 @@ MUTANTS = {
                     ("(pid * K + (total[pid] - 1))", "(pid * K + (total[pid] - 1) % K)")],
     "x_min_for_y": [("(y - g->y_min) / g->vy", "(y - g->x_min) / g->vy")],
     "map_zero_for_dropped": [("point_pillar[i] = -1;", "point_pillar[i] = 0;")],
+    # voxel-grid downsampling
+    "ds_float_accumulator": [("sum[4 * pid + c] += (double)p[c];  /* input order, double precision */",
+                              "sum[4 * pid + c] = (double)((float)sum[4 * pid + c] + p[c]);")],
+    "ds_count_plus_one": [("centroids[4 * pid + c] = (float)(sum[4 * pid + c] / (double)total[pid]);",
+                           "centroids[4 * pid + c] = (float)(sum[4 * pid + c] / (double)(total[pid] + 1));")],
+    "ds_channel_swap": [("centroids[4 * pid + c] = (float)(sum[4 * pid + c] / (double)total[pid]);",
+                         "centroids[4 * pid + c] = (float)(sum[4 * pid + (c ^ 1)] / (double)total[pid]);")],
+    "ds_counts_capped_at_1": [("        counts[pid] = (int32_t)total[pid];",
+                               "        counts[pid] = 1;")],
+    "ds_skip_first_point": [("            continue;  /* its voxel is past the cap */\n        }\n        for (int c = 0; c < 4; c++)",
+                             "            continue;  /* its voxel is past the cap */\n        }\n        if (total[pid] == 0 && sum[4 * pid] == 0.0) { total[pid] += 1; continue; }\n        for (int c = 0; c < 4; c++)")],
     "map_only_kept_rows": [("        if (point_pillar)\n            point_pillar[i] = (int32_t)pid;\n        total[pid] += 1;\n        if (total[pid] <= K) {",
                             "        total[pid] += 1;\n        if (total[pid] <= K) {\n            if (point_pillar)\n                point_pillar[i] = (int32_t)pid;")],
 }
@@ -134,6 +145,25 @@ def _battery(lib):
         if not _same(got, sort_then_segment(pts, r, (vx, vy, 4.0), (gx, gy, 1), K, M)):
             fails.append("brute:random")
             break
+    # voxel-grid downsampling against numpy grouping and a discriminating case
+    for name, n in (("kitti_frame", None), ("tiny", None), ("voxel3d", 100000)):
+        p = get_config(name).params
+        pts, _ = generate(name, n=n)
+        got = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels, lib=lib)
+        want = downsample_np(pts, p.range_, p.cell, p.grid, p.max_voxels)
+        if not (same_f32(got[0], want[0]) and np.array_equal(got[1], want[1])
+                and np.array_equal(got[2], want[2])):
+            fails.append("downsample:" + name)
+    x = np.array([1000.269775390625, 1000.0409545898438, 1000.0165405273438,
+                  1000.8132934570312, 1000.9127807617188, 1000.6066284179688,
+                  1000.7294921875, 1000.5436401367188, 1000.93505859375,
+                  1000.8158569335938], F32)
+    pts = np.zeros((x.size, 4), F32)
+    pts[:, 0] = x
+    cen, _, _ = oracle.downsample(pts, (999.0, 0.0, -1.0, 1003.0, 4.0, 1.0), (1.0, 1.0, 2.0),
+                                  (4, 4, 1), 4, lib=lib)
+    if cen.shape != (1, 4) or cen[0, 0] != F32(1000.5684204101562):
+        fails.append("downsample:double_sum")
     return fails
 
 
