@@ -202,6 +202,39 @@ int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,
              int32_t* bucket_cap);
 
 /*
+ * Voxel-grid downsampling (NEXT row f3; the voxel_downsample operation, section
+ * 4.4 "operation 1", of the GPU K-D tree ICP page, which truncates the cell
+ * index and averages with float atomics). One mean point per kept voxel:
+ *   - binning, voxel numbering in first-occurrence order and the max_voxels
+ *     cap are voxelize()'s (floorf cell index, same reject rules);
+ *   - centroids[p] (x, y, z, intensity) = for each channel, the sum over the
+ *     voxel's points in input order in double precision, divided by the count
+ *     in double precision, rounded once to float (round to nearest); NaN and
+ *     Inf propagate through the sums;
+ *   - coords[p] = (z, y, x) of the voxel, counts[p] = all of its points.
+ * points: device [N,4] f32, 16-byte aligned. centroids: device [max_voxels,4]
+ * f32, 16-byte aligned; coords [max_voxels,3] i32; counts [max_voxels] i32;
+ * num_voxels [1] i32 receives V or a VOX_STATUS_* code, as for voxelize().
+ * Rows [0, V) are written, rows past V untouched. options: table_slots,
+ * prefix_points, hash and compact_table apply; select_path must be 0 or 3
+ * (the route with rows carried is the only one); max_voxels <= 262144.
+ * chunked = 1 inserts chunk by chunk with a host sync between chunks (needed
+ * when the status is VOX_STATUS_NEEDS_CHUNKED). The workspace follows the
+ * rules of vox_workspace_bytes() with the two sizes below. Asynchronous on
+ * `stream` unless chunked; allocates nothing. Returns VOX_OK or a negative
+ * code (VOX_EINVAL, VOX_EWORKSPACE, VOX_EHIP).
+ */
+int vox_downsample(const float* points, int64_t n_points, const float range[6],
+                   const float cell[3], const int32_t grid[3], int32_t max_voxels,
+                   float* centroids, int32_t* coords, int32_t* counts, int32_t* num_voxels,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                   const vox_options* options, int32_t chunked);
+int64_t vox_downsample_workspace_bytes(int64_t n_points, int32_t max_voxels,
+                                       const vox_options* options);
+int64_t vox_downsample_workspace_zero_bytes(int64_t n_points, int32_t max_voxels,
+                                            const vox_options* options);
+
+/*
  * The per-point binning step alone ("Binning a point"), for parity tests:
  * valid[i] = 1 if point i is kept, else 0; key[i] = (cz * gy + cy) * gx + cx
  * as int64 (cz = 0 in pillar mode), or -1. valid and key are device arrays of

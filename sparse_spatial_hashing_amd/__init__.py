@@ -68,6 +68,13 @@ def _load() -> ctypes.CDLL:
     lib.vox_workspace_zero_bytes.restype = i64
     lib.vox_select_route.argtypes = [i64, i32, i32, op]
     lib.vox_select_route.restype = i32
+    lib.vox_downsample_workspace_bytes.argtypes = [i64, i32, op]
+    lib.vox_downsample_workspace_bytes.restype = i64
+    lib.vox_downsample_workspace_zero_bytes.argtypes = [i64, i32, op]
+    lib.vox_downsample_workspace_zero_bytes.restype = i64
+    lib.vox_downsample.argtypes = [vp, i64, vp, vp, vp, i32, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                   vp, op, i32]
+    lib.vox_downsample.restype = ctypes.c_int
     common = [vp, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.voxelize.argtypes = common
     lib.voxelize.restype = ctypes.c_int
@@ -258,6 +265,56 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     if point_map:
         return voxels[:V], coords[:V], counts[:V], pmap
     return voxels[:V], coords[:V], counts[:V]
+
+
+def downsample_workspace_bytes(n_points: int, max_voxels: int, **opts) -> Tuple[int, int]:
+    """(workspace bytes, bytes of its zero part) for vox_downsample."""
+    o = _options(**opts)
+    n = _lib.vox_downsample_workspace_bytes(int(n_points), int(max_voxels), o)
+    z = _lib.vox_downsample_workspace_zero_bytes(int(n_points), int(max_voxels), o)
+    if n < 0 or z < 0:
+        raise VoxError(int(min(n, z)), "vox_downsample_workspace_bytes")
+    return int(n), int(z)
+
+
+@torch.no_grad()
+def downsample(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
+               grid: Sequence[int], max_voxels: int, *, table_slots: int = 0,
+               prefix_points: int = 0, hash: int = 0, compact_table: int = 0,
+               chunked: bool = False):
+    """Voxel-grid downsampling: (centroids [V,4] f32 (x, y, z, intensity means),
+    coords [V,3] i32 (z, y, x), counts [V] i32) for the first max_voxels voxels
+    in first-occurrence order. The chunked route is taken when the single pass
+    reports that the cap could not be decided."""
+    _check_points(points)
+    dev = points.device
+    N, M = points.shape[0], int(max_voxels)
+    kw = dict(table_slots=table_slots, prefix_points=prefix_points, hash=hash,
+              compact_table=compact_table)
+    opts = _options(**kw)
+    nbytes, zbytes = downsample_workspace_bytes(N, M, **kw)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        ws = _workspaces.get(dev, stream, nbytes, zbytes)
+        cen = torch.empty((M, 4), dtype=torch.float32, device=dev)
+        coords = torch.empty((M, 3), dtype=torch.int32, device=dev)
+        counts = torch.empty((M,), dtype=torch.int32, device=dev)
+        nv = torch.empty((1,), dtype=torch.int32, device=dev)
+        r, c, g = _host_params(range_, cell, grid)
+        args = [ctypes.c_void_p(points.data_ptr()), N, r, c, g, M,
+                ctypes.c_void_p(cen.data_ptr()), ctypes.c_void_p(coords.data_ptr()),
+                ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(nv.data_ptr()),
+                ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                ctypes.c_void_p(stream), opts]
+        _check(_lib.vox_downsample(*args, 1 if chunked else 0), "vox_downsample")
+        V = int(nv.item())
+        if V == VOX_STATUS_NEEDS_CHUNKED and not chunked:
+            _check(_lib.vox_downsample(*args, 1), "vox_downsample (chunked)")
+            V = int(nv.item())
+        if V < 0:
+            _workspaces.drop(dev, stream)
+            raise VoxError(V, "vox_downsample (device status)")
+    return cen[:V], coords[:V], counts[:V]
 
 
 @torch.no_grad()

@@ -1326,6 +1326,164 @@ void k_bins(
     }
 }
 
+// ------------------------------------------------- voxel-grid downsampling --
+//
+// One mean point per kept voxel (the voxel_downsample operation of the GPU
+// K-D tree ICP page, "operation 1" of its section 4.4): the pipeline up to
+// k_part (with rows carried) is the one above; k_centroid takes one block
+// per bin like k_bins and ranks each arrival in its voxel the same way. Each
+// round's arrivals are placed in LDS grouped by voxel in arrival order, which
+// is input order, and one thread per voxel adds its group into four double
+// sums in that order; the means are the sums over the counts, rounded once to
+// float. The sums are sequential in input order, so the result is the same
+// on every run and matches any other double-precision implementation of the
+// same order.
+
+template <int NW>
+__device__ __forceinline__ void wave_scan_pids(unsigned* cnt_round, unsigned* seg, int G,
+                                               int lane) {
+    // exclusive prefix over pids 0..G-1 by one wavefront (pids lane, lane+64, ...)
+    unsigned carry = 0;
+    for (int p0 = 0; p0 < G; p0 += kWave) {
+        const int p = p0 + lane;
+        const unsigned c = p < G ? cnt_round[p] : 0u;
+        const unsigned incl = wave_incl_scan(c, lane);
+        if (p < G) seg[p] = carry + incl - c;
+        carry += (unsigned)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    }
+}
+
+__global__ __launch_bounds__(kBinBlock) void k_centroid(
+    const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
+    const float4* __restrict__ stage_pt, long long ptiles, int ptile, int gshift, int nbits,
+    int M, long long* __restrict__ kept_key, unsigned long long* __restrict__ compact, unsigned C,
+    int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ centroids,
+    int* __restrict__ coords, int* __restrict__ counts, int* __restrict__ num_voxels,
+    int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
+    unsigned long long* __restrict__ tile_state, long long ntiles, Header* __restrict__ hdr) {
+    extern __shared__ float4 lds_rows[];
+    const int G = 1 << gshift;
+    float4* rowbuf = lds_rows;                   // [kBinBlock] this round's rows, by voxel
+    unsigned* running = reinterpret_cast<unsigned*>(rowbuf + kBinBlock);  // [G] arrivals so far
+    unsigned* wbuf = running + G;                // [3][kBinWaves * G] per-wavefront counts
+    unsigned* roff = wbuf + 3 * kBinWaves * G;   // [kBinBlock + 1]
+    unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock]
+    unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
+    unsigned* before = wsum + kBinWaves;         // [G] arrivals before this round
+    unsigned* cnt_round = before + G;            // [G] arrivals in this round
+    unsigned* seg = cnt_round + G;               // [G] start of the voxel's group in rowbuf
+
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = t / kWave;
+    const long long b = blockIdx.x;
+    unsigned e = 0u;
+    if ((long long)t < ptiles) e = cm[(size_t)b * ptiles + t];
+    const int status = hdr->status;
+    const long long V = status > 0 ? status : 0;
+    const long long distinct = hdr->distinct;
+    if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    release_workspace(b * kBinBlock + t, (long long)gridDim.x * kBinBlock, distinct, V, M,
+                      occ_slot, table, S, kept_key, compact, C, kept_cslot, tile_state, ntiles,
+                      hdr, num_voxels);
+    if (status <= 0) return;
+
+    const long long nbins = 1ll << nbits;
+    const int Gb = b < V ? (int)((V - b + nbins - 1) >> nbits) : 0;
+    for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
+    for (int x = t; x < 3 * kBinWaves * G; x += kBinBlock) wbuf[x] = 0u;
+    double sx = 0.0, sy = 0.0, sz = 0.0, sw = 0.0;  // thread t < Gb: voxel t's sums
+    unsigned round = 0;
+    for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
+        const long long tt = tg + t;
+        if (tg > 0) {
+            e = 0u;
+            if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
+        }
+        unsigned ng;
+        const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
+        roff[t] = ro;
+        rsrc[t] = e & 0xffffu;
+        const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+        __syncthreads();
+        for (unsigned x0 = 0; x0 < ng; x0 += kBinBlock) {
+            const unsigned x = x0 + (unsigned)t;
+            bool valid = x < ng;
+            unsigned pl = 0u;
+            float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (valid) {
+                int lo = 0, hi = nruns;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (roff[mid] <= x) lo = mid;
+                    else hi = mid;
+                }
+                const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
+                pl = staging[src] >> 16;
+                row = stage_pt[src];
+                if (pl >= (unsigned)Gb) {  // not on a clean workspace
+                    report_error(hdr, num_voxels, 4u);
+                    valid = false;
+                    pl = 0u;
+                }
+            }
+            unsigned* cur = wbuf + (round % 3u) * (kBinWaves * G);
+            unsigned* nxt = wbuf + ((round + 1u) % 3u) * (kBinWaves * G);
+            for (int y = t; y < kBinWaves * G; y += kBinBlock) nxt[y] = 0u;
+            const unsigned long long m = match_mask(pl, valid, gshift);
+            const unsigned rank = (unsigned)__popcll(m & lanes_below(lane));
+            if (valid && (m & lanes_above(lane)) == 0ull) cur[w * G + pl] = (unsigned)__popcll(m);
+            __syncthreads();
+            if (w == 0) {
+                // per voxel: prefix over the wavefronts on top of the earlier
+                // arrivals, this round's count, then the groups' starts
+                for (int p = lane; p < G; p += kWave) {
+                    unsigned acc = running[p];
+                    before[p] = acc;
+                    for (int ww = 0; ww < kBinWaves; ++ww) {
+                        const unsigned cw = cur[ww * G + p];
+                        cur[ww * G + p] = acc;
+                        acc += cw;
+                    }
+                    cnt_round[p] = acc - before[p];
+                    running[p] = acc;
+                }
+                wave_scan_pids<kBinWaves>(cnt_round, seg, G, lane);
+            }
+            __syncthreads();
+            if (valid) {
+                const unsigned r = cur[w * G + pl] + rank;  // arrival rank in the voxel
+                rowbuf[seg[pl] + (r - before[pl])] = row;
+            }
+            __syncthreads();
+            if (t < Gb) {
+                // this voxel's rows of the round, in input order
+                const unsigned s0 = seg[t], n = cnt_round[t];
+                for (unsigned k = 0; k < n; ++k) {
+                    const float4 q = rowbuf[s0 + k];
+                    sx += (double)q.x;
+                    sy += (double)q.y;
+                    sz += (double)q.z;
+                    sw += (double)q.w;
+                }
+            }
+            __syncthreads();  // rowbuf and the per-voxel words are reused
+            ++round;
+        }
+    }
+    if (t < Gb) {
+        const long long pp = b + ((long long)t << nbits);
+        const unsigned n = running[t];
+        const double dn = (double)n;
+        centroids[pp] = make_float4((float)(sx / dn), (float)(sy / dn), (float)(sz / dn),
+                                    (float)(sw / dn));
+        counts[pp] = (int)n;
+        write_coords(coords, pp, kept_key[pp], gx, gy);
+        kept_key[pp] = 0;
+        if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
+    }
+}
+
 // -------------------------------------------------------------- bin only --
 
 __global__ __launch_bounds__(kBlock) void k_bin(const float4* __restrict__ pts, long long N,
@@ -1371,6 +1529,11 @@ struct Plan {
 inline size_t bins_lds_bytes(int G, int K, bool carry) {
     return 4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves +
                          (carry ? 0 : G * K));
+}
+// LDS of one k_centroid block for bins of G voxels
+inline size_t centroid_lds_bytes(int G) {
+    return 16u * (size_t)kBinBlock +
+           4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + 3 * G);
 }
 // Clouds of at least this many points carry rows through staging by default.
 constexpr long long kCarryMinPoints = 1ll << 19;
@@ -1702,6 +1865,64 @@ int run_pipeline(const float* points, const Grid& g, const Plan& pl, const Buffe
                        ev ? ev + 6 : nullptr);
 }
 
+// Fill the table chunk by chunk while fewer than M cells are in it, reading
+// the claim count on the host between chunks. Before each chunk `have` < M
+// cells are present, so a chunk of S/2 - have points keeps the load at or
+// below one half. *done = the points inserted (the prefix rank then scans).
+int insert_chunked(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
+                   hipStream_t stream, long long* done_out) {
+    long long done = 0;
+    long long have = 0;
+    const long long half = pl.S / 2;
+    int rc;
+    while (done < pl.N && have < pl.M) {
+        long long chunk = half - have;
+        if (chunk > pl.N - done) chunk = pl.N - done;
+        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream, 1, nullptr)) !=
+            VOX_OK)
+            return rc;
+        done += chunk;
+        unsigned claims = 0;
+        hipError_t e = hipMemcpyAsync(&claims, &bf.hdr->claims, sizeof(claims),
+                                      hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+        have = claims;
+    }
+    *done_out = done;
+    return VOX_OK;
+}
+
+// Downsampling runs the partitioned route with rows carried and no max_points
+// (the plan takes K = 1); options may set select_path to 0 or 3 only.
+int downsample_plan(long long N, int M, const vox_options* options, Plan* pl) {
+    vox_options o;
+    if (options) {
+        o = *options;
+        if (o.select_path != 0 && o.select_path != 3) return VOX_EINVAL;
+    } else {
+        memset(&o, 0, sizeof(o));
+    }
+    o.select_path = 3;
+    const int rc = make_plan(N, M, 1, &o, pl);
+    if (rc != VOX_OK) return rc;
+    pl->lds = centroid_lds_bytes(1 << pl->gshift);
+    return VOX_OK;
+}
+
+int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& g,
+                    float* centroids, int32_t* coords, int32_t* counts, int32_t* num_voxels,
+                    hipStream_t st) {
+    const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
+    hipExtLaunchKernelGGL(k_centroid, dim3((unsigned)pl.nbins), dim3(kBinBlock),
+                          (unsigned)pl.lds, st, nullptr, nullptr, 0, bf.cm, bf.stage,
+                          bf.stage_pt, pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.M,
+                          bf.kept, bf.compact, (unsigned)pl.C, bf.kcs, g.gx, g.gy,
+                          reinterpret_cast<float4*>(centroids), coords, counts, num_voxels,
+                          bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
+    return last_launch();
+}
+
 }  // namespace
 
 // =================================================================== C ABI ==
@@ -1796,26 +2017,8 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
     if (!chunked)
         return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels,
                             point_pillar, stream, nullptr);
-    // Fill the table chunk by chunk while fewer than M cells are in it. Before
-    // each chunk `have` < M cells are present, so a chunk of S/2 - have points
-    // keeps the load at or below one half.
     long long done = 0;
-    long long have = 0;
-    const long long half = pl.S / 2;
-    while (done < pl.N && have < pl.M) {
-        long long chunk = half - have;
-        if (chunk > pl.N - done) chunk = pl.N - done;
-        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream, 1, nullptr)) !=
-            VOX_OK)
-            return rc;
-        done += chunk;
-        unsigned claims = 0;
-        hipError_t e = hipMemcpyAsync(&claims, &bf.hdr->claims, sizeof(claims),
-                                      hipMemcpyDeviceToHost, stream);
-        if (e == hipSuccess) e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return hip_fail(e);
-        have = claims;
-    }
+    if ((rc = insert_chunked(points, g, pl, bf, stream, &done)) != VOX_OK) return rc;
     Plan p2 = pl;
     p2.P = done;
     if ((rc = launch_rank(done, p2, bf, num_voxels, stream, nullptr)) != VOX_OK) return rc;
@@ -1841,6 +2044,52 @@ int vox_bin_points(const float* points, int64_t n_points, const float range[6],
                        reinterpret_cast<const float4*>(points), (long long)n_points, g, valid,
                        reinterpret_cast<long long*>(key));
     return last_launch();
+}
+
+int64_t vox_downsample_workspace_bytes(int64_t n_points, int32_t max_voxels,
+                                       const vox_options* options) {
+    Plan pl;
+    const int rc = downsample_plan(n_points, max_voxels, options, &pl);
+    return rc != VOX_OK ? rc : (int64_t)pl.bytes;
+}
+
+int64_t vox_downsample_workspace_zero_bytes(int64_t n_points, int32_t max_voxels,
+                                            const vox_options* options) {
+    Plan pl;
+    const int rc = downsample_plan(n_points, max_voxels, options, &pl);
+    return rc != VOX_OK ? rc : (int64_t)pl.zero_bytes;
+}
+
+int vox_downsample(const float* points, int64_t n_points, const float range[6],
+                   const float cell[3], const int32_t grid[3], int32_t max_voxels,
+                   float* centroids, int32_t* coords, int32_t* counts, int32_t* num_voxels,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                   const vox_options* options, int32_t chunked) {
+    if (!centroids || !coords || !counts || !num_voxels || !workspace) return VOX_EINVAL;
+    if (n_points > 0 && !points) return VOX_EINVAL;
+    if ((points && ((uintptr_t)points & 15u)) || ((uintptr_t)centroids & 15u) ||
+        ((uintptr_t)coords & 3u) || ((uintptr_t)counts & 3u) || ((uintptr_t)num_voxels & 3u))
+        return VOX_EINVAL;
+    Grid g;
+    int rc = check_grid(range, cell, grid, &g);
+    if (rc != VOX_OK) return rc;
+    Plan pl;
+    if ((rc = downsample_plan(n_points, max_voxels, options, &pl)) != VOX_OK) return rc;
+    if (((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes) return VOX_EWORKSPACE;
+    const Buffers bf = carve(workspace, pl);
+    long long P = pl.P;
+    if (chunked) {
+        if ((rc = insert_chunked(points, g, pl, bf, stream, &P)) != VOX_OK) return rc;
+    } else if ((rc = launch_insert(points, 0, P, g, pl, bf, stream, 0, nullptr)) != VOX_OK) {
+        return rc;
+    }
+    Plan p2 = pl;
+    p2.P = P;
+    if ((rc = launch_rank(P, p2, bf, num_voxels, stream, nullptr)) != VOX_OK) return rc;
+    if ((rc = launch_select(points, P, g, p2, bf, num_voxels, nullptr, stream, nullptr)) !=
+        VOX_OK)
+        return rc;
+    return launch_centroid(p2, P, bf, g, centroids, coords, counts, num_voxels, stream);
 }
 
 int vox_profile_stages(const float* points, int64_t n_points, const float range[6],

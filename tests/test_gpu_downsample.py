@@ -1,0 +1,134 @@
+"""GPU parity of voxel-grid downsampling against the CPU oracle.
+
+Coordinates and counts must be equal; centroids bit for bit, except that any
+NaN matches any NaN (NaN payloads are not part of the definition). Inputs come
+from the seeded generators only.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import sparse_spatial_hashing_amd as vox  # noqa: E402
+from bruteforce import same_f32  # noqa: E402
+from workloads import config_names, generate, get_config  # noqa: E402
+
+DEV = torch.device("cuda:0")
+F32 = np.float32
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_ds(pts, r, c, g, M, **kw):
+    say(f"  gpu downsample N={pts.shape[0]} M={M} {kw}")
+    out = vox.downsample(torch.from_numpy(np.ascontiguousarray(pts)).to(DEV), r, c, g, M, **kw)
+    torch.cuda.synchronize()
+    return tuple(t.cpu().numpy() for t in out)
+
+
+def check(got, want, what):
+    assert np.array_equal(got[1], want[1]), f"{what}: coords differ"
+    assert np.array_equal(got[2], want[2]), f"{what}: counts differ"
+    assert same_f32(got[0], want[0]), f"{what}: centroids differ"
+
+
+@pytest.mark.parametrize("name", config_names())
+def test_downsample_parity(name):
+    p = get_config(name).params
+    pts, _ = generate(name)
+    say(f"downsample parity {name}")
+    want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    check(gpu_ds(pts, p.range_, p.cell, p.grid, p.max_voxels), want, name)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+@pytest.mark.parametrize("name", ["kitti_frame", "voxel3d"])
+def test_downsample_other_seeds(name, seed):
+    p = get_config(name).params
+    pts, _ = generate(name, seed=seed)
+    say(f"downsample parity {name} seed={seed}")
+    want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    check(gpu_ds(pts, p.range_, p.cell, p.grid, p.max_voxels), want, f"{name}/{seed}")
+
+
+@pytest.mark.parametrize("name", ["kitti_frame", "dense_multisweep"])
+def test_downsample_options_and_chunked(name):
+    p = get_config(name).params
+    pts, _ = generate(name)
+    want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    M = p.max_voxels
+    for kw in (dict(hash=1), dict(hash=2), dict(compact_table=1), dict(table_slots=3 * M),
+               dict(prefix_points=4096), dict(chunked=True)):
+        say(f"downsample {name} {kw}")
+        check(gpu_ds(pts, p.range_, p.cell, p.grid, M, **kw), want, f"{name} {kw}")
+
+
+def test_downsample_fuzz():
+    rng = np.random.default_rng(77)
+    for t in range(40):
+        gx, gy = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        gz = int(rng.choice([1, 1, 3]))
+        vx, vy, vz = (float(F32(rng.choice(v))) for v in ([0.1, 0.25, 1.0], [0.2, 0.5], [0.5, 1.0]))
+        x0, y0, z0 = float(F32(rng.uniform(-5, 5))), float(F32(rng.uniform(-5, 5))), -1.0
+        z1 = z0 + (gz * vz if gz > 1 else 2.0)
+        n = int(rng.choice([1, 63, 64, 65, 1000, 1025, 5000, 20000]))
+        spread = float(rng.choice([1.0, 0.2, 0.02]))
+        pts = np.zeros((n, 4), F32)
+        pts[:, 0] = (x0 + (rng.random(n) * spread * 1.2 - 0.1) * gx * vx).astype(F32)
+        pts[:, 1] = (y0 + (rng.random(n) * spread * 1.2 - 0.1) * gy * vy).astype(F32)
+        pts[:, 2] = (z0 + rng.uniform(-0.1, 1.1, n) * (z1 - z0)).astype(F32)
+        pts[:, 3] = rng.normal(0, 100, n).astype(F32)
+        pts[rng.random(n) < 0.02, 3] = np.nan
+        M = int(rng.choice([1, 3, 50, 1000, 100000]))
+        r = (x0, y0, z0, x0 + gx * vx, y0 + gy * vy, z1)
+        say(f"downsample fuzz {t}: N={n} grid=({gx},{gy},{gz}) M={M}")
+        want = oracle.downsample(pts, r, (vx, vy, vz), (gx, gy, gz), M)
+        check(gpu_ds(pts, r, (vx, vy, vz), (gx, gy, gz), M), want, f"fuzz {t}")
+
+
+def test_downsample_heavy_voxel_and_edge_cases():
+    rng = np.random.default_rng(9)
+    n = 60000
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = rng.uniform(10.01, 10.15, n).astype(F32)
+    pts[:, 1] = rng.uniform(0.01, 0.15, n).astype(F32)
+    pts[:, 2] = F32(-1.0)
+    pts[:, 3] = rng.random(n).astype(F32)
+    r, c, g = (0.0, -39.68, -3.0, 69.12, 39.68, 1.0), (0.16, 0.16, 4.0), (432, 496, 1)
+    say("downsample single heavy voxel")
+    check(gpu_ds(pts, r, c, g, 100), oracle.downsample(pts, r, c, g, 100), "heavy voxel")
+    say("downsample empty / all rejected")
+    grid = ((0, 0, -1, 4, 4, 1), (1, 1, 2), (4, 4, 1))
+    got = gpu_ds(np.zeros((0, 4), F32), *grid, 8)
+    assert got[0].shape == (0, 4)
+    bad = np.array([[np.nan, 0.5, 0, 0], [4.0, 0.5, 0, 0], [0.5, 0.5, 1.0, 0]], F32)
+    assert gpu_ds(bad, *grid, 8)[0].shape == (0, 4)
+
+
+def test_downsample_then_voxelize_share_one_workspace():
+    """Both entry points reuse the binding's cached workspace; each leaves its
+    zero part zero, and results stay exact when they alternate."""
+    stream = torch.cuda.current_stream(DEV).cuda_stream
+    for name in ("kitti_frame", "voxel3d", "kitti_frame"):
+        p = get_config(name).params
+        pts, _ = generate(name, n=50000)
+        say(f"alternate {name}")
+        want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+        check(gpu_ds(pts, p.range_, p.cell, p.grid, p.max_voxels), want, name)
+        ws = vox._workspaces._cache[(DEV.index, stream)]
+        zb = vox.downsample_workspace_bytes(pts.shape[0], p.max_voxels)[1]
+        assert vox.workspace_is_clean(ws, zb)
+        x = torch.from_numpy(pts).to(DEV)
+        got = vox.voxelize(x, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+        wv = oracle.voxelize(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+        assert np.array_equal(got[1].cpu().numpy(), wv[1])

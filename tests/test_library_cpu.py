@@ -181,3 +181,17 @@ def test_select_route_rules():
         vox.workspace_bytes(122880, 12000, 32, select_path=2)
     assert vox.workspace_zero_bytes(122880, 12000, 32, select_path=3) == \
         vox.workspace_zero_bytes(122880, 12000, 32, select_path=2)
+
+
+def test_downsample_workspace_and_limits():
+    n, z = vox.downsample_workspace_bytes(122880, 12000)
+    assert 256 <= z <= n
+    assert vox.downsample_workspace_bytes(122880, 262144)[0] > 0
+    for bad in (dict(max_voxels=262145), dict(max_voxels=0)):
+        with pytest.raises(vox.VoxError):
+            vox.downsample_workspace_bytes(1000, **bad)
+    # only the carried-rows route exists for downsampling
+    for path in (1, 2):
+        with pytest.raises(vox.VoxError):
+            vox.downsample_workspace_bytes(1000, 100, select_path=path)
+    assert vox.downsample_workspace_bytes(1000, 100, select_path=3)[0] > 0
