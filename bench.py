@@ -217,6 +217,33 @@ def run_workload(name, steps, warmup, profile_iters, torch, vox):
                 total_ms=total_ms, alg=alg, P=P, kept=kept, kernels=kernels)
 
 
+def downsample_line(name, steps, warmup, torch, vox):
+    """Voxel-grid downsampling on one workload: µs per call (HIP events on the
+    call's stream, inputs resident) and parity with the oracle."""
+    import oracle
+    from workloads import generate, get_config
+
+    def same_f32(a, b):  # bitwise, except that any NaN equals any NaN
+        na, nb = np.isnan(a), np.isnan(b)
+        return bool(a.shape == b.shape and np.array_equal(na, nb) and
+                    np.array_equal(a.view(np.uint32)[~na], b.view(np.uint32)[~nb]))
+
+    p = get_config(name).params
+    pts, _ = generate(name)
+    x = torch.from_numpy(pts).to("cuda:0")
+    ds = vox.Downsampler(pts.shape[0], p.range_, p.cell, p.grid, p.max_voxels, device="cuda:0")
+    ms = time_calls(ds, x, steps, warmup, torch)
+    ds.run(x)
+    torch.cuda.synchronize()
+    got = tuple(t.cpu().numpy() for t in ds.outputs())
+    want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    ok = (np.array_equal(got[1], want[1]) and np.array_equal(got[2], want[2])
+          and same_f32(got[0], want[0]))
+    return {"op": "downsample", "workload": name, "N": pts.shape[0], "V": int(got[0].shape[0]),
+            "us_per_call": round(ms * 1e3, 2), "mpoints_s": round(pts.shape[0] / (ms * 1e-3) / 1e6, 1),
+            "parity": bool(ok)}
+
+
 def main():
     args = parse()
     if args.rocprof_summary:
@@ -276,6 +303,9 @@ def main():
         line["cpu_baseline"] = cpu_baseline(r["pts"], p, args.cpu_seconds)
     if args.all:
         from workloads import config_names
+        for name in config_names():
+            print(json.dumps(downsample_line(name, args.steps, args.warmup, torch, vox)),
+                  file=sys.stderr, flush=True)
         for name in config_names():
             q = run_workload(name, args.steps, args.warmup, args.profile_iters, torch, vox)
             print(json.dumps({

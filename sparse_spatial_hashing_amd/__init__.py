@@ -389,3 +389,41 @@ class Voxelizer:
         if V < 0:
             raise VoxError(V, "voxelize (device status)")
         return self.voxels[:V], self.coords[:V], self.num_points[:V]
+
+
+class Downsampler:
+    """Pre-allocated outputs and workspace for repeated voxel-grid
+    downsampling calls with one shape; ``run(points)`` enqueues one call on
+    the current stream (nothing allocated or synchronised per call)."""
+
+    def __init__(self, n_points: int, range_, cell, grid, max_voxels: int, device="cuda",
+                 **opts):
+        self.N, self.M = int(n_points), int(max_voxels)
+        self.device = torch.device(device)
+        self._opts = _options(**opts)
+        self.nbytes, self.zero_bytes = downsample_workspace_bytes(self.N, self.M, **opts)
+        self.workspace = torch.zeros(self.nbytes, dtype=torch.uint8, device=self.device)
+        self.centroids = torch.empty((self.M, 4), dtype=torch.float32, device=self.device)
+        self.coords = torch.empty((self.M, 3), dtype=torch.int32, device=self.device)
+        self.counts = torch.empty((self.M,), dtype=torch.int32, device=self.device)
+        self.num_voxels = torch.zeros((1,), dtype=torch.int32, device=self.device)
+        self._r, self._c, self._g = _host_params(range_, cell, grid)
+
+    def run(self, points: torch.Tensor) -> torch.Tensor:
+        _check_points(points)
+        if points.shape[0] != self.N:
+            raise ValueError(f"expected {self.N} points, got {points.shape[0]}")
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _check(_lib.vox_downsample(
+            ctypes.c_void_p(points.data_ptr()), self.N, self._r, self._c, self._g, self.M,
+            ctypes.c_void_p(self.centroids.data_ptr()), ctypes.c_void_p(self.coords.data_ptr()),
+            ctypes.c_void_p(self.counts.data_ptr()), ctypes.c_void_p(self.num_voxels.data_ptr()),
+            ctypes.c_void_p(self.workspace.data_ptr()), ctypes.c_size_t(self.nbytes),
+            ctypes.c_void_p(stream), self._opts, 0), "vox_downsample")
+        return self.num_voxels
+
+    def outputs(self):
+        V = int(self.num_voxels.item())
+        if V < 0:
+            raise VoxError(V, "vox_downsample (device status)")
+        return self.centroids[:V], self.coords[:V], self.counts[:V]
