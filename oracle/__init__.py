@@ -4,7 +4,7 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg use this package. The GPU library never imports, links or calls it, and it
 imports nothing from the GPU library.
 
-``voxelize``, ``voxelize_map``, ``downsample`` and ``bin_points`` wrap the
+``voxelize``, ``voxelize_map``, ``downsample``, ``spherical`` and ``bin_points`` wrap the
 sequential C definitions in ``voxelize_oracle.c`` (see its comments for the
 passages each step follows and the readings taken where the pages are
 silent).
@@ -27,9 +27,14 @@ _lib: Optional[ctypes.CDLL] = None
 
 
 def build(source: str = SOURCE, output: str = LIBRARY) -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    cmd = ["gcc", *CFLAGS, "-o", output, source, "-lm"]
+    """Compile the oracle with gcc (no fast-math, no FMA contraction).
+
+    The library is written under a temporary name and renamed into place, so
+    a process loading it never sees a partly written file."""
+    tmp = f"{output}.{os.getpid()}.tmp"
+    cmd = ["gcc", *CFLAGS, "-o", tmp, source, "-lm"]
     subprocess.run(cmd, check=True)
+    os.replace(tmp, output)
     return output
 
 
@@ -55,6 +60,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.oracle_downsample.argtypes = [vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int32, vp, vp, vp,
                                       vp]
     lib.oracle_downsample.restype = ctypes.c_int
+    lib.oracle_spherical.argtypes = [vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_spherical.restype = ctypes.c_int
     if path == LIBRARY:
         _lib = lib
     return lib
@@ -161,6 +168,27 @@ def downsample(points: np.ndarray, range_: Sequence[float], cell: Sequence[float
         raise MemoryError("oracle_downsample could not allocate")
     V = int(nv[0])
     return cen[:V].copy(), coords[:V].copy(), counts[:V].copy()
+
+
+def spherical(points: np.ndarray, sph_min: Sequence[float], sph_cell: Sequence[float],
+              bins: Sequence[int], lib: Optional[ctypes.CDLL] = None):
+    """Spherical binning and voxel-contiguous order: (voxel_of [N] i32 (-1 when
+    not kept), offsets [nvox+1] i32, order [n_kept] i32)."""
+    lib = lib or load()
+    p = _points(points)
+    mn = np.ascontiguousarray(np.asarray(sph_min, dtype=np.float32).reshape(3))
+    ce = np.ascontiguousarray(np.asarray(sph_cell, dtype=np.float32).reshape(3))
+    b = np.ascontiguousarray(np.asarray(bins, dtype=np.int32).reshape(3))
+    nvox = int(b[0]) * int(b[1]) * int(b[2])
+    vof = np.full(p.shape[0], -2, dtype=np.int32)
+    off = np.full(nvox + 1, -1, dtype=np.int32)
+    order = np.full(max(p.shape[0], 1), -1, dtype=np.int32)
+    nk = np.zeros(1, dtype=np.int32)
+    rc = lib.oracle_spherical(_ptr(p), p.shape[0], _ptr(mn), _ptr(ce), _ptr(b), _ptr(vof),
+                              _ptr(off), _ptr(order), _ptr(nk))
+    if rc != 0:
+        raise MemoryError("oracle_spherical could not allocate")
+    return vof, off, order[:int(nk[0])].copy()
 
 
 def voxelize_params(points: np.ndarray, params, lib: Optional[ctypes.CDLL] = None):

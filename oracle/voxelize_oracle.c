@@ -31,8 +31,10 @@
  *   - range tests are made on the float floor value before any conversion,
  *     every operation in IEEE fp32 round-to-nearest, no FMA contraction.
  *
- * oracle_downsample (end of file) adds voxel-grid downsampling, one mean
- * point per kept voxel, from a second page (see its comment).
+ * oracle_downsample adds voxel-grid downsampling, one mean point per kept
+ * voxel, from a second page; oracle_spherical (end of file) adds the
+ * spherical binning and voxel-contiguous reorder that the RadiusFPS page
+ * runs before its sampler (see each function's comment).
  *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fPIC -shared
  */
@@ -330,5 +332,166 @@ int oracle_downsample(const float *points, int64_t n, const float range[6], cons
     free(sum);
     free(total);
     map_free(&dict);
+    return 0;
+}
+
+/*
+ * Spherical-coordinate binning and voxel-contiguous reorder: the
+ * preprocessing of the RadiusFPS page ("Spherical voxel partition" and the
+ * preprocessing step of RadiusFPS-G): each point gets spherical coordinates
+ * r = sqrt(x^2 + y^2 + z^2), elevation theta = atan2(z, sqrt(x^2 + y^2)) and
+ * azimuth phi = atan2(y, x), each axis is split uniformly, and the points are
+ * sorted by voxel id so that a voxel's points are contiguous. Readings taken:
+ *   - r in float: sqrtf((x*x + y*y) + z*z), correctly rounded; r bin =
+ *     floorf((r - r_min) / dr), kept when in [0, nr) (the same rule as the
+ *     Cartesian axes of "Binning a point");
+ *   - angles are not rounded: a point is in angular bin k when its direction
+ *     is at or above boundary k and below boundary k + 1. Boundary angle
+ *     a_k = a_min + k * da is taken in double from the float parameters.
+ *     A boundary at or below the axis's lowest angle (-pi/2 for elevation,
+ *     -pi for azimuth) has every direction above it; one above the axis's
+ *     highest angle (pi/2, pi) has none. Any other boundary is the direction
+ *     (cos a_k, sin a_k) rounded to float. Elevation uses the direction
+ *     (sqrtf(x*x + y*y), z); azimuth uses (x, y) with angles in (-pi, pi]
+ *     (a zero y of either sign counts as 0, so the negative x axis has angle
+ *     pi). Every comparison of two directions is the sign of a cross product
+ *     of float operands evaluated in double, which is exact. The bin is the
+ *     largest k at or below which the direction lies;
+ *   - a point with x = y = 0 has azimuth 0; a point at the origin has no
+ *     elevation and is not kept; NaN/Inf coordinates are not kept;
+ *   - voxel id = (ir * ntheta + itheta) * nphi + iphi;
+ *   - the sort is by voxel id; inside a voxel the points are in input order
+ *     here (the page does not fix that order).
+ * sph_min = (r_min, theta_min, phi_min), sph_cell = (dr, dtheta, dphi),
+ * bins = (nr, ntheta, nphi). Outputs: voxel_of[N] (id or -1), offsets[nvox + 1]
+ * (start of each voxel in the sorted order), order[N] (indices of kept points
+ * by voxel), *n_kept. Returns 0, or -1 if memory is unavailable.
+ */
+
+/* half-plane index of a direction for angles in (-pi, pi]:
+ * 0 = angle in (-pi, 0), 1 = [0, pi), 2 = pi */
+static int angle_half(double x, double y)
+{
+    if (y < 0.0)
+        return 0;
+    if (y > 0.0 || x > 0.0)
+        return 1;
+    return 2;
+}
+
+/* angle of direction p >= angle of direction d, both in (-pi, pi], exact */
+static int angle_ge(double px, double py, double dx, double dy)
+{
+    int hp = angle_half(px, py), hd = angle_half(dx, dy);
+    if (hp != hd)
+        return hp > hd;
+    return dx * py - dy * px >= 0.0; /* float operands: exact products */
+}
+
+/* pi and pi/2 rounded to double; both roundings fall below the true value */
+#define SPH_PI 3.141592653589793
+#define SPH_HALF_PI 1.5707963267948966
+
+/* One boundary: cls -1 = below the axis (every direction passes),
+ * +1 = above it (none passes), 0 = compare with the direction (c, s).
+ * lim is the axis's half-width (pi/2 or pi) as the nearest double below it,
+ * so a < -lim exactly when a <= -half-width, and a > lim when a > half-width. */
+typedef struct {
+    int cls;
+    float c, s;
+} sph_bound;
+
+static void sph_bounds(sph_bound *b, int nb, float a_min, float da, double lim)
+{
+    for (int k = 0; k <= nb; k++) {
+        double a = (double)a_min + (double)k * (double)da;
+        b[k].cls = a < -lim ? -1 : (a > lim ? 1 : 0);
+        b[k].c = (float)cos(a);
+        b[k].s = (float)sin(a);
+    }
+}
+
+/* largest k whose boundary the direction is at or above, -1 if none */
+static int sph_bin_elev(const sph_bound *b, int nb, double rxy, double z)
+{
+    int bin = -1;
+    for (int k = 0; k <= nb; k++) {
+        int ge = b[k].cls < 0 ||
+                 (b[k].cls == 0 && (double)b[k].c * z - (double)b[k].s * rxy >= 0.0);
+        if (ge)
+            bin = k;
+    }
+    return bin;
+}
+
+static int sph_bin_azim(const sph_bound *b, int nb, double x, double y)
+{
+    int bin = -1;
+    for (int k = 0; k <= nb; k++) {
+        int ge = b[k].cls < 0 ||
+                 (b[k].cls == 0 && angle_ge(x, y, (double)b[k].c, (double)b[k].s));
+        if (ge)
+            bin = k;
+    }
+    return bin;
+}
+
+int oracle_spherical(const float *points, int64_t n, const float sph_min[3],
+                     const float sph_cell[3], const int32_t bins[3], int32_t *voxel_of,
+                     int32_t *offsets, int32_t *order, int32_t *n_kept)
+{
+    const int nr = bins[0], nt = bins[1], np_ = bins[2];
+    const int64_t nvox = (int64_t)nr * nt * np_;
+    sph_bound *tb = (sph_bound *)malloc(sizeof(sph_bound) * (size_t)(nt + 1));
+    sph_bound *pb = (sph_bound *)malloc(sizeof(sph_bound) * (size_t)(np_ + 1));
+    int64_t *cnt = (int64_t *)calloc((size_t)nvox + 1, sizeof(int64_t));
+    if (!tb || !pb || !cnt) {
+        free(tb);
+        free(pb);
+        free(cnt);
+        return -1;
+    }
+    sph_bounds(tb, nt, sph_min[1], sph_cell[1], SPH_HALF_PI);
+    sph_bounds(pb, np_, sph_min[2], sph_cell[2], SPH_PI);
+    for (int64_t i = 0; i < n; i++) {
+        const float *p = points + 4 * i;
+        float x = p[0], y = p[1], z = p[2];
+        voxel_of[i] = -1;
+        if (!isfinite(x) || !isfinite(y) || !isfinite(z))
+            continue;
+        float xx = x * x, yy = y * y, zz = z * z;
+        float sxy = xx + yy;
+        float r = sqrtf(sxy + zz);
+        float rxy = sqrtf(sxy);
+        if (r == 0.0f)
+            continue; /* no direction */
+        float fr = floorf((r - sph_min[0]) / sph_cell[0]);
+        if (!(fr >= 0.0f && fr < (float)nr))
+            continue;
+        int it = sph_bin_elev(tb, nt, (double)rxy, (double)z);
+        if (it < 0 || it >= nt)
+            continue;
+        int ip = (x == 0.0f && y == 0.0f) ? sph_bin_azim(pb, np_, 1.0, 0.0)
+                                          : sph_bin_azim(pb, np_, (double)x, (double)y);
+        if (ip < 0 || ip >= np_)
+            continue;
+        int64_t v = ((int64_t)fr * nt + it) * np_ + ip;
+        voxel_of[i] = (int32_t)v;
+        cnt[v] += 1;
+    }
+    int64_t run = 0;
+    for (int64_t v = 0; v < nvox; v++) {
+        offsets[v] = (int32_t)run;
+        run += cnt[v];
+        cnt[v] = offsets[v]; /* cursor */
+    }
+    offsets[nvox] = (int32_t)run;
+    for (int64_t i = 0; i < n; i++) /* counting sort, input order inside a voxel */
+        if (voxel_of[i] >= 0)
+            order[cnt[voxel_of[i]]++] = (int32_t)i;
+    *n_kept = (int32_t)run;
+    free(tb);
+    free(pb);
+    free(cnt);
     return 0;
 }

@@ -150,3 +150,59 @@ def same_f32(a, b) -> bool:
     na, nb = np.isnan(a), np.isnan(b)
     return bool(np.array_equal(na, nb) and
                 np.array_equal(a.view(np.uint32)[~na], b.view(np.uint32)[~nb]))
+
+
+# ----------------------------------------------------------- spherical binning --
+
+def spherical_np(points, sph_min, sph_cell, bins, eps=1e-6):
+    """Spherical bins by the atan2 route, in float64, from the float32 direction.
+
+    r is binned with the float32 rules of "Binning a point" on
+    r = sqrt((x*x + y*y) + z*z). Elevation is atan2(z, sqrt(x*x + y*y)) and
+    azimuth atan2(y, x) (a -0 y taken as +0, azimuth 0 at x = y = 0), both in
+    float64 on the float32 values, binned by floor((a - a_min) / da) with
+    a_min and da the float32 parameters widened to float64. This route never
+    forms a boundary direction, so near a boundary it can disagree with an
+    exact direction test: ``ambiguous`` marks points whose angle lies within
+    ``eps`` radians of one, where either neighbouring bin is acceptable.
+    Returns (voxel id or -1, ambiguous).
+    """
+    p = np.asarray(points, dtype=F32)
+    x, y, z = p[:, 0], p[:, 1], p[:, 2]
+    nr, nt, nph = (int(v) for v in bins)
+    r0, t0, p0 = (float(F32(v)) for v in sph_min)
+    dr32 = F32(sph_cell[0])
+    dt, dp = float(F32(sph_cell[1])), float(F32(sph_cell[2]))
+    with np.errstate(all="ignore"):
+        ok = np.isfinite(x) & np.isfinite(y) & np.isfinite(z)
+        sxy = x * x + y * y
+        r = np.sqrt(sxy + z * z)
+        rxy = np.sqrt(sxy)
+        ok &= r != F32(0)
+        fr = np.floor((r - F32(r0)) / dr32)
+        ok &= (fr >= F32(0)) & (fr < F32(nr))
+        th = np.arctan2(z.astype(np.float64), rxy.astype(np.float64))
+        yy = y.astype(np.float64) + 0.0
+        ph = np.where((x == 0) & (y == 0), 0.0, np.arctan2(yy, x.astype(np.float64)))
+        it = np.floor((th - t0) / dt)
+        ip = np.floor((ph - p0) / dp)
+        ok &= (it >= 0) & (it < nt) & (ip >= 0) & (ip < nph)
+        amb = np.zeros(p.shape[0], dtype=bool)
+        for a, a0, da, nb in ((th, t0, dt, nt), (ph, p0, dp, nph)):
+            kb = np.round((a - a0) / da)
+            near = np.abs(a - (a0 + kb * da)) < eps
+            amb |= np.isfinite(a) & near & (kb >= 0) & (kb <= nb)
+    v = np.where(ok, (fr.astype(np.int64) * nt + np.where(ok, it, 0).astype(np.int64)) * nph
+                 + np.where(ok, ip, 0).astype(np.int64), -1)
+    return v.astype(np.int64), amb & np.isfinite(r) & (r != F32(0))
+
+
+def sort_by_voxel_np(voxel_of, nvox):
+    """Counting sort by voxel id with numpy: (offsets [nvox+1], order [n_kept]),
+    points of one voxel in input order."""
+    v = np.asarray(voxel_of, dtype=np.int64)
+    kept = np.flatnonzero(v >= 0)
+    counts = np.bincount(v[kept], minlength=nvox)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    order = kept[np.argsort(v[kept], kind="stable")]
+    return offsets, order

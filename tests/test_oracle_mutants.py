@@ -13,8 +13,10 @@ import numpy as np
 import pytest
 
 import oracle
-from bruteforce import bin_np, downsample_np, exact_cell, same_f32, sort_then_segment
-from workloads import generate, get_config
+from bruteforce import (bin_np, downsample_np, exact_cell, same_f32, sort_by_voxel_np,
+                        sort_then_segment, spherical_np)
+from test_oracle_spherical import SMALL, _angles, _boundary_dirs, _rot, _vid
+from workloads import generate, get_config, get_sph_config
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 F32 = np.float32
@@ -51,6 +53,22 @@ MUTANTS = {
                                "        counts[pid] = 1;")],
     "ds_skip_first_point": [("            continue;  /* its voxel is past the cap */\n        }\n        for (int c = 0; c < 4; c++)",
                              "            continue;  /* its voxel is past the cap */\n        }\n        if (total[pid] == 0 && sum[4 * pid] == 0.0) { total[pid] += 1; continue; }\n        for (int c = 0; c < 4; c++)")],
+    # spherical binning and reorder
+    "sph_elev_strict": [("(double)b[k].c * z - (double)b[k].s * rxy >= 0.0)",
+                         "(double)b[k].c * z - (double)b[k].s * rxy > 0.0)")],
+    "sph_azim_strict": [("return dx * py - dy * px >= 0.0;", "return dx * py - dy * px > 0.0;")],
+    "sph_elev_args_swapped": [("sph_bin_elev(tb, nt, (double)rxy, (double)z)",
+                               "sph_bin_elev(tb, nt, (double)z, (double)rxy)")],
+    "sph_r_without_z": [("float r = sqrtf(sxy + zz);", "float r = sqrtf(sxy);")],
+    "sph_no_range_class": [("b[k].cls = a < -lim ? -1 : (a > lim ? 1 : 0);", "b[k].cls = 0;")],
+    "sph_negative_zero_y": [("    if (y < 0.0)\n        return 0;",
+                             "    if (y < 0.0 || (y == 0.0 && signbit(y)))\n        return 0;")],
+    "sph_id_axes_swapped": [("((int64_t)fr * nt + it) * np_ + ip", "((int64_t)fr * np_ + ip) * nt + it")],
+    "sph_reversed_in_voxel": [("for (int64_t i = 0; i < n; i++) /* counting sort",
+                               "for (int64_t i = n - 1; i >= 0; i--) /* counting sort")],
+    "sph_origin_azimuth_pi": [("sph_bin_azim(pb, np_, 1.0, 0.0)", "sph_bin_azim(pb, np_, -1.0, 0.0)")],
+    "sph_offsets_inclusive": [("        offsets[v] = (int32_t)run;\n        run += cnt[v];\n        cnt[v] = offsets[v];",
+                               "        int64_t start = run;\n        run += cnt[v];\n        offsets[v] = (int32_t)run;\n        cnt[v] = start;")],
     "map_only_kept_rows": [("        if (point_pillar)\n            point_pillar[i] = (int32_t)pid;\n        total[pid] += 1;\n        if (total[pid] <= K) {",
                             "        total[pid] += 1;\n        if (total[pid] <= K) {\n            if (point_pillar)\n                point_pillar[i] = (int32_t)pid;")],
 }
@@ -164,6 +182,43 @@ def _battery(lib):
                                   (4, 4, 1), 4, lib=lib)
     if cen.shape != (1, 4) or cen[0, 0] != F32(1000.5684204101562):
         fails.append("downsample:double_sum")
+    fails += _sph_battery(lib)
+    return fails
+
+
+def _sph_battery(lib):
+    """Spherical binning pins: hand-placed points, boundary directions and a
+    float step either side, the atan2 route and a numpy counting sort."""
+    fails = []
+    pts = np.array([[1, 0, 0, 0], [0, 1, 0, 0], [-1, 0, 0, 0], [0, -1, 0, 0], [1, 1, 1, 0],
+                    [0, 0, 1, 0], [0, 0, 0, 0], [2, 0.1, 0, 0], [0, 0, -1, 0],
+                    [-1, -0.0, 0, 0], [3.5, -3.5, 0, 0]], F32)
+    v, off, order = oracle.spherical(pts, *SMALL, lib=lib)
+    want = [_vid(1, 4, 4), _vid(1, 4, 5), _vid(1, 4, 7), _vid(1, 4, 2), _vid(1, 5, 5),
+            _vid(1, 7, 4), -1, _vid(2, 4, 4), _vid(1, 0, 4), _vid(1, 4, 7), -1]
+    if v.tolist() != want or order.tolist() != [8, 3, 0, 1, 2, 9, 4, 5, 7]:
+        fails.append("sph:hand")
+    for axis, (lo, hi) in ((2, (-np.pi + 1e-3, np.pi - 1e-3)), (1, (-np.pi / 2 + 1e-3, np.pi / 2 - 1e-3))):
+        rows, exp = [], []
+        nb = SMALL[2][axis]
+        for k, c, s in _boundary_dirs(SMALL[0][axis], SMALL[1][axis], nb, lo, hi):
+            for steps, kk in ((0, k), (-1, k - 1), (1, k)):
+                cc, ss = _rot(c, s, steps)
+                rows.append([2 * cc, 2 * ss, 0.0, 0.0] if axis == 2 else [2 * cc, 0.0, 2 * ss, 0.0])
+                ok = 0 <= kk < nb
+                exp.append((_vid(0, 4, kk) if axis == 2 else _vid(0, kk, 4)) if ok else -1)
+        v, _, _ = oracle.spherical(np.array(rows, F32), *SMALL, lib=lib)
+        if _angles(v) != exp:
+            fails.append(f"sph:boundary{axis}")
+    p = get_sph_config("lidar_scan_64k").params
+    pts, _ = generate("lidar_scan_64k")
+    v, off, order = oracle.spherical(pts, p.sph_min, p.sph_cell, p.bins, lib=lib)
+    vn, amb = spherical_np(pts, p.sph_min, p.sph_cell, p.bins)
+    if np.any((v != vn) & ~amb):
+        fails.append("sph:atan2")
+    offn, ordn = sort_by_voxel_np(v, int(np.prod(p.bins)))
+    if not (np.array_equal(off, offn) and np.array_equal(order, ordn)):
+        fails.append("sph:sort")
     return fails
 
 

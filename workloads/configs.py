@@ -92,3 +92,65 @@ def get_config(name: str) -> Config:
     if name not in CONFIGS:
         raise KeyError(f"unknown workload {name!r}; known: {', '.join(CONFIGS)}")
     return CONFIGS[name]
+
+
+# ------------------------------------------------- spherical binning workloads --
+# The RadiusFPS page measures its sampler on one LiDAR scan of N = 65,536
+# points and splits (r, elevation, azimuth) uniformly without giving the bin
+# counts. The grid below is a plain choice: r in [0, 80) m in 5 m shells,
+# elevation over the whole [-pi/2, pi/2) in 10 degree bands, azimuth over
+# [-pi, pi) in 5 degree slices (20,736 voxels). The angle parameters are the
+# float32 roundings of these values.
+
+@dataclass(frozen=True)
+class SphParams:
+    """Arguments of one spherical binning call (everything except the points)."""
+    sph_min: Tuple[float, float, float]    # r_min, elevation_min, azimuth_min
+    sph_cell: Tuple[float, float, float]   # dr, d_elevation, d_azimuth
+    bins: Tuple[int, int, int]             # n_r, n_elevation, n_azimuth
+
+
+@dataclass(frozen=True)
+class SphConfig:
+    name: str
+    description: str
+    params: SphParams
+    generator: str
+    gen_kwargs: Dict = field(default_factory=dict)
+    seed: int = 0
+
+
+def _deg(d: float) -> float:
+    return d * 3.141592653589793 / 180.0
+
+
+SPH_GRID = SphParams((0.0, -3.141592653589793 / 2, -3.141592653589793),
+                     (5.0, _deg(10.0), _deg(5.0)), (16, 18, 72))
+
+SPH_CONFIGS: Dict[str, SphConfig] = {}
+
+
+def _add_sph(c: SphConfig) -> None:
+    SPH_CONFIGS[c.name] = c
+
+
+_add_sph(SphConfig(
+    name="lidar_scan_64k",
+    description="one 64-beam 360 degree LiDAR scan, N = 65,536: elevations -24.9 to +2.0 "
+                "degrees, ground returns from a sensor 1.73 m up, obstacles at log-uniform "
+                "range, unordered",
+    params=SPH_GRID, generator="lidar_scan", gen_kwargs=dict(n=65536)))
+_add_sph(SphConfig(
+    name="lidar_scan_1m",
+    description="the same scan recipe at N = 1,048,576 (a dense multi-frame cloud)",
+    params=SPH_GRID, generator="lidar_scan", gen_kwargs=dict(n=1048576), seed=1))
+
+
+def sph_config_names():
+    return list(SPH_CONFIGS)
+
+
+def get_sph_config(name: str) -> SphConfig:
+    if name not in SPH_CONFIGS:
+        raise KeyError(f"unknown spherical workload {name!r}; known: {', '.join(SPH_CONFIGS)}")
+    return SPH_CONFIGS[name]

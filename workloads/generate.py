@@ -18,7 +18,7 @@ from typing import Dict, List, Tuple
 
 import numpy as np
 
-from .configs import Config, get_config
+from .configs import SPH_CONFIGS, Config, get_config, get_sph_config
 
 F32 = np.float32
 
@@ -169,8 +169,32 @@ def _voxel3d(rng, n: int):
     return np.ascontiguousarray(np.stack([x, y, z, w], axis=1).astype(F32)), {}
 
 
+def _lidar_scan(rng, n: int):
+    """A 64-beam spinning LiDAR at the origin, 1.73 m above flat ground.
+
+    Beam elevations are spread evenly over [-24.9, 2.0] degrees (jittered by
+    0.02 degrees), azimuth is uniform over the full turn. A beam returns from
+    the ground where it points down and meets it, or from an obstacle at a
+    log-uniform range in [1, 120] m (drawn for 40% of the rays) when that is
+    nearer; rays with neither return at 120 m. Range noise is 2 cm.
+    """
+    beam = rng.integers(0, 64, size=n)
+    elev = np.radians(-24.9 + 26.9 * beam / 63.0 + rng.normal(0.0, 0.02, size=n))
+    az = rng.uniform(-math.pi, math.pi, size=n)
+    down = np.maximum(-np.sin(elev), 1e-9)
+    ground = np.where(elev < 0.0, 1.73 / down, np.inf)
+    obstacle = np.where(rng.random(n) < 0.4,
+                        np.exp(rng.uniform(math.log(1.0), math.log(120.0), size=n)), np.inf)
+    r = np.minimum(np.minimum(ground, obstacle), 120.0) + rng.normal(0.0, 0.02, size=n)
+    x = r * np.cos(elev) * np.cos(az)
+    y = r * np.cos(elev) * np.sin(az)
+    z = r * np.sin(elev)
+    w = rng.beta(2.0, 5.0, size=n)
+    return np.ascontiguousarray(np.stack([x, y, z, w], axis=1).astype(F32)), {}
+
+
 _GENERATORS = dict(tiny=_tiny, kitti=_kitti, uniform=_uniform, multisweep=_multisweep,
-                   voxel3d=_voxel3d)
+                   voxel3d=_voxel3d, lidar_scan=_lidar_scan)
 
 
 def generate(config, seed: int | None = None, n: int | None = None) -> Tuple[np.ndarray, Dict]:
@@ -181,7 +205,10 @@ def generate(config, seed: int | None = None, n: int | None = None) -> Tuple[np.
     smaller cloud with the same shape. ``info`` carries the tiny workload's
     edge-point positions; it is empty otherwise.
     """
-    cfg: Config = get_config(config) if isinstance(config, str) else config
+    if isinstance(config, str):
+        cfg = get_sph_config(config) if config in SPH_CONFIGS else get_config(config)
+    else:
+        cfg = config
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     kw = dict(cfg.gen_kwargs)
     if n is not None:
