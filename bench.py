@@ -13,7 +13,9 @@ iterations after warm-up, inputs on the GPU). Prints one JSON line.
   HIP events between the stages) against MI355X's 8 TB/s HBM peak, using the
   kernel's algorithmic bytes per launch.
 * cpu_baseline: the CPU oracle (one thread) on the same cloud on this host.
-* --all: one extra JSON line per workload (to stderr) for the results table.
+* --all: one extra JSON line per workload (to stderr) for the results table:
+  voxel-grid downsampling, spherical binning + reorder, then voxelization.
+* --spherical: only the spherical binning + reorder lines (stderr).
 """
 from __future__ import annotations
 
@@ -45,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--spherical", action="store_true",
+                    help="also time the spherical binning and reorder per workload (stderr)")
     ap.add_argument("--profile-iters", type=int, default=50)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run 10 plain device copies of this many MiB (counter calibration)")
@@ -244,6 +248,43 @@ def downsample_line(name, steps, warmup, torch, vox):
             "parity": bool(ok)}
 
 
+def spherical_line(name, steps, warmup, profile_iters, torch, vox):
+    """Spherical binning and voxel-contiguous reorder on one workload: µs per
+    call (HIP events on the call's stream, inputs resident), per-kernel
+    times, algorithmic bytes and parity with the oracle.
+
+    Algorithmic bytes of a call: each point read (16 B) with its voxel id and
+    its index in the order written (4 + 4 B); each kept row gathered and
+    written in sorted order (16 + 16 B); the voxel offsets (4 B x (voxels + 1))."""
+    import oracle
+    from workloads import generate, get_sph_config
+
+    p = get_sph_config(name).params
+    pts, _ = generate(name)
+    x = torch.from_numpy(pts).to("cuda:0")
+    s = vox.SphericalSorter(pts.shape[0], p.sph_min, p.sph_cell, p.bins, device="cuda:0")
+    ms = time_calls(s, x, steps, warmup, torch)
+    stage_ms, total_ms = s.profile(x, profile_iters)
+    torch.cuda.synchronize()
+    v, off, order, rows = (t.cpu().numpy() for t in s.outputs())
+    want = oracle.spherical(pts, p.sph_min, p.sph_cell, p.bins)
+    ok = (np.array_equal(v, want[0]) and np.array_equal(off, want[1])
+          and np.array_equal(order, want[2])
+          and np.array_equal(rows.view(np.uint32), pts[want[2]].view(np.uint32)))
+    N, kept, nvox = pts.shape[0], int(order.size), int(np.prod(p.bins))
+    # algorithmic bytes of the whole call: read each point, write its voxel id,
+    # its index and (kept) row in sorted order, and the voxel offsets
+    alg = 16 * N + 4 * N + 4 * N + 32 * kept + 4 * (nvox + 1)
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"op": "spherical", "workload": name, "N": N, "kept": kept, "voxels": nvox,
+            "us_per_call": round(ms * 1e3, 2),
+            "mpoints_s": round(N / (ms * 1e-3) / 1e6, 1),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+            "kernels_us": round(total_ms * 1e3, 2),
+            "alg_bytes": alg, "gbs_alg": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "parity": bool(ok)}
+
+
 def main():
     args = parse()
     if args.rocprof_summary:
@@ -301,6 +342,11 @@ def main():
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["pts"], p, args.cpu_seconds)
+    if args.all or args.spherical:
+        from workloads import sph_config_names
+        for name in sph_config_names():
+            print(json.dumps(spherical_line(name, args.steps, args.warmup, args.profile_iters,
+                                            torch, vox)), file=sys.stderr, flush=True)
     if args.all:
         from workloads import config_names
         for name in config_names():

@@ -25,6 +25,7 @@ VOX_EWORKSPACE = -2
 VOX_EHIP = -4
 VOX_STATUS_NEEDS_CHUNKED = -16
 VOX_STATUS_DEVICE_ERROR = -17
+SPH_STATUS_BAD_TABLE = -18
 STAGES = ("insert", "rank", "select", "pack")
 HEADER_BYTES = 256          # the workspace's first 256 bytes hold the result words
 
@@ -52,6 +53,11 @@ class Options(ctypes.Structure):
     _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
                 ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32),
                 ("compact_table", ctypes.c_int32), ("select_path", ctypes.c_int32)]
+
+
+class SphOptions(ctypes.Structure):
+    _fields_ = [("points_per_thread", ctypes.c_int32), ("digit_bits", ctypes.c_int32),
+                ("sort_tile", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -91,6 +97,22 @@ def _load() -> ctypes.CDLL:
     lib.vox_bin_points.restype = ctypes.c_int
     lib.vox_profile_stages.argtypes = common + [op, i32, vp, vp]
     lib.vox_profile_stages.restype = ctypes.c_int
+    sop = ctypes.POINTER(SphOptions)
+    lib.sph_table_bytes.argtypes = [vp]
+    lib.sph_table_bytes.restype = i64
+    lib.sph_make_table.argtypes = [vp, vp, vp, vp, i64]
+    lib.sph_make_table.restype = ctypes.c_int
+    lib.sph_workspace_bytes.argtypes = [i64, vp, sop]
+    lib.sph_workspace_bytes.restype = i64
+    lib.sph_workspace_zero_bytes.argtypes = [i64, vp, sop]
+    lib.sph_workspace_zero_bytes.restype = i64
+    lib.sph_num_kernels.argtypes = [i64, vp, sop]
+    lib.sph_num_kernels.restype = i32
+    sph_common = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, sop, vp]
+    lib.sph_reorder.argtypes = sph_common
+    lib.sph_reorder.restype = ctypes.c_int
+    lib.sph_profile_stages.argtypes = sph_common + [i32, vp, vp]
+    lib.sph_profile_stages.restype = ctypes.c_int
     lib.vox_stage_name.argtypes = [i32]
     lib.vox_stage_name.restype = ctypes.c_char_p
     lib.vox_strerror.argtypes = [i32]
@@ -427,3 +449,153 @@ class Downsampler:
         if V < 0:
             raise VoxError(V, "vox_downsample (device status)")
         return self.centroids[:V], self.coords[:V], self.counts[:V]
+
+
+# ------------------------------------------------------ spherical binning --
+
+def _sph_params(sph_min, sph_cell, bins):
+    mn = (ctypes.c_float * 3)(*[float(v) for v in sph_min])
+    ce = (ctypes.c_float * 3)(*[float(v) for v in sph_cell])
+    b = (ctypes.c_int32 * 3)(*[int(v) for v in bins])
+    return mn, ce, b
+
+
+def _sph_options(points_per_thread: int = 0, digit_bits: int = 0, sort_tile: int = 0):
+    if not (points_per_thread or digit_bits or sort_tile):
+        return None
+    return ctypes.pointer(SphOptions(int(points_per_thread), int(digit_bits), int(sort_tile)))
+
+
+def sph_table(sph_min: Sequence[float], sph_cell: Sequence[float],
+              bins: Sequence[int]) -> bytes:
+    """The boundary table of these parameters (host bytes, from sph_make_table)."""
+    mn, ce, b = _sph_params(sph_min, sph_cell, bins)
+    n = _lib.sph_table_bytes(b)
+    if n < 0:
+        raise VoxError(int(n), "sph_table_bytes")
+    buf = (ctypes.c_uint8 * int(n))()
+    _check(_lib.sph_make_table(mn, ce, b, buf, int(n)), "sph_make_table")
+    return bytes(buf)
+
+
+class _SphTables:
+    """Device copies of boundary tables, one per (device, parameters); each is
+    made once (one host-to-device copy) and kept."""
+
+    def __init__(self):
+        self._lock = threading.Lock()
+        self._cache: Dict[Tuple, torch.Tensor] = {}
+
+    def get(self, device: torch.device, sph_min, sph_cell, bins) -> torch.Tensor:
+        f32 = lambda v: ctypes.c_float(float(v)).value  # noqa: E731  (float32 rounding)
+        key = (device.index, tuple(f32(v) for v in sph_min), tuple(f32(v) for v in sph_cell),
+               tuple(int(v) for v in bins))
+        with self._lock:
+            t = self._cache.get(key)
+            if t is None:
+                host = torch.frombuffer(bytearray(sph_table(sph_min, sph_cell, bins)),
+                                        dtype=torch.uint8)
+                t = host.to(device)
+                self._cache[key] = t
+            return t
+
+
+_sph_tables = _SphTables()
+
+
+def sph_workspace_bytes(n_points: int, bins: Sequence[int], **opts) -> Tuple[int, int]:
+    """(workspace bytes, bytes of its zero part) for sph_reorder."""
+    b = (ctypes.c_int32 * 3)(*[int(v) for v in bins])
+    o = _sph_options(**opts)
+    n = _lib.sph_workspace_bytes(int(n_points), b, o)
+    z = _lib.sph_workspace_zero_bytes(int(n_points), b, o)
+    if n < 0 or z < 0:
+        raise VoxError(int(min(n, z)), "sph_workspace_bytes")
+    return int(n), int(z)
+
+
+def sph_stage_names(n_points: int, bins: Sequence[int], **opts) -> Tuple[str, ...]:
+    """Names of the kernels one call launches, in order: key, pass0.., final."""
+    b = (ctypes.c_int32 * 3)(*[int(v) for v in bins])
+    k = _lib.sph_num_kernels(int(n_points), b, _sph_options(**opts))
+    if k < 0:
+        raise VoxError(int(k), "sph_num_kernels")
+    return ("key",) + tuple(f"pass{q}" for q in range(k - 2)) + ("final",)
+
+
+class SphericalSorter:
+    """Pre-allocated outputs and workspace for repeated spherical binning and
+    reorder calls with one shape; ``run(points)`` enqueues one call on the
+    current stream (nothing allocated or synchronised per call)."""
+
+    def __init__(self, n_points: int, sph_min, sph_cell, bins, device="cuda", sorted_rows=True,
+                 **opts):
+        self.N = int(n_points)
+        self.device = torch.device(device)
+        self.bins = tuple(int(v) for v in bins)
+        self.nvox = self.bins[0] * self.bins[1] * self.bins[2]
+        self._opts = _sph_options(**opts)
+        self._mn, self._ce, self._b = _sph_params(sph_min, sph_cell, bins)
+        self.table = _sph_tables.get(self.device, sph_min, sph_cell, bins)
+        self.nbytes, self.zero_bytes = sph_workspace_bytes(self.N, bins, **opts)
+        self.stages = sph_stage_names(self.N, bins, **opts)
+        # the zero part must be zero before the first call; each call leaves it so
+        self.workspace = torch.zeros(max(self.nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.voxel_of = torch.empty((self.N,), dtype=torch.int32, device=self.device)
+        self.offsets = torch.empty((self.nvox + 1,), dtype=torch.int32, device=self.device)
+        self.order = torch.empty((max(self.N, 1),), dtype=torch.int32, device=self.device)
+        self.sorted = (torch.empty((max(self.N, 1), 4), dtype=torch.float32, device=self.device)
+                       if sorted_rows else None)
+        self.n_kept = torch.zeros((1,), dtype=torch.int32, device=self.device)
+
+    def _args(self, points: torch.Tensor, stream: int):
+        _check_points(points)
+        if points.shape[0] != self.N:
+            raise ValueError(f"expected {self.N} points, got {points.shape[0]}")
+        if points.device != self.device:
+            raise ValueError(f"points are on {points.device}, the sorter on {self.device}")
+        return [ctypes.c_void_p(points.data_ptr()), self.N, self._mn, self._ce, self._b,
+                ctypes.c_void_p(self.table.data_ptr()), ctypes.c_void_p(self.voxel_of.data_ptr()),
+                ctypes.c_void_p(self.offsets.data_ptr()), ctypes.c_void_p(self.order.data_ptr()),
+                ctypes.c_void_p(self.sorted.data_ptr()) if self.sorted is not None else None,
+                ctypes.c_void_p(self.n_kept.data_ptr()), ctypes.c_void_p(self.workspace.data_ptr()),
+                self.nbytes, self._opts, ctypes.c_void_p(stream)]
+
+    def run(self, points: torch.Tensor) -> torch.Tensor:
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _check(_lib.sph_reorder(*self._args(points, stream)), "sph_reorder")
+        return self.n_kept
+
+    def profile(self, points: torch.Tensor, iters: int) -> Tuple[Dict[str, float], float]:
+        """Mean milliseconds per kernel and per call, from HIP events on the call's stream."""
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        stage = (ctypes.c_float * len(self.stages))()
+        total = ctypes.c_float()
+        _check(_lib.sph_profile_stages(*self._args(points, stream), int(iters), stage,
+                                       ctypes.byref(total)), "sph_profile_stages")
+        return {name: float(stage[k]) for k, name in enumerate(self.stages)}, float(total.value)
+
+    def outputs(self):
+        """(voxel_of [N], offsets [nvox+1], order [n_kept], sorted rows [n_kept, 4] or None).
+        ``self.order`` holds all N indices: the kept ones sorted, then the rest."""
+        n = int(self.n_kept.item())
+        if n < 0:
+            raise VoxError(n, "sph_reorder (device status)")
+        rows = self.sorted[:n] if self.sorted is not None else None
+        return self.voxel_of, self.offsets, self.order[:n], rows
+
+
+@torch.no_grad()
+def spherical(points: torch.Tensor, sph_min: Sequence[float], sph_cell: Sequence[float],
+              bins: Sequence[int], *, sorted_rows: bool = True, points_per_thread: int = 0,
+              digit_bits: int = 0, sort_tile: int = 0):
+    """Spherical binning and voxel-contiguous reorder: (voxel_of [N] i32, -1 when
+    not kept; offsets [nvox+1] i32; order [n_kept] i32; the kept rows in that
+    order [n_kept, 4] f32, or None). Reads the kept count back (one sync)."""
+    _check_points(points)
+    s = SphericalSorter(points.shape[0], sph_min, sph_cell, bins, device=points.device,
+                        sorted_rows=sorted_rows, points_per_thread=points_per_thread,
+                        digit_bits=digit_bits, sort_tile=sort_tile)
+    with torch.cuda.device(points.device):
+        s.run(points)
+        return s.outputs()

@@ -14,7 +14,8 @@ import sys
 CSRC = os.path.dirname(os.path.abspath(__file__))
 HERE = os.path.dirname(CSRC)
 ROOT = os.path.dirname(HERE)
-SOURCE = os.path.join(CSRC, "voxelize.hip")
+SOURCES = [os.path.join(CSRC, "voxelize.hip"), os.path.join(CSRC, "spherical.hip")]
+SOURCE = SOURCES[0]
 HEADER = os.path.join(ROOT, "include", "voxelize.h")
 LIBRARY = os.path.join(HERE, "libvoxelize.so")
 ARCH = os.environ.get("VOX_OFFLOAD_ARCH", "gfx950")
@@ -35,7 +36,7 @@ def hipcc() -> str:
 
 def build(output: str = LIBRARY, quiet: bool = False) -> str:
     tmp = output + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.dirname(HEADER), "-o", tmp, SOURCE]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.dirname(HEADER), "-o", tmp, *SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)

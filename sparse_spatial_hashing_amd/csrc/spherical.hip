@@ -1,0 +1,775 @@
+// Spherical binning and voxel-contiguous reorder for MI355X (gfx950).
+//
+// The preprocessing of the RadiusFPS page (hankli.space, "RadiusFPS"):
+// spherical coordinates per point and uniform bins per axis (section
+// "Spherical voxel partition"), then one sort of the cloud by voxel id so a
+// voxel's points are contiguous and the voxel is a [start, end) range (the
+// preprocessing step and voxel record of RadiusFPS-G). The exact binning
+// rules are stated in spherical.h.
+//
+// The sort is a least-significant-digit radix sort of (voxel id, point
+// index) pairs, so every kernel does the same work per tile whatever the
+// spread of points over voxels (a LiDAR scan puts most of its points in a few
+// near shells):
+//   k_sph_key    bins each point, writes its voxel id (a dropped point gets
+//                the key nvox, which sorts after every voxel) and adds the
+//                block's digit counts of every pass to global histograms.
+//   k_sph_pass   one per digit (at most 8 bits): each tile of 256 x PER
+//                entries ranks its entries by digit stably in LDS, finds
+//                where each digit's run goes from the global histogram and a
+//                decoupled look-back over the preceding tiles' counts, and
+//                writes the tile out in digit order (coalesced runs). Stable
+//                passes from the lowest digit up leave the pairs sorted by
+//                voxel id and, inside a voxel, by input index.
+//   k_sph_final  voxel offsets from the boundaries between sorted keys, the
+//                kept count, the rows gathered in sorted order, and the
+//                histograms reset to zero for the next call.
+//
+// Angle bins: an atan2f estimate of the bin is refined by exact direction
+// tests against the table's boundary directions (cross products of float
+// operands in double), so atan2f's rounding never decides a bin.
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <math.h>
+#include <string.h>
+
+#include "spherical.h"
+#include "wave_ops.h"
+
+int ssh_hip_fail(hipError_t e);  // records the error for vox_last_hip_error()
+
+namespace {
+
+constexpr int kSBlock = 256;                 // 4 wavefronts (binning and final kernels)
+constexpr int kSPassBlock = 1024;            // 16 wavefronts (sort passes)
+constexpr int kSPassWaves = kSPassBlock / kWave;
+constexpr int kSMaxDigitBits = 8;
+constexpr int kSMaxDigits = 1 << kSMaxDigitBits;
+constexpr int kSMaxPasses = 23;              // 1-bit digits over a 23-bit key
+constexpr int kSHistWords = 768;             // digits summed over the passes, at most
+constexpr long long kSMaxTiles = 65536;
+constexpr int kSHistCopies = 16;             // global histograms, block b adds to copy b % 16
+constexpr int kSTableLds = 2048;             // boundary directions staged in LDS, at most
+constexpr int kSLookBack = 32;               // predecessor tiles read per look-back round trip
+constexpr unsigned kSMagic = 0x31485053u;    // "SPH1"
+constexpr unsigned kSSpinLimit = 1u << 22;   // look-back poll bound (never reached in practice)
+constexpr unsigned kSAgg = 1u << 30;         // look-back word: flag bits 31..30, count below
+constexpr unsigned kSIncl = 2u << 30;
+constexpr unsigned kSValue = (1u << 30) - 1u;
+constexpr double kSPi = 3.141592653589793;       // both roundings lie below the true value
+constexpr double kSHalfPi = 1.5707963267948966;
+
+// Head of the boundary table; elevation then azimuth directions follow as
+// float2 (cos, sin), n + 1 per axis.
+struct SphHeader {
+    unsigned magic;
+    int nr, nt, np;
+    float mn[3];
+    float cell[3];
+    int t_lo, t_hi;   // elevation boundaries k < t_lo: every direction is at or above;
+    int p_lo, p_hi;   // k > t_hi: none is. Same for azimuth.
+    unsigned bytes, pad;
+};
+static_assert(sizeof(SphHeader) == 64, "table header is 64 bytes");
+
+struct SphArgs {
+    float mn[3];
+    float cell[3];
+    int nr, nt, np;
+    int nvox;         // also the key of a dropped point
+    int ntiles;       // binning kernel: tiles of 256 x PER points
+    int tile;
+    int sort_tiles;   // sort passes: tiles of 1024 x PER entries
+    int sort_tile;
+};
+
+// Digit layout of the passes: pass p sorts by (key >> shift[p]) & (2^bits[p] - 1);
+// its counts sit at hoff[p] in the histogram words.
+struct SphDigits {
+    int passes;
+    int shift[kSMaxPasses];
+    int bits[kSMaxPasses];
+    int hoff[kSMaxPasses];
+    int hist_words;
+};
+
+__device__ __forceinline__ unsigned load_relaxed32(const unsigned* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed32(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool table_ok(const SphHeader* __restrict__ h, const SphArgs& a) {
+    bool ok = h->magic == kSMagic && h->nr == a.nr && h->nt == a.nt && h->np == a.np;
+#pragma unroll
+    for (int d = 0; d < 3; ++d)
+        ok = ok && __float_as_uint(h->mn[d]) == __float_as_uint(a.mn[d]) &&
+             __float_as_uint(h->cell[d]) == __float_as_uint(a.cell[d]);
+    return ok;
+}
+
+// ---------------------------------------------------------------- binning --
+
+// Half-turn of a direction for angles in (-pi, pi]: 0 below the x axis,
+// 1 for [0, pi), 2 for the negative x axis (angle pi).
+__device__ __forceinline__ int half_turn(float x, float y) {
+    return y < 0.0f ? 0 : ((y > 0.0f || x > 0.0f) ? 1 : 2);
+}
+
+// Largest k in [-1, n] whose boundary the direction is at or above, starting
+// from the estimate k0; ge(k) is monotone (true up to some k, then false).
+template <typename Ge>
+__device__ __forceinline__ int refine(int k0, int n, Ge ge) {
+    int k = k0;
+    while (k >= 0 && !ge(k)) --k;
+    while (k < n && ge(k + 1)) ++k;
+    return k;
+}
+
+__device__ __forceinline__ int clamp_estimate(float f, int n) {
+    return (int)fminf(fmaxf(f, -1.0f), (float)n);
+}
+
+// Voxel id of one point, -1 when not kept.
+__device__ __forceinline__ int sph_voxel(float4 p, const SphArgs& a, const SphHeader* __restrict__ h,
+                                         const float2* __restrict__ tb,
+                                         const float2* __restrict__ pb) {
+    const float x = p.x, y = p.y, z = p.z;
+    if (!(isfinite(x) && isfinite(y) && isfinite(z))) return -1;
+    const float sxy = x * x + y * y;          // no contraction: two products, one sum
+    const float r = sqrtf(sxy + z * z);       // correctly rounded
+    if (r == 0.0f) return -1;
+    const float fr = floorf((r - a.mn[0]) / a.cell[0]);
+    if (!(fr >= 0.0f && fr < (float)a.nr)) return -1;
+    const float rxy = sqrtf(sxy);
+
+    const int t_lo = h->t_lo, t_hi = h->t_hi;
+    const int it = refine(
+        clamp_estimate(floorf((atan2f(z, rxy) - a.mn[1]) / a.cell[1]), a.nt), a.nt, [&](int k) {
+            if (k < t_lo) return true;
+            if (k > t_hi) return false;
+            const float2 d = tb[k];
+            return (double)d.x * (double)z - (double)d.y * (double)rxy >= 0.0;
+        });
+    if (it < 0 || it >= a.nt) return -1;
+
+    float ax = x, ay = y + 0.0f;              // -0 + 0 = +0
+    if (x == 0.0f && y == 0.0f) {
+        ax = 1.0f;
+        ay = 0.0f;
+    }
+    const int hp = half_turn(ax, ay);
+    const int p_lo = h->p_lo, p_hi = h->p_hi;
+    const int ip = refine(
+        clamp_estimate(floorf((atan2f(ay, ax) - a.mn[2]) / a.cell[2]), a.np), a.np, [&](int k) {
+            if (k < p_lo) return true;
+            if (k > p_hi) return false;
+            const float2 d = pb[k];
+            const int hd = half_turn(d.x, d.y);
+            if (hp != hd) return hp > hd;
+            return (double)d.x * (double)ay - (double)d.y * (double)ax >= 0.0;
+        });
+    if (ip < 0 || ip >= a.np) return -1;
+    return (int)(((long long)fr * a.nt + it) * a.np + ip);
+}
+
+// ------------------------------------------------------------------- keys --
+
+// Tile t = blockIdx.x holds points [t T, t T + T), T = 256 PER; wavefront w
+// takes [t T + 64 PER w, t T + 64 PER (w + 1)), 64 at a time (the layout of
+// every kernel here). Also clears the look-back words of every pass and the
+// error word the passes may set. The digit counts go to one of 16 copies of
+// the histograms (by block), so no counter takes an add from every block.
+template <int PER, bool LDS_TABLE>
+__global__ __launch_bounds__(kSBlock) void k_sph_key(const float4* __restrict__ pts, long long N,
+                                                     SphArgs a, const SphHeader* __restrict__ tab,
+                                                     SphDigits dg, int* __restrict__ voxel_of,
+                                                     unsigned* __restrict__ ghist,
+                                                     unsigned* __restrict__ state,
+                                                     long long state_words,
+                                                     unsigned* __restrict__ err) {
+    __shared__ unsigned h[kSHistWords];
+    __shared__ float2 stab[LDS_TABLE ? kSTableLds : 1];
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
+    const long long stride = (long long)gridDim.x * kSBlock;
+    for (long long j = (long long)blockIdx.x * kSBlock + tid; j < state_words; j += stride)
+        state[j] = 0u;
+    if (blockIdx.x == 0 && tid == 0) *err = 0u;
+    if (!table_ok(tab, a)) return;   // same for every block
+    const float2* gtb = reinterpret_cast<const float2*>(tab + 1);
+    const int ndirs = a.nt + 1 + a.np + 1;
+    if (LDS_TABLE)
+        for (int j = tid; j < ndirs; j += kSBlock) stab[j] = gtb[j];
+    const float2* tb = LDS_TABLE ? stab : gtb;
+    const float2* pb = tb + (a.nt + 1);
+    for (int j = tid; j < dg.hist_words; j += kSBlock) h[j] = 0u;
+    const long long wbase = (long long)blockIdx.x * a.tile + (long long)w * kWave * PER;
+    float4 p[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const long long i = wbase + k * kWave + lane;
+        p[k] = i < N ? pts[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();   // h cleared, directions staged
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const long long i = wbase + k * kWave + lane;
+        if (i >= N) continue;
+        const int v = sph_voxel(p[k], a, tab, tb, pb);
+        voxel_of[i] = v;
+        const unsigned key = v < 0 ? (unsigned)a.nvox : (unsigned)v;
+        for (int q = 0; q < dg.passes; ++q)
+            atomicAdd(&h[dg.hoff[q] + ((key >> dg.shift[q]) & ((1u << dg.bits[q]) - 1u))], 1u);
+    }
+    __syncthreads();
+    unsigned* gcopy = ghist + (blockIdx.x % kSHistCopies) * dg.hist_words;
+    for (int j = tid; j < dg.hist_words; j += kSBlock)
+        if (h[j]) atomicAdd(&gcopy[j], h[j]);
+}
+
+// ------------------------------------------------------------------ passes --
+
+// One stable pass by the digit (key >> shift) & (2^dbits - 1). keys_in is
+// the voxel_of array on the first pass (a negative id reads as nvox) and
+// vals_in is then null (the value is the point index). ghist holds this
+// pass's global digit counts (16 copies, hist_words apart), state its look-back words (ntiles x 2^dbits,
+// zero at launch). Every tile publishes its digit counts before it looks
+// back, so the wait only covers tiles that have not counted yet.
+template <int PER>
+__global__ __launch_bounds__(kSPassBlock) void k_sph_pass(
+    const int* __restrict__ keys_in, const unsigned* __restrict__ vals_in,
+    unsigned* __restrict__ keys_out, unsigned* __restrict__ vals_out, long long N, SphArgs a,
+    const SphHeader* __restrict__ tab, int shift, int dbits, const unsigned* __restrict__ ghist,
+    int hist_words, unsigned* __restrict__ state, unsigned* __restrict__ err) {
+    constexpr int T = kSPassBlock * PER;
+    constexpr int NW = kSPassWaves;
+    __shared__ unsigned hist[NW * kSMaxDigits];
+    __shared__ unsigned sk[T], sv[T];
+    __shared__ unsigned lstart[kSMaxDigits], gbase[kSMaxDigits];
+    __shared__ unsigned wsum[NW];
+    if (!table_ok(tab, a)) return;
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
+    const int tile = blockIdx.x;
+    const int nb = 1 << dbits;
+    const unsigned dmask = (unsigned)nb - 1u;
+    for (int j = tid; j < NW * nb; j += kSPassBlock) hist[j] = 0u;
+    // this digit's global count (thread tid owns digit tid), loaded early
+    unsigned gd = 0;
+    if (tid < nb)
+#pragma unroll
+        for (int c = 0; c < kSHistCopies; ++c) gd += ghist[c * hist_words + tid];
+    const long long base = (long long)tile * T;
+    const long long wbase = base + (long long)w * kWave * PER;
+    unsigned key[PER], val[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const long long i = wbase + k * kWave + lane;
+        key[k] = 0u;
+        val[k] = (unsigned)i;
+        if (i < N) {
+            const int kin = keys_in[i];
+            key[k] = kin < 0 ? (unsigned)a.nvox : (unsigned)kin;
+            if (vals_in) val[k] = vals_in[i];
+        }
+    }
+    __syncthreads();   // hist cleared
+
+    // stable rank inside (wavefront, digit): earlier k first, then lower lanes
+    unsigned* hw = hist + w * nb;
+    unsigned rk[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const bool ok = wbase + k * kWave + lane < N;
+        const unsigned d = (key[k] >> shift) & dmask;
+        const unsigned long long peers = match_mask(d, ok, dbits);
+        rk[k] = ok ? hw[d] + (unsigned)__popcll(peers & lanes_below(lane)) : 0u;
+        if (ok && (peers & lanes_above(lane)) == 0ull) hw[d] += (unsigned)__popcll(peers);
+    }
+    __syncthreads();
+
+    // thread d owns digit d: tile count, per-wavefront prefix, publication
+    const int d = tid;
+    unsigned c = 0;
+    if (d < nb) {
+        for (int ww = 0; ww < NW; ++ww) {
+            const unsigned x = hist[ww * nb + d];
+            hist[ww * nb + d] = c;
+            c += x;
+        }
+        store_relaxed32(&state[(long long)tile * nb + d], (tile == 0 ? kSIncl : kSAgg) | c);
+    }
+    // the first look-back window is in flight while the block scans run
+    int hi = tile - 1;
+    unsigned sw[kSLookBack];
+#pragma unroll
+    for (int j = 0; j < kSLookBack; ++j)
+        sw[j] = (d < nb && hi - j >= 0) ? load_relaxed32(&state[(long long)(hi - j) * nb + d])
+                                        : kSIncl;
+    unsigned tile_total, all;
+    const unsigned ls = block_excl_scan<NW>(d < nb ? c : 0u, wsum, &tile_total);
+    const unsigned g0 = block_excl_scan<NW>(gd, wsum, &all);
+    if (d < nb) {
+        // kSLookBack predecessors per round trip, nearest first: add their
+        // counts up to the nearest inclusive prefix; a tile that has not
+        // published yet is polled again (the counts before it are final)
+        unsigned excl = 0;
+        unsigned polls = 0;
+        while (true) {
+            bool done = false, wait = false;
+            int used = 0;
+#pragma unroll
+            for (int j = 0; j < kSLookBack; ++j) {
+                if (done || wait) continue;
+                const unsigned flag = sw[j] & ~kSValue;
+                if (flag == 0u) {
+                    wait = true;
+                } else {
+                    excl += sw[j] & kSValue;
+                    used = j + 1;
+                    done = flag == kSIncl;
+                }
+            }
+            if (done) break;
+            hi -= used;
+            if (wait) {
+                if (++polls > kSSpinLimit) {
+                    atomicOr(err, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+#pragma unroll
+            for (int j = 0; j < kSLookBack; ++j)
+                sw[j] = hi - j >= 0 ? load_relaxed32(&state[(long long)(hi - j) * nb + d]) : kSIncl;
+        }
+        if (tile > 0) store_relaxed32(&state[(long long)tile * nb + d], kSIncl | (excl + c));
+        lstart[d] = ls;
+        gbase[d] = g0 + excl;
+    }
+    __syncthreads();
+
+    // the tile in digit order in LDS, then written out run by run
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (wbase + k * kWave + lane >= N) continue;
+        const unsigned dd = (key[k] >> shift) & dmask;
+        const unsigned lp = lstart[dd] + hist[w * nb + dd] + rk[k];
+        sk[lp] = key[k];
+        sv[lp] = val[k];
+    }
+    __syncthreads();
+    const int n_here = (int)(N - base < T ? N - base : T);
+    for (int q = tid; q < n_here; q += kSPassBlock) {
+        const unsigned kq = sk[q];
+        const unsigned dd = (kq >> shift) & dmask;
+        const unsigned out = gbase[dd] + ((unsigned)q - lstart[dd]);
+        keys_out[out] = kq;
+        vals_out[out] = sv[q];
+    }
+}
+
+// ------------------------------------------------------------------- final --
+
+// offsets[v] = q for v in [lo, hi] (empty when lo > hi). Ranges longer than
+// a few entries are written by the whole wavefront together; every lane of
+// the wavefront must call this.
+__device__ __forceinline__ void fill_offsets(int* __restrict__ offsets, long long lo, long long hi,
+                                             int value, int lane) {
+    const bool longr = hi - lo >= 16;
+    if (!longr)
+        for (long long v = lo; v <= hi; ++v) offsets[v] = value;
+    unsigned long long m = __ballot(longr);
+    while (m) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1ull;
+        const long long l0 = __shfl(lo, src), h0 = __shfl(hi, src);
+        const int val = __shfl(value, src);
+        for (long long v = l0 + lane; v <= h0; v += kWave) offsets[v] = val;
+    }
+}
+
+// Sorted keys -> voxel offsets: position q starts every voxel in
+// (key[q - 1], key[q]]; after the last kept key, the voxels up to nvox start
+// at the kept count. Rows are gathered in sorted order. Block 0 resets the
+// digit histograms (every pass has read them) and writes the status when
+// there is one; with a status, no block reads the sorted arrays.
+__global__ __launch_bounds__(kSBlock) void k_sph_final(
+    const unsigned* __restrict__ skeys, const int* __restrict__ order,
+    const float4* __restrict__ pts, float4* __restrict__ sorted, int* __restrict__ offsets,
+    int* __restrict__ n_kept, long long N, SphArgs a, const SphHeader* __restrict__ tab,
+    unsigned* __restrict__ ghist, int hist_words, const unsigned* __restrict__ err) {
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
+    const bool ok = table_ok(tab, a);
+    const bool failed = *err != 0u;   // set by a pass, cleared only by the next call's first kernel
+    if (blockIdx.x == 0) {
+        for (int j = tid; j < kSHistCopies * hist_words; j += kSBlock) ghist[j] = 0u;
+        if (tid == 0) {
+            if (!ok) *n_kept = SPH_STATUS_BAD_TABLE;
+            else if (failed) *n_kept = VOX_STATUS_DEVICE_ERROR;
+        }
+    }
+    if (!ok || failed) return;
+    const long long nvox = a.nvox;
+    if (N == 0) {
+        for (long long v = (long long)blockIdx.x * kSBlock + tid; v <= nvox;
+             v += (long long)gridDim.x * kSBlock)
+            offsets[v] = 0;
+        if (blockIdx.x == 0 && tid == 0) *n_kept = 0;
+        return;
+    }
+    const long long stride = (long long)gridDim.x * kSBlock;
+    for (long long q0 = (long long)blockIdx.x * kSBlock + w * kWave; q0 < N; q0 += stride) {
+        const long long q = q0 + lane;
+        const bool valid = q < N;
+        const long long key = valid ? (long long)skeys[q] : 0;
+        const long long prev = (valid && q > 0) ? (long long)skeys[q - 1] : -1;
+        const bool starts = valid && key != prev;
+        fill_offsets(offsets, starts ? prev + 1 : 1, starts ? key : 0, (int)q, lane);
+        if (starts && key == nvox) *n_kept = (int)q;
+        const bool last_kept = valid && q == N - 1 && key < nvox;
+        fill_offsets(offsets, last_kept ? key + 1 : 1, last_kept ? nvox : 0, (int)N, lane);
+        if (last_kept) *n_kept = (int)N;
+        if (valid && key < nvox && sorted) sorted[q] = pts[order[q]];
+    }
+}
+
+// ------------------------------------------------------------------- host --
+
+inline long long s_cdiv(long long a, long long b) { return (a + b - 1) / b; }
+inline size_t s_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SPlan {
+    int per, tile, ntiles, sort_per, sort_tile, sort_tiles;
+    long long nvox;
+    SphDigits dg;
+    size_t off_hist, zero_bytes, off_state, off_k0, off_v0, off_k1, off_v1, bytes;
+    long long state_words;
+    int final_blocks;
+};
+
+bool bins_ok(const int32_t bins[3]) {
+    if (!bins) return false;
+    for (int d = 0; d < 3; ++d)
+        if (bins[d] < 1) return false;
+    if (bins[1] > SPH_MAX_ANGLE_BINS || bins[2] > SPH_MAX_ANGLE_BINS) return false;
+    return (long long)bins[0] * bins[1] * bins[2] <= SPH_MAX_VOXELS;
+}
+
+bool params_ok(const float mn[3], const float cell[3]) {
+    if (!mn || !cell) return false;
+    for (int d = 0; d < 3; ++d)
+        if (!isfinite(mn[d]) || !isfinite(cell[d]) || !(cell[d] > 0.0f)) return false;
+    return true;
+}
+
+int make_splan(long long N, const int32_t bins[3], const sph_options* opt, SPlan* p) {
+    if (N < 0 || N > SPH_MAX_POINTS || !bins_ok(bins)) return VOX_EINVAL;
+    p->nvox = (long long)bins[0] * bins[1] * bins[2];
+    const int per_opt = opt ? opt->points_per_thread : 0;
+    if (per_opt != 0 && per_opt != 1 && per_opt != 2 && per_opt != 4 && per_opt != 8)
+        return VOX_EINVAL;
+    // measured on the 64-beam scan recipe: 2 per thread at 2^16 points, 4 at 2^20
+    p->per = per_opt ? per_opt : (N <= (1ll << 17) ? 2 : N <= (1ll << 21) ? 4 : 8);
+    p->tile = kSBlock * p->per;
+    p->ntiles = (int)(N > 0 ? s_cdiv(N, p->tile) : 1);
+    if (p->ntiles > kSMaxTiles) return VOX_EINVAL;
+    const int st_opt = opt ? opt->sort_tile : 0;
+    if (st_opt != 0 && st_opt != 1024 && st_opt != 2048 && st_opt != 4096) return VOX_EINVAL;
+    // large tiles keep the look-back short (each round trip to another tile's
+    // word costs about a microsecond)
+    p->sort_tile = st_opt ? st_opt : (N <= (1ll << 17) ? 2048 : 4096);
+    p->sort_per = p->sort_tile / kSPassBlock;
+    p->sort_tiles = (int)(N > 0 ? s_cdiv(N, p->sort_tile) : 1);
+    const int db_opt = opt ? opt->digit_bits : 0;
+    if (db_opt < 0 || db_opt > kSMaxDigitBits) return VOX_EINVAL;
+    // keys run over [0, nvox] (nvox = a dropped point)
+    int key_bits = 1;
+    while ((1ll << key_bits) <= p->nvox) ++key_bits;
+    const int db = db_opt ? db_opt : kSMaxDigitBits;
+    SphDigits& dg = p->dg;
+    dg.passes = (key_bits + db - 1) / db;
+    const int each = (key_bits + dg.passes - 1) / dg.passes;   // spread the bits evenly
+    int shift = 0, hoff = 0;
+    for (int q = 0; q < dg.passes; ++q) {
+        const int bits = key_bits - shift < each ? key_bits - shift : each;
+        dg.shift[q] = shift;
+        dg.bits[q] = bits;
+        dg.hoff[q] = hoff;
+        shift += bits;
+        hoff += 1 << bits;
+    }
+    dg.hist_words = hoff;
+    if (dg.passes > kSMaxPasses || hoff > kSHistWords) return VOX_EINVAL;
+    for (int q = dg.passes; q < kSMaxPasses; ++q) dg.shift[q] = dg.bits[q] = dg.hoff[q] = 0;
+    p->state_words = 0;
+    for (int q = 0; q < dg.passes; ++q) p->state_words += (long long)p->sort_tiles << dg.bits[q];
+    const size_t n4 = sizeof(unsigned) * (size_t)(N > 0 ? N : 1);
+    p->off_hist = 0;
+    p->zero_bytes =   // the histogram copies and the error word
+        s_align256(sizeof(unsigned) * ((size_t)kSHistCopies * dg.hist_words + 1));
+    p->off_state = p->zero_bytes;
+    p->off_k0 = s_align256(p->off_state + sizeof(unsigned) * (size_t)p->state_words);
+    p->off_v0 = s_align256(p->off_k0 + n4);
+    p->off_k1 = s_align256(p->off_v0 + n4);
+    p->off_v1 = s_align256(p->off_k1 + n4);
+    p->bytes = dg.passes >= 3 ? s_align256(p->off_v1 + n4) : p->off_v1;
+    const long long fb = s_cdiv(N > p->nvox + 1 ? N : p->nvox + 1, kSBlock);
+    p->final_blocks = (int)(fb < 4096 ? fb : 4096);
+    return VOX_OK;
+}
+
+SphArgs make_args(const float mn[3], const float cell[3], const int32_t bins[3], const SPlan& p) {
+    SphArgs a;
+    for (int d = 0; d < 3; ++d) {
+        a.mn[d] = mn[d];
+        a.cell[d] = cell[d];
+    }
+    a.nr = bins[0];
+    a.nt = bins[1];
+    a.np = bins[2];
+    a.nvox = (int)p.nvox;
+    a.ntiles = p.ntiles;
+    a.tile = p.tile;
+    a.sort_tiles = p.sort_tiles;
+    a.sort_tile = p.sort_tile;
+    return a;
+}
+
+// Boundaries [0, lo) lie at or below the axis's lowest angle, (hi, n] above
+// its highest (a_k never decreases in k); lim is that half-width rounded to
+// double, which is below the true one, so a < -lim exactly when a is at or
+// below -half-width, and a > lim exactly when a is above half-width.
+void axis_bounds(float a_min, float da, int n, double lim, float2* dirs, int* lo, int* hi) {
+    *lo = 0;
+    *hi = n;
+    bool above = false;
+    for (int k = 0; k <= n; ++k) {
+        const double ak = (double)a_min + (double)k * (double)da;
+        dirs[k].x = (float)cos(ak);
+        dirs[k].y = (float)sin(ak);
+        if (ak < -lim) *lo = k + 1;
+        if (!above && ak > lim) {
+            *hi = k - 1;
+            above = true;
+        }
+    }
+}
+
+int check_call(const float* points, long long N, const float mn[3], const float cell[3],
+               const int32_t bins[3], const void* table, int32_t* voxel_of, int32_t* offsets,
+               int32_t* order, float* sorted, int32_t* n_kept, void* ws, long long ws_bytes,
+               const sph_options* opt, SPlan* p) {
+    if (!params_ok(mn, cell)) return VOX_EINVAL;
+    const int rc = make_splan(N, bins, opt, p);
+    if (rc != VOX_OK) return rc;
+    if (!table || !offsets || !n_kept) return VOX_EINVAL;
+    if (N > 0 && (!points || !voxel_of || !order)) return VOX_EINVAL;
+    if (points && (reinterpret_cast<uintptr_t>(points) & 15u)) return VOX_EINVAL;
+    if (sorted && (reinterpret_cast<uintptr_t>(sorted) & 15u)) return VOX_EINVAL;
+    if (reinterpret_cast<uintptr_t>(table) & 3u) return VOX_EINVAL;
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) || ws_bytes < (long long)p->bytes)
+        return VOX_EWORKSPACE;
+    return VOX_OK;
+}
+
+int s_last_launch() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? VOX_OK : ssh_hip_fail(e);
+}
+
+template <int PER>
+void launch_pass(const int* kin, const unsigned* vin, unsigned* kout, unsigned* vout, long long N,
+                 const SphArgs& a, const SphHeader* tab, int shift, int bits, const unsigned* gh,
+                 int hist_words, unsigned* state, unsigned* err, hipStream_t st, hipEvent_t e0,
+                 hipEvent_t e1) {
+    hipExtLaunchKernelGGL(k_sph_pass<PER>, dim3((unsigned)a.sort_tiles), dim3(kSPassBlock), 0, st, e0, e1,
+                          0, kin, vin, kout, vout, N, a, tab, shift, bits, gh, hist_words, state,
+                          err);
+}
+
+template <int PER>
+void launch_key(const float4* pts, long long N, const SphArgs& a, const SphHeader* tab,
+                const SphDigits& dg, int* voxel_of, unsigned* gh, unsigned* state,
+                long long state_words, unsigned* err, hipStream_t st, hipEvent_t e0,
+                hipEvent_t e1) {
+    if (a.nt + 1 + a.np + 1 <= kSTableLds)
+        hipExtLaunchKernelGGL(k_sph_key<PER, true>, dim3((unsigned)a.ntiles), dim3(kSBlock), 0, st,
+                              e0, e1, 0, pts, N, a, tab, dg, voxel_of, gh, state, state_words, err);
+    else
+        hipExtLaunchKernelGGL(k_sph_key<PER, false>, dim3((unsigned)a.ntiles), dim3(kSBlock), 0, st,
+                              e0, e1, 0, pts, N, a, tab, dg, voxel_of, gh, state, state_words, err);
+}
+
+// ev (optional): a start and a stop event per kernel, passes + 2 kernels.
+int run_sph(const float* points, long long N, const SphArgs& a, const SPlan& p, const void* table,
+            int32_t* voxel_of, int32_t* offsets, int32_t* order, float* sorted, int32_t* n_kept,
+            void* ws, hipStream_t st, hipEvent_t* ev) {
+    char* w = static_cast<char*>(ws);
+    unsigned* gh = reinterpret_cast<unsigned*>(w + p.off_hist);
+    unsigned* err = gh + kSHistCopies * p.dg.hist_words;
+    unsigned* state = reinterpret_cast<unsigned*>(w + p.off_state);
+    unsigned* kbuf[2] = {reinterpret_cast<unsigned*>(w + p.off_k0),
+                         reinterpret_cast<unsigned*>(w + p.off_k1)};
+    unsigned* vbuf[2] = {reinterpret_cast<unsigned*>(w + p.off_v0),
+                         reinterpret_cast<unsigned*>(w + p.off_v1)};
+    const float4* pts = reinterpret_cast<const float4*>(points);
+    const SphHeader* tab = static_cast<const SphHeader*>(table);
+    auto evs = [&](int k) { return ev ? ev[2 * k] : nullptr; };
+    auto eve = [&](int k) { return ev ? ev[2 * k + 1] : nullptr; };
+    switch (p.per) {
+        case 1: launch_key<1>(pts, N, a, tab, p.dg, voxel_of, gh, state, p.state_words, err, st, evs(0), eve(0)); break;
+        case 2: launch_key<2>(pts, N, a, tab, p.dg, voxel_of, gh, state, p.state_words, err, st, evs(0), eve(0)); break;
+        case 4: launch_key<4>(pts, N, a, tab, p.dg, voxel_of, gh, state, p.state_words, err, st, evs(0), eve(0)); break;
+        default: launch_key<8>(pts, N, a, tab, p.dg, voxel_of, gh, state, p.state_words, err, st, evs(0), eve(0)); break;
+    }
+    int rc = s_last_launch();
+    long long soff = 0;
+    for (int q = 0; rc == VOX_OK && q < p.dg.passes; ++q) {
+        const int* kin = q == 0 ? voxel_of : reinterpret_cast<const int*>(kbuf[(q - 1) & 1]);
+        const unsigned* vin = q == 0 ? nullptr : vbuf[(q - 1) & 1];
+        unsigned* kout = kbuf[q & 1];
+        unsigned* vout = q == p.dg.passes - 1 ? reinterpret_cast<unsigned*>(order) : vbuf[q & 1];
+        const unsigned* ghq = gh + p.dg.hoff[q];
+        unsigned* sq = state + soff;
+        soff += (long long)p.sort_tiles << p.dg.bits[q];
+        switch (p.sort_per) {
+            case 1: launch_pass<1>(kin, vin, kout, vout, N, a, tab, p.dg.shift[q], p.dg.bits[q], ghq, p.dg.hist_words, sq, err, st, evs(1 + q), eve(1 + q)); break;
+            case 2: launch_pass<2>(kin, vin, kout, vout, N, a, tab, p.dg.shift[q], p.dg.bits[q], ghq, p.dg.hist_words, sq, err, st, evs(1 + q), eve(1 + q)); break;
+            default: launch_pass<4>(kin, vin, kout, vout, N, a, tab, p.dg.shift[q], p.dg.bits[q], ghq, p.dg.hist_words, sq, err, st, evs(1 + q), eve(1 + q)); break;
+        }
+        rc = s_last_launch();
+    }
+    if (rc != VOX_OK) return rc;
+    const int last = 1 + p.dg.passes;
+    hipExtLaunchKernelGGL(k_sph_final, dim3((unsigned)p.final_blocks), dim3(kSBlock), 0, st,
+                          evs(last), eve(last), 0, kbuf[(p.dg.passes - 1) & 1], order, pts,
+                          reinterpret_cast<float4*>(sorted), offsets, n_kept, N, a, tab, gh,
+                          p.dg.hist_words, err);
+    return s_last_launch();
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t sph_table_bytes(const int32_t bins[3]) {
+    if (!bins_ok(bins)) return VOX_EINVAL;
+    return (int64_t)sizeof(SphHeader) + (int64_t)sizeof(float2) * ((int64_t)bins[1] + 1 + bins[2] + 1);
+}
+
+int sph_make_table(const float sph_min[3], const float sph_cell[3], const int32_t bins[3],
+                   void* table, int64_t table_bytes) {
+    if (!params_ok(sph_min, sph_cell) || !bins_ok(bins) || !table) return VOX_EINVAL;
+    const int64_t need = sph_table_bytes(bins);
+    if (table_bytes < need) return VOX_EINVAL;
+    SphHeader h;
+    memset(&h, 0, sizeof h);
+    h.magic = kSMagic;
+    h.nr = bins[0];
+    h.nt = bins[1];
+    h.np = bins[2];
+    for (int d = 0; d < 3; ++d) {
+        h.mn[d] = sph_min[d];
+        h.cell[d] = sph_cell[d];
+    }
+    h.bytes = (unsigned)need;
+    float2* tb = reinterpret_cast<float2*>(static_cast<char*>(table) + sizeof(SphHeader));
+    float2* pb = tb + (bins[1] + 1);
+    axis_bounds(sph_min[1], sph_cell[1], bins[1], kSHalfPi, tb, &h.t_lo, &h.t_hi);
+    axis_bounds(sph_min[2], sph_cell[2], bins[2], kSPi, pb, &h.p_lo, &h.p_hi);
+    memcpy(table, &h, sizeof h);
+    return VOX_OK;
+}
+
+int64_t sph_workspace_bytes(int64_t n_points, const int32_t bins[3], const sph_options* options) {
+    SPlan p;
+    const int rc = make_splan(n_points, bins, options, &p);
+    return rc == VOX_OK ? (int64_t)p.bytes : rc;
+}
+
+int64_t sph_workspace_zero_bytes(int64_t n_points, const int32_t bins[3],
+                                 const sph_options* options) {
+    SPlan p;
+    const int rc = make_splan(n_points, bins, options, &p);
+    return rc == VOX_OK ? (int64_t)p.zero_bytes : rc;
+}
+
+int32_t sph_num_kernels(int64_t n_points, const int32_t bins[3], const sph_options* options) {
+    SPlan p;
+    const int rc = make_splan(n_points, bins, options, &p);
+    return rc == VOX_OK ? p.dg.passes + 2 : rc;
+}
+
+int sph_reorder(const float* points, int64_t n_points, const float sph_min[3],
+                const float sph_cell[3], const int32_t bins[3], const void* table,
+                int32_t* voxel_of, int32_t* offsets, int32_t* order, float* sorted,
+                int32_t* n_kept, void* workspace, int64_t workspace_bytes,
+                const sph_options* options, hipStream_t stream) {
+    SPlan p;
+    const int rc = check_call(points, n_points, sph_min, sph_cell, bins, table, voxel_of, offsets,
+                              order, sorted, n_kept, workspace, workspace_bytes, options, &p);
+    if (rc != VOX_OK) return rc;
+    const SphArgs a = make_args(sph_min, sph_cell, bins, p);
+    return run_sph(points, n_points, a, p, table, voxel_of, offsets, order, sorted, n_kept,
+                   workspace, stream, nullptr);
+}
+
+int sph_profile_stages(const float* points, int64_t n_points, const float sph_min[3],
+                       const float sph_cell[3], const int32_t bins[3], const void* table,
+                       int32_t* voxel_of, int32_t* offsets, int32_t* order, float* sorted,
+                       int32_t* n_kept, void* workspace, int64_t workspace_bytes,
+                       const sph_options* options, hipStream_t stream, int32_t iters,
+                       float* stage_ms, float* total_ms) {
+    if (iters < 1 || !stage_ms || !total_ms) return VOX_EINVAL;
+    SPlan p;
+    int rc = check_call(points, n_points, sph_min, sph_cell, bins, table, voxel_of, offsets,
+                        order, sorted, n_kept, workspace, workspace_bytes, options, &p);
+    if (rc != VOX_OK) return rc;
+    const SphArgs a = make_args(sph_min, sph_cell, bins, p);
+    const int nk = p.dg.passes + 2;
+    const int nev = 2 * nk;
+    hipEvent_t* ev = new hipEvent_t[(size_t)iters * nev];
+    int created = 0;
+    for (; created < iters * nev; ++created) {
+        const hipError_t e = hipEventCreate(&ev[created]);
+        if (e != hipSuccess) {
+            rc = ssh_hip_fail(e);
+            break;
+        }
+    }
+    for (int it = 0; rc == VOX_OK && it < iters; ++it)
+        rc = run_sph(points, n_points, a, p, table, voxel_of, offsets, order, sorted, n_kept,
+                     workspace, stream, ev + (size_t)it * nev);
+    if (rc == VOX_OK) {
+        const hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) rc = ssh_hip_fail(e);
+    }
+    if (rc == VOX_OK) {
+        double acc[kSMaxPasses + 2] = {0};
+        double tot = 0;
+        for (int it = 0; it < iters && rc == VOX_OK; ++it) {
+            hipEvent_t* e = ev + (size_t)it * nev;
+            for (int k = 0; k < nk; ++k) {
+                float ms = 0;
+                const hipError_t he = hipEventElapsedTime(&ms, e[2 * k], e[2 * k + 1]);
+                if (he != hipSuccess) {
+                    rc = ssh_hip_fail(he);
+                    break;
+                }
+                acc[k] += ms;
+            }
+            float ms = 0;
+            if (hipEventElapsedTime(&ms, e[0], e[nev - 1]) == hipSuccess) tot += ms;
+        }
+        for (int k = 0; k < nk; ++k) stage_ms[k] = (float)(acc[k] / iters);
+        *total_ms = (float)(tot / iters);
+    }
+    for (int k = 0; k < created; ++k) (void)hipEventDestroy(ev[k]);
+    delete[] ev;
+    return rc;
+}
+
+}  // extern "C"

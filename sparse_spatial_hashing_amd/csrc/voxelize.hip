@@ -47,6 +47,9 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include "wave_ops.h"
+#include "spherical.h"
+
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -56,7 +59,6 @@
 namespace {
 
 constexpr int kBlock = 256;                 // 4 wavefronts of 64 lanes
-constexpr int kWave = 64;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kRankTile = 1024;             // points per look-back tile
 constexpr int kRankIters = kRankTile / kBlock;
@@ -287,19 +289,6 @@ __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pt
 constexpr unsigned long long kFlagAgg = 1ull << 62;
 constexpr unsigned long long kFlagIncl = 2ull << 62;
 constexpr unsigned long long kValueMask = (1ull << 62) - 1ull;
-
-__device__ __forceinline__ unsigned long long load_relaxed(const unsigned long long* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_relaxed(unsigned long long* p, unsigned long long v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
 
 // Exclusive prefix of this tile from its predecessors' published words, read
 // 64 tiles per poll by the whole wavefront (lane l looks at tile - 1 - l).
@@ -845,64 +834,6 @@ constexpr int kBinsPerThread = kMaxBins / kBlock;
 constexpr int kBinBlock = 1024;                // k_bins threads (16 wavefronts)
 constexpr int kBinWaves = kBinBlock / kWave;
 constexpr unsigned kNoPid = 0xffffffffu;
-
-__device__ __forceinline__ unsigned wave_incl_scan(unsigned v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const unsigned o = (unsigned)__shfl_up((int)v, d);
-        if (lane >= d) v += o;
-    }
-    return v;
-}
-
-// Exclusive prefix sum over the block (NW wavefronts); *total gets the sum.
-// wsum is an LDS array of NW words. Contains two barriers.
-template <int NW>
-__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, unsigned* total) {
-    const int lane = __lane_id();
-    const int w = threadIdx.x / kWave;
-    const unsigned incl = wave_incl_scan(v, lane);
-    if (lane == kWave - 1) wsum[w] = incl;
-    __syncthreads();
-    unsigned off = 0, tot = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-        const unsigned x = wsum[ww];
-        if (ww < w) off += x;
-        tot += x;
-    }
-    __syncthreads();
-    *total = tot;
-    return off + incl - v;
-}
-
-// Block bid of a grid of n blocks -> tile: XCD x = bid % 8 takes the
-// contiguous tiles [x q + min(x, r), ...) with q = n / 8, r = n % 8 (a
-// bijection onto [0, n)).
-__device__ __forceinline__ long long xcd_tile(long long bid, long long n) {
-    const long long q = n / 8, r = n % 8;
-    const long long x = bid % 8, y = bid / 8;
-    return x * q + (x < r ? x : r) + y;
-}
-
-// Lanes of the wavefront whose value v (nbits low bits) equals this lane's,
-// among the lanes with `valid` set: one ballot per bit. Every lane calls it.
-__device__ __forceinline__ unsigned long long match_mask(unsigned v, bool valid, int nbits) {
-    unsigned long long m = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-        const bool bit = ((v >> b) & 1u) != 0u;
-        const unsigned long long bb = __ballot(valid && bit);
-        m &= bit ? bb : ~bb;
-    }
-    return m;
-}
-
-__device__ __forceinline__ unsigned long long lanes_below(int lane) {
-    return (1ull << lane) - 1ull;
-}
-__device__ __forceinline__ unsigned long long lanes_above(int lane) {
-    return ~((2ull << lane) - 1ull);  // lane 63: 2 << 63 wraps to 0, mask 0
-}
 
 // CARRY: also copy each kept point's row into a scratch array next to its
 // staging word, so that k_bins copies rows from there instead of gathering
@@ -1925,6 +1856,10 @@ int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& 
 
 }  // namespace
 
+// Records a HIP error for vox_last_hip_error(); used by the library's other
+// translation units.
+__attribute__((visibility("hidden"))) int ssh_hip_fail(hipError_t e) { return hip_fail(e); }
+
 // =================================================================== C ABI ==
 
 extern "C" {
@@ -2163,6 +2098,7 @@ const char* vox_strerror(int32_t code) {
         case VOX_STATUS_NEEDS_CHUNKED:
             return "cap not decidable in one pass: repeat with voxelize_chunked";
         case VOX_STATUS_DEVICE_ERROR: return "internal device bound exceeded";
+        case SPH_STATUS_BAD_TABLE: return "boundary table does not match the call's parameters";
         default: return "unknown error";
     }
 }

@@ -1,0 +1,81 @@
+// Wavefront and block primitives shared by the library's kernels (gfx950,
+// 64-lane wavefronts). Device code only.
+#ifndef SSH_WAVE_OPS_H
+#define SSH_WAVE_OPS_H
+
+#include <hip/hip_runtime.h>
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ unsigned long long load_relaxed(const unsigned long long* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const unsigned o = (unsigned)__shfl_up((int)v, d);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the block (NW wavefronts); *total gets the sum.
+// wsum is an LDS array of NW words. Contains two barriers.
+template <int NW>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, unsigned* total) {
+    const int lane = __lane_id();
+    const int w = threadIdx.x / kWave;
+    const unsigned incl = wave_incl_scan(v, lane);
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    unsigned off = 0, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+        const unsigned x = wsum[ww];
+        if (ww < w) off += x;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + incl - v;
+}
+
+// Block bid of a grid of n blocks -> tile: XCD x = bid % 8 takes the
+// contiguous tiles [x q + min(x, r), ...) with q = n / 8, r = n % 8 (a
+// bijection onto [0, n)).
+__device__ __forceinline__ long long xcd_tile(long long bid, long long n) {
+    const long long q = n / 8, r = n % 8;
+    const long long x = bid % 8, y = bid / 8;
+    return x * q + (x < r ? x : r) + y;
+}
+
+// Lanes of the wavefront whose value v (nbits low bits) equals this lane's,
+// among the lanes with `valid` set: one ballot per bit. Every lane calls it.
+__device__ __forceinline__ unsigned long long match_mask(unsigned v, bool valid, int nbits) {
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = ((v >> b) & 1u) != 0u;
+        const unsigned long long bb = __ballot(valid && bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+__device__ __forceinline__ unsigned long long lanes_below(int lane) {
+    return (1ull << lane) - 1ull;
+}
+__device__ __forceinline__ unsigned long long lanes_above(int lane) {
+    return ~((2ull << lane) - 1ull);  // lane 63: 2 << 63 wraps to 0, mask 0
+}
+
+#endif  // SSH_WAVE_OPS_H

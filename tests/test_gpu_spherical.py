@@ -1,0 +1,224 @@
+"""GPU parity of the spherical binning and voxel-contiguous reorder against the
+CPU oracle, through the C ABI (sph_reorder via the binding).
+
+Everything is integer work decided by exact comparisons, so the bar is bit
+equality: voxel_of, offsets and order equal the oracle's, and the sorted rows
+are bit copies of points[order]. Inputs come from the seeded generators only.
+"""
+import ctypes
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import sparse_spatial_hashing_amd as vox  # noqa: E402
+from test_oracle_spherical import SMALL, _boundary_dirs, _rot  # noqa: E402
+from workloads import generate, get_sph_config, sph_config_names  # noqa: E402
+
+DEV = torch.device("cuda:0")
+F32 = np.float32
+PI = math.pi
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+_last = {}
+
+
+def last_sorter_order():
+    return _last["order"]
+
+
+def gpu_sph(pts, sph_min, sph_cell, bins, sorted_rows=True, **kw):
+    say(f"  gpu spherical N={pts.shape[0]} bins={tuple(bins)} {kw}")
+    t = torch.from_numpy(np.ascontiguousarray(pts, dtype=F32)).to(DEV)
+    s = vox.SphericalSorter(t.shape[0], sph_min, sph_cell, bins, device=DEV,
+                            sorted_rows=sorted_rows, **kw)
+    s.run(t)
+    v, off, order, rows = s.outputs()
+    torch.cuda.synchronize()
+    _last["order"] = s.order[:t.shape[0]].cpu().numpy()
+    return (v.cpu().numpy(), off.cpu().numpy(), order.cpu().numpy(),
+            None if rows is None else rows.cpu().numpy())
+
+
+def check(pts, sph_min, sph_cell, bins, what, **kw):
+    want = oracle.spherical(pts, sph_min, sph_cell, bins)
+    got = gpu_sph(pts, sph_min, sph_cell, bins, **kw)
+    full = last_sorter_order()
+    dropped = np.flatnonzero(want[0] < 0)
+    assert np.array_equal(full[want[2].size:], dropped), f"{what}: dropped points not last"
+    assert np.array_equal(got[0], want[0]), f"{what}: voxel_of differs"
+    assert np.array_equal(got[1], want[1]), f"{what}: offsets differ"
+    assert np.array_equal(got[2], want[2]), f"{what}: order differs"
+    if got[3] is not None:
+        assert np.array_equal(got[3].view(np.uint32), pts[want[2]].view(np.uint32)), \
+            f"{what}: sorted rows differ"
+    return got
+
+
+@pytest.mark.parametrize("name", sph_config_names())
+def test_parity_workloads(name):
+    p = get_sph_config(name).params
+    pts, _ = generate(name)
+    say(f"spherical parity {name}")
+    check(pts, p.sph_min, p.sph_cell, p.bins, name)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_parity_other_seeds(seed):
+    p = get_sph_config("lidar_scan_64k").params
+    pts, _ = generate("lidar_scan_64k", seed=seed)
+    say(f"spherical parity seed={seed}")
+    check(pts, p.sph_min, p.sph_cell, p.bins, f"seed {seed}")
+
+
+def _ball(n, seed, rmax=5.0):
+    rng = np.random.default_rng(seed)
+    d = rng.normal(size=(n, 3))
+    d /= np.linalg.norm(d, axis=1, keepdims=True)
+    pts = np.zeros((n, 4), F32)
+    pts[:, :3] = (d * rng.uniform(0.0, rmax, size=(n, 1))).astype(F32)
+    pts[:, 3] = np.arange(n, dtype=F32)
+    return pts
+
+
+def test_parity_ball_coarse_and_fine_grids():
+    pts = _ball(300001, 11)
+    say("spherical parity ball coarse")
+    check(pts, *SMALL, "ball coarse")
+    say("spherical parity ball fine")
+    check(pts, (0.5, -1.2, -3.0), (0.25, 0.01, 0.013), (16, 240, 461), "ball fine")
+
+
+@pytest.mark.parametrize("per,sort_tile", [(1, 1024), (2, 2048), (4, 4096), (8, 1024)])
+@pytest.mark.parametrize("digit_bits", [8, 5, 3, 1])
+def test_parity_launch_options(per, sort_tile, digit_bits):
+    """Every tile size and digit width (2 to 15 passes) gives the same result,
+    with a ragged last tile (N not a multiple of any tile)."""
+    p = get_sph_config("lidar_scan_64k").params
+    pts, _ = generate("lidar_scan_64k", n=70001)
+    say(f"spherical options per={per} sort_tile={sort_tile} digit_bits={digit_bits}")
+    check(pts, p.sph_min, p.sph_cell, p.bins, f"per={per} tile={sort_tile} bits={digit_bits}",
+          points_per_thread=per, sort_tile=sort_tile, digit_bits=digit_bits)
+
+
+def test_single_voxel_grid():
+    """bins (1, 1, 1): a one-bit key (kept or not), one pass."""
+    pts = _ball(30000, 6, rmax=2.0)
+    check(pts, (0.5, -PI / 2, -PI), (1.0, PI, 2 * PI), (1, 1, 1), "one voxel grid")
+
+
+def test_hand_points_and_boundaries():
+    rows = [[1, 0, 0, 0], [0, 1, 0, 0], [-1, 0, 0, 0], [0, -1, 0, 0], [1, 1, 1, 0],
+            [0, 0, 1, 0], [0, 0, 0, 0], [2, 0.1, 0, 0], [0, 0, -1, 0], [-1, -0.0, 0, 0],
+            [3.5, -3.5, 0, 0], [np.nan, 1, 0, 0], [1, np.inf, 0, 0], [0.5, 0, 0, np.nan],
+            [1e-30, 0, 0, 0], [1e-20, 0, 0, 0], [-1, 1e-7, 0, 0], [-1, -1e-7, 0, 0]]
+    for axis, (lo, hi) in ((2, (-PI + 1e-3, PI - 1e-3)), (1, (-PI / 2 + 1e-3, PI / 2 - 1e-3))):
+        for k, c, s in _boundary_dirs(SMALL[0][axis], SMALL[1][axis], SMALL[2][axis], lo, hi):
+            for steps in (0, -1, 1):
+                cc, ss = _rot(c, s, steps)
+                rows.append([2 * cc, 2 * ss, 0, 0] if axis == 2 else [2 * cc, 0, 2 * ss, 0])
+                rows.append([2 * cc, 2 * ss, 0.5, 0] if axis == 2 else [2 * cc, 0, 2 * ss, 0])
+    pts = np.array(rows, F32)
+    check(pts, *SMALL, "hand")
+
+
+def test_empty_one_and_all_dropped():
+    check(np.zeros((0, 4), F32), *SMALL, "empty")
+    check(np.array([[1.5, 0.2, -0.3, 7.0]], F32), *SMALL, "one point")
+    check(np.zeros((1000, 4), F32), *SMALL, "all at the origin")
+    far = np.full((3000, 4), 100.0, F32)
+    check(far, *SMALL, "all past the last shell")
+
+
+def test_one_voxel_holds_everything():
+    """Every point in one voxel: one digit run per pass, and the offsets of
+    every other voxel are filled by long runs."""
+    rng = np.random.default_rng(2)
+    n = 40000
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = rng.uniform(1.1, 1.9, n).astype(F32)
+    pts[:, 1] = rng.uniform(0.01, 0.02, n).astype(F32)
+    pts[:, 2] = rng.uniform(0.01, 0.02, n).astype(F32)
+    got = check(pts, *SMALL, "one voxel")
+    assert np.count_nonzero(np.diff(got[1])) == 1
+
+
+def test_sorted_rows_optional():
+    p = get_sph_config("lidar_scan_64k").params
+    pts, _ = generate("lidar_scan_64k", n=20000)
+    got = check(pts, p.sph_min, p.sph_cell, p.bins, "no rows", sorted_rows=False)
+    assert got[3] is None
+
+
+def test_maximum_voxels():
+    """2^22 voxels (the limit), a million points."""
+    pts = _ball(1 << 20, 9, rmax=8.0)
+    check(pts, (0.0, -PI / 2, -PI), (0.125, PI / 256, PI / 128), (64, 256, 256), "max voxels")
+
+
+def test_maximum_points():
+    """2^24 points (the limit) on the 64-beam scan recipe and its grid."""
+    p = get_sph_config("lidar_scan_1m").params
+    pts, _ = generate("lidar_scan_1m", n=1 << 24)
+    say("spherical parity 2^24 points")
+    check(pts, p.sph_min, p.sph_cell, p.bins, "max points", sorted_rows=False)
+
+
+def test_repeated_calls_reuse_the_workspace():
+    """Each call leaves the workspace's zero part zero: a sorter called on one
+    cloud, then on another, then on the first again, matches the oracle every
+    time."""
+    p = get_sph_config("lidar_scan_64k").params
+    a, _ = generate("lidar_scan_64k", seed=21)
+    b, _ = generate("lidar_scan_64k", seed=22)
+    s = vox.SphericalSorter(a.shape[0], p.sph_min, p.sph_cell, p.bins, device=DEV)
+    for pts in (a, b, a):
+        s.run(torch.from_numpy(pts).to(DEV))
+        v, off, order, rows = s.outputs()
+        want = oracle.spherical(pts, p.sph_min, p.sph_cell, p.bins)
+        assert np.array_equal(v.cpu().numpy(), want[0])
+        assert np.array_equal(off.cpu().numpy(), want[1])
+        assert np.array_equal(order.cpu().numpy(), want[2])
+        assert np.array_equal(rows.cpu().numpy().view(np.uint32), pts[want[2]].view(np.uint32))
+        assert not s.workspace[:s.zero_bytes].any()
+
+
+def test_mismatched_table_reports_status():
+    """A table made for other parameters is refused on the device: n_kept gets
+    SPH_STATUS_BAD_TABLE and every kernel exits."""
+    p = get_sph_config("lidar_scan_64k").params
+    pts, _ = generate("lidar_scan_64k", n=5000)
+    s = vox.SphericalSorter(pts.shape[0], p.sph_min, p.sph_cell, p.bins, device=DEV)
+    other = vox.sph_table(p.sph_min, (4.0,) + tuple(p.sph_cell[1:]), p.bins)
+    s.table = torch.frombuffer(bytearray(other), dtype=torch.uint8).to(DEV)
+    s.run(torch.from_numpy(pts).to(DEV))
+    torch.cuda.synchronize()
+    assert int(s.n_kept.item()) == vox.SPH_STATUS_BAD_TABLE
+    with pytest.raises(vox.VoxError):
+        s.outputs()
+
+
+def test_profile_stages_runs():
+    p = get_sph_config("lidar_scan_64k").params
+    pts, _ = generate("lidar_scan_64k")
+    s = vox.SphericalSorter(pts.shape[0], p.sph_min, p.sph_cell, p.bins, device=DEV)
+    t = torch.from_numpy(pts).to(DEV)
+    stages, total = s.profile(t, 5)
+    assert list(stages) == ["key", "pass0", "pass1", "final"]
+    assert all(v > 0 for v in stages.values())
+    assert total >= max(stages.values())
+    want = oracle.spherical(pts, p.sph_min, p.sph_cell, p.bins)
+    assert np.array_equal(s.outputs()[2].cpu().numpy(), want[2])
