@@ -81,16 +81,16 @@ def rocprof_summary(root):
         out.append(f"# {os.path.relpath(f, root)}")
         out.append(f"{'kernel':28s} {'calls':>7s} {'mean_us':>9s} {'min_us':>9s} {'max_us':>9s}")
         for r in csv.DictReader(open(f)):
-            m = re.search(r"k_(\w+?(?:<\d+>)?)\(", r["Name"])
-            name = "k_" + m.group(1) if m else r["Name"][:28]
+            m = re.search(r"k_(\w+)(<[^>]*>)?\(", r["Name"])
+            name = "k_" + m.group(1) + (m.group(2) or "") if m else r["Name"][:28]
             out.append(f"{name:28s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
                        f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}")
     for f in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
         acc = {}
         for r in csv.DictReader(open(f)):
-            m = re.search(r"k_(\w+?(?:<\d+>)?)\(", r["Kernel_Name"])
+            m = re.search(r"k_(\w+)(<[^>]*>)?\(", r["Kernel_Name"])
             if m:
-                name = "k_" + m.group(1)
+                name = "k_" + m.group(1) + (m.group(2) or "")
             elif "copy" in r["Kernel_Name"].lower():
                 name = "copy(" + r["Grid_Size"] + ")"
             else:
@@ -128,17 +128,24 @@ def algorithmic_bytes(N, P, V, K, rows, kept, route):
                 select=16 * (N - P) + 4 * P + stage + carried, pack=out + 16 * rows + stage)
 
 
+def voxelize_source_hash():
+    """sha256 prefix over the sources of the voxelization kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("voxelize.hip", "wave_ops.h"):
+        h.update(open(os.path.join(ROOT, "sparse_spatial_hashing_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def recorded_traffic(workload, stage):
     """HBM bytes per launch of the kernel running `stage` from the committed
     counter summary (profiles/<workload>_traffic.txt), or None when it is
     missing or was taken on a different library source than the one built
     now."""
-    import hashlib
-    src = os.path.join(ROOT, "sparse_spatial_hashing_amd", "csrc", "voxelize.hip")
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = voxelize_source_hash()
     recorded, found = None, None
     for line in open(path):
         if line.startswith("source_sha256:"):
