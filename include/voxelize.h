@@ -91,7 +91,7 @@ typedef struct vox_options {
                                gathered from the cloud; 3 = partitioned, rows carried
                                through the workspace's scratch; 0 = automatic: 3 from
                                2^19 points up, else 2, when K <= 64 and max_voxels <=
-                               262144 (<= 131072 when K > 32), else 1. 2 and 3 outside
+                               262144, else 1. 2 and 3 outside
                                those limits: VOX_EINVAL. */
 } vox_options;
 

@@ -1110,6 +1110,8 @@ void k_bins(
     // bin b holds the ids b, b + nbins, b + 2 nbins, ... below V
     const long long nbins = 1ll << nbits;
     const int Gb = b < V ? (int)((V - b + nbins - 1) >> nbits) : 0;
+    // the coordinates' keys, needed only at the end, are loaded now
+    const long long key_t = t < Gb ? kept_key[b + ((long long)t << nbits)] : 0;
     for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
     for (int x = t; x < 3 * kBinWaves * G; x += kBinBlock) wbuf[x] = 0u;
     unsigned round = 0;
@@ -1251,7 +1253,7 @@ void k_bins(
     for (int p = t; p < Gb; p += kBinBlock) {
         const long long pp = b + ((long long)p << nbits);
         num_points[pp] = (int)(running[p] < (unsigned)K ? running[p] : (unsigned)K);
-        write_coords(coords, pp, kept_key[pp], gx, gy);
+        write_coords(coords, pp, p == t ? key_t : kept_key[pp], gx, gy);
         kept_key[pp] = 0;
         if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
     }
@@ -1530,8 +1532,8 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     // Select/pack route: per-bin partition (no per-point device atomic) when
     // K <= 64 and the ids fit kMaxBins bins of at most 128; buckets otherwise.
     const int path = opt ? opt->select_path : 0;
-    // bins of at most 128 ids (64 when K > 32, to keep k_bins within 64 KB of LDS)
-    const int max_per_bin = K > 32 ? 64 : 128;
+    // bins of at most 128 ids (k_bins' LDS holds at most 128 x 64 selected indices)
+    const int max_per_bin = 128;
     const bool part_ok = K <= kSortLanes && cdiv(M, max_per_bin) <= kMaxBins;
     if (path >= 2 && !part_ok) return VOX_EINVAL;
     pl->part = (path >= 2 || (path == 0 && part_ok)) ? 1 : 0;
@@ -1550,7 +1552,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         pl->nbins = 1 << pl->nbits;
         const long long per_bin = cdiv(M, pl->nbins);
         while ((1ll << pl->gshift) < per_bin) ++pl->gshift;
-        pl->lds = bins_lds_bytes(1 << pl->gshift, K, pl->carry);  // <= 50 KB
+        pl->lds = bins_lds_bytes(1 << pl->gshift, K, pl->carry);  // <= 66 KB
         // points per k_part thread: the largest power of two up to 16 that
         // still gives about 1024 tiles (small clouds spread over every CU)
         int per = 1;

@@ -126,8 +126,7 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_select_path_option_limits():
-    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 262144, or
-    <= 131072 when K > 32)."""
+    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 262144)."""
     auto = vox.workspace_bytes(100000, 60000, 32)
     assert auto == vox.workspace_bytes(100000, 60000, 32, select_path=2)
     assert auto != vox.workspace_bytes(100000, 60000, 32, select_path=1)
@@ -139,8 +138,8 @@ def test_select_path_option_limits():
     for bad in (dict(select_path=-1), dict(select_path=4)):
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(1000, 100, 32, **bad)
-    assert vox.workspace_bytes(1000, 131072, 64, select_path=2) > 0
-    for args in ((1000, 100, 65), (1000, 262145, 32), (1000, 131073, 33)):
+    assert vox.workspace_bytes(1000, 262144, 64, select_path=2) > 0
+    for args in ((1000, 100, 65), (1000, 262145, 32), (1000, 262145, 64)):
         assert vox.workspace_bytes(*args) > 0
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(*args, select_path=2)
