@@ -89,10 +89,9 @@ typedef struct vox_options {
                                1 = per-pillar buckets filled by one device atomic per
                                point; 2 = partitioned by pillar-id bins in LDS, rows
                                gathered from the cloud; 3 = partitioned, rows carried
-                               through the workspace's scratch; 0 = automatic: 3 from
-                               2^19 points up, else 2, when K <= 64 and max_voxels <=
-                               262144, else 1. 2 and 3 outside
-                               those limits: VOX_EINVAL. */
+                               through the workspace's scratch; 0 = automatic: 2 when
+                               K <= 64 and max_voxels <= 262144, else 1. 2 and 3
+                               outside those limits: VOX_EINVAL. */
 } vox_options;
 
 /*

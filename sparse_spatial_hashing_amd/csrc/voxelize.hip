@@ -1469,7 +1469,6 @@ inline size_t centroid_lds_bytes(int G) {
            4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + 3 * G);
 }
 // Clouds of at least this many points carry rows through staging by default.
-constexpr long long kCarryMinPoints = 1ll << 19;
 
 inline bool finite_f(float v) { return isfinite(v); }
 
@@ -1537,7 +1536,9 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     const bool part_ok = K <= kSortLanes && cdiv(M, max_per_bin) <= kMaxBins;
     if (path >= 2 && !part_ok) return VOX_EINVAL;
     pl->part = (path >= 2 || (path == 0 && part_ok)) ? 1 : 0;
-    pl->carry = pl->part && (path == 3 || (path == 0 && N >= kCarryMinPoints)) ? 1 : 0;
+    // rows are carried only on request: gathering the selected rows in k_bins
+    // measured faster than carrying every kept point's row through k_part
+    pl->carry = pl->part && path == 3 ? 1 : 0;
     pl->gshift = 0;
     pl->nbins = 0;
     pl->nbits = 0;

@@ -169,11 +169,11 @@ def test_workspace_zero_part():
 
 
 def test_select_route_rules():
-    """Automatic route: partitioned with carried rows from 2^19 points up,
-    partitioned with gathered rows below, buckets for K > 64."""
+    """Automatic route: partitioned with gathered rows, buckets for K > 64;
+    carried rows only on request."""
     assert vox.select_route(122880, 12000, 32) == 2
-    assert vox.select_route(1 << 19, 12000, 32) == 3
-    assert vox.select_route(2097152, 60000, 32) == 3
+    assert vox.select_route(1 << 19, 12000, 32) == 2
+    assert vox.select_route(2097152, 60000, 32) == 2
     assert vox.select_route(1000, 100, 65) == 1
     for p in (1, 2, 3):
         assert vox.select_route(122880, 12000, 32, select_path=p) == p
