@@ -52,7 +52,8 @@ class Options(ctypes.Structure):
     """Mirror of ``vox_options`` (0 fields mean defaults)."""
     _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
                 ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32),
-                ("compact_table", ctypes.c_int32), ("select_path", ctypes.c_int32)]
+                ("compact_table", ctypes.c_int32), ("select_path", ctypes.c_int32),
+                ("kept_map", ctypes.c_int32)]
 
 
 class SphOptions(ctypes.Structure):
@@ -141,11 +142,12 @@ def _check(rc: int, what: str) -> None:
 
 
 def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             compact_table: int = 0, select_path: int = 0):
-    if not (table_slots or prefix_points or hash or bucket_cap or compact_table or select_path):
+             compact_table: int = 0, select_path: int = 0, kept_map: int = 0):
+    if not (table_slots or prefix_points or hash or bucket_cap or compact_table or select_path
+            or kept_map):
         return None
     return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), int(bucket_cap),
-                                  int(compact_table), int(select_path)))
+                                  int(compact_table), int(select_path), int(kept_map)))
 
 
 def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
@@ -241,8 +243,9 @@ def _check_points(points: torch.Tensor) -> None:
 def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
              grid: Sequence[int], max_points: int, max_voxels: int, *,
              table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             compact_table: int = 0, select_path: int = 0, chunked: bool = False,
-             point_map: bool = False, return_device_outputs: bool = False):
+             compact_table: int = 0, select_path: int = 0, kept_map: int = 0,
+             chunked: bool = False, point_map: bool = False,
+             return_device_outputs: bool = False):
     """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
 
     Returns ``(voxels[V, K, 4] f32, coords[V, 3] i32 (z, y, x), num_points[V] i32)``
@@ -255,7 +258,8 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     dev = points.device
     N, K, M = points.shape[0], int(max_points), int(max_voxels)
     kw = dict(table_slots=table_slots, prefix_points=prefix_points, hash=hash,
-              bucket_cap=bucket_cap, compact_table=compact_table, select_path=select_path)
+              bucket_cap=bucket_cap, compact_table=compact_table, select_path=select_path,
+              kept_map=kept_map)
     opts = _options(**kw)
     nbytes = workspace_bytes(N, M, K, **kw)
     zbytes = workspace_zero_bytes(N, M, K, **kw)
@@ -302,7 +306,7 @@ def downsample_workspace_bytes(n_points: int, max_voxels: int, **opts) -> Tuple[
 @torch.no_grad()
 def downsample(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
                grid: Sequence[int], max_voxels: int, *, table_slots: int = 0,
-               prefix_points: int = 0, hash: int = 0, compact_table: int = 0,
+               prefix_points: int = 0, hash: int = 0, compact_table: int = 0, kept_map: int = 0,
                chunked: bool = False):
     """Voxel-grid downsampling: (centroids [V,4] f32 (x, y, z, intensity means),
     coords [V,3] i32 (z, y, x), counts [V] i32) for the first max_voxels voxels
@@ -312,7 +316,7 @@ def downsample(points: torch.Tensor, range_: Sequence[float], cell: Sequence[flo
     dev = points.device
     N, M = points.shape[0], int(max_voxels)
     kw = dict(table_slots=table_slots, prefix_points=prefix_points, hash=hash,
-              compact_table=compact_table)
+              compact_table=compact_table, kept_map=kept_map)
     opts = _options(**kw)
     nbytes, zbytes = downsample_workspace_bytes(N, M, **kw)
     with torch.cuda.device(dev):

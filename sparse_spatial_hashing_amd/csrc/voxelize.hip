@@ -332,6 +332,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, int* __restrict__ occ_slot,
                                                  long long* __restrict__ kept_key,
+                                                 unsigned* __restrict__ kmap,
                                                  Header* __restrict__ hdr,
                                                  int* __restrict__ num_voxels) {
     __shared__ unsigned tile_sh;
@@ -441,6 +442,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
         if (r < M) {
             table[slot[k]] = (key1[k] << kKeyShift) | kKeptFlag | (unsigned long long)r;
             kept_key[r] = (long long)(key1[k] - 1ull);
+            if (kmap) kmap[key1[k] - 1ull] = (unsigned)r + 1u;  // the kept-cell map
             if (C > 0) {
                 // the kept cells also go into a small table that lookups past
                 // the prefix probe instead of the big one (it stays in L2)
@@ -651,7 +653,8 @@ __device__ __forceinline__ void release_workspace(long long gtid, long long nthr
                                                   unsigned long long* __restrict__ compact,
                                                   unsigned C, int* __restrict__ kept_cslot,
                                                   unsigned long long* __restrict__ tile_state,
-                                                  long long ntiles, Header* __restrict__ hdr,
+                                                  long long ntiles, unsigned* __restrict__ kmap,
+                                                  Header* __restrict__ hdr,
                                                   int* __restrict__ num_voxels) {
     const long long kept_written = distinct < M ? distinct : M;
     for (long long r = gtid; r < distinct; r += nthreads) {
@@ -663,6 +666,7 @@ __device__ __forceinline__ void release_workspace(long long gtid, long long nthr
             report_error(hdr, num_voxels, 16u);
         }
         if (r >= V && r < kept_written) {
+            if (kmap) kmap[kept_key[r]] = 0u;
             kept_key[r] = 0;
             if (C > 0) clear_compact(compact, C, kept_cslot, r, hdr, num_voxels);
         }
@@ -797,7 +801,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 
     // 2) return the rest of the workspace to zero
     release_workspace(gtid, nthreads, distinct, V, M, occ_slot, table, S, kept_key, compact, C,
-                      kept_cslot, tile_state, ntiles, hdr, num_voxels);
+                      kept_cslot, tile_state, ntiles, nullptr, hdr, num_voxels);
 }
 
 // ------------------------------------------------- partitioned select/pack --
@@ -849,6 +853,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                                                  unsigned S,
                                                  const unsigned long long* __restrict__ compact,
                                                  unsigned C, int hash, int* __restrict__ slot_of,
+                                                 const unsigned* __restrict__ kmap,
                                                  int nbits, long long ptiles,
                                                  unsigned* __restrict__ cm,
                                                  unsigned* __restrict__ staging,
@@ -901,7 +906,28 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
             row[k0 + k] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (base < N && (CARRY || any_rest)) row[k0 + k] = pts[ii[k] < N ? ii[k] : N - 1];
         }
-        if (any_prefix) {
+        if (kmap && any_rest) {
+            // the kept-cell map answers every point of a tile that reaches
+            // past the prefix with one 4-byte load; its prefix points only
+            // return their slot_of entries to zero (tiles inside the prefix
+            // take the slot_of path below)
+            if (any_prefix) {
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    if (ii[k] < P) slot_of[ii[k]] = 0;
+            }
+            if (status > 0 && base < N) {
+                unsigned mv[PER_B];
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k) {
+                    const long long key = ii[k] < N ? bin_key(row[k0 + k], g) : -1;
+                    mv[k] = key >= 0 ? kmap[key] : 0u;
+                }
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    wd[k] = mv[k] ? (kKeptFlag | (unsigned long long)(mv[k] - 1u)) : 0ull;
+            }
+        } else if (any_prefix) {
             // prefix points: the slot insert recorded, then its word
             int sl[PER_B];
 #pragma unroll
@@ -922,7 +948,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                     if (ii[k] < P) wd[k] = w[k];
             }
         }
-        if (any_rest) {
+        if (any_rest && !kmap) {
             // later points: bin, then probe the home pair, then (rarely) lines
             long long key[PER_B];
             unsigned h[PER_B];
@@ -1079,7 +1105,8 @@ void k_bins(
     int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ voxels,
     int* __restrict__ coords, int* __restrict__ num_points, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
-    unsigned long long* __restrict__ tile_state, long long ntiles, Header* __restrict__ hdr) {
+    unsigned long long* __restrict__ tile_state, long long ntiles, unsigned* __restrict__ kmap,
+    Header* __restrict__ hdr) {
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
     unsigned* running = lds;                     // [G] arrivals so far per pillar
@@ -1104,7 +1131,7 @@ void k_bins(
     // the release touches nothing below; its memory traffic overlaps the bins
     release_workspace(b * kBinBlock + t, (long long)gridDim.x * kBinBlock, distinct, V, M,
                       occ_slot, table, S, kept_key, compact, C, kept_cslot, tile_state, ntiles,
-                      hdr, num_voxels);
+                      kmap, hdr, num_voxels);
     if (status <= 0) return;  // nothing was staged
 
     // bin b holds the ids b, b + nbins, b + 2 nbins, ... below V
@@ -1253,7 +1280,9 @@ void k_bins(
     for (int p = t; p < Gb; p += kBinBlock) {
         const long long pp = b + ((long long)p << nbits);
         num_points[pp] = (int)(running[p] < (unsigned)K ? running[p] : (unsigned)K);
-        write_coords(coords, pp, p == t ? key_t : kept_key[pp], gx, gy);
+        const long long key = p == t ? key_t : kept_key[pp];
+        write_coords(coords, pp, key, gx, gy);
+        if (kmap) kmap[key] = 0u;
         kept_key[pp] = 0;
         if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
     }
@@ -1293,7 +1322,8 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
     int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ centroids,
     int* __restrict__ coords, int* __restrict__ counts, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
-    unsigned long long* __restrict__ tile_state, long long ntiles, Header* __restrict__ hdr) {
+    unsigned long long* __restrict__ tile_state, long long ntiles, unsigned* __restrict__ kmap,
+    Header* __restrict__ hdr) {
     extern __shared__ float4 lds_rows[];
     const int G = 1 << gshift;
     float4* rowbuf = lds_rows;                   // [kBinBlock] this round's rows, by voxel
@@ -1318,7 +1348,7 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
     if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
     release_workspace(b * kBinBlock + t, (long long)gridDim.x * kBinBlock, distinct, V, M,
                       occ_slot, table, S, kept_key, compact, C, kept_cslot, tile_state, ntiles,
-                      hdr, num_voxels);
+                      kmap, hdr, num_voxels);
     if (status <= 0) return;
 
     const long long nbins = 1ll << nbits;
@@ -1411,7 +1441,9 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
         centroids[pp] = make_float4((float)(sx / dn), (float)(sy / dn), (float)(sz / dn),
                                     (float)(sw / dn));
         counts[pp] = (int)n;
-        write_coords(coords, pp, kept_key[pp], gx, gy);
+        const long long key = kept_key[pp];
+        write_coords(coords, pp, key, gx, gy);
+        if (kmap) kmap[key] = 0u;
         kept_key[pp] = 0;
         if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
     }
@@ -1443,6 +1475,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
     long long N, P, S, C;  // C: compact kept-cell table slots (0 = not used)
+    long long mapn;        // kept-cell map entries (0 = no map region)
     int K, M, hash, cap;
     long long ntiles;
     // partitioned select/pack (part = 1): bins of 2^gshift pillar ids, ptiles
@@ -1454,7 +1487,7 @@ struct Plan {
     // byte offsets into the workspace; [0, zero_bytes) is zero between calls,
     // [zero_bytes, bytes) is scratch every call writes before reading
     size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf,
-        off_compact, off_kcs, off_cm, off_stage, off_stage_pt, zero_bytes, bytes;
+        off_compact, off_kcs, off_map, off_cm, off_stage, off_stage_pt, zero_bytes, bytes;
 };
 
 // LDS of one k_bins block for bins of G pillars (plus the selection when rows
@@ -1498,6 +1531,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         if (opt->hash < 0 || opt->hash > 2) return VOX_EINVAL;
         if (opt->compact_table < 0 || opt->compact_table > 1) return VOX_EINVAL;
         if (opt->select_path < 0 || opt->select_path > 3) return VOX_EINVAL;
+        if (opt->kept_map < 0 || opt->kept_map > 1) return VOX_EINVAL;
         hash = opt->hash;
         P = opt->prefix_points;
         if (opt->bucket_cap > 0 && K <= kSortLanes) {
@@ -1584,6 +1618,11 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     off = align256(off + (size_t)pl->C * sizeof(unsigned long long));
     pl->off_kcs = off;
     off = align256(off + (pl->C > 0 ? (size_t)M * sizeof(int) : 0));
+    // the kept-cell map: 2 S cells of 4 bytes (the table's own size), used
+    // when the grid has at most that many cells
+    pl->mapn = (pl->part && pl->C == 0 && !(opt && opt->kept_map == 1)) ? 2 * S : 0;
+    pl->off_map = off;
+    off = align256(off + (size_t)pl->mapn * sizeof(unsigned));
     pl->zero_bytes = off;  // the scratch tail starts here
     pl->off_cm = off;
     off = align256(off + (size_t)pl->nbins * (size_t)pl->ptiles * sizeof(unsigned));
@@ -1648,9 +1687,10 @@ struct Buffers {
     unsigned* cm;
     unsigned* stage;
     float4* stage_pt;
+    unsigned* kmap;  // the kept-cell map, or null when the grid does not fit it
 };
 
-Buffers carve(void* ws, const Plan& pl) {
+Buffers carve(void* ws, const Plan& pl, const Grid& g) {
     char* b = static_cast<char*>(ws);
     Buffers x;
     x.hdr = reinterpret_cast<Header*>(b);
@@ -1667,6 +1707,10 @@ Buffers carve(void* ws, const Plan& pl) {
     x.cm = reinterpret_cast<unsigned*>(b + pl.off_cm);
     x.stage = reinterpret_cast<unsigned*>(b + pl.off_stage);
     x.stage_pt = reinterpret_cast<float4*>(b + pl.off_stage_pt);
+    const long long cells = (long long)g.gx * g.gy * g.gz;
+    // no map when the prefix holds every point: nothing would look it up
+    x.kmap = (pl.mapn > 0 && cells <= pl.mapn && pl.P < pl.N)
+                 ? reinterpret_cast<unsigned*>(b + pl.off_map) : nullptr;
     return x;
 }
 
@@ -1698,7 +1742,7 @@ int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_vox
     hipExtLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, ev_start(ev),
                           ev_stop(ev), 0, P, pl.N, pl.M,
                        bf.table, bf.compact, (unsigned)pl.C, pl.hash, bf.kcs, bf.slot_of,
-                       bf.tiles, ntiles, bf.occ, bf.kept, bf.hdr, num_voxels);
+                       bf.tiles, ntiles, bf.occ, bf.kept, bf.kmap, bf.hdr, num_voxels);
     return last_launch();
 }
 
@@ -1718,8 +1762,8 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
                               ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
                            (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of,
-                           pl.nbits, pl.ptiles, bf.cm, bf.stage, bf.stage_pt, bf.hdr, num_voxels,
-                           point_pillar);
+                           bf.kmap, pl.nbits, pl.ptiles, bf.cm, bf.stage, bf.stage_pt, bf.hdr,
+                           num_voxels, point_pillar);
         return last_launch();
     }
     const unsigned blocks = (unsigned)(pl.N > 0 ? cdiv(pl.N, kBlock) : 1);
@@ -1745,7 +1789,7 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                            bf.kept, bf.compact,
                            (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                            reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
-                           bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
+                           bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr);
         return last_launch();
     }
     // lanes per pillar: next power of two >= max(K, 8) (a whole wave if K > 64)
@@ -1853,7 +1897,7 @@ int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& 
                           bf.stage_pt, pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.M,
                           bf.kept, bf.compact, (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                           reinterpret_cast<float4*>(centroids), coords, counts, num_voxels,
-                          bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
+                          bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr);
     return last_launch();
 }
 
@@ -1914,7 +1958,7 @@ int voxelize_ex(const float* points, int64_t n_points, const float range[6],
                            coords, num_points, num_voxels, workspace, workspace_bytes, options,
                            &g, &pl);
     if (rc != VOX_OK) return rc;
-    const Buffers bf = carve(workspace, pl);
+    const Buffers bf = carve(workspace, pl, g);
     return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, nullptr,
                         stream, nullptr);
 }
@@ -1951,7 +1995,7 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
                      &pl);
     if (rc != VOX_OK) return rc;
     if (n_points > 0 && point_pillar && ((uintptr_t)point_pillar & 3u)) return VOX_EINVAL;
-    const Buffers bf = carve(workspace, pl);
+    const Buffers bf = carve(workspace, pl, g);
     if (!chunked)
         return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels,
                             point_pillar, stream, nullptr);
@@ -2014,7 +2058,7 @@ int vox_downsample(const float* points, int64_t n_points, const float range[6],
     Plan pl;
     if ((rc = downsample_plan(n_points, max_voxels, options, &pl)) != VOX_OK) return rc;
     if (((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes) return VOX_EWORKSPACE;
-    const Buffers bf = carve(workspace, pl);
+    const Buffers bf = carve(workspace, pl, g);
     long long P = pl.P;
     if (chunked) {
         if ((rc = insert_chunked(points, g, pl, bf, stream, &P)) != VOX_OK) return rc;
@@ -2043,7 +2087,7 @@ int vox_profile_stages(const float* points, int64_t n_points, const float range[
                      coords, num_points, num_voxels, workspace, workspace_bytes, options, &g,
                      &pl);
     if (rc != VOX_OK) return rc;
-    const Buffers bf = carve(workspace, pl);
+    const Buffers bf = carve(workspace, pl, g);
     const int nev = 2 * VOX_NUM_STAGES;  // a start and a stop per kernel
     hipEvent_t* ev = new hipEvent_t[(size_t)iters * nev];
     int created = 0;

@@ -237,7 +237,9 @@ def test_result_independent_of_table_and_hash(name):
                dict(select_path=1, compact_table=1, bucket_cap=1),
                dict(select_path=2, table_slots=3 * M, hash=1),
                dict(select_path=1, table_slots=3 * M, hash=2), dict(select_path=2),
-               dict(select_path=3), dict(select_path=3, compact_table=1)):
+               dict(select_path=3), dict(select_path=3, compact_table=1),
+               dict(kept_map=1), dict(kept_map=1, select_path=3),
+               dict(table_slots=3 * M), dict(table_slots=3 * M, hash=1, kept_map=1)):
         say(f"invariance {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
 

@@ -70,10 +70,27 @@ def test_workspace_bytes_bucket_cap_option():
 
 
 def test_compact_table_option():
-    assert vox.workspace_bytes(1000, 100, 32, compact_table=1) > vox.workspace_bytes(1000, 100, 32)
+    # the compact table replaces the kept-cell map (which it turns off)
+    assert vox.workspace_bytes(1000, 100, 32, compact_table=1) > \
+        vox.workspace_bytes(1000, 100, 32, kept_map=1)
     assert vox.plan(1000, 100, 32)["prefix_points"] == 400   # min(N, 4 * max_voxels)
     with pytest.raises(vox.VoxError):
         vox.workspace_bytes(1000, 100, 32, compact_table=2)
+
+
+def test_kept_map_option():
+    """The kept-cell map (2 x table_slots cells of 4 bytes) sits in the zero part
+    on the partitioned routes; kept_map=1 leaves it out; the bucket route never
+    has it."""
+    S = vox.plan(122880, 12000, 32)["table_slots"]
+    with_map = vox.workspace_zero_bytes(122880, 12000, 32)
+    without = vox.workspace_zero_bytes(122880, 12000, 32, kept_map=1)
+    assert with_map - without >= 8 * S
+    assert vox.workspace_zero_bytes(122880, 12000, 32, select_path=1) == \
+        vox.workspace_zero_bytes(122880, 12000, 32, select_path=1, kept_map=1)
+    for bad in (-1, 2):
+        with pytest.raises(vox.VoxError):
+            vox.workspace_bytes(1000, 100, 32, kept_map=bad)
 
 
 def test_workspace_bytes_rejects_small_table():
