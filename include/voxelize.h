@@ -58,7 +58,7 @@ extern "C" {
 #define VOX_EHIP -4        /* a HIP call failed; vox_last_hip_error() returns its code */
 
 /* ---- device status written to num_voxels[0] instead of V ----------------- */
-/* The single-pass path inserts the first P = min(N, table_slots/4) points into
+/* The single-pass path inserts the first P points into
  * the table and decides the max_voxels cap among them. When N > P and those P
  * points hold fewer than max_voxels distinct cells, the cap cannot be decided
  * in one pass: num_voxels[0] is set to VOX_STATUS_NEEDS_CHUNKED, the outputs
@@ -75,7 +75,8 @@ typedef struct vox_options {
     int64_t table_slots;    /* hash table slots S; 0 = 16 * max_voxels (at least 64);
                                otherwise 2 * max_voxels <= S <= 2^31 - 16; rounded up to
                                a multiple of 16 (one 128-byte line) */
-    int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N, S/4);
+    int64_t prefix_points;  /* points inserted before the cap is decided; 0 = min(N,
+                               2 max_voxels, S/4);
                                at most S/2 (and N) */
     int32_t hash;           /* home slot: 0 = key folded to 32 bits times 0x9E3779B1, then a
                                multiply-high reduction to [0, S); 1 = key mod S; 2 = a

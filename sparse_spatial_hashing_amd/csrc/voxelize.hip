@@ -1544,7 +1544,12 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     // cache line (16 slots) at a time, so S is rounded up to a multiple of 16.
     if (S < 2ll * M || S > 2147483647ll - 15) return VOX_EINVAL;
     S = (S + (long long)kLineSlots - 1) / (long long)kLineSlots * (long long)kLineSlots;
-    if (P == 0) P = S / 4;
+    // Default prefix: 2 max_voxels points (at most S/4). The cap is decided by
+    // the first max_voxels distinct cells, which on the measured clouds occur
+    // within 1.0-1.75 max_voxels points; a cloud that needs more reports
+    // VOX_STATUS_NEEDS_CHUNKED and takes the chunked entry point. Inserting
+    // fewer points makes both the insert and the rank shorter.
+    if (P == 0) P = S / 4 < 2ll * M ? S / 4 : 2ll * M;
     if (P > S / 2) P = S / 2;
     if (P > N) P = N;
     pl->N = N;

@@ -281,6 +281,33 @@ def test_needs_chunked_status_is_reported_and_workspace_stays_clean():
     assert vox.workspace_is_clean(v.workspace, v.zero_bytes)
 
 
+def test_default_prefix_too_short_takes_the_chunked_route():
+    """The default prefix is 2 max_voxels points: a cloud whose first 300
+    points share one cell (max_voxels 100) cannot decide its cap there. The
+    single pass reports it, the binding repeats the call on the chunked
+    route, and the result equals the oracle's."""
+    cfg = get_config("tiny")
+    p = cfg.params
+    rng = np.random.default_rng(13)
+    head = np.tile(np.array([[10.05, 0.05, 0.0, 1.0]], F32), (300, 1))
+    rest = np.zeros((5000, 4), F32)
+    rest[:, 0] = rng.uniform(0.0, 69.0, 5000)
+    rest[:, 1] = rng.uniform(-39.0, 39.0, 5000)
+    rest[:, 2] = rng.uniform(-2.9, 0.9, 5000)
+    pts = np.ascontiguousarray(np.concatenate([head, rest]).astype(F32))
+    M = 100
+    say("default prefix too short")
+    v = vox.Voxelizer(pts.shape[0], p.range_, p.cell, p.grid, p.max_points, M, device=DEV)
+    nv = v.run(torch.from_numpy(pts).to(DEV))
+    torch.cuda.synchronize()
+    assert int(nv.item()) == vox.VOX_STATUS_NEEDS_CHUNKED
+    assert vox.workspace_is_clean(v.workspace, v.zero_bytes)
+    want = oracle.voxelize(pts, p.range_, p.cell, p.grid, p.max_points, M)
+    got = vox.voxelize(torch.from_numpy(pts).to(DEV), p.range_, p.cell, p.grid, p.max_points, M)
+    torch.cuda.synchronize()
+    assert_bitwise(tuple(t.cpu().numpy() for t in got), want, "chunked retry")
+
+
 def test_repeated_calls_identical_and_workspace_zero():
     cfg = get_config("dense_multisweep")
     p = cfg.params

@@ -73,7 +73,9 @@ def test_compact_table_option():
     # the compact table replaces the kept-cell map (which it turns off)
     assert vox.workspace_bytes(1000, 100, 32, compact_table=1) > \
         vox.workspace_bytes(1000, 100, 32, kept_map=1)
-    assert vox.plan(1000, 100, 32)["prefix_points"] == 400   # min(N, 4 * max_voxels)
+    assert vox.plan(1000, 100, 32)["prefix_points"] == 200   # min(N, 2 max_voxels, S/4)
+    assert vox.plan(1000, 100, 32, table_slots=400)["prefix_points"] == 100   # S/4
+    assert vox.plan(150, 100, 32)["prefix_points"] == 150   # N
     with pytest.raises(vox.VoxError):
         vox.workspace_bytes(1000, 100, 32, compact_table=2)
 
