@@ -65,14 +65,21 @@ extern "C" {
 #define SPH_STATUS_BAD_TABLE (-18)
 
 /* ---- options (tests and tuning; NULL = defaults) ------------------------- */
-/* The sort is a least-significant-digit radix sort over the keys [0, nvox]
- * (nvox marks a point that is not kept): ceil(key bits / digit bits) stable
- * passes. */
+/* Two routes give the same results.
+ *   Two kernels: when nvox <= 65536 (kept keys of at most 16 bits) and
+ *   digit_bits is 0. The binning kernel also groups each tile's kept points
+ *   by the key's low digit; the second kernel reads each group of low digits
+ *   across all tiles, in input order, and places the points by the high
+ *   digit (at most 8 bits) after a look-back over the preceding groups.
+ *   Radix passes otherwise: a least-significant-digit radix sort over the
+ *   keys [0, nvox] (nvox marks a point that is not kept), ceil(key bits /
+ *   digit bits) stable passes, then a kernel for the offsets and rows. */
 typedef struct sph_options {
     int32_t points_per_thread; /* binning kernel: 0 = automatic; else 1, 2, 4 or 8
                                   (256-thread blocks, tile = 256 x this) */
-    int32_t digit_bits;        /* bits sorted per pass: 0 = 8 (the most); else 1..8 */
-    int32_t sort_tile;         /* entries per block in a sort pass (1024 threads):
+    int32_t digit_bits;        /* bits sorted per radix pass: 0 = 8 (the most), or the
+                                  two-kernel route when it applies; 1..8 = radix passes */
+    int32_t sort_tile;         /* entries per block in a radix pass (1024 threads):
                                   0 = automatic; else 1024, 2048 or 4096 */
 } sph_options;
 
@@ -103,13 +110,15 @@ int sph_make_table(const float sph_min[3], const float sph_cell[3], const int32_
  */
 int64_t sph_workspace_bytes(int64_t n_points, const int32_t bins[3], const sph_options* options);
 
-/* Z above (16 copies of the global digit histograms, beside an error word
- * that each call clears itself), or VOX_EINVAL. */
+/* Z above (16 copies of the global digit histograms, an error word that each
+ * call clears itself and, on the two-kernel route, a block counter), or
+ * VOX_EINVAL. */
 int64_t sph_workspace_zero_bytes(int64_t n_points, const int32_t bins[3],
                                  const sph_options* options);
 
-/* Kernels one call launches (the binning kernel, one per sort pass, the
- * final kernel), or VOX_EINVAL: the length of sph_profile_stages' stage_ms. */
+/* Kernels one call launches, or VOX_EINVAL: 2 on the two-kernel route, else
+ * the binning kernel, one per radix pass and the final kernel (at least 3).
+ * The length of sph_profile_stages' stage_ms. */
 int32_t sph_num_kernels(int64_t n_points, const int32_t bins[3], const sph_options* options);
 
 /*
@@ -120,9 +129,9 @@ int32_t sph_num_kernels(int64_t n_points, const int32_t bins[3], const sph_optio
  *   offsets  [nvox + 1] int32   first sorted position of each voxel; the
  *                               voxel's points are order[offsets[v] ..
  *                               offsets[v + 1]); offsets[nvox] = kept count
- *   order    [n_points] int32   a permutation of the input indices: the kept
- *                               points sorted (the first n_kept entries),
- *                               then the points not kept, in input order
+ *   order    [n_points] int32   the first n_kept entries: input indices of the
+ *                               kept points in sorted order; the entries past
+ *                               n_kept are unspecified
  *   sorted   [n_points, 4] f32  optional (NULL = skipped): the kept rows in
  *                               sorted order, bit copies of the input rows
  *   n_kept   [1] int32          kept count, or SPH_STATUS_BAD_TABLE, or
@@ -139,10 +148,11 @@ int sph_reorder(const float* points, int64_t n_points, const float sph_min[3],
 /*
  * Run sph_reorder `iters` times (same arguments) and report the mean
  * duration of each kernel in milliseconds, from events recorded with the
- * kernel launches, in launch order: stage_ms[0] the binning kernel,
- * stage_ms[1 .. passes] the sort passes, stage_ms[passes + 1] the final
- * kernel (sph_num_kernels() entries); *total_ms the mean time from the first
- * kernel's start to the last one's end. Synchronises the stream.
+ * kernel launches, in launch order (sph_num_kernels() entries): on the
+ * two-kernel route the binning kernel and the placing kernel; else the
+ * binning kernel, the radix passes and the final kernel. *total_ms is the
+ * mean time from the first kernel's start to the last one's end.
+ * Synchronises the stream.
  */
 int sph_profile_stages(const float* points, int64_t n_points, const float sph_min[3],
                        const float sph_cell[3], const int32_t bins[3], const void* table,

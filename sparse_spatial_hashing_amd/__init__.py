@@ -519,11 +519,14 @@ def sph_workspace_bytes(n_points: int, bins: Sequence[int], **opts) -> Tuple[int
 
 
 def sph_stage_names(n_points: int, bins: Sequence[int], **opts) -> Tuple[str, ...]:
-    """Names of the kernels one call launches, in order: key, pass0.., final."""
+    """Names of the kernels one call launches, in order: (lowpart, place) on the
+    two-kernel route (keys of at most 16 bits), else key, pass0.., final."""
     b = (ctypes.c_int32 * 3)(*[int(v) for v in bins])
     k = _lib.sph_num_kernels(int(n_points), b, _sph_options(**opts))
     if k < 0:
         raise VoxError(int(k), "sph_num_kernels")
+    if k == 2:
+        return ("lowpart", "place")
     return ("key",) + tuple(f"pass{q}" for q in range(k - 2)) + ("final",)
 
 
@@ -581,7 +584,7 @@ class SphericalSorter:
 
     def outputs(self):
         """(voxel_of [N], offsets [nvox+1], order [n_kept], sorted rows [n_kept, 4] or None).
-        ``self.order`` holds all N indices: the kept ones sorted, then the rest."""
+        Entries of ``self.order`` past n_kept are unspecified."""
         n = int(self.n_kept.item())
         if n < 0:
             raise VoxError(n, "sph_reorder (device status)")

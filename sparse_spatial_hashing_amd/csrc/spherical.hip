@@ -7,10 +7,17 @@
 // preprocessing step and voxel record of RadiusFPS-G). The exact binning
 // rules are stated in spherical.h.
 //
-// The sort is a least-significant-digit radix sort of (voxel id, point
-// index) pairs, so every kernel does the same work per tile whatever the
-// spread of points over voxels (a LiDAR scan puts most of its points in a few
-// near shells):
+// Grids of up to 65,536 voxels (kept keys of at most 16 bits) take two
+// kernels, k_sph_lowpart and k_sph_place (described where they are defined):
+// the binning kernel groups each tile's kept points by the key's low digit,
+// and the placing kernel reads one group of low digits across every tile in
+// input order and places the points by the high digit, so no pass over all
+// points is needed between binning and the final write.
+//
+// Larger grids, or a digit width given in the options, take a
+// least-significant-digit radix sort of (voxel id, point index) pairs, so
+// every kernel does the same work per tile whatever the spread of points
+// over voxels (a LiDAR scan puts most of its points in a few near shells):
 //   k_sph_key    bins each point, writes its voxel id (a dropped point gets
 //                the key nvox, which sorts after every voxel) and adds the
 //                block's digit counts of every pass to global histograms.
@@ -53,6 +60,13 @@ constexpr long long kSMaxTiles = 65536;
 constexpr int kSHistCopies = 16;             // global histograms, block b adds to copy b % 16
 constexpr int kSTableLds = 2048;             // boundary directions staged in LDS, at most
 constexpr int kSLookBack = 32;               // predecessor tiles read per look-back round trip
+constexpr int kSLookBackLane = 24;           // predecessors per lane in look_back_wide
+constexpr int kSWavesPart = kSBlock / kWave; // wavefronts of a binning block
+constexpr int kSMaxRuns = 4096;              // runs one k_sph_place block reads, at most
+
+constexpr int kSPlacePer = 6;                // entries per thread in a k_sph_place chunk
+constexpr int kSPairsMax = 4096;             // (low digit, high digit) counters per block, at most
+constexpr int kSMaxLowBits = 11;             // low digit of the two-kernel route, at most
 constexpr unsigned kSMagic = 0x31485053u;    // "SPH1"
 constexpr unsigned kSSpinLimit = 1u << 22;   // look-back poll bound (never reached in practice)
 constexpr unsigned kSAgg = 1u << 30;         // look-back word: flag bits 31..30, count below
@@ -436,6 +450,495 @@ __global__ __launch_bounds__(kSBlock) void k_sph_final(
     }
 }
 
+// ------------------------------------------------------ two-kernel route --
+//
+// For keys of at most 16 bits (grids of up to 65,536 voxels) the sort takes
+// two kernels. The key is split into a low digit (b0 bits) and a high digit
+// (b1 <= 8 bits); only kept points are sorted. A point's voxel is
+// (high digit << b0) | low digit, so sorted order is high digit first.
+//   k_sph_lowpart  bins the points (as k_sph_key) and partitions each tile of
+//                  256 x PER points stably by the low digit in LDS: the tile's
+//                  kept entries (and rows) go out to its staging slice grouped
+//                  by low digit, one (start, length) word per (low digit,
+//                  tile) goes to cm, and the high digits are counted into 16
+//                  copies of a global histogram.
+//   k_sph_place    one 1,024-thread block per (group of per_block low digits,
+//                  range of tiles); a group split over several ranges has one
+//                  low digit. Reading the block's runs digit by digit, tile by
+//                  tile, visits its entries in the order a stable pass by the
+//                  low digit would leave them. The block counts them per (low
+//                  digit, high digit), takes each high digit's start from the
+//                  global histogram and a look-back over the preceding blocks
+//                  (blocks ordered group-major, range-minor, which is that
+//                  same order), writes the offsets of its voxels, sorts its
+//                  entries by high digit in LDS and writes them out, each
+//                  high digit's entries to one contiguous range.
+// The last block to finish (a counter in the zero part) writes the kept
+// count and returns the histograms and the counter to zero.
+
+// Tile layout of k_sph_key; the tile index is spread so that each XCD takes
+// neighbouring tiles. LDS (dynamic): hist[4 x 2^b0], the boundary directions
+// when staged, then the tile's partitioned words [T] and rows [T] (rows only
+// when srows is set).
+template <int PER, bool LDS_TABLE>
+__global__ __launch_bounds__(kSBlock) void k_sph_lowpart(
+    const float4* __restrict__ pts, long long N, SphArgs a, const SphHeader* __restrict__ tab,
+    int b0, int b1, int* __restrict__ voxel_of, unsigned* __restrict__ cm,
+    unsigned* __restrict__ swords, float4* __restrict__ srows, unsigned* __restrict__ ghist,
+    unsigned* __restrict__ state, long long state_words, unsigned* __restrict__ err) {
+    constexpr int T = kSBlock * PER;
+    extern __shared__ __align__(16) unsigned lds[];
+    __shared__ unsigned h1[kSMaxDigits];
+    __shared__ unsigned wsum[kSWavesPart];
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
+    const long long stride = (long long)gridDim.x * kSBlock;
+    for (long long j = (long long)blockIdx.x * kSBlock + tid; j < state_words; j += stride)
+        state[j] = 0u;
+    if (blockIdx.x == 0 && tid == 0) *err = 0u;
+    if (!table_ok(tab, a)) return;   // same for every block
+    const int nb0 = 1 << b0, nb1 = 1 << b1;
+    const unsigned m0 = (unsigned)nb0 - 1u;
+    const int ndirs = a.nt + 1 + a.np + 1;
+    unsigned* hist = lds;
+    float2* stab = reinterpret_cast<float2*>(lds + kSWavesPart * nb0);   // 16-byte aligned
+    const int ndl = LDS_TABLE ? ((ndirs + 1) & ~1) : 0;                  // keeps 16-byte alignment
+    unsigned* tw = reinterpret_cast<unsigned*>(stab + ndl);
+    float4* tr = reinterpret_cast<float4*>(tw + T);
+    const float2* gtb = reinterpret_cast<const float2*>(tab + 1);
+    if (LDS_TABLE)
+        for (int j = tid; j < ndirs; j += kSBlock) stab[j] = gtb[j];
+    const float2* tb = LDS_TABLE ? stab : gtb;
+    const float2* pb = tb + (a.nt + 1);
+    for (int j = tid; j < kSWavesPart * nb0; j += kSBlock) hist[j] = 0u;
+    for (int j = tid; j < nb1; j += kSBlock) h1[j] = 0u;
+    const long long ntiles = a.ntiles;
+    const long long tile = xcd_tile(blockIdx.x, ntiles);
+    const long long base = tile * T;
+    const long long wbase = base + (long long)w * kWave * PER;
+    float4 p[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const long long i = wbase + k * kWave + lane;
+        p[k] = i < N ? pts[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();   // hist, h1 cleared; directions staged
+    int vox[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const long long i = wbase + k * kWave + lane;
+        int v = -1;
+        if (i < N) {
+            v = sph_voxel(p[k], a, tab, tb, pb);
+            voxel_of[i] = v;
+            if (v >= 0) atomicAdd(&h1[(unsigned)v >> b0], 1u);
+        }
+        vox[k] = v;
+    }
+    // stable rank inside (wavefront, low digit): earlier k first, then lower lanes
+    unsigned* hw = hist + w * nb0;
+    unsigned rk[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const bool ok = vox[k] >= 0;
+        const unsigned d0 = ok ? ((unsigned)vox[k] & m0) : 0u;
+        const unsigned long long peers = match_mask(d0, ok, b0);
+        rk[k] = ok ? hw[d0] + (unsigned)__popcll(peers & lanes_below(lane)) : 0u;
+        if (ok && (peers & lanes_above(lane)) == 0ull) hw[d0] += (unsigned)__popcll(peers);
+    }
+    __syncthreads();
+    // digit-major offsets: each thread owns bpt consecutive low digits
+    const int bpt = (nb0 + kSBlock - 1) / kSBlock;
+    const int d0s = tid * bpt;
+    unsigned mine = 0;
+    for (int j = 0; j < bpt; ++j) {
+        const int d = d0s + j;
+        if (d < nb0)
+            for (int ww = 0; ww < kSWavesPart; ++ww) mine += hist[ww * nb0 + d];
+    }
+    unsigned kept;
+    unsigned run = block_excl_scan<kSWavesPart>(mine, wsum, &kept);
+    for (int j = 0; j < bpt; ++j) {
+        const int d = d0s + j;
+        if (d >= nb0) break;
+        const unsigned start = run;
+        for (int ww = 0; ww < kSWavesPart; ++ww) {
+            const unsigned c = hist[ww * nb0 + d];
+            hist[ww * nb0 + d] = run;
+            run += c;
+        }
+        cm[(long long)d * ntiles + tile] = start | ((run - start) << 16);
+    }
+    __syncthreads();
+    // the tile in low-digit order in LDS, then written out contiguously
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (vox[k] < 0) continue;
+        const unsigned v = (unsigned)vox[k];
+        const unsigned pos = hw[v & m0] + rk[k];
+        tw[pos] = ((v >> b0) << 16) | (unsigned)(w * kWave * PER + k * kWave + lane);
+        if (srows) tr[pos] = p[k];
+    }
+    __syncthreads();
+    for (int q = tid; q < (int)kept; q += kSBlock) {
+        swords[base + q] = tw[q];
+        if (srows) srows[base + q] = tr[q];
+    }
+    unsigned* gcopy = ghist + (blockIdx.x % kSHistCopies) * nb1;
+    for (int j = tid; j < nb1; j += kSBlock)
+        if (h1[j]) atomicAdd(&gcopy[j], h1[j]);
+}
+
+// Stable rank of a chunk's entries by high digit (word >> 16): entry (w, k,
+// lane) comes after the chunk's earlier entries in wavefront w (lower k, then
+// lower lanes); hist[w * nb1 + d] gets wavefront w's count of digit d.
+template <int E>
+__device__ __forceinline__ void rank_high(const unsigned (&word)[E], const bool (&ok)[E],
+                                          unsigned (&rk)[E], unsigned* hist, int w, int lane,
+                                          int b1) {
+    unsigned* hw = hist + w * (1 << b1);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const unsigned d = word[k] >> 16;
+        const unsigned long long peers = match_mask(d, ok[k], b1);
+        rk[k] = ok[k] ? hw[d] + (unsigned)__popcll(peers & lanes_below(lane)) : 0u;
+        if (ok[k] && (peers & lanes_above(lane)) == 0ull) hw[d] += (unsigned)__popcll(peers);
+    }
+}
+
+// Entries e0 + 64 k (k < E) of the block's run list. The run of entry e is
+// the largest r < R with runpref[r] <= e, found by binary searches of fixed
+// depth (top = the largest power of two <= R), the E searches side by side;
+// rpos[r] is the run's first staging position. word[k] = (high digit << 16)
+// | low digit within the block, idx[k] = point index, pos[k] = staging
+// position, ok[k] = e < total. An entry past the total reads entry 0 (the
+// caller ensures total > 0), so every load is unconditional.
+template <int E>
+__device__ __forceinline__ void load_chunk(const unsigned* __restrict__ swords,
+                                           const unsigned* runpref, const unsigned* rpos, int R,
+                                           int top, int nt, int lgT, unsigned total, unsigned e0,
+                                           unsigned (&word)[E], unsigned (&idx)[E],
+                                           unsigned (&pos)[E], bool (&ok)[E]) {
+    unsigned e[E];
+    int r[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        e[k] = e0 + k * kWave;
+        ok[k] = e[k] < total;
+        if (!ok[k]) e[k] = 0u;
+        r[k] = 0;
+    }
+    for (int step = top; step > 0; step >>= 1)
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const int c = r[k] + step;
+            const unsigned pv = runpref[c < R ? c : R];
+            r[k] = (c < R && pv <= e[k]) ? c : r[k];
+        }
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        pos[k] = rpos[r[k]] + (e[k] - runpref[r[k]]);
+        word[k] = swords[pos[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        idx[k] = ((pos[k] >> lgT) << lgT) | (word[k] & 0xffffu);
+        word[k] = (word[k] & 0xffff0000u) | (unsigned)(r[k] / nt);
+    }
+}
+
+// Global count of high digit d: the sum of the 16 histogram copies.
+__device__ __forceinline__ unsigned gd_of(const unsigned* __restrict__ ghist, int nb1, int d) {
+    unsigned g = 0;
+#pragma unroll
+    for (int c = 0; c < kSHistCopies; ++c) g += ghist[c * nb1 + d];
+    return g;
+}
+
+// Decoupled look-back over the preceding blocks' words of one digit,
+// state[b' * nb1 + d] = flag | count, by the S lanes (a power of two, at most
+// a wavefront, aligned) that serve the digit: lane s of the group reads
+// predecessors hi - s W - j (j < W), so one round trip covers S W blocks,
+// nearest first. The counts are added up to the nearest inclusive prefix; at
+// a block that has not published, the words before it are kept and it is
+// polled again. Returns the sum of the counts of blocks before b (the same
+// in every lane of the group). Every lane of the wavefront calls this;
+// `idle` lanes (their group has nothing to do) return 0. A poll limit that
+// runs out sets *err.
+__device__ __forceinline__ unsigned look_back_wide(const unsigned* state, int nb1, int b, int d,
+                                                   int S, bool idle, int lane, unsigned* err) {
+    constexpr int W = kSLookBackLane;
+    const int gbase = lane & ~(S - 1);
+    const int s = lane - gbase;
+    const unsigned long long gmask = S == kWave ? ~0ull : ((1ull << S) - 1ull) << gbase;
+    int hi = b - 1;
+    unsigned excl = 0, polls = 0;
+    bool fin = idle;
+    while (__ballot(!fin) != 0ull) {
+        unsigned v[W];
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int pb = hi - s * W - j;
+            v[j] = (!fin && pb >= 0) ? load_relaxed32(&state[(long long)pb * nb1 + d]) : kSIncl;
+        }
+        // this lane's part: counts before its first unpublished or inclusive
+        // word, plus that inclusive word's count
+        int stop = W;
+        bool incl = false;
+        unsigned part = 0;
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            if (stop != W) continue;
+            const unsigned flag = v[j] & ~kSValue;
+            if (flag == 0u) {
+                stop = j;
+            } else {
+                part += v[j] & kSValue;
+                if (flag == kSIncl) {
+                    stop = j;
+                    incl = true;
+                }
+            }
+        }
+        const unsigned long long sm = __ballot(stop != W) & gmask;
+        const int first = sm ? __builtin_ctzll(sm) - gbase : S;
+        const int src = gbase + (first < S ? first : 0);
+        const int stop_j = __shfl(stop, src);
+        const bool stop_incl = __shfl((int)incl, src) != 0;
+        unsigned tot = s <= first ? part : 0u;
+        for (int off = S >> 1; off > 0; off >>= 1) tot += (unsigned)__shfl_xor((int)tot, off);
+        if (!fin) {
+            excl += tot;
+            if (first == S) {
+                hi -= S * W;
+            } else if (stop_incl) {
+                fin = true;
+            } else {
+                hi -= first * W + stop_j;
+                if (++polls > kSSpinLimit) {
+                    *err = 1u;
+                    fin = true;
+                } else {
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+        }
+    }
+    return idle ? 0u : excl;
+}
+
+// Block b = (group g = b / nsplit of per_block low digits, tile range
+// s = b % nsplit of tps tiles); nsplit > 1 only with per_block = 1.
+// LDS (dynamic): runpref[R + 1], rpos[R] (R = per_block x the range's tiles),
+// cnt2[per_block x nb1], hist[16 x nb1], running[nb1], base[nb1].
+// Entries are taken in chunks of CH = 1,024 x kSPlacePer; entry e of a chunk
+// is held by wavefront e / (64 E), register (e / 64) % E, lane e % 64. The
+// first chunk (nearly always the only one) is loaded before the look-back,
+// and its rows are in flight during it.
+__global__ __launch_bounds__(kSPassBlock) void k_sph_place(
+    long long N, SphArgs a, const SphHeader* __restrict__ tab, int b0, int b1, int per_block,
+    int nsplit, int tps, const unsigned* __restrict__ cm, const unsigned* __restrict__ swords,
+    const float4* __restrict__ srows, unsigned* __restrict__ ghist, unsigned* __restrict__ state,
+    unsigned* __restrict__ done, int* __restrict__ offsets, int* __restrict__ order,
+    float4* __restrict__ sorted, int* __restrict__ n_kept) {
+    constexpr int NW = kSPassWaves;
+    constexpr int E = kSPlacePer;
+    constexpr int CH = kSPassBlock * E;
+    constexpr int RPT = kSMaxRuns / kSPassBlock;
+    extern __shared__ __align__(16) unsigned lds[];
+    __shared__ unsigned wsum[NW];
+    __shared__ unsigned gsum_sh, blk_err;
+    __shared__ bool last_sh, failed_sh;
+    const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
+    const int b = blockIdx.x;
+    if (!table_ok(tab, a)) {
+        if (b == 0 && tid == 0) *n_kept = SPH_STATUS_BAD_TABLE;
+        return;
+    }
+    if (tid == 0) blk_err = 0u;
+    const int ntiles = a.ntiles, T = a.tile;
+    const int lgT = __builtin_ctz((unsigned)T);
+    const int nb1 = 1 << b1;
+    const int g = b / nsplit, sp = b - g * nsplit;
+    const int t0 = sp * tps;
+    const int t1 = t0 + tps < ntiles ? t0 + tps : ntiles;
+    const int nt = t1 > t0 ? t1 - t0 : 0;
+    const int R = per_block * nt;
+    unsigned* runpref = lds;
+    unsigned* rpos = runpref + (R + 1);
+    unsigned* cnt2 = rpos + R;
+    unsigned* hist = cnt2 + per_block * nb1;
+    unsigned* running = hist + NW * nb1;
+    unsigned* basev = running + nb1;
+    for (int j = tid; j < (per_block + NW + 1) * nb1; j += kSPassBlock) cnt2[j] = 0u;
+    // lanes [S d1, S d1 + S) serve high digit d1 in the look-back (S = 1,024 /
+    // nb1, at most a wavefront); the group's first lane loads the digit's
+    // global count now
+    const int S = nb1 >= 16 ? kSPassBlock / nb1 : kWave;
+    const int d1 = tid / S;
+    const bool lead = d1 < nb1 && (tid & (S - 1)) == 0;
+    const unsigned gd = lead ? gd_of(ghist, nb1, d1) : 0u;
+
+    // the block's runs, low digit by low digit, tile by tile (cm is
+    // digit-major); thread t holds runs [t rpt, t rpt + rpt)
+    const int rpt = (R + kSPassBlock - 1) / kSPassBlock;
+    unsigned cw[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int r = tid * rpt + q;
+        const int rr = r < R ? r : (R > 0 ? R - 1 : 0);
+        const int j = nt > 0 ? rr / nt : 0;
+        cw[q] = R > 0 ? cm[(long long)(g * per_block + j) * ntiles + t0 + (rr - j * nt)] : 0u;
+    }
+    unsigned mine = 0;
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int r = tid * rpt + q;
+        if (q < rpt && r < R) {
+            const int j = r / nt;
+            rpos[r] = (unsigned)((t0 + (r - j * nt)) * T) + (cw[q] & 0xffffu);
+            mine += cw[q] >> 16;
+        }
+    }
+    unsigned total;
+    unsigned run = block_excl_scan<NW>(mine, wsum, &total);
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int r = tid * rpt + q;
+        if (q < rpt && r < R) {
+            runpref[r] = run;
+            run += cw[q] >> 16;
+        }
+    }
+    if (tid == 0) runpref[R] = total;
+    __syncthreads();
+
+    // first chunk: words and rows in registers; counts of every chunk
+    int top = 1;
+    while (top * 2 <= R) top *= 2;
+    const unsigned ebase = (unsigned)(w * kWave * E + lane);
+    unsigned word[E], rk[E], idx[E], spos[E];
+    bool ok[E];
+    float4 row[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        word[k] = idx[k] = spos[k] = rk[k] = 0u;
+        ok[k] = false;
+        row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (total > 0) {   // uniform
+        load_chunk<E>(swords, runpref, rpos, R, top, nt, lgT, total, ebase, word, idx, spos, ok);
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if (ok[k]) atomicAdd(&cnt2[(word[k] & 0xffffu) * nb1 + (word[k] >> 16)], 1u);
+    }
+    for (unsigned c0 = CH; c0 < total; c0 += CH) {   // later chunks: counts only
+        unsigned wd[E], ix[E], ps[E];
+        bool okk[E];
+        load_chunk<E>(swords, runpref, rpos, R, top, nt, lgT, total, c0 + ebase, wd, ix, ps, okk);
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if (okk[k]) atomicAdd(&cnt2[(wd[k] & 0xffffu) * nb1 + (wd[k] >> 16)], 1u);
+    }
+    rank_high<E>(word, ok, rk, hist, w, lane, b1);
+    // rows last, so no wait for a word or a count waits for them
+    if (total > 0 && sorted)
+#pragma unroll
+        for (int k = 0; k < E; ++k) row[k] = srows[spos[k]];
+    __syncthreads();
+
+    // the digit's count in this block, publication, look-back, global start
+    unsigned c = 0;
+    if (d1 < nb1) {
+        for (int j = 0; j < per_block; ++j) c += cnt2[j * nb1 + d1];
+        if (lead) store_relaxed32(&state[(long long)b * nb1 + d1], (b == 0 ? kSIncl : kSAgg) | c);
+    }
+    unsigned gall;
+    const unsigned g0 = block_excl_scan<NW>(gd, wsum, &gall);
+    const unsigned excl = look_back_wide(state, nb1, b, d1 < nb1 ? d1 : 0, S, d1 >= nb1 || b == 0,
+                                         lane, &blk_err);
+    if (lead) {
+        if (b > 0) store_relaxed32(&state[(long long)b * nb1 + d1], kSIncl | (excl + c));
+        basev[d1] = g0 + excl;
+    }
+    if (tid == 0) gsum_sh = gall;
+
+    // offsets of the group's voxels, by the block holding the first tiles:
+    // (high digit, low digit) -> the start of the high digit's run plus this
+    // block's earlier low digits of it
+    const long long nvox = a.nvox;
+    __syncthreads();
+    if (sp == 0 && tid < nb1) {
+        unsigned at = basev[tid];
+        for (int j = 0; j < per_block; ++j) {
+            const long long v = ((long long)tid << b0) | ((long long)g * per_block + j);
+            if (v < nvox) offsets[v] = (int)at;
+            at += cnt2[j * nb1 + tid];
+        }
+    }
+
+    // chunks: per-wavefront starts of each digit, then every entry stored
+    // after the block's earlier entries of its digit
+    for (unsigned c0 = 0; c0 < total; c0 += CH) {   // uniform: total is the block's
+        if (c0 > 0) {
+            __syncthreads();   // the previous chunk's hist reads and resets are done
+            load_chunk<E>(swords, runpref, rpos, R, top, nt, lgT, total, c0 + ebase, word, idx, spos,
+                          ok);
+            rank_high<E>(word, ok, rk, hist, w, lane, b1);
+            if (sorted)
+#pragma unroll
+                for (int k = 0; k < E; ++k) row[k] = srows[spos[k]];
+            __syncthreads();
+        }
+        unsigned chunk_n = 0;
+        if (tid < nb1)
+            for (int ww = 0; ww < NW; ++ww) {
+                const unsigned x = hist[ww * nb1 + tid];
+                hist[ww * nb1 + tid] = chunk_n;
+                chunk_n += x;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            if (!ok[k]) continue;
+            const unsigned d = word[k] >> 16;
+            const unsigned pos = basev[d] + running[d] + hist[w * nb1 + d] + rk[k];
+            if (pos < gsum_sh && idx[k] < N) {   // always, unless the workspace was disturbed
+                order[pos] = (int)idx[k];
+                if (sorted) sorted[pos] = row[k];
+            } else {
+                blk_err = 1u;
+            }
+        }
+        __syncthreads();
+        if (tid < nb1) {
+            running[tid] += chunk_n;
+            for (int ww = 0; ww < NW; ++ww) hist[ww * nb1 + tid] = 0u;
+        }
+    }
+
+    // the last block: kept count, status, and the zero part back to zero.
+    // The counter's low 16 bits count finished blocks, the bits above count
+    // blocks that met an error, so it carries everything the last block
+    // needs; every block has read the histograms before it counts itself.
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned mine_done = 1u + (blk_err ? 0x10000u : 0u);
+        const unsigned prev =
+            __hip_atomic_fetch_add(done, mine_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_sh = (prev & 0xffffu) + 1u == gridDim.x;
+        failed_sh = (prev >> 16) != 0u || blk_err != 0u;
+    }
+    __syncthreads();
+    if (!last_sh) return;
+    for (int j = tid; j < kSHistCopies * nb1; j += kSPassBlock) ghist[j] = 0u;
+    if (tid == 0) {
+        const int kept = (int)gsum_sh;
+        offsets[nvox] = kept;
+        *n_kept = failed_sh ? VOX_STATUS_DEVICE_ERROR : kept;
+        *done = 0u;
+    }
+}
+
 // ------------------------------------------------------------------- host --
 
 inline long long s_cdiv(long long a, long long b) { return (a + b - 1) / b; }
@@ -448,6 +951,11 @@ struct SPlan {
     size_t off_hist, zero_bytes, off_state, off_k0, off_v0, off_k1, off_v1, bytes;
     long long state_words;
     int final_blocks;
+    // two-kernel route (fused = true): low digit b0 bits, high digit b1 bits,
+    // pblocks k_sph_place blocks of pk low digits each
+    bool fused;
+    int b0, b1, pk, nsplit, tps, pblocks;
+    size_t off_cm, off_stage, off_rows, place_lds;
 };
 
 bool bins_ok(const int32_t bins[3]) {
@@ -462,6 +970,72 @@ bool params_ok(const float mn[3], const float cell[3]) {
     if (!mn || !cell) return false;
     for (int d = 0; d < 3; ++d)
         if (!isfinite(mn[d]) || !isfinite(cell[d]) || !(cell[d] > 0.0f)) return false;
+    return true;
+}
+
+// The two-kernel route, when the kept keys [0, nvox) fit 16 bits; false
+// leaves the radix passes to make_splan. At least 2,048 entries per
+// k_sph_place block, at most 256 blocks up to 2^20 points; the high digit
+// takes up to 8 bits, fewer
+// when two look-back round trips (1,024 x kSLookBackLane block words each)
+// would not reach back over every block; a group of low digits is split over
+// tile ranges when there are fewer groups than blocks.
+bool plan_fused(long long N, SPlan* p) {
+    int kb = 0;
+    while ((1ll << kb) < p->nvox) ++kb;
+    if (kb > 16) return false;
+    // every block resident at once (one 1,024-thread block a CU): N / 256 a
+    // block, at least 2,048
+    const long long per_block_target = N / 256 > 2048 ? (N + 255) / 256 : 2048;
+    int lgb = 0;
+    while ((per_block_target << lgb) < N) ++lgb;
+    int b1 = kb < kSMaxDigitBits ? kb : kSMaxDigitBits;
+    while (b1 > 0 && ((1ll << lgb) << b1) > 2ll * kSPassBlock * kSLookBackLane &&
+           kb - (b1 - 1) <= kSMaxLowBits)
+        --b1;
+    const int b0 = kb - b1;
+    if (b0 > kSMaxLowBits) return false;
+    const long long nb0 = 1ll << b0;
+    long long pk = 1, nsplit = 1;
+    if ((1ll << lgb) <= nb0)
+        pk = nb0 >> lgb;
+    else
+        nsplit = (1ll << lgb) / nb0;
+    if (nsplit > p->ntiles) nsplit = p->ntiles;
+    while ((pk << b1) > kSPairsMax) pk >>= 1;
+    long long tps = (p->ntiles + nsplit - 1) / nsplit;
+    while (pk * tps > kSMaxRuns) {
+        if (pk > 1) {
+            pk >>= 1;
+        } else {
+            nsplit *= 2;
+            tps = (p->ntiles + nsplit - 1) / nsplit;
+        }
+    }
+    nsplit = (p->ntiles + tps - 1) / tps;   // no empty range
+    if ((nb0 / pk) * nsplit > 0xffff) return false;   // the block counter's width
+    p->fused = true;
+    p->b0 = b0;
+    p->b1 = b1;
+    p->pk = (int)pk;
+    p->nsplit = (int)nsplit;
+    p->tps = (int)tps;
+    p->pblocks = (int)((nb0 / pk) * nsplit);
+    const long long R = pk * tps;
+    const long long nb1 = 1ll << b1;
+    p->place_lds = (size_t)(4 * ((2 * R + 1) + (pk + kSPassWaves + 2) * nb1));
+    p->state_words = (long long)p->pblocks * nb1;
+    p->off_hist = 0;
+    p->zero_bytes =   // the high-digit histogram copies, the error word, the block counter
+        s_align256(sizeof(unsigned) * ((size_t)kSHistCopies * nb1 + 2));
+    p->off_state = p->zero_bytes;
+    p->off_cm = s_align256(p->off_state + sizeof(unsigned) * (size_t)p->state_words);
+    p->off_stage = s_align256(p->off_cm + sizeof(unsigned) * ((size_t)p->ntiles << b0));
+    p->off_rows = s_align256(p->off_stage + sizeof(unsigned) * (size_t)p->ntiles * p->tile);
+    p->bytes = s_align256(p->off_rows + sizeof(float4) * (size_t)p->ntiles * p->tile);
+    p->dg.passes = 0;
+    p->dg.hist_words = (int)nb1;
+    p->final_blocks = 0;
     return true;
 }
 
@@ -485,6 +1059,8 @@ int make_splan(long long N, const int32_t bins[3], const sph_options* opt, SPlan
     p->sort_tiles = (int)(N > 0 ? s_cdiv(N, p->sort_tile) : 1);
     const int db_opt = opt ? opt->digit_bits : 0;
     if (db_opt < 0 || db_opt > kSMaxDigitBits) return VOX_EINVAL;
+    p->fused = false;
+    if (db_opt == 0 && plan_fused(N, p)) return VOX_OK;
     // keys run over [0, nvox] (nvox = a dropped point)
     int key_bits = 1;
     while ((1ll << key_bits) <= p->nvox) ++key_bits;
@@ -603,10 +1179,66 @@ void launch_key(const float4* pts, long long N, const SphArgs& a, const SphHeade
                               e0, e1, 0, pts, N, a, tab, dg, voxel_of, gh, state, state_words, err);
 }
 
+template <int PER>
+void launch_lowpart(const float4* pts, long long N, const SphArgs& a, const SphHeader* tab,
+                    const SPlan& p, int* voxel_of, unsigned* cm, unsigned* swords, float4* srows,
+                    unsigned* gh, unsigned* state, unsigned* err, hipStream_t st, hipEvent_t e0,
+                    hipEvent_t e1) {
+    const int ndirs = a.nt + 1 + a.np + 1;
+    const bool lt = ndirs <= kSTableLds;
+    const unsigned lds = (unsigned)(sizeof(unsigned) * kSWavesPart << p.b0) +
+                         (lt ? (unsigned)sizeof(float2) * ((ndirs + 1) & ~1) : 0u) +
+                         (unsigned)(sizeof(unsigned) + (srows ? sizeof(float4) : 0)) * p.tile;
+    if (lt)
+        hipExtLaunchKernelGGL(k_sph_lowpart<PER, true>, dim3((unsigned)a.ntiles), dim3(kSBlock), lds,
+                              st, e0, e1, 0, pts, N, a, tab, p.b0, p.b1, voxel_of, cm, swords, srows,
+                              gh, state, p.state_words, err);
+    else
+        hipExtLaunchKernelGGL(k_sph_lowpart<PER, false>, dim3((unsigned)a.ntiles), dim3(kSBlock),
+                              lds, st, e0, e1, 0, pts, N, a, tab, p.b0, p.b1, voxel_of, cm, swords,
+                              srows, gh, state, p.state_words, err);
+}
+
+int run_fused(const float* points, long long N, const SphArgs& a, const SPlan& p,
+              const void* table, int32_t* voxel_of, int32_t* offsets, int32_t* order,
+              float* sorted, int32_t* n_kept, void* ws, hipStream_t st, hipEvent_t* ev) {
+    char* w = static_cast<char*>(ws);
+    unsigned* gh = reinterpret_cast<unsigned*>(w + p.off_hist);
+    unsigned* err = gh + kSHistCopies * (1 << p.b1);
+    unsigned* done = err + 1;
+    unsigned* state = reinterpret_cast<unsigned*>(w + p.off_state);
+    unsigned* cm = reinterpret_cast<unsigned*>(w + p.off_cm);
+    unsigned* swords = reinterpret_cast<unsigned*>(w + p.off_stage);
+    float4* srows = sorted ? reinterpret_cast<float4*>(w + p.off_rows) : nullptr;
+    const float4* pts = reinterpret_cast<const float4*>(points);
+    const SphHeader* tab = static_cast<const SphHeader*>(table);
+    hipEvent_t e[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (ev)
+        for (int k = 0; k < 4; ++k) e[k] = ev[k];
+    switch (p.per) {
+        case 1: launch_lowpart<1>(pts, N, a, tab, p, voxel_of, cm, swords, srows, gh, state, err, st, e[0], e[1]); break;
+        case 2: launch_lowpart<2>(pts, N, a, tab, p, voxel_of, cm, swords, srows, gh, state, err, st, e[0], e[1]); break;
+        case 4: launch_lowpart<4>(pts, N, a, tab, p, voxel_of, cm, swords, srows, gh, state, err, st, e[0], e[1]); break;
+        default: launch_lowpart<8>(pts, N, a, tab, p, voxel_of, cm, swords, srows, gh, state, err, st, e[0], e[1]); break;
+    }
+    int rc = s_last_launch();
+    if (rc != VOX_OK) return rc;
+    hipExtLaunchKernelGGL(k_sph_place, dim3((unsigned)p.pblocks), dim3(kSPassBlock),
+                          (unsigned)p.place_lds, st, e[2], e[3], 0, N, a, tab, p.b0, p.b1, p.pk,
+                          p.nsplit, p.tps, cm, swords, srows, gh, state, done, offsets, order,
+                          reinterpret_cast<float4*>(sorted), n_kept);
+    return s_last_launch();
+}
+
+int num_kernels(const SPlan& p) { return p.fused ? 2 : p.dg.passes + 2; }
+
 // ev (optional): a start and a stop event per kernel, passes + 2 kernels.
 int run_sph(const float* points, long long N, const SphArgs& a, const SPlan& p, const void* table,
             int32_t* voxel_of, int32_t* offsets, int32_t* order, float* sorted, int32_t* n_kept,
             void* ws, hipStream_t st, hipEvent_t* ev) {
+    if (p.fused)
+        return run_fused(points, N, a, p, table, voxel_of, offsets, order, sorted, n_kept, ws, st,
+                         ev);
     char* w = static_cast<char*>(ws);
     unsigned* gh = reinterpret_cast<unsigned*>(w + p.off_hist);
     unsigned* err = gh + kSHistCopies * p.dg.hist_words;
@@ -700,7 +1332,7 @@ int64_t sph_workspace_zero_bytes(int64_t n_points, const int32_t bins[3],
 int32_t sph_num_kernels(int64_t n_points, const int32_t bins[3], const sph_options* options) {
     SPlan p;
     const int rc = make_splan(n_points, bins, options, &p);
-    return rc == VOX_OK ? p.dg.passes + 2 : rc;
+    return rc == VOX_OK ? num_kernels(p) : rc;
 }
 
 int sph_reorder(const float* points, int64_t n_points, const float sph_min[3],
@@ -729,7 +1361,7 @@ int sph_profile_stages(const float* points, int64_t n_points, const float sph_mi
                         order, sorted, n_kept, workspace, workspace_bytes, options, &p);
     if (rc != VOX_OK) return rc;
     const SphArgs a = make_args(sph_min, sph_cell, bins, p);
-    const int nk = p.dg.passes + 2;
+    const int nk = num_kernels(p);
     const int nev = 2 * nk;
     hipEvent_t* ev = new hipEvent_t[(size_t)iters * nev];
     int created = 0;

@@ -2,8 +2,11 @@
 CPU oracle, through the C ABI (sph_reorder via the binding).
 
 Everything is integer work decided by exact comparisons, so the bar is bit
-equality: voxel_of, offsets and order equal the oracle's, and the sorted rows
-are bit copies of points[order]. Inputs come from the seeded generators only.
+equality: voxel_of, offsets and the first n_kept entries of order equal the
+oracle's, and the sorted rows are bit copies of points[order]. Inputs come
+from the seeded generators only. Grids of up to 65,536 voxels take the
+two-kernel route by default and the radix passes when a digit width is given;
+both are run.
 """
 import ctypes
 import math
@@ -33,13 +36,6 @@ def say(msg):
     sys.stdout.flush()
 
 
-_last = {}
-
-
-def last_sorter_order():
-    return _last["order"]
-
-
 def gpu_sph(pts, sph_min, sph_cell, bins, sorted_rows=True, **kw):
     say(f"  gpu spherical N={pts.shape[0]} bins={tuple(bins)} {kw}")
     t = torch.from_numpy(np.ascontiguousarray(pts, dtype=F32)).to(DEV)
@@ -48,7 +44,6 @@ def gpu_sph(pts, sph_min, sph_cell, bins, sorted_rows=True, **kw):
     s.run(t)
     v, off, order, rows = s.outputs()
     torch.cuda.synchronize()
-    _last["order"] = s.order[:t.shape[0]].cpu().numpy()
     return (v.cpu().numpy(), off.cpu().numpy(), order.cpu().numpy(),
             None if rows is None else rows.cpu().numpy())
 
@@ -56,9 +51,6 @@ def gpu_sph(pts, sph_min, sph_cell, bins, sorted_rows=True, **kw):
 def check(pts, sph_min, sph_cell, bins, what, **kw):
     want = oracle.spherical(pts, sph_min, sph_cell, bins)
     got = gpu_sph(pts, sph_min, sph_cell, bins, **kw)
-    full = last_sorter_order()
-    dropped = np.flatnonzero(want[0] < 0)
-    assert np.array_equal(full[want[2].size:], dropped), f"{what}: dropped points not last"
     assert np.array_equal(got[0], want[0]), f"{what}: voxel_of differs"
     assert np.array_equal(got[1], want[1]), f"{what}: offsets differ"
     assert np.array_equal(got[2], want[2]), f"{what}: order differs"
@@ -68,12 +60,13 @@ def check(pts, sph_min, sph_cell, bins, what, **kw):
     return got
 
 
+@pytest.mark.parametrize("digit_bits", [0, 8])
 @pytest.mark.parametrize("name", sph_config_names())
-def test_parity_workloads(name):
+def test_parity_workloads(name, digit_bits):
     p = get_sph_config(name).params
     pts, _ = generate(name)
-    say(f"spherical parity {name}")
-    check(pts, p.sph_min, p.sph_cell, p.bins, name)
+    say(f"spherical parity {name} digit_bits={digit_bits}")
+    check(pts, p.sph_min, p.sph_cell, p.bins, name, digit_bits=digit_bits)
 
 
 @pytest.mark.parametrize("seed", [3, 4])
@@ -103,10 +96,11 @@ def test_parity_ball_coarse_and_fine_grids():
 
 
 @pytest.mark.parametrize("per,sort_tile", [(1, 1024), (2, 2048), (4, 4096), (8, 1024)])
-@pytest.mark.parametrize("digit_bits", [8, 5, 3, 1])
+@pytest.mark.parametrize("digit_bits", [0, 8, 5, 3, 1])
 def test_parity_launch_options(per, sort_tile, digit_bits):
-    """Every tile size and digit width (2 to 15 passes) gives the same result,
-    with a ragged last tile (N not a multiple of any tile)."""
+    """Every tile size, the two-kernel route (digit_bits 0) and every digit
+    width (2 to 15 radix passes) give the same result, with a ragged last tile
+    (N not a multiple of any tile)."""
     p = get_sph_config("lidar_scan_64k").params
     pts, _ = generate("lidar_scan_64k", n=70001)
     say(f"spherical options per={per} sort_tile={sort_tile} digit_bits={digit_bits}")
@@ -114,10 +108,22 @@ def test_parity_launch_options(per, sort_tile, digit_bits):
           points_per_thread=per, sort_tile=sort_tile, digit_bits=digit_bits)
 
 
-def test_single_voxel_grid():
-    """bins (1, 1, 1): a one-bit key (kept or not), one pass."""
+@pytest.mark.parametrize("digit_bits", [0, 8])
+def test_single_voxel_grid(digit_bits):
+    """bins (1, 1, 1): a zero-bit key on the two-kernel route; on the radix
+    route a one-bit key (kept or not), one pass."""
     pts = _ball(30000, 6, rmax=2.0)
-    check(pts, (0.5, -PI / 2, -PI), (1.0, PI, 2 * PI), (1, 1, 1), "one voxel grid")
+    check(pts, (0.5, -PI / 2, -PI), (1.0, PI, 2 * PI), (1, 1, 1), "one voxel grid",
+          digit_bits=digit_bits)
+
+
+@pytest.mark.parametrize("bins", [(16, 64, 64), (17, 64, 64)])
+def test_sixteen_bit_grid_edge(bins):
+    """65,536 voxels (16-bit keys, the largest grid of the two-kernel route)
+    and 69,632 (the radix route) on the same 400,000-point ball."""
+    pts = _ball(400000, 13, rmax=float(bins[0]) * 0.3)
+    say(f"spherical 16-bit edge bins={bins}")
+    check(pts, (0.1, -PI / 2, -PI), (0.3, PI / 64, PI / 32), bins, f"bins {bins}")
 
 
 def test_hand_points_and_boundaries():
@@ -154,6 +160,21 @@ def test_one_voxel_holds_everything():
     pts[:, 2] = rng.uniform(0.01, 0.02, n).astype(F32)
     got = check(pts, *SMALL, "one voxel")
     assert np.count_nonzero(np.diff(got[1])) == 1
+
+
+def test_one_voxel_holds_a_block_many_times_over():
+    """40,000 points in one voxel of a 65,536-voxel grid (plus 200 anywhere):
+    one placing block takes ten chunks of entries and the other blocks nearly
+    none."""
+    rng = np.random.default_rng(2)
+    n = 40000
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = rng.uniform(1.1, 1.9, n).astype(F32)
+    pts[:, 1] = rng.uniform(0.01, 0.02, n).astype(F32)
+    pts[:, 2] = rng.uniform(0.01, 0.02, n).astype(F32)
+    pts[:200, :3] = rng.uniform(-3, 3, (200, 3)).astype(F32)
+    pts[:, 3] = np.arange(n, dtype=F32)
+    check(pts, (0.1, -PI / 2, -PI), (0.3, PI / 64, PI / 32), (16, 64, 64), "one voxel, 16-bit grid")
 
 
 def test_sorted_rows_optional():
@@ -217,8 +238,12 @@ def test_profile_stages_runs():
     s = vox.SphericalSorter(pts.shape[0], p.sph_min, p.sph_cell, p.bins, device=DEV)
     t = torch.from_numpy(pts).to(DEV)
     stages, total = s.profile(t, 5)
-    assert list(stages) == ["key", "pass0", "pass1", "final"]
+    assert list(stages) == ["lowpart", "place"]
     assert all(v > 0 for v in stages.values())
     assert total >= max(stages.values())
     want = oracle.spherical(pts, p.sph_min, p.sph_cell, p.bins)
     assert np.array_equal(s.outputs()[2].cpu().numpy(), want[2])
+    r = vox.SphericalSorter(pts.shape[0], p.sph_min, p.sph_cell, p.bins, device=DEV, digit_bits=8)
+    stages, total = r.profile(t, 3)
+    assert list(stages) == ["key", "pass0", "pass1", "final"]
+    assert np.array_equal(r.outputs()[2].cpu().numpy(), want[2])

@@ -255,23 +255,51 @@ def test_sph_workspace_rejects(n, bins, opts):
 
 
 def test_sph_workspace_sizes():
+    # two-kernel route (20,736 voxels: 15 key bits): the staging words and rows
+    # (20 bytes a point, rounded up to whole tiles) and the (low digit, tile)
+    # run words
     a, za = vox.sph_workspace_bytes(65536, SPH_BINS)
     b, zb = vox.sph_workspace_bytes(1 << 20, SPH_BINS)
-    assert 65536 * 12 < a < 65536 * 24 and (1 << 20) * 12 < b < (1 << 20) * 16
+    assert 65536 * 20 < a < 65536 * 24 and (1 << 20) * 20 < b < (1 << 20) * 24
+    # 16 copies of the high-digit counts (8 bits at 2^16 points; 7 at 2^20,
+    # where 256 placing blocks keep the look-back short), the error word and
+    # the block counter
+    assert za == (16 * 256 * 4 + 8 + 255) // 256 * 256
+    assert zb == (16 * 128 * 4 + 8 + 255) // 256 * 256
+    # radix passes: keys, values and two ping-pong buffers
+    c, zc = vox.sph_workspace_bytes(65536, SPH_BINS, digit_bits=8)
+    assert 65536 * 12 < c < 65536 * 24
     # 15 key bits as 8 + 7: 16 copies of 256 + 128 counts, and the error word
-    assert za == zb == (16 * 384 * 4 + 4 + 255) // 256 * 256
+    assert zc == (16 * 384 * 4 + 4 + 255) // 256 * 256
     assert vox.sph_workspace_bytes(0, SPH_BINS)[0] > 0
     assert vox.sph_workspace_bytes(1 << 24, (64, 256, 256))[0] > 0
+    assert vox.sph_workspace_bytes(1 << 24, SPH_BINS)[0] > 0
 
 
 @pytest.mark.parametrize("bins,digit_bits,kernels", [
-    (SPH_BINS, 0, 4), (SPH_BINS, 8, 4), (SPH_BINS, 5, 5), (SPH_BINS, 1, 17),
-    ((1, 1, 1), 0, 3), ((64, 256, 256), 0, 5), ((64, 256, 256), 1, 25)])
+    (SPH_BINS, 0, 2), (SPH_BINS, 8, 4), (SPH_BINS, 5, 5), (SPH_BINS, 1, 17),
+    ((1, 1, 1), 0, 2), ((1, 1, 1), 8, 3), ((16, 64, 64), 0, 2), ((17, 64, 64), 0, 5),
+    ((64, 256, 256), 0, 5), ((64, 256, 256), 1, 25)])
 def test_sph_pass_count(bins, digit_bits, kernels):
-    """Keys run over [0, nvox]: 20,736 voxels need 15 bits (2 passes of 8, 3 of
-    5, 15 of 1); one voxel needs 1 bit; 2^22 voxels need 23 bits."""
+    """Grids of up to 65,536 voxels take the two-kernel route unless a digit
+    width is asked for. Radix keys run over [0, nvox]: 20,736 voxels need 15
+    bits (2 passes of 8, 3 of 5, 15 of 1); one voxel needs 1 bit; 69,632
+    voxels and 2^22 voxels need 17 and 23 bits (3 passes of 8)."""
     names = vox.sph_stage_names(1000, bins, digit_bits=digit_bits)
-    assert len(names) == kernels and names[0] == "key" and names[-1] == "final"
+    assert len(names) == kernels
+    if kernels == 2:
+        assert names == ("lowpart", "place")
+    else:
+        assert names[0] == "key" and names[-1] == "final"
+
+
+def test_sph_route_limits():
+    """The two-kernel route holds up to 2^24 points on a 16-bit grid, also with
+    one point per thread (65,536 tiles, split into ranges of 4,096 per placing
+    block); a 17-bit grid takes the radix passes."""
+    assert len(vox.sph_stage_names(1 << 24, (16, 64, 64))) == 2
+    assert len(vox.sph_stage_names(1 << 24, SPH_BINS, points_per_thread=1)) == 2
+    assert len(vox.sph_stage_names(1 << 24, (17, 64, 64))) == 5
 
 
 def test_sph_reorder_rejects_on_host():
