@@ -105,6 +105,22 @@ struct Grid {
     int gx, gy, gz;
 };
 
+// The kept-cell map: pillar id + 1 per grid cell, 0 = not kept. Entries are
+// 16-bit when every id + 1 fits (max_voxels <= 65,534), halving the footprint
+// that random lookups cover; p is null when there is no map.
+struct KMap {
+    void* p;
+    int narrow;
+    __device__ __forceinline__ unsigned get(long long key) const {
+        return narrow ? (unsigned)static_cast<const unsigned short*>(p)[key]
+                      : static_cast<const unsigned*>(p)[key];
+    }
+    __device__ __forceinline__ void put(long long key, unsigned v) const {
+        if (narrow) static_cast<unsigned short*>(p)[key] = (unsigned short)v;
+        else static_cast<unsigned*>(p)[key] = v;
+    }
+};
+
 // ---------------------------------------------------------------- binning --
 
 // "Binning a point": NaN/Inf check on x, y, z; z-slab z_min <= z < z_max;
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
                                                  unsigned long long* __restrict__ tile_state,
                                                  long long ntiles, int* __restrict__ occ_slot,
                                                  long long* __restrict__ kept_key,
-                                                 unsigned* __restrict__ kmap,
+                                                 KMap kmap,
                                                  Header* __restrict__ hdr,
                                                  int* __restrict__ num_voxels) {
     __shared__ unsigned tile_sh;
@@ -442,7 +458,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
         if (r < M) {
             table[slot[k]] = (key1[k] << kKeyShift) | kKeptFlag | (unsigned long long)r;
             kept_key[r] = (long long)(key1[k] - 1ull);
-            if (kmap) kmap[key1[k] - 1ull] = (unsigned)r + 1u;  // the kept-cell map
+            if (kmap.p) kmap.put((long long)(key1[k] - 1ull), (unsigned)r + 1u);  // the kept-cell map
             if (C > 0) {
                 // the kept cells also go into a small table that lookups past
                 // the prefix probe instead of the big one (it stays in L2)
@@ -653,7 +669,7 @@ __device__ __forceinline__ void release_workspace(long long gtid, long long nthr
                                                   unsigned long long* __restrict__ compact,
                                                   unsigned C, int* __restrict__ kept_cslot,
                                                   unsigned long long* __restrict__ tile_state,
-                                                  long long ntiles, unsigned* __restrict__ kmap,
+                                                  long long ntiles, KMap kmap,
                                                   Header* __restrict__ hdr,
                                                   int* __restrict__ num_voxels) {
     const long long kept_written = distinct < M ? distinct : M;
@@ -666,7 +682,7 @@ __device__ __forceinline__ void release_workspace(long long gtid, long long nthr
             report_error(hdr, num_voxels, 16u);
         }
         if (r >= V && r < kept_written) {
-            if (kmap) kmap[kept_key[r]] = 0u;
+            if (kmap.p) kmap.put(kept_key[r], 0u);
             kept_key[r] = 0;
             if (C > 0) clear_compact(compact, C, kept_cslot, r, hdr, num_voxels);
         }
@@ -801,7 +817,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 
     // 2) return the rest of the workspace to zero
     release_workspace(gtid, nthreads, distinct, V, M, occ_slot, table, S, kept_key, compact, C,
-                      kept_cslot, tile_state, ntiles, nullptr, hdr, num_voxels);
+                      kept_cslot, tile_state, ntiles, KMap{nullptr, 0}, hdr, num_voxels);
 }
 
 // ------------------------------------------------- partitioned select/pack --
@@ -853,7 +869,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                                                  unsigned S,
                                                  const unsigned long long* __restrict__ compact,
                                                  unsigned C, int hash, int* __restrict__ slot_of,
-                                                 const unsigned* __restrict__ kmap,
+                                                 KMap kmap,
                                                  int nbits, long long ptiles,
                                                  unsigned* __restrict__ cm,
                                                  unsigned* __restrict__ staging,
@@ -906,7 +922,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
             row[k0 + k] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (base < N && (CARRY || any_rest)) row[k0 + k] = pts[ii[k] < N ? ii[k] : N - 1];
         }
-        if (kmap && any_rest) {
+        if (kmap.p && any_rest) {
             // the kept-cell map answers every point of a tile that reaches
             // past the prefix with one 4-byte load; its prefix points only
             // return their slot_of entries to zero (tiles inside the prefix
@@ -921,7 +937,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
 #pragma unroll
                 for (int k = 0; k < PER_B; ++k) {
                     const long long key = ii[k] < N ? bin_key(row[k0 + k], g) : -1;
-                    mv[k] = key >= 0 ? kmap[key] : 0u;
+                    mv[k] = key >= 0 ? kmap.get(key) : 0u;
                 }
 #pragma unroll
                 for (int k = 0; k < PER_B; ++k)
@@ -948,7 +964,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                     if (ii[k] < P) wd[k] = w[k];
             }
         }
-        if (any_rest && !kmap) {
+        if (any_rest && !kmap.p) {
             // later points: bin, then probe the home pair, then (rarely) lines
             long long key[PER_B];
             unsigned h[PER_B];
@@ -1105,7 +1121,7 @@ void k_bins(
     int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ voxels,
     int* __restrict__ coords, int* __restrict__ num_points, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
-    unsigned long long* __restrict__ tile_state, long long ntiles, unsigned* __restrict__ kmap,
+    unsigned long long* __restrict__ tile_state, long long ntiles, KMap kmap,
     Header* __restrict__ hdr) {
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
@@ -1282,7 +1298,7 @@ void k_bins(
         num_points[pp] = (int)(running[p] < (unsigned)K ? running[p] : (unsigned)K);
         const long long key = p == t ? key_t : kept_key[pp];
         write_coords(coords, pp, key, gx, gy);
-        if (kmap) kmap[key] = 0u;
+        if (kmap.p) kmap.put(key, 0u);
         kept_key[pp] = 0;
         if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
     }
@@ -1322,7 +1338,7 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
     int* __restrict__ kept_cslot, int gx, int gy, float4* __restrict__ centroids,
     int* __restrict__ coords, int* __restrict__ counts, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
-    unsigned long long* __restrict__ tile_state, long long ntiles, unsigned* __restrict__ kmap,
+    unsigned long long* __restrict__ tile_state, long long ntiles, KMap kmap,
     Header* __restrict__ hdr) {
     extern __shared__ float4 lds_rows[];
     const int G = 1 << gshift;
@@ -1443,7 +1459,7 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
         counts[pp] = (int)n;
         const long long key = kept_key[pp];
         write_coords(coords, pp, key, gx, gy);
-        if (kmap) kmap[key] = 0u;
+        if (kmap.p) kmap.put(key, 0u);
         kept_key[pp] = 0;
         if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
     }
@@ -1692,7 +1708,7 @@ struct Buffers {
     unsigned* cm;
     unsigned* stage;
     float4* stage_pt;
-    unsigned* kmap;  // the kept-cell map, or null when the grid does not fit it
+    KMap kmap;  // the kept-cell map (p null when the grid does not fit it)
 };
 
 Buffers carve(void* ws, const Plan& pl, const Grid& g) {
@@ -1714,8 +1730,8 @@ Buffers carve(void* ws, const Plan& pl, const Grid& g) {
     x.stage_pt = reinterpret_cast<float4*>(b + pl.off_stage_pt);
     const long long cells = (long long)g.gx * g.gy * g.gz;
     // no map when the prefix holds every point: nothing would look it up
-    x.kmap = (pl.mapn > 0 && cells <= pl.mapn && pl.P < pl.N)
-                 ? reinterpret_cast<unsigned*>(b + pl.off_map) : nullptr;
+    x.kmap.p = (pl.mapn > 0 && cells <= pl.mapn && pl.P < pl.N) ? b + pl.off_map : nullptr;
+    x.kmap.narrow = pl.M <= 65534 ? 1 : 0;
     return x;
 }
 

@@ -388,6 +388,31 @@ def test_max_voxels_variants(M):
     assert_bitwise(gpu_vox(pts, prm, compact_table=1), want, f"M={M} compact")
 
 
+@pytest.mark.parametrize("M", [65534, 65535, 70000])
+def test_kept_cell_map_entry_widths(M):
+    """400,000 uniform points on the 864 x 992 grid (about 320,000 occupied
+    cells): the prefix (2 max_voxels points) leaves points to look up in the
+    kept-cell map, whose entries are 16-bit up to max_voxels = 65,534 and
+    32-bit from 65,535 (ids past 65,535 included)."""
+    cfg = get_config("dense_multisweep")
+    p = cfg.params
+    rng = np.random.default_rng(7)
+    n = 400000
+    x0, y0, z0, x1, y1, z1 = p.range_
+    pts = np.zeros((n, 4), F32)
+    pts[:, 0] = rng.uniform(x0, x1, n).astype(F32)
+    pts[:, 1] = rng.uniform(y0, y1, n).astype(F32)
+    pts[:, 2] = rng.uniform(z0, z1, n).astype(F32)
+    pts[:, 3] = rng.random(n).astype(F32)
+    prm = (p.range_, p.cell, p.grid, p.max_points, M)
+    say(f"kept-cell map widths M={M}")
+    want = oracle.voxelize_map(pts, *prm)
+    assert want[0].shape[0] == M
+    got = gpu_vox(pts, prm, point_map=True)
+    assert_bitwise(got[:3], want[:3], f"M={M}")
+    assert np.array_equal(got[3], want[3]), f"M={M}: point map differs"
+
+
 def test_single_cell_heavy_pillar():
     """Every point in one cell: one pillar keeps the 32 lowest of 100,000."""
     rng = np.random.default_rng(5)
