@@ -1317,21 +1317,7 @@ void k_bins(
 // on every run and matches any other double-precision implementation of the
 // same order.
 
-template <int NW>
-__device__ __forceinline__ void wave_scan_pids(unsigned* cnt_round, unsigned* seg, int G,
-                                               int lane) {
-    // exclusive prefix over pids 0..G-1 by one wavefront (pids lane, lane+64, ...)
-    unsigned carry = 0;
-    for (int p0 = 0; p0 < G; p0 += kWave) {
-        const int p = p0 + lane;
-        const unsigned c = p < G ? cnt_round[p] : 0u;
-        const unsigned incl = wave_incl_scan(c, lane);
-        if (p < G) seg[p] = carry + incl - c;
-        carry += (unsigned)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-    }
-}
-
-__global__ __launch_bounds__(kBinBlock) void k_centroid(
+__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) void k_centroid(
     const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
     const float4* __restrict__ stage_pt, long long ptiles, int ptile, int gshift, int nbits,
     int M, long long* __restrict__ kept_key, unsigned long long* __restrict__ compact, unsigned C,
@@ -1413,22 +1399,32 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
             const unsigned rank = (unsigned)__popcll(m & lanes_below(lane));
             if (valid && (m & lanes_above(lane)) == 0ull) cur[w * G + pl] = (unsigned)__popcll(m);
             __syncthreads();
-            if (w == 0) {
-                // per voxel: prefix over the wavefronts on top of the earlier
-                // arrivals, this round's count, then the groups' starts
-                for (int p = lane; p < G; p += kWave) {
-                    unsigned acc = running[p];
-                    before[p] = acc;
-                    for (int ww = 0; ww < kBinWaves; ++ww) {
-                        const unsigned cw = cur[ww * G + p];
-                        cur[ww * G + p] = acc;
-                        acc += cw;
+            // thread p < G, voxel p: prefix over the wavefronts on top of the
+            // earlier arrivals (eight reads in flight, then eight writes) and
+            // this round's count; then the groups' starts in rowbuf
+            unsigned cnt = 0u;
+            if (t < G) {
+                const unsigned b0 = running[t];
+                unsigned acc = b0;
+#pragma unroll
+                for (int h0 = 0; h0 < kBinWaves; h0 += 8) {
+                    unsigned cw[8];
+#pragma unroll
+                    for (int ww = 0; ww < 8; ++ww) cw[ww] = cur[(h0 + ww) * G + t];
+#pragma unroll
+                    for (int ww = 0; ww < 8; ++ww) {
+                        cur[(h0 + ww) * G + t] = acc;
+                        acc += cw[ww];
                     }
-                    cnt_round[p] = acc - before[p];
-                    running[p] = acc;
                 }
-                wave_scan_pids<kBinWaves>(cnt_round, seg, G, lane);
+                before[t] = b0;
+                cnt = acc - b0;
+                cnt_round[t] = cnt;
+                running[t] = acc;
             }
+            unsigned round_total;
+            const unsigned sg = block_excl_scan<kBinWaves>(cnt, wsum, &round_total);
+            if (t < G) seg[t] = sg;
             __syncthreads();
             if (valid) {
                 const unsigned r = cur[w * G + pl] + rank;  // arrival rank in the voxel
@@ -1436,9 +1432,23 @@ __global__ __launch_bounds__(kBinBlock) void k_centroid(
             }
             __syncthreads();
             if (t < Gb) {
-                // this voxel's rows of the round, in input order
+                // this voxel's rows of the round, added in input order; the
+                // LDS reads go four at a time ahead of the additions
                 const unsigned s0 = seg[t], n = cnt_round[t];
-                for (unsigned k = 0; k < n; ++k) {
+                unsigned k = 0;
+                for (; k + 4u <= n; k += 4u) {
+                    float4 q[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) q[j] = rowbuf[s0 + k + j];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sx += (double)q[j].x;
+                        sy += (double)q[j].y;
+                        sz += (double)q[j].z;
+                        sw += (double)q[j].w;
+                    }
+                }
+                for (; k < n; ++k) {
                     const float4 q = rowbuf[s0 + k];
                     sx += (double)q.x;
                     sy += (double)q.y;
