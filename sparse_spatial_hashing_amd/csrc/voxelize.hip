@@ -1357,7 +1357,8 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     const int Gb = b < V ? (int)((V - b + nbins - 1) >> nbits) : 0;
     for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
     for (int x = t; x < 3 * kBinWaves * G; x += kBinBlock) wbuf[x] = 0u;
-    double sx = 0.0, sy = 0.0, sz = 0.0, sw = 0.0;  // thread t < Gb: voxel t's sums
+    // thread t < 4 Gb: component t % 4 (x, y, z, intensity) of voxel t / 4
+    double sum = 0.0;
     unsigned round = 0;
     for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
         const long long tt = tg + t;
@@ -1431,41 +1432,36 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
                 rowbuf[seg[pl] + (r - before[pl])] = row;
             }
             __syncthreads();
-            if (t < Gb) {
-                // this voxel's rows of the round, added in input order; the
-                // LDS reads go four at a time ahead of the additions
-                const unsigned s0 = seg[t], n = cnt_round[t];
+            if (t < 4 * Gb) {
+                // one component of this voxel's rows of the round, added in
+                // input order; the LDS reads go four at a time ahead of the
+                // additions
+                const unsigned s0 = seg[t >> 2], n = cnt_round[t >> 2];
+                const float* col = reinterpret_cast<const float*>(rowbuf + s0) + (t & 3);
                 unsigned k = 0;
                 for (; k + 4u <= n; k += 4u) {
-                    float4 q[4];
+                    float f[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) q[j] = rowbuf[s0 + k + j];
+                    for (int j = 0; j < 4; ++j) f[j] = col[4 * (k + j)];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        sx += (double)q[j].x;
-                        sy += (double)q[j].y;
-                        sz += (double)q[j].z;
-                        sw += (double)q[j].w;
-                    }
+                    for (int j = 0; j < 4; ++j) sum += (double)f[j];
                 }
-                for (; k < n; ++k) {
-                    const float4 q = rowbuf[s0 + k];
-                    sx += (double)q.x;
-                    sy += (double)q.y;
-                    sz += (double)q.z;
-                    sw += (double)q.w;
-                }
+                for (; k < n; ++k) sum += (double)col[4 * k];
             }
             __syncthreads();  // rowbuf and the per-voxel words are reused
             ++round;
         }
     }
+    // the four sums of voxel p meet in LDS (rowbuf is free now)
+    double* dsum = reinterpret_cast<double*>(rowbuf);
+    if (t < 4 * Gb) dsum[t] = sum;
+    __syncthreads();
     if (t < Gb) {
         const long long pp = b + ((long long)t << nbits);
         const unsigned n = running[t];
         const double dn = (double)n;
-        centroids[pp] = make_float4((float)(sx / dn), (float)(sy / dn), (float)(sz / dn),
-                                    (float)(sw / dn));
+        centroids[pp] = make_float4((float)(dsum[4 * t] / dn), (float)(dsum[4 * t + 1] / dn),
+                                    (float)(dsum[4 * t + 2] / dn), (float)(dsum[4 * t + 3] / dn));
         counts[pp] = (int)n;
         const long long key = kept_key[pp];
         write_coords(coords, pp, key, gx, gy);
