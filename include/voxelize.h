@@ -94,8 +94,9 @@ typedef struct vox_options {
                                K <= 64 and max_voxels <= 262144, else 1. 2 and 3
                                outside those limits: VOX_EINVAL. */
     int32_t kept_map;       /* partitioned routes: 0 = rank also writes a map from grid
-                               cell to kept pillar (4 bytes per cell, in the
-                               workspace's zero part, 2 x table_slots cells at most)
+                               cell to kept pillar (2 bytes per cell when max_voxels
+                               <= 65534, else 4; in the workspace's zero part,
+                               2 x table_slots cells at most)
                                and lookups past the prefix read it when the grid has
                                at most that many cells; 1 = lookups probe the table.
                                The map is not used with compact_table = 1. */

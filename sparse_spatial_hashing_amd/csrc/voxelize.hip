@@ -924,7 +924,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         }
         if (kmap.p && any_rest) {
             // the kept-cell map answers every point of a tile that reaches
-            // past the prefix with one 4-byte load; its prefix points only
+            // past the prefix with one 2- or 4-byte load; its prefix points only
             // return their slot_of entries to zero (tiles inside the prefix
             // take the slot_of path below)
             if (any_prefix) {
