@@ -63,7 +63,6 @@ constexpr int kSLookBack = 32;               // predecessor tiles read per look-
 constexpr int kSLookBackLane = 24;           // predecessors per lane in look_back_wide
 constexpr int kSWavesPart = kSBlock / kWave; // wavefronts of a binning block
 constexpr int kSMaxRuns = 4096;              // runs one k_sph_place block reads, at most
-
 constexpr int kSPlacePer = 6;                // entries per thread in a k_sph_place chunk
 constexpr int kSPairsMax = 4096;             // (low digit, high digit) counters per block, at most
 constexpr int kSMaxLowBits = 11;             // low digit of the two-kernel route, at most
