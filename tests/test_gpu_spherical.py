@@ -177,6 +177,34 @@ def test_one_voxel_holds_a_block_many_times_over():
     check(pts, (0.1, -PI / 2, -PI), (0.3, PI / 64, PI / 32), (16, 64, 64), "one voxel, 16-bit grid")
 
 
+def test_seeded_fuzz_two_kernel_route():
+    """Random grids of up to 65,536 voxels (the two-kernel route), random
+    cloud sizes and binning tile sizes: low/high digit splits, groups of one
+    or several low digits, tile ranges and multi-chunk blocks all occur."""
+    rng = np.random.default_rng(31)
+    for case in range(24):
+        nr = int(rng.integers(1, 33))
+        nt = int(rng.integers(1, 65))
+        npz = int(rng.integers(1, 129))
+        while nr * nt * npz > 65536:
+            npz = max(1, npz // 2)
+        n = int(rng.choice([1, 17, 4096, 30001, 120000, 250000]))
+        rmax = float(rng.uniform(0.5, 20.0))
+        pts = _ball(n, 100 + case, rmax=rmax)
+        if case % 3 == 0:   # a dense clump that fills a few voxels
+            m = n // 2
+            pts[:m, :3] = (np.array([1.0, 0.5, 0.2], F32) * rmax * 0.4
+                           + rng.normal(scale=0.01, size=(m, 3))).astype(F32)
+        mn = (float(rng.uniform(0.0, 0.2 * rmax)), float(rng.uniform(-PI / 2, 0.0)),
+              float(rng.uniform(-PI, 0.0)))
+        ce = (float((rmax - mn[0]) / nr * rng.uniform(0.7, 1.3)),
+              float((PI / 2 - mn[1]) / nt * rng.uniform(0.7, 1.3)),
+              float((PI - mn[2]) / npz * rng.uniform(0.7, 1.3)))
+        per = int(rng.choice([0, 1, 2, 4, 8]))
+        say(f"fuzz case {case}: N={n} bins={(nr, nt, npz)} per={per}")
+        check(pts, mn, ce, (nr, nt, npz), f"fuzz {case}", points_per_thread=per)
+
+
 def test_sorted_rows_optional():
     p = get_sph_config("lidar_scan_64k").params
     pts, _ = generate("lidar_scan_64k", n=20000)
