@@ -853,8 +853,9 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     }
     unsigned gall;
     const unsigned g0 = block_excl_scan<NW>(gd, wsum, &gall);
-    const unsigned excl = look_back_wide(state, nb1, b, d1 < nb1 ? d1 : 0, S, d1 >= nb1 || b == 0,
-                                         lane, &blk_err);
+    unsigned excl = 0;
+    if (b > 0)   // block-uniform: the first block has no predecessor
+        excl = look_back_wide(state, nb1, b, d1 < nb1 ? d1 : 0, S, d1 >= nb1, lane, &blk_err);
     if (lead) {
         if (b > 0) store_relaxed32(&state[(long long)b * nb1 + d1], kSIncl | (excl + c));
         basev[d1] = g0 + excl;
