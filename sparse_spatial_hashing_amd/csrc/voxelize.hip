@@ -1096,15 +1096,30 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         run += c[q];
     }
     __syncthreads();
+    // With CARRY and a tile's rows fitting the histogram's LDS (PER <= 8),
+    // the rows are placed there in staging order and written out in one
+    // contiguous run; otherwise each row goes straight to its position.
+    constexpr bool kRowsViaLds = CARRY && kBlock * PER * sizeof(float4) <= sizeof(hist);
+    unsigned lat[PER];  // position within the tile's staging slice
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
+        lat[k] = 0u;
         if (pid[k] == kNoPid) continue;
         const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);  // in the tile
         const unsigned bin = pid[k] & bmask;
         const unsigned id = pid[k] >> nbits;  // id within the bin
-        const long long at = base + hist[w][bin] + pos[k];
-        staging[at] = (id << 16) | local;
-        if (CARRY) stage_pt[at] = row[k];  // the row itself, bit for bit
+        lat[k] = hist[w][bin] + pos[k];
+        staging[base + lat[k]] = (id << 16) | local;
+        if (CARRY && !kRowsViaLds) stage_pt[base + lat[k]] = row[k];  // the row, bit for bit
+    }
+    if (kRowsViaLds) {
+        float4* trow = reinterpret_cast<float4*>(&hist[0][0]);
+        __syncthreads();   // every position is read from hist
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (pid[k] != kNoPid) trow[lat[k]] = row[k];
+        __syncthreads();
+        for (unsigned q = t; q < total; q += kBlock) stage_pt[base + q] = trow[q];
     }
 }
 
