@@ -32,9 +32,9 @@
 //                kept count, the rows gathered in sorted order, and the
 //                histograms reset to zero for the next call.
 //
-// Angle bins: an atan2f estimate of the bin is refined by exact direction
-// tests against the table's boundary directions (cross products of float
-// operands in double), so atan2f's rounding never decides a bin.
+// Angle bins: an estimate of the bin (a polynomial atan2) is refined by
+// exact direction tests against the table's boundary directions (cross
+// products of float operands in double), so the estimate never decides a bin.
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -90,6 +90,7 @@ static_assert(sizeof(SphHeader) == 64, "table header is 64 bytes");
 struct SphArgs {
     float mn[3];
     float cell[3];
+    float inv_cell[3];   // 1 / cell, for the angle estimates only
     int nr, nt, np;
     int nvox;         // also the key of a dropped point
     int ntiles;       // binning kernel: tiles of 256 x PER points
@@ -143,7 +144,30 @@ __device__ __forceinline__ int refine(int k0, int n, Ge ge) {
 }
 
 __device__ __forceinline__ int clamp_estimate(float f, int n) {
-    return (int)fminf(fmaxf(f, -1.0f), (float)n);
+    return (int)fminf(fmaxf(f, -1.0f), (float)n);   // NaN -> -1
+}
+
+// Angle of the direction (x, y) in [-pi, pi], as an estimate only: the bin
+// it suggests is refined by exact tests, so its error decides nothing but
+// the number of refinement steps. Octant reduction to t = min/max in [0, 1],
+// then atan(t) ~ t P(t^2) with P of degree 6 fitted to atan(t)/t by least
+// squares on [0, 1] (at most 7e-7 rad off in float arithmetic). x = y = 0
+// gives NaN, which the caller's clamp turns into a start at -1.
+__device__ __forceinline__ float atan2_estimate(float y, float x) {
+    const float ax = fabsf(x), ay = fabsf(y);
+    const float t = fminf(ax, ay) * __builtin_amdgcn_rcpf(fmaxf(ax, ay));
+    const float u = t * t;
+    float q = 0.008096857f;
+    q = q * u - 0.03775049f;
+    q = q * u + 0.0847584382f;
+    q = q * u - 0.13537614f;
+    q = q * u + 0.198950127f;
+    q = q * u - 0.333279759f;
+    q = q * u + 0.999999702f;
+    float r = t * q;
+    if (ay > ax) r = 1.57079633f - r;
+    if (x < 0.0f) r = 3.14159265f - r;
+    return y < 0.0f ? -r : r;
 }
 
 // Voxel id of one point, -1 when not kept.
@@ -161,7 +185,8 @@ __device__ __forceinline__ int sph_voxel(float4 p, const SphArgs& a, const SphHe
 
     const int t_lo = h->t_lo, t_hi = h->t_hi;
     const int it = refine(
-        clamp_estimate(floorf((atan2f(z, rxy) - a.mn[1]) / a.cell[1]), a.nt), a.nt, [&](int k) {
+        clamp_estimate(floorf((atan2_estimate(z, rxy) - a.mn[1]) * a.inv_cell[1]), a.nt), a.nt,
+        [&](int k) {
             if (k < t_lo) return true;
             if (k > t_hi) return false;
             const float2 d = tb[k];
@@ -177,7 +202,8 @@ __device__ __forceinline__ int sph_voxel(float4 p, const SphArgs& a, const SphHe
     const int hp = half_turn(ax, ay);
     const int p_lo = h->p_lo, p_hi = h->p_hi;
     const int ip = refine(
-        clamp_estimate(floorf((atan2f(ay, ax) - a.mn[2]) / a.cell[2]), a.np), a.np, [&](int k) {
+        clamp_estimate(floorf((atan2_estimate(ay, ax) - a.mn[2]) * a.inv_cell[2]), a.np), a.np,
+        [&](int k) {
             if (k < p_lo) return true;
             if (k > p_hi) return false;
             const float2 d = pb[k];
@@ -1102,6 +1128,7 @@ SphArgs make_args(const float mn[3], const float cell[3], const int32_t bins[3],
     for (int d = 0; d < 3; ++d) {
         a.mn[d] = mn[d];
         a.cell[d] = cell[d];
+        a.inv_cell[d] = 1.0f / cell[d];
     }
     a.nr = bins[0];
     a.nt = bins[1];
