@@ -495,9 +495,10 @@ __global__ __launch_bounds__(kSBlock) void k_sph_final(
 //                  digit, high digit), takes each high digit's start from the
 //                  global histogram and a look-back over the preceding blocks
 //                  (blocks ordered group-major, range-minor, which is that
-//                  same order), writes the offsets of its voxels, sorts its
-//                  entries by high digit in LDS and writes them out, each
-//                  high digit's entries to one contiguous range.
+//                  same order), writes the offsets of its voxels, ranks its
+//                  entries stably by high digit (per-wavefront counts in
+//                  LDS) and stores each at its sorted position: the block's
+//                  entries of one high digit fill one contiguous range.
 // The last block to finish (a counter in the zero part) writes the kept
 // count and returns the histograms and the counter to zero.
 
