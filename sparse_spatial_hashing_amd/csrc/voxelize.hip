@@ -60,8 +60,8 @@ namespace {
 
 constexpr int kBlock = 256;                 // 4 wavefronts of 64 lanes
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kRankTile = 1024;             // points per look-back tile
-constexpr int kRankIters = kRankTile / kBlock;
+constexpr int kRankTileMin = kBlock;         // points per look-back tile: 256, 512 or 1024
+constexpr int kRankTilesAim = 128;           // the smallest tile leaving at most this many
 constexpr unsigned kSpinLimit = 1u << 22;   // look-back poll bound (never reached in practice)
 constexpr int kPackMaxBlocks = 4096;
 constexpr int kSortLanes = 64;              // pillars with K <= 64 use the bucket + bitonic path
@@ -339,6 +339,7 @@ __device__ unsigned long long look_back(unsigned long long* tile_state, long lon
     }
 }
 
+template <int ITERS>
 __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M,
                                                  unsigned long long* __restrict__ table,
                                                  unsigned long long* __restrict__ compact,
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
                                                  Header* __restrict__ hdr,
                                                  int* __restrict__ num_voxels) {
     __shared__ unsigned tile_sh;
-    __shared__ unsigned wave_cnt[kRankIters][kWavesPerBlock];
+    __shared__ unsigned wave_cnt[ITERS][kWavesPerBlock];
     __shared__ unsigned long long excl_sh;
     __shared__ int failed_sh;
 
@@ -366,14 +367,14 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
     }
     __syncthreads();
     const long long tile = tile_sh;
-    const long long base = tile * kRankTile;
+    const long long base = tile * (kBlock * ITERS);
 
-    bool is_first[kRankIters];
-    int slot[kRankIters];
-    unsigned long long key1[kRankIters];
-    unsigned before[kRankIters];  // first occurrences before this lane in its wave
+    bool is_first[ITERS];
+    int slot[ITERS];
+    unsigned long long key1[ITERS];
+    unsigned before[ITERS];  // first occurrences before this lane in its wave
 #pragma unroll
-    for (int k = 0; k < kRankIters; ++k) {
+    for (int k = 0; k < ITERS; ++k) {
         const long long i = base + (long long)k * kBlock + t;
         is_first[k] = false;
         slot[k] = -1;
@@ -398,10 +399,10 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
 
     // Tile-local exclusive offset of this lane's points (index order is
     // k-major, then wave, then lane).
-    unsigned local[kRankIters];
+    unsigned local[ITERS];
     unsigned run = 0;
 #pragma unroll
-    for (int k = 0; k < kRankIters; ++k) {
+    for (int k = 0; k < ITERS; ++k) {
         unsigned off = run;
         for (int ww = 0; ww < kWavesPerBlock; ++ww) {
             if (ww < w) off += wave_cnt[k][ww];
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
     const unsigned long long excl = excl_sh;
 
 #pragma unroll
-    for (int k = 0; k < kRankIters; ++k) {
+    for (int k = 0; k < ITERS; ++k) {
         if (!is_first[k]) continue;
         const long long r = (long long)excl + local[k];
         if (r >= P) {  // cannot happen: there are at most P first occurrences
@@ -1508,6 +1509,17 @@ inline int hip_fail(hipError_t e) {
 }
 
 inline long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+// k_rank's tile for a prefix of P points: the smallest of 256, 512 and 1,024
+// points that leaves at most kRankTilesAim tiles (many small tiles spread the
+// two dependent loads of a small prefix over more CUs; past that, the
+// look-back over many tiles costs more than it saves).
+inline int rank_tile(long long P) {
+    int tile = kRankTileMin;
+    while (tile < 4 * kRankTileMin && cdiv(P, tile) > kRankTilesAim) tile *= 2;
+    return tile;
+}
+inline long long rank_tiles(long long P) { return P > 0 ? cdiv(P, rank_tile(P)) : 1; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
@@ -1603,7 +1615,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
                 ? (4ll * M + kLineSlots - 1) / kLineSlots * kLineSlots : 0;
     // arrays indexed by point go to N: the chunked path can insert every point
     const long long Nw = N > 0 ? N : 1;
-    pl->ntiles = cdiv(Nw, kRankTile);
+    pl->ntiles = cdiv(Nw, kRankTileMin);   // look-back words for the smallest tile
     // Select/pack route: per-bin partition (no per-point device atomic) when
     // K <= 64 and the ids fit kMaxBins bins of at most 128; buckets otherwise.
     const int path = opt ? opt->select_path : 0;
@@ -1780,8 +1792,10 @@ int launch_insert(const float* points, long long begin, long long end, const Gri
 
 int launch_rank(long long P, const Plan& pl, const Buffers& bf, int32_t* num_voxels,
                 hipStream_t st, hipEvent_t* ev) {
-    const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
-    hipExtLaunchKernelGGL(k_rank, dim3((unsigned)ntiles), dim3(kBlock), 0, st, ev_start(ev),
+    const long long ntiles = rank_tiles(P);
+    const int tile = P > 0 ? rank_tile(P) : kRankTileMin;
+    decltype(&k_rank<1>) kern = tile == 1024 ? &k_rank<4> : tile == 512 ? &k_rank<2> : &k_rank<1>;
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(kBlock), 0, st, ev_start(ev),
                           ev_stop(ev), 0, P, pl.N, pl.M,
                        bf.table, bf.compact, (unsigned)pl.C, pl.hash, bf.kcs, bf.slot_of,
                        bf.tiles, ntiles, bf.occ, bf.kept, bf.kmap, bf.hdr, num_voxels);
@@ -1819,7 +1833,7 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
 int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                 const Buffers& bf, float* voxels, int32_t* coords, int32_t* num_points,
                 int32_t* num_voxels, hipStream_t st, hipEvent_t* ev) {
-    const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
+    const long long ntiles = rank_tiles(P);
     if (pl.part) {
         // one block per bin; all blocks share the workspace release
         hipExtLaunchKernelGGL(pl.carry ? k_bins<true> : k_bins<false>, dim3((unsigned)pl.nbins),
@@ -1933,7 +1947,7 @@ int downsample_plan(long long N, int M, const vox_options* options, Plan* pl) {
 int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& g,
                     float* centroids, int32_t* coords, int32_t* counts, int32_t* num_voxels,
                     hipStream_t st) {
-    const long long ntiles = P > 0 ? cdiv(P, kRankTile) : 1;
+    const long long ntiles = rank_tiles(P);
     hipExtLaunchKernelGGL(k_centroid, dim3((unsigned)pl.nbins), dim3(kBinBlock),
                           (unsigned)pl.lds, st, nullptr, nullptr, 0, bf.cm, bf.stage,
                           bf.stage_pt, pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.M,
