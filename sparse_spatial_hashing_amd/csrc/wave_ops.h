@@ -64,9 +64,10 @@ __device__ __forceinline__ long long xcd_tile(long long bid, long long n) {
 __device__ __forceinline__ unsigned long long match_mask(unsigned v, bool valid, int nbits) {
     unsigned long long m = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
-        const bool bit = ((v >> b) & 1u) != 0u;
-        const unsigned long long bb = __ballot(valid && bit);
-        m &= bit ? bb : ~bb;
+        const unsigned bit = (v >> b) & 1u;
+        const unsigned long long bb = __ballot(bit != 0u);  // m already excludes invalid lanes
+        const unsigned long long flip = (unsigned long long)bit - 1ull;  // bit clear: all ones
+        m &= bb ^ flip;  // lanes with the bit set keep bb, the others its complement
     }
     return m;
 }
