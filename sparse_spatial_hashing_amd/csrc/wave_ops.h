@@ -62,14 +62,17 @@ __device__ __forceinline__ long long xcd_tile(long long bid, long long n) {
 // Lanes of the wavefront whose value v (nbits low bits) equals this lane's,
 // among the lanes with `valid` set: one ballot per bit. Every lane calls it.
 __device__ __forceinline__ unsigned long long match_mask(unsigned v, bool valid, int nbits) {
-    unsigned long long m = __ballot(valid);
+    const unsigned long long m0 = __ballot(valid);
+    unsigned lo = (unsigned)m0, hi = (unsigned)(m0 >> 32);
     for (int b = 0; b < nbits; ++b) {
-        const unsigned bit = (v >> b) & 1u;
-        const unsigned long long bb = __ballot(bit != 0u);  // m already excludes invalid lanes
-        const unsigned long long flip = (unsigned long long)bit - 1ull;  // bit clear: all ones
-        m &= bb ^ flip;  // lanes with the bit set keep bb, the others its complement
+        const unsigned s = (unsigned)__builtin_amdgcn_sbfe((int)v, b, 1);  // bit b, as 0 or all ones
+        const unsigned long long bb = __ballot(s != 0u);  // m already excludes invalid lanes
+        // keep the lanes whose bit b equals this lane's: m & ~(bb ^ s), one
+        // three-input bit operation per half (truth table 0x90 over m, bb, s)
+        lo = __builtin_amdgcn_bitop3_b32(lo, (unsigned)bb, s, 0x90);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (unsigned)(bb >> 32), s, 0x90);
     }
-    return m;
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ unsigned long long lanes_below(int lane) {
