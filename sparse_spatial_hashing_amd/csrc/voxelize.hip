@@ -850,8 +850,8 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 
 constexpr int kPartMaxPer = 16;                // points per k_part thread, at most
 constexpr int kPartBatch = 4;                  // lookups in flight per thread
+constexpr int kWideBlock = 2 * kBlock;         // k_part threads from 4 points per thread
 constexpr int kMaxBins = 2048;                 // bins per call (k_part: one LDS histogram per wavefront)
-constexpr int kBinsPerThread = kMaxBins / kBlock;
 constexpr int kBinBlock = 1024;                // k_bins threads (16 wavefronts)
 constexpr int kBinWaves = kBinBlock / kWave;
 constexpr unsigned kNoPid = 0xffffffffu;
@@ -859,12 +859,13 @@ constexpr unsigned kNoPid = 0xffffffffu;
 // CARRY: also copy each kept point's row into a scratch array next to its
 // staging word, so that k_bins copies rows from there instead of gathering
 // them from the cloud (pays off for large clouds).
-// PER points per thread: wavefront w of the block takes the contiguous
-// points [base + 64 PER w, base + 64 PER (w + 1)), 64 at a time. Lookups go
+// BLK threads and PER points per thread: wavefront w of the block takes the
+// contiguous points [base + 64 PER w, base + 64 PER (w + 1)), 64 at a time.
+// The hist LDS holds one 2048-bin histogram per wavefront. Lookups go
 // PER_B at a time: within a batch every load is issued before any result is
 // used, and only block-uniform branches guard them.
-template <int PER, bool CARRY>
-__global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts, long long N,
+template <int PER, bool CARRY, int BLK>
+__global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, long long N,
                                                  long long P, Grid g,
                                                  const unsigned long long* __restrict__ table,
                                                  unsigned S,
@@ -878,10 +879,12 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
                                                  Header* __restrict__ hdr,
                                                  int* __restrict__ num_voxels,
                                                  int* __restrict__ point_pillar) {
-    constexpr int TILE = kBlock * PER;
+    constexpr int TILE = BLK * PER;
+    constexpr int WPB = BLK / kWave;      // wavefronts per block
+    constexpr int BPT = kMaxBins / BLK;   // bins per thread in the tile's scan
     constexpr int PER_B = PER < kPartBatch ? PER : kPartBatch;
-    __shared__ unsigned hist[kWavesPerBlock][kMaxBins];  // one histogram per wavefront
-    __shared__ unsigned wsum[kWavesPerBlock];
+    __shared__ unsigned hist[WPB][kMaxBins];  // one histogram per wavefront
+    __shared__ unsigned wsum[WPB];
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int w = t / kWave;
@@ -899,9 +902,9 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
     const int nbins = 1 << nbits;
     const unsigned bmask = (unsigned)nbins - 1u;
     const int nb = status > 0 ? nbins : 0;
-    for (int b = t; b < nb; b += kBlock) {
+    for (int b = t; b < nb; b += BLK) {
 #pragma unroll
-        for (int ww = 0; ww < kWavesPerBlock; ++ww) hist[ww][b] = 0u;
+        for (int ww = 0; ww < WPB; ++ww) hist[ww][b] = 0u;
     }
     __syncthreads();
 
@@ -1066,29 +1069,29 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
     __syncthreads();
 
     // bin starts within the tile, then each wavefront's start within its bin;
-    // each thread owns kBinsPerThread bins
-    unsigned c[kBinsPerThread];
+    // each thread owns BPT bins
+    unsigned c[BPT];
     unsigned mine = 0;
 #pragma unroll
-    for (int q = 0; q < kBinsPerThread; ++q) {
-        const int b = t * kBinsPerThread + q;
+    for (int q = 0; q < BPT; ++q) {
+        const int b = t * BPT + q;
         c[q] = 0u;
         if (b < nb) {
 #pragma unroll
-            for (int ww = 0; ww < kWavesPerBlock; ++ww) c[q] += hist[ww][b];
+            for (int ww = 0; ww < WPB; ++ww) c[q] += hist[ww][b];
         }
         mine += c[q];
     }
     unsigned total;
-    unsigned run = block_excl_scan<kWavesPerBlock>(mine, wsum, &total);
+    unsigned run = block_excl_scan<WPB>(mine, wsum, &total);
 #pragma unroll
-    for (int q = 0; q < kBinsPerThread; ++q) {
-        const int b = t * kBinsPerThread + q;
+    for (int q = 0; q < BPT; ++q) {
+        const int b = t * BPT + q;
         if (b < nb) {
             cm[(size_t)b * ptiles + tile] = run | (c[q] << 16);
             unsigned at = run;
 #pragma unroll
-            for (int ww = 0; ww < kWavesPerBlock; ++ww) {
+            for (int ww = 0; ww < WPB; ++ww) {
                 const unsigned cw = hist[ww][b];
                 hist[ww][b] = at;
                 at += cw;
@@ -1100,7 +1103,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
     // With CARRY and a tile's rows fitting the histogram's LDS (PER <= 8),
     // the rows are placed there in staging order and written out in one
     // contiguous run; otherwise each row goes straight to its position.
-    constexpr bool kRowsViaLds = CARRY && kBlock * PER * sizeof(float4) <= sizeof(hist);
+    constexpr bool kRowsViaLds = CARRY && BLK * PER * sizeof(float4) <= sizeof(hist);
     unsigned lat[PER];  // position within the tile's staging slice
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -1120,7 +1123,7 @@ __global__ __launch_bounds__(kBlock) void k_part(const float4* __restrict__ pts,
         for (int k = 0; k < PER; ++k)
             if (pid[k] != kNoPid) trow[lat[k]] = row[k];
         __syncthreads();
-        for (unsigned q = t; q < total; q += kBlock) stage_pt[base + q] = trow[q];
+        for (unsigned q = t; q < total; q += BLK) stage_pt[base + q] = trow[q];
     }
 }
 
@@ -1151,7 +1154,10 @@ void k_bins(
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int w = t / kWave;
-    const long long b = blockIdx.x;
+    // Blocks are dealt to the 8 XCDs round-robin; each XCD takes a contiguous
+    // range of bins, whose runs lie side by side in every k_part tile, so the
+    // staging lines they share come through one L2.
+    const long long b = xcd_tile(blockIdx.x, gridDim.x);
     // the first group's count entries do not depend on the header: load them
     // together with it
     unsigned e = 0u;
@@ -1160,10 +1166,12 @@ void k_bins(
     const long long V = status > 0 ? status : 0;
     const long long distinct = hdr->distinct;
     if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
-    // the release touches nothing below; its memory traffic overlaps the bins
-    release_workspace(b * kBinBlock + t, (long long)gridDim.x * kBinBlock, distinct, V, M,
-                      occ_slot, table, S, kept_key, compact, C, kept_cslot, tile_state, ntiles,
-                      kmap, hdr, num_voxels);
+    // the release touches nothing below; its memory traffic overlaps the bins.
+    // It goes by block index, not by bin: clearing in bin order measured
+    // slower in the next call's inserts.
+    release_workspace((long long)blockIdx.x * kBinBlock + t, (long long)gridDim.x * kBinBlock,
+                      distinct, V, M, occ_slot, table, S, kept_key, compact, C, kept_cslot,
+                      tile_state, ntiles, kmap, hdr, num_voxels);
     if (status <= 0) return;  // nothing was staged
 
     // bin b holds the ids b, b + nbins, b + 2 nbins, ... below V
@@ -1357,16 +1365,16 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int w = t / kWave;
-    const long long b = blockIdx.x;
+    const long long b = xcd_tile(blockIdx.x, gridDim.x);  // contiguous bins per XCD, as k_bins
     unsigned e = 0u;
     if ((long long)t < ptiles) e = cm[(size_t)b * ptiles + t];
     const int status = hdr->status;
     const long long V = status > 0 ? status : 0;
     const long long distinct = hdr->distinct;
     if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
-    release_workspace(b * kBinBlock + t, (long long)gridDim.x * kBinBlock, distinct, V, M,
-                      occ_slot, table, S, kept_key, compact, C, kept_cslot, tile_state, ntiles,
-                      kmap, hdr, num_voxels);
+    release_workspace((long long)blockIdx.x * kBinBlock + t, (long long)gridDim.x * kBinBlock,
+                      distinct, V, M, occ_slot, table, S, kept_key, compact, C, kept_cslot,
+                      tile_state, ntiles, kmap, hdr, num_voxels);
     if (status <= 0) return;
 
     const long long nbins = 1ll << nbits;
@@ -1528,9 +1536,9 @@ struct Plan {
     int K, M, hash, cap;
     long long ntiles;
     // partitioned select/pack (part = 1): bins of 2^gshift pillar ids, ptiles
-    // k_part tiles of 256 pper points, nbits = bits of a bin number, lds bytes
-    // of a k_bins block
-    int part, carry, gshift, nbins, nbits, pper;
+    // k_part tiles of pblock x pper points, nbits = bits of a bin number, lds
+    // bytes of a k_bins block
+    int part, carry, gshift, nbins, nbits, pper, pblock;
     long long ptiles;
     size_t lds;
     // byte offsets into the workspace; [0, zero_bytes) is zero between calls,
@@ -1631,6 +1639,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->nbins = 0;
     pl->nbits = 0;
     pl->pper = 0;
+    pl->pblock = kBlock;
     pl->ptiles = 0;
     pl->lds = 0;
     if (pl->part) {
@@ -1647,7 +1656,11 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         int per = 1;
         while (per < kPartMaxPer && Nw >= (long long)per * 2 * kBlock * 1024) per *= 2;
         pl->pper = per;
-        pl->ptiles = cdiv(Nw, (long long)kBlock * per);
+        // from 4 points per thread the tiles take 512 threads: as many threads
+        // per CU (two blocks instead of four), half the tiles, so every bin's
+        // run in a tile, which k_bins reads, is twice as long
+        pl->pblock = per >= 4 ? kWideBlock : kBlock;
+        pl->ptiles = cdiv(Nw, (long long)pl->pblock * per);
         cap = 0;  // no buckets
     }
     pl->cap = cap;
@@ -1681,9 +1694,9 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->off_cm = off;
     off = align256(off + (size_t)pl->nbins * (size_t)pl->ptiles * sizeof(unsigned));
     pl->off_stage = off;
-    off = align256(off + (size_t)pl->ptiles * (size_t)(kBlock * pl->pper) * sizeof(unsigned));
+    off = align256(off + (size_t)pl->ptiles * (size_t)(pl->pblock * pl->pper) * sizeof(unsigned));
     pl->off_stage_pt = off;
-    off = align256(off + (pl->carry ? (size_t)pl->ptiles * (size_t)(kBlock * pl->pper) *
+    off = align256(off + (pl->carry ? (size_t)pl->ptiles * (size_t)(pl->pblock * pl->pper) *
                                           sizeof(float4)
                                     : 0));
     pl->bytes = off;
@@ -1806,15 +1819,23 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
                   const Buffers& bf, int32_t* num_voxels, int32_t* point_pillar,
                   hipStream_t st, hipEvent_t* ev) {
     if (pl.part) {
-        decltype(&k_part<1, false>) kern = pl.carry ? &k_part<1, true> : &k_part<1, false>;
+        // 256-thread tiles below 4 points per thread, 512-thread tiles from 4
+        decltype(&k_part<1, false, kBlock>) kern =
+            pl.carry ? &k_part<1, true, kBlock> : &k_part<1, false, kBlock>;
         switch (pl.pper) {
-            case 2: kern = pl.carry ? &k_part<2, true> : &k_part<2, false>; break;
-            case 4: kern = pl.carry ? &k_part<4, true> : &k_part<4, false>; break;
-            case 8: kern = pl.carry ? &k_part<8, true> : &k_part<8, false>; break;
-            case 16: kern = pl.carry ? &k_part<16, true> : &k_part<16, false>; break;
+            case 2: kern = pl.carry ? &k_part<2, true, kBlock> : &k_part<2, false, kBlock>; break;
+            case 4:
+                kern = pl.carry ? &k_part<4, true, kWideBlock> : &k_part<4, false, kWideBlock>;
+                break;
+            case 8:
+                kern = pl.carry ? &k_part<8, true, kWideBlock> : &k_part<8, false, kWideBlock>;
+                break;
+            case 16:
+                kern = pl.carry ? &k_part<16, true, kWideBlock> : &k_part<16, false, kWideBlock>;
+                break;
             default: break;
         }
-        hipExtLaunchKernelGGL(kern, dim3((unsigned)pl.ptiles), dim3(kBlock), 0, st, ev_start(ev),
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)pl.ptiles), dim3(pl.pblock), 0, st, ev_start(ev),
                               ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, P, g, bf.table,
                            (unsigned)pl.S, bf.compact, (unsigned)pl.C, pl.hash, bf.slot_of,
@@ -1840,7 +1861,7 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                               dim3(kBinBlock), (unsigned)pl.lds, st,
                               ev_start(ev), ev_stop(ev), 0,
                            reinterpret_cast<const float4*>(points), pl.N, bf.cm, bf.stage,
-                           bf.stage_pt, pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.K,
+                           bf.stage_pt, pl.ptiles, pl.pblock * pl.pper, pl.gshift, pl.nbits, pl.K,
                            pl.M,
                            bf.kept, bf.compact,
                            (unsigned)pl.C, bf.kcs, g.gx, g.gy,
@@ -1950,7 +1971,7 @@ int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& 
     const long long ntiles = rank_tiles(P);
     hipExtLaunchKernelGGL(k_centroid, dim3((unsigned)pl.nbins), dim3(kBinBlock),
                           (unsigned)pl.lds, st, nullptr, nullptr, 0, bf.cm, bf.stage,
-                          bf.stage_pt, pl.ptiles, kBlock * pl.pper, pl.gshift, pl.nbits, pl.M,
+                          bf.stage_pt, pl.ptiles, pl.pblock * pl.pper, pl.gshift, pl.nbits, pl.M,
                           bf.kept, bf.compact, (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                           reinterpret_cast<float4*>(centroids), coords, counts, num_voxels,
                           bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr);
