@@ -133,14 +133,17 @@ __device__ __forceinline__ long long bin_key(float4 p, const Grid& g) {
     const float fx = floorf((p.x - g.x_min) / g.vx);
     const float fy = floorf((p.y - g.y_min) / g.vy);
     ok &= (int)(fx >= 0.0f) & (int)(fx < (float)g.gx) & (int)(fy >= 0.0f) & (int)(fy < (float)g.gy);
-    long long cz = 0;
+    float fz = 0.0f;
     if (g.gz > 1) {
-        const float fz = floorf((p.z - g.z_min) / g.vz);
+        fz = floorf((p.z - g.z_min) / g.vz);
         ok &= (int)(fz >= 0.0f) & (int)(fz < (float)g.gz);
-        cz = ok ? (long long)fz : 0;
     }
     if (!ok) return -1;
-    return (cz * g.gy + (long long)fy) * g.gx + (long long)fx;
+    // each index is a whole number below 2^24 here, so 32-bit conversions are
+    // exact, and the key is below 2^33 (the host bounds gx gy gz)
+    const unsigned ix = (unsigned)(int)fx, iy = (unsigned)(int)fy, iz = (unsigned)(int)fz;
+    const unsigned long long row = (unsigned long long)iz * (unsigned)g.gy + iy;
+    return (long long)(row * (unsigned)g.gx + ix);
 }
 
 // ------------------------------------------------------------------ table --
