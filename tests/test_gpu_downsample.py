@@ -61,6 +61,17 @@ def test_downsample_other_seeds(name, seed):
     check(gpu_ds(pts, p.range_, p.cell, p.grid, p.max_voxels), want, f"{name}/{seed}")
 
 
+@pytest.mark.parametrize("name", ["kitti_frame", "voxel3d"])
+def test_downsample_largest_partition_tiles(name):
+    """2^22 + 12,345 points: k_part's 512 x 16-point tiles with rows carried,
+    a ragged last tile, then k_centroid."""
+    p = get_config(name).params
+    pts, _ = generate(name, n=(1 << 22) + 12345)
+    say(f"downsample largest tiles {name} N={pts.shape[0]}")
+    want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    check(gpu_ds(pts, p.range_, p.cell, p.grid, p.max_voxels), want, name)
+
+
 @pytest.mark.parametrize("name", ["kitti_frame", "dense_multisweep"])
 def test_downsample_options_and_chunked(name):
     p = get_config(name).params

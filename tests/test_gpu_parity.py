@@ -430,6 +430,19 @@ def test_single_cell_heavy_pillar():
     assert_bitwise(gpu_vox(pts, prm, select_path=3), want, "heavy cell, carried rows")
 
 
+@pytest.mark.parametrize("name", ["kitti_frame", "voxel3d"])
+def test_largest_partition_tiles(name):
+    """From 2^22 points k_part takes its largest tiles (512 threads x 16
+    points); 2^22 + 12,345 points leave a ragged last tile. Rows gathered
+    and carried, on the 2D grid (kept-cell map) and the 3D one (table probes)."""
+    cfg = get_config(name)
+    pts, _ = generate(name, n=(1 << 22) + 12345)
+    say(f"largest tiles {name} N={pts.shape[0]}")
+    want = oracle.voxelize_params(pts, cfg.params)
+    assert_bitwise(gpu_vox(pts, params_of(cfg)), want, f"{name} gathered")
+    assert_bitwise(gpu_vox(pts, params_of(cfg), select_path=3), want, f"{name} carried")
+
+
 @pytest.mark.parametrize("per_cell,K", [(70, 64), (200, 32), (40, 5)])
 def test_bin_spanning_several_chunks(per_cell, K):
     """64 cells that share one pillar-id bin, with more candidates than one
