@@ -376,23 +376,30 @@ __global__ __launch_bounds__(kBlock) void k_rank(long long P, long long N, int M
     int slot[ITERS];
     unsigned long long key1[ITERS];
     unsigned before[ITERS];  // first occurrences before this lane in its wave
+    // every slot load, then every word load, unconditionally (clamped
+    // indices): two round trips for the ITERS points, not two per point
+    int sl[ITERS];
+    unsigned long long wd[ITERS];
+#pragma unroll
+    for (int k = 0; k < ITERS; ++k) {
+        const long long i = base + (long long)k * kBlock + t;
+        sl[k] = slot_of[i < P ? i : (P > 0 ? P - 1 : 0)];
+    }
+#pragma unroll
+    for (int k = 0; k < ITERS; ++k) wd[k] = table[sl[k] >= 0 ? sl[k] : 0];
 #pragma unroll
     for (int k = 0; k < ITERS; ++k) {
         const long long i = base + (long long)k * kBlock + t;
         is_first[k] = false;
         slot[k] = -1;
         key1[k] = 0;
-        if (i < P) {
-            const int s = slot_of[i];
-            if (s >= 0) {
-                const unsigned long long wd = table[s];
-                slot[k] = s;
-                key1[k] = slot_key1(wd);
-                // a kept word was tagged by the tile of its own first point,
-                // so a flagged word never marks a first occurrence here
-                is_first[k] = (wd & (kKeptFlag | kIdxMask)) ==
-                              ((unsigned long long)(~(unsigned)i) & kIdxMask);
-            }
+        if (i < P && sl[k] >= 0) {
+            slot[k] = sl[k];
+            key1[k] = slot_key1(wd[k]);
+            // a kept word was tagged by the tile of its own first point,
+            // so a flagged word never marks a first occurrence here
+            is_first[k] = (wd[k] & (kKeptFlag | kIdxMask)) ==
+                          ((unsigned long long)(~(unsigned)i) & kIdxMask);
         }
         const unsigned long long b = __ballot(is_first[k]);
         before[k] = (unsigned)__popcll(b & ((1ull << lane) - 1ull));
