@@ -904,6 +904,20 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     const long long tile = xcd_tile(blockIdx.x, ptiles);
     const long long base = tile * TILE;
     const long long wbase = base + (long long)w * (kWave * PER);
+    const bool any_prefix = base < P;                              // block-uniform
+    // The first batch's point rows and slot entries do not depend on the
+    // header: they are loaded before the barrier that waits for its status.
+    const bool rest_range = base + TILE > P && base < N;          // block-uniform
+    float4 row0[PER_B];
+    int sl0[PER_B];
+#pragma unroll
+    for (int k = 0; k < PER_B; ++k) {
+        const long long i0 = wbase + (long long)k * kWave + lane;
+        row0[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (base < N && (CARRY || rest_range)) row0[k] = pts[i0 < N ? i0 : N - 1];
+        sl0[k] = -1;
+        if (any_prefix) sl0[k] = slot_of[i0 < P ? i0 : P - 1];
+    }
     if (blockIdx.x == 0 && t == 0) {
         hdr->rank_ticket = 0u;  // rank is done with it
         if (hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
@@ -921,8 +935,7 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     // lookups go to the kept-cell table when there is one (found = kept)
     const unsigned long long* __restrict__ look = C > 0 ? compact : table;
     const unsigned LS = C > 0 ? C : S;
-    const bool any_prefix = base < P;                              // block-uniform
-    const bool any_rest = status > 0 && base + TILE > P && base < N;
+    const bool any_rest = status > 0 && rest_range;
     unsigned pid[PER];
     float4 row[PER];  // each point's row (kept to the end when CARRY)
 #pragma unroll
@@ -933,8 +946,12 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
         for (int k = 0; k < PER_B; ++k) {
             ii[k] = wbase + (long long)(k0 + k) * kWave + lane;
             wd[k] = 0ull;
-            row[k0 + k] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (base < N && (CARRY || any_rest)) row[k0 + k] = pts[ii[k] < N ? ii[k] : N - 1];
+            if (k0 == 0) {
+                row[k] = row0[k];
+            } else {
+                row[k0 + k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (base < N && (CARRY || any_rest)) row[k0 + k] = pts[ii[k] < N ? ii[k] : N - 1];
+            }
         }
         if (kmap.p && any_rest) {
             // the kept-cell map answers every point of a tile that reaches
@@ -961,7 +978,8 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
             // prefix points: the slot insert recorded, then its word
             int sl[PER_B];
 #pragma unroll
-            for (int k = 0; k < PER_B; ++k) sl[k] = slot_of[ii[k] < P ? ii[k] : P - 1];
+            for (int k = 0; k < PER_B; ++k)
+                sl[k] = k0 == 0 ? sl0[k] : slot_of[ii[k] < P ? ii[k] : P - 1];
 #pragma unroll
             for (int k = 0; k < PER_B; ++k)
                 if (ii[k] < P) slot_of[ii[k]] = 0;  // last reader: back to zero
