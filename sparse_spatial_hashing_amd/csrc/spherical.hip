@@ -780,10 +780,6 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     __shared__ bool last_sh, failed_sh;
     const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
     const int b = blockIdx.x;
-    if (!table_ok(tab, a)) {
-        if (b == 0 && tid == 0) *n_kept = SPH_STATUS_BAD_TABLE;
-        return;
-    }
     if (tid == 0) blk_err = 0u;
     const int ntiles = a.ntiles, T = a.tile;
     const int lgT = __builtin_ctz((unsigned)T);
@@ -818,6 +814,13 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
         const int rr = r < R ? r : (R > 0 ? R - 1 : 0);
         const int j = nt > 0 ? rr / nt : 0;
         cw[q] = R > 0 ? cm[(long long)(g * per_block + j) * ntiles + t0 + (rr - j * nt)] : 0u;
+    }
+    // The table header is checked once the run words are on their way (their
+    // addresses come from the plan alone); nothing read through them is used,
+    // and nothing is written, before the check. Uniform: every thread returns.
+    if (!table_ok(tab, a)) {
+        if (b == 0 && tid == 0) *n_kept = SPH_STATUS_BAD_TABLE;
+        return;
     }
     unsigned mine = 0;
 #pragma unroll
