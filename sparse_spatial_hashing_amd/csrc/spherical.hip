@@ -64,6 +64,7 @@ constexpr int kSLookBackLane = 24;           // predecessors per lane in look_ba
 constexpr int kSWavesPart = kSBlock / kWave; // wavefronts of a binning block
 constexpr int kSMaxRuns = 4096;              // runs one k_sph_place block reads, at most
 constexpr int kSPlacePer = 6;                // entries per thread in a k_sph_place chunk
+constexpr int kSPlacePerSmall = 3;           // the same up to 2,048 points per placing block
 constexpr int kSPairsMax = 4096;             // (low digit, high digit) counters per block, at most
 constexpr int kSMaxLowBits = 11;             // low digit of the two-kernel route, at most
 constexpr unsigned kSMagic = 0x31485053u;    // "SPH1"
@@ -756,13 +757,14 @@ __device__ __forceinline__ unsigned look_back_wide(const unsigned* state, int nb
 // s = b % nsplit of tps tiles); nsplit > 1 only with per_block = 1.
 // LDS (dynamic): runpref[R + 1], rpos[R] (R = per_block x the range's tiles),
 // cnt2[per_block x nb1], hist[16 x nb1], running[nb1], base[nb1].
-// Entries are taken in chunks of CH = 1,024 x kSPlacePer; entry e of a chunk
+// Entries are taken in chunks of CH = 1,024 x E; entry e of a chunk
 // is held by wavefront e / (64 E), register (e / 64) % E, lane e % 64. The
 // first chunk (nearly always the only one) is loaded before the look-back.
 // With rows_early its rows are in flight during the look-back; otherwise they
 // are loaded after it: vector loads complete in order, so a look-back poll
 // also waits for every row load issued before it, which on large scans (many
 // rows in flight across the chip) costs more than the overlap gains.
+template <int E>
 __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     long long N, SphArgs a, const SphHeader* __restrict__ tab, int b0, int b1, int per_block,
     int nsplit, int tps, int rows_early, const unsigned* __restrict__ cm,
@@ -771,7 +773,6 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     unsigned* __restrict__ done, int* __restrict__ offsets, int* __restrict__ order,
     float4* __restrict__ sorted, int* __restrict__ n_kept) {
     constexpr int NW = kSPassWaves;
-    constexpr int E = kSPlacePer;
     constexpr int CH = kSPassBlock * E;
     constexpr int RPT = kSMaxRuns / kSPassBlock;
     extern __shared__ __align__(16) unsigned lds[];
@@ -991,7 +992,7 @@ struct SPlan {
     // two-kernel route (fused = true): low digit b0 bits, high digit b1 bits,
     // pblocks k_sph_place blocks of pk low digits each
     bool fused;
-    int b0, b1, pk, nsplit, tps, pblocks, rows_early;
+    int b0, b1, pk, nsplit, tps, pblocks, rows_early, place_per;
     size_t off_cm, off_stage, off_rows, place_lds;
 };
 
@@ -1061,6 +1062,11 @@ bool plan_fused(long long N, SPlan* p) {
     // rows in flight during the look-back up to 2^18 points: one MI355X
     // measured 0.7 us faster that way at 2^16 points and 3.7 us slower at 2^20
     p->rows_early = N <= (1ll << 18) ? 1 : 0;
+    // entries per thread in a placing chunk: 3 up to 2,048 points per block
+    // (one chunk of 3,072 holds nearly every block), 6 beyond. Measured on
+    // one MI355X: 26.6 us at 2^16 points with 3 against 30.9 with 6, and at
+    // 2^20 points 59.9 us with 6 against 62.9 to 67.6 with 3, 4 or 5.
+    p->place_per = N <= (long long)p->pblocks * 2048 ? kSPlacePerSmall : kSPlacePer;
     const long long R = pk * tps;
     const long long nb1 = 1ll << b1;
     p->place_lds = (size_t)(4 * ((2 * R + 1) + (pk + kSPassWaves + 2) * nb1));
@@ -1264,7 +1270,9 @@ int run_fused(const float* points, long long N, const SphArgs& a, const SPlan& p
     }
     int rc = s_last_launch();
     if (rc != VOX_OK) return rc;
-    hipExtLaunchKernelGGL(k_sph_place, dim3((unsigned)p.pblocks), dim3(kSPassBlock),
+    hipExtLaunchKernelGGL(p.place_per == kSPlacePerSmall ? k_sph_place<kSPlacePerSmall>
+                                                         : k_sph_place<kSPlacePer>,
+                          dim3((unsigned)p.pblocks), dim3(kSPassBlock),
                           (unsigned)p.place_lds, st, e[2], e[3], 0, N, a, tab, p.b0, p.b1, p.pk,
                           p.nsplit, p.tps, p.rows_early, cm, swords, srows, gh, state, done,
                           offsets, order,
