@@ -512,7 +512,8 @@ __global__ __launch_bounds__(kSBlock) void k_sph_lowpart(
     const float4* __restrict__ pts, long long N, SphArgs a, const SphHeader* __restrict__ tab,
     int b0, int b1, int* __restrict__ voxel_of, unsigned* __restrict__ cm,
     unsigned* __restrict__ swords, float4* __restrict__ srows, unsigned* __restrict__ ghist,
-    unsigned* __restrict__ state, long long state_words, unsigned* __restrict__ err) {
+    unsigned* __restrict__ state, long long state_words, unsigned* __restrict__ err,
+    int nt_stores) {
     constexpr int T = kSBlock * PER;
     extern __shared__ __align__(16) unsigned lds[];
     __shared__ unsigned h1[kSMaxDigits];
@@ -606,9 +607,28 @@ __global__ __launch_bounds__(kSBlock) void k_sph_lowpart(
         if (srows) tr[pos] = p[k];
     }
     __syncthreads();
-    for (int q = tid; q < (int)kept; q += kSBlock) {
-        swords[base + q] = tw[q];
-        if (srows) srows[base + q] = tr[q];
+    if (nt_stores) {   // block-uniform
+        // streaming stores: on large scans they measured faster than
+        // ordinary ones, the staging slices being read only once, by the
+        // placing kernel
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        for (int q = tid; q < (int)kept; q += kSBlock) {
+            __builtin_nontemporal_store(tw[q], &swords[base + q]);
+            if (srows) {
+                const float4 r = tr[q];
+                v4f x;
+                x.x = r.x;
+                x.y = r.y;
+                x.z = r.z;
+                x.w = r.w;
+                __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(&srows[base + q]));
+            }
+        }
+    } else {
+        for (int q = tid; q < (int)kept; q += kSBlock) {
+            swords[base + q] = tw[q];
+            if (srows) srows[base + q] = tr[q];
+        }
     }
     unsigned* gcopy = ghist + (blockIdx.x % kSHistCopies) * nb1;
     for (int j = tid; j < nb1; j += kSBlock)
@@ -992,7 +1012,7 @@ struct SPlan {
     // two-kernel route (fused = true): low digit b0 bits, high digit b1 bits,
     // pblocks k_sph_place blocks of pk low digits each
     bool fused;
-    int b0, b1, pk, nsplit, tps, pblocks, rows_early, place_per;
+    int b0, b1, pk, nsplit, tps, pblocks, rows_early, place_per, nt_stores;
     size_t off_cm, off_stage, off_rows, place_lds;
 };
 
@@ -1062,6 +1082,9 @@ bool plan_fused(long long N, SPlan* p) {
     // rows in flight during the look-back up to 2^18 points: one MI355X
     // measured 0.7 us faster that way at 2^16 points and 3.7 us slower at 2^20
     p->rows_early = N <= (1ll << 18) ? 1 : 0;
+    // streaming staging stores past 2^18 points: one MI355X measured 1.7 us
+    // faster that way at 2^20 points and 1.3 us slower at 2^16
+    p->nt_stores = N > (1ll << 18) ? 1 : 0;
     // entries per thread in a placing chunk: 3 up to 2,048 points per block
     // (one chunk of 3,072 holds nearly every block), 6 beyond. Measured on
     // one MI355X: 26.6 us at 2^16 points with 3 against 30.9 with 6, and at
@@ -1239,11 +1262,11 @@ void launch_lowpart(const float4* pts, long long N, const SphArgs& a, const SphH
     if (lt)
         hipExtLaunchKernelGGL(k_sph_lowpart<PER, true>, dim3((unsigned)a.ntiles), dim3(kSBlock), lds,
                               st, e0, e1, 0, pts, N, a, tab, p.b0, p.b1, voxel_of, cm, swords, srows,
-                              gh, state, p.state_words, err);
+                              gh, state, p.state_words, err, p.nt_stores);
     else
         hipExtLaunchKernelGGL(k_sph_lowpart<PER, false>, dim3((unsigned)a.ntiles), dim3(kSBlock),
                               lds, st, e0, e1, 0, pts, N, a, tab, p.b0, p.b1, voxel_of, cm, swords,
-                              srows, gh, state, p.state_words, err);
+                              srows, gh, state, p.state_words, err, p.nt_stores);
 }
 
 int run_fused(const float* points, long long N, const SphArgs& a, const SPlan& p,
