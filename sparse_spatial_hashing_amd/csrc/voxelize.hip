@@ -1169,7 +1169,7 @@ void k_bins(
     int* __restrict__ coords, int* __restrict__ num_points, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
     unsigned long long* __restrict__ tile_state, long long ntiles, KMap kmap,
-    Header* __restrict__ hdr) {
+    Header* __restrict__ hdr, int nt_out) {
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
     unsigned* running = lds;                     // [G] arrivals so far per pillar
@@ -1341,7 +1341,18 @@ void k_bins(
             for (int u = 0; u < 4; ++u) {
                 if (xx[u] >= rows) continue;
                 const int p = xx[u] / K;
-                voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)] = rw[u];
+                float4* dst = &voxels[(b + ((long long)p << nbits)) * K + (xx[u] - p * K)];
+                if (nt_out) {   // uniform
+                    typedef float v4f __attribute__((ext_vector_type(4)));
+                    v4f x;
+                    x.x = rw[u].x;
+                    x.y = rw[u].y;
+                    x.z = rw[u].z;
+                    x.w = rw[u].w;
+                    __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(dst));
+                } else {
+                    *dst = rw[u];
+                }
             }
         }
     }
@@ -1884,6 +1895,10 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                 int32_t* num_voxels, hipStream_t st, hipEvent_t* ev) {
     const long long ntiles = rank_tiles(P);
     if (pl.part) {
+        // Outputs of 16 MiB and more are written with streaming stores (one
+        // MI355X measured 0.7 us faster that way on a 30.7 MB stack; on
+        // stacks of a few MB it was level or slower).
+        const int nt_out = (double)pl.M * pl.K * sizeof(float4) >= 16.0 * 1024 * 1024 ? 1 : 0;
         // one block per bin; all blocks share the workspace release
         hipExtLaunchKernelGGL(pl.carry ? k_bins<true> : k_bins<false>, dim3((unsigned)pl.nbins),
                               dim3(kBinBlock), (unsigned)pl.lds, st,
@@ -1894,7 +1909,8 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                            bf.kept, bf.compact,
                            (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                            reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
-                           bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr);
+                           bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr,
+                           nt_out);
         return last_launch();
     }
     // lanes per pillar: next power of two >= max(K, 8) (a whole wave if K > 64)
