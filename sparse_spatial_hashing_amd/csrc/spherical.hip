@@ -1114,8 +1114,11 @@ int make_splan(long long N, const int32_t bins[3], const sph_options* opt, SPlan
     const int per_opt = opt ? opt->points_per_thread : 0;
     if (per_opt != 0 && per_opt != 1 && per_opt != 2 && per_opt != 4 && per_opt != 8)
         return VOX_EINVAL;
-    // measured on the 64-beam scan recipe: 2 per thread at 2^16 points, 4 at 2^20
-    p->per = per_opt ? per_opt : (N <= (1ll << 17) ? 2 : N <= (1ll << 21) ? 4 : 8);
+    // measured on the 64-beam scan recipe: 1 per thread at 2^16 points (25.8 us
+    // against 26.4 with 2 and 29.9 with 4), 4 at 2^20 (57.7 us against 59.4
+    // with 2 and 62.8 with 8)
+    p->per = per_opt ? per_opt
+                     : (N <= (1ll << 16) ? 1 : N <= (1ll << 17) ? 2 : N <= (1ll << 21) ? 4 : 8);
     p->tile = kSBlock * p->per;
     p->ntiles = (int)(N > 0 ? s_cdiv(N, p->tile) : 1);
     if (p->ntiles > kSMaxTiles) return VOX_EINVAL;
