@@ -88,11 +88,16 @@ typedef struct vox_options {
                                probe the main table (default) */
     int32_t select_path;    /* route from lookups to rows (the output is the same):
                                1 = per-pillar buckets filled by one device atomic per
-                               point; 2 = partitioned by pillar-id bins in LDS, rows
-                               gathered from the cloud; 3 = partitioned, rows carried
-                               through the workspace's scratch; 0 = automatic: 2 when
-                               K <= 64 and max_voxels <= 262144, else 1. 2 and 3
-                               outside those limits: VOX_EINVAL. */
+                               point; 2 = partitioned by pillar-id bins in LDS after a
+                               rank kernel, rows gathered from the cloud; 3 = as 2, rows
+                               carried through the workspace's scratch; 4 = partitioned
+                               by first-index bins with no rank kernel (pillar ids from
+                               per-tile counts), rows gathered; 0 = automatic: 4 when
+                               K <= 64, the prefix is at most 262,144 points and
+                               K x (its pillar slots per bin) <= 8192, else 2 when
+                               K <= 64 and max_voxels <= 262144, else 1. 2, 3 and 4
+                               outside their limits: VOX_EINVAL. The chunked path
+                               always takes route 2 (or 1). */
     int32_t kept_map;       /* partitioned routes: 0 = rank also writes a map from grid
                                cell to kept pillar (2 bytes per cell when max_voxels
                                <= 65534, else 4; in the workspace's zero part,
@@ -100,6 +105,19 @@ typedef struct vox_options {
                                and lookups past the prefix read it when the grid has
                                at most that many cells; 1 = lookups probe the table.
                                The map is not used with compact_table = 1. */
+    int32_t first_map;      /* route 4: 0 = the claim step writes a map from grid cell to
+                               the cell's lowest prefix index (4 bytes per cell, in the
+                               kept-cell map's region) when the grid has at most
+                               2 x table_slots cells, else it fills the table; 1 = always
+                               the table */
+    int32_t lane_merge;     /* 1 = lanes of a wavefront that fall in the same cell are
+                               merged before the claim atomics (one atomic per distinct
+                               cell per wavefront); 0 = one atomic per point (default) */
+    int32_t bin_ids;        /* route 4: pillar slots per bin (a power of two, 16 to 256,
+                               with max_points x bin_ids <= 8192; 0 = 128, or 256 when
+                               128 would need more than 512 bins and max_points <= 32):
+                               bins = prefix_points / bin_ids rounded up to a power of
+                               two, at most 2048 */
 } vox_options;
 
 /*
@@ -183,7 +201,13 @@ int voxelize_chunked(const float* points, int64_t n_points, const float range[6]
  *                 max_points), else -1 (rejected point, or pillar past the cap).
  *                 Written unless num_voxels reports a VOX_STATUS_* code.
  *   chunked       0: single pass, asynchronous (as voxelize_ex());
- *                 1: the chunked path (as voxelize_chunked(), synchronising).
+ *                 1: the chunked path (as voxelize_chunked(), synchronising);
+ *                 2: automatic: the single pass, then SYNCHRONISES `stream` once
+ *                    to read num_voxels, and only when it reports
+ *                    VOX_STATUS_NEEDS_CHUNKED runs the chunked path (which leaves
+ *                    the final V or status in num_voxels). The single pass leaves
+ *                    the workspace clean, so nothing else is needed between them.
+ *                 Other values: VOX_EINVAL.
  * This is what a consumer needs to send per-pillar results back to points.
  */
 int voxelize_map(const float* points, int64_t n_points, const float range[6],

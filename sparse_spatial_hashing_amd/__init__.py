@@ -53,7 +53,8 @@ class Options(ctypes.Structure):
     _fields_ = [("table_slots", ctypes.c_int64), ("prefix_points", ctypes.c_int64),
                 ("hash", ctypes.c_int32), ("bucket_cap", ctypes.c_int32),
                 ("compact_table", ctypes.c_int32), ("select_path", ctypes.c_int32),
-                ("kept_map", ctypes.c_int32)]
+                ("kept_map", ctypes.c_int32), ("first_map", ctypes.c_int32),
+                ("lane_merge", ctypes.c_int32), ("bin_ids", ctypes.c_int32)]
 
 
 class SphOptions(ctypes.Structure):
@@ -142,12 +143,13 @@ def _check(rc: int, what: str) -> None:
 
 
 def _options(table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
-             compact_table: int = 0, select_path: int = 0, kept_map: int = 0):
-    if not (table_slots or prefix_points or hash or bucket_cap or compact_table or select_path
-            or kept_map):
+             compact_table: int = 0, select_path: int = 0, kept_map: int = 0, first_map: int = 0,
+             lane_merge: int = 0, bin_ids: int = 0):
+    vals = (table_slots, prefix_points, hash, bucket_cap, compact_table, select_path, kept_map,
+            first_map, lane_merge, bin_ids)
+    if not any(vals):
         return None
-    return ctypes.pointer(Options(int(table_slots), int(prefix_points), int(hash), int(bucket_cap),
-                                  int(compact_table), int(select_path), int(kept_map)))
+    return ctypes.pointer(Options(*[int(v) for v in vals]))
 
 
 def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
@@ -158,8 +160,9 @@ def workspace_bytes(n_points: int, max_voxels: int, max_points: int, **opts) -> 
 
 
 def select_route(n_points: int, max_voxels: int, max_points: int, **opts) -> int:
-    """The route a call takes: 1 buckets, 2 partitioned (rows gathered from the
-    cloud), 3 partitioned (rows carried through scratch)."""
+    """The route a single-pass call takes: 1 buckets, 2 partitioned by pillar id
+    (rows gathered from the cloud), 3 as 2 with rows carried through scratch,
+    4 partitioned by first index (no rank kernel)."""
     r = _lib.vox_select_route(int(n_points), int(max_voxels), int(max_points), _options(**opts))
     if r < 0:
         raise VoxError(int(r), "vox_select_route")
@@ -244,6 +247,7 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
              grid: Sequence[int], max_points: int, max_voxels: int, *,
              table_slots: int = 0, prefix_points: int = 0, hash: int = 0, bucket_cap: int = 0,
              compact_table: int = 0, select_path: int = 0, kept_map: int = 0,
+             first_map: int = 0, lane_merge: int = 0, bin_ids: int = 0,
              chunked: bool = False, point_map: bool = False,
              return_device_outputs: bool = False):
     """Pillar / voxel binning of one [N, 4] float32 cloud on the GPU.
@@ -251,15 +255,16 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     Returns ``(voxels[V, K, 4] f32, coords[V, 3] i32 (z, y, x), num_points[V] i32)``
     as views of freshly allocated outputs, and with ``point_map=True`` also
     ``point_pillar[N] i32`` (pillar id of each point's cell when kept, else -1).
-    ``chunked=True`` calls the chunked path directly; otherwise it is used only
-    when the single-pass call reports that the cap could not be decided.
+    ``chunked=True`` calls the chunked path directly; otherwise the library's
+    automatic mode runs the single pass and takes the chunked path only when
+    the single pass reports that the cap could not be decided.
     """
     _check_points(points)
     dev = points.device
     N, K, M = points.shape[0], int(max_points), int(max_voxels)
     kw = dict(table_slots=table_slots, prefix_points=prefix_points, hash=hash,
               bucket_cap=bucket_cap, compact_table=compact_table, select_path=select_path,
-              kept_map=kept_map)
+              kept_map=kept_map, first_map=first_map, lane_merge=lane_merge, bin_ids=bin_ids)
     opts = _options(**kw)
     nbytes = workspace_bytes(N, M, K, **kw)
     zbytes = workspace_zero_bytes(N, M, K, **kw)
@@ -278,11 +283,11 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
                 ctypes.c_void_p(pmap.data_ptr() if pmap is not None else 0),
                 ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                 ctypes.c_void_p(stream), opts]
-        _check(_lib.voxelize_map(*args, 1 if chunked else 0), "voxelize")
+        rc = _lib.voxelize_map(*args, 1 if chunked else 2)
+        if rc not in (VOX_OK, VOX_EINVAL, VOX_EWORKSPACE):
+            _workspaces.drop(dev, stream)  # kernels may have run: the workspace may be dirty
+        _check(rc, "voxelize")
         V = int(nv.item())
-        if V == VOX_STATUS_NEEDS_CHUNKED and not chunked:
-            _check(_lib.voxelize_map(*args, 1), "voxelize (chunked)")
-            V = int(nv.item())
         if V < 0:
             _workspaces.drop(dev, stream)
             raise VoxError(V, "voxelize (device status)")
@@ -332,10 +337,16 @@ def downsample(points: torch.Tensor, range_: Sequence[float], cell: Sequence[flo
                 ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(nv.data_ptr()),
                 ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                 ctypes.c_void_p(stream), opts]
-        _check(_lib.vox_downsample(*args, 1 if chunked else 0), "vox_downsample")
+        rc = _lib.vox_downsample(*args, 1 if chunked else 0)
+        if rc not in (VOX_OK, VOX_EINVAL, VOX_EWORKSPACE):
+            _workspaces.drop(dev, stream)  # kernels may have run: the workspace may be dirty
+        _check(rc, "vox_downsample")
         V = int(nv.item())
         if V == VOX_STATUS_NEEDS_CHUNKED and not chunked:
-            _check(_lib.vox_downsample(*args, 1), "vox_downsample (chunked)")
+            rc = _lib.vox_downsample(*args, 1)
+            if rc not in (VOX_OK, VOX_EINVAL, VOX_EWORKSPACE):
+                _workspaces.drop(dev, stream)
+            _check(rc, "vox_downsample (chunked)")
             V = int(nv.item())
         if V < 0:
             _workspaces.drop(dev, stream)

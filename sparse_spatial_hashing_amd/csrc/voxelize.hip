@@ -256,18 +256,41 @@ __device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsig
 
 // ----------------------------------------------------------------- insert --
 
+// Lanes of the wavefront whose 64-bit value equals this lane's (among lanes
+// with `valid`), over the low nbits bits: match_mask on each half.
+__device__ __forceinline__ unsigned long long match_mask64(unsigned long long v, bool valid,
+                                                           int nbits) {
+    const unsigned long long lo = match_mask((unsigned)v, valid, nbits < 32 ? nbits : 32);
+    if (nbits <= 32) return lo;
+    return lo & match_mask((unsigned)(v >> 32), valid, nbits - 32);
+}
+
+// merge = 1: lanes of a wavefront that fall in the same cell are merged
+// before the atomics ("one atomic per distinct cell per wavefront"): the
+// lowest such lane (the lowest index, lanes follow the input order) claims
+// or lowers the slot for all of them and the others take its slot. kbits
+// is the number of significant key bits (the match costs one ballot each).
 __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pts,
                                                    long long begin, long long end, Grid g,
                                                    unsigned long long* __restrict__ table,
                                                    unsigned S, int hash,
                                                    int* __restrict__ slot_of,
-                                                   Header* __restrict__ hdr, int count_claims) {
+                                                   Header* __restrict__ hdr, int count_claims,
+                                                   int merge, int kbits) {
     const long long i = begin + (long long)blockIdx.x * kBlock + threadIdx.x;
+    const int lane = __lane_id();
     bool claimed = false;
+    const long long key = i < end ? bin_key(pts[i], g) : -1;
+    bool lead = key >= 0;
+    int leader = lane;
+    if (merge) {  // uniform branch: every lane of the wavefront takes part
+        const unsigned long long m = match_mask64((unsigned long long)key, key >= 0, kbits);
+        if (key >= 0) leader = __builtin_ctzll(m);
+        lead = key >= 0 && leader == lane;
+    }
+    int out = -1;
     if (i < end) {
-        int out = -1;
-        const long long key = bin_key(pts[i], g);
-        if (key >= 0) {
+        if (lead) {
             const unsigned long long k1 = (unsigned long long)key + 1ull;
             const unsigned long long mine = slot_word(k1, (unsigned)i);
             unsigned s = home_slot(key, S, hash);
@@ -294,13 +317,36 @@ __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pt
                 }
             }
         }
-        slot_of[i] = out;
     }
+    if (merge) {
+        // the merged lanes take their leader's slot (every lane shuffles)
+        const int ls = __shfl(out, leader);
+        if (key >= 0) out = ls;
+    }
+    if (i < end) slot_of[i] = out;
     if (count_claims) {
         // only the chunked path reads the number of cells; one atomic per wave
         const unsigned long long b = __ballot(claimed);
         if (__lane_id() == 0 && b != 0ull) atomicAdd(&hdr->claims, (unsigned)__popcll(b));
     }
+}
+
+// Direct cell map (grids small enough to index by cell): first[key] holds
+// ~(the lowest prefix index in the cell), 0 while no prefix point fell in it.
+// One non-returning 32-bit atomicMax per valid prefix point, no probing:
+// the larger ~i is the lower index, so the last value is the lowest index.
+// merge as for k_insert (kbits <= 32 here).
+__global__ __launch_bounds__(kBlock) void k_claim(const float4* __restrict__ pts, long long P,
+                                                  Grid g, unsigned* __restrict__ first, int merge,
+                                                  int kbits) {
+    const long long i = (long long)blockIdx.x * kBlock + threadIdx.x;
+    const long long key = i < P ? bin_key(pts[i], g) : -1;
+    bool issue = key >= 0;
+    if (merge) {  // uniform branch
+        const unsigned long long m = match_mask((unsigned)key, key >= 0, kbits);
+        issue = issue && (m & lanes_below(__lane_id())) == 0ull;
+    }
+    if (issue) atomicMax(&first[key], ~(unsigned)i);
 }
 
 // ------------------------------------------------------------------- rank --
@@ -1155,6 +1201,288 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     }
 }
 
+// ------------------------------------------------ first-index route (4) --
+//
+// The same partition without a rank kernel. A pillar is named by i0, the
+// lowest prefix index of its cell, which the claim step leaves in the cell's
+// map entry (direct) or table word (hashed) and which is final once the
+// claim kernel has ended. k_part_fb bins every point of a prefix cell by
+// i0 mod nbins (id within the bin i0 / nbins), as k_part bins by pillar id;
+// points whose cell holds no prefix point belong to no kept pillar (the cap
+// is decided within the prefix) and are dropped. Its prefix tiles also count
+// their first occurrences (points with i0 == i): the tile's count, and each
+// first occurrence's rank inside the tile, with the cell key. A pillar's id,
+// its rank in first-occurrence order, is then the count of the tiles before
+// i0's tile plus i0's rank inside it: k_bins_fb scans the few tile counts
+// itself (every block), keeps the ids below max_voxels and gathers rows as
+// k_bins does. No kernel waits on another block.
+
+// Lookups of a batch of keys in the table (home pair first, then pair by
+// pair with every pending probe of the batch issued together each round).
+// w[k] gets the cell's word, or 0 when the key is absent (or key[k] < 0).
+template <int NB>
+__device__ __forceinline__ void probe_batch(const unsigned long long* __restrict__ look,
+                                            unsigned LS, int hash, const long long key[NB],
+                                            unsigned long long w[NB], Header* __restrict__ hdr) {
+    unsigned h[NB];
+    uint4 q[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        h[k] = home_slot(key[k] >= 0 ? key[k] : 0, LS, hash);
+        q[k] = load_pair(look, h[k]);
+    }
+    bool pend[NB];
+    unsigned cur[NB], seen[NB];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        w[k] = 0ull;
+        pend[k] = false;
+        cur[k] = 0u;
+        seen[k] = 0u;
+        if (key[k] >= 0) {
+            const unsigned long long k1 = (unsigned long long)key[k] + 1ull;
+            if (!pair_settles(q[k], h[k], k1, &w[k])) {
+                pend[k] = true;
+                any = true;
+                const unsigned nx = (h[k] | 1u) + 1u;  // next aligned pair
+                cur[k] = nx == LS ? 0u : nx;
+                seen[k] = 2u - (h[k] & 1u);
+            }
+        }
+    }
+    while (__ballot(any) != 0ull) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+            if (pend[k]) q[k] = load_pair(look, cur[k]);
+        any = false;
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            if (!pend[k]) continue;
+            const unsigned long long k1 = (unsigned long long)key[k] + 1ull;
+            if (pair_settles(q[k], cur[k], k1, &w[k])) {  // cur is even
+                pend[k] = false;
+                continue;
+            }
+            seen[k] += 2u;
+            if (seen[k] >= LS) {  // every slot seen: cannot happen
+                atomicOr(&hdr->error, 1u);
+                w[k] = 0ull;
+                pend[k] = false;
+                continue;
+            }
+            cur[k] = cur[k] + 2u == LS ? 0u : cur[k] + 2u;
+            any = true;
+        }
+    }
+}
+
+// DIRECT: the cell's entry in the direct map `first` (grids of at most
+// 2 S cells); otherwise prefix points read their word through slot_of and
+// later points probe the table. Block layout, ranking by bin, the count
+// table and the staging words are k_part's.
+template <int PER, int BLK, bool DIRECT>
+__global__ __launch_bounds__(BLK) void k_part_fb(
+    const float4* __restrict__ pts, long long N, long long P, Grid g,
+    const unsigned long long* __restrict__ table, unsigned S, int hash,
+    const unsigned* __restrict__ first, int* __restrict__ slot_of, int nbits, long long ptiles,
+    unsigned* __restrict__ cm, unsigned* __restrict__ staging,
+    unsigned long long* __restrict__ fkey, unsigned* __restrict__ frank,
+    unsigned* __restrict__ tile_firsts, Header* __restrict__ hdr,
+    int* __restrict__ point_pillar) {
+    constexpr int TILE = BLK * PER;
+    constexpr int WPB = BLK / kWave;
+    constexpr int BPT = kMaxBins / BLK;
+    constexpr int PER_B = PER < kPartBatch ? PER : kPartBatch;
+    __shared__ unsigned hist[WPB][kMaxBins];
+    __shared__ unsigned wsum[WPB];
+    __shared__ unsigned wfirst[WPB];
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = t / kWave;
+    const long long tile = xcd_tile(blockIdx.x, ptiles);
+    const long long base = tile * TILE;
+    const long long wbase = base + (long long)w * (kWave * PER);
+    const bool any_prefix = base < P;                      // block-uniform
+    const bool any_rest = base + TILE > P && base < N;     // block-uniform
+    const int nbins = 1 << nbits;
+    const unsigned bmask = (unsigned)nbins - 1u;
+    for (int b = t; b < nbins; b += BLK) {
+#pragma unroll
+        for (int ww = 0; ww < WPB; ++ww) hist[ww][b] = 0u;
+    }
+
+    unsigned i0v[PER];             // the point's pillar as its first index, or kNoPid
+    bool isf[PER];                 // a first occurrence (i0 == i)
+    unsigned long long k1v[PER];   // cell key + 1 (first occurrences)
+#pragma unroll
+    for (int k0 = 0; k0 < PER; k0 += PER_B) {
+        long long ii[PER_B];
+        long long key[PER_B];
+        unsigned long long wd[PER_B];  // direct: ~i0 or 0; hashed: the cell's word or 0
+#pragma unroll
+        for (int k = 0; k < PER_B; ++k) {
+            ii[k] = wbase + (long long)(k0 + k) * kWave + lane;
+            key[k] = -1;
+            wd[k] = 0ull;
+        }
+        if (DIRECT) {
+            float4 row[PER_B];
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) {
+                row[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (base < N) row[k] = pts[ii[k] < N ? ii[k] : N - 1];
+            }
+            unsigned f[PER_B];
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) {
+                key[k] = ii[k] < N ? bin_key(row[k], g) : -1;
+                f[k] = key[k] >= 0 ? first[key[k]] : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < PER_B; ++k) wd[k] = f[k];
+        } else {
+            if (any_prefix) {
+                int sl[PER_B];
+                unsigned long long tw[PER_B];
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k) sl[k] = slot_of[ii[k] < P ? ii[k] : P - 1];
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k) {
+                    const bool ok = ii[k] < P && sl[k] >= 0 && (unsigned)sl[k] < S;
+                    tw[k] = table[ok ? sl[k] : 0];
+                    if (!ok) tw[k] = 0ull;
+                }
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    if (ii[k] < P) wd[k] = tw[k];
+            }
+            if (any_rest) {
+                float4 row[PER_B];
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    row[k] = pts[ii[k] < N ? ii[k] : N - 1];
+                long long rk[PER_B];
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    rk[k] = (ii[k] >= P && ii[k] < N) ? bin_key(row[k], g) : -1;
+                unsigned long long rw[PER_B];
+                probe_batch<PER_B>(table, S, hash, rk, rw, hdr);
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    if (ii[k] >= P) wd[k] = rw[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PER_B; ++k) {
+            const long long i = ii[k];
+            unsigned i0 = kNoPid;
+            bool f = false;
+            unsigned long long k1 = 0ull;
+            if (i < N && wd[k] != 0ull) {
+                if (DIRECT) {
+                    i0 = ~(unsigned)wd[k];
+                    k1 = (unsigned long long)key[k] + 1ull;
+                } else {
+                    i0 = (unsigned)(~wd[k] & kIdxMask);
+                    k1 = slot_key1(wd[k]);
+                }
+                if ((long long)i0 >= P) {  // not on a clean workspace
+                    atomicOr(&hdr->error, 4u);
+                    i0 = kNoPid;
+                }
+                f = i < P && (long long)i0 == i;
+            }
+            i0v[k0 + k] = i0;
+            isf[k0 + k] = f;
+            k1v[k0 + k] = k1;
+            // last reader of a prefix point's slot; first occurrences keep
+            // theirs until k_bins_fb has cleared their table slot
+            if (!DIRECT && i < P && !f) slot_of[i] = 0;
+            if (point_pillar && i < N && i0 == kNoPid) point_pillar[i] = -1;
+        }
+    }
+
+    // first occurrences in index order within the wavefront's stretch
+    unsigned fb[PER];
+    unsigned wf = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const unsigned long long bb = __ballot(isf[k]);
+        fb[k] = wf + (unsigned)__popcll(bb & lanes_below(lane));
+        wf += (unsigned)__popcll(bb);
+    }
+    if (lane == 0) wfirst[w] = wf;
+    __syncthreads();  // histograms cleared, wavefront counts in
+
+    // rank among equal bins inside this wavefront's stretch (as k_part)
+    unsigned pos[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const bool valid = i0v[k] != kNoPid;
+        const unsigned bin = valid ? i0v[k] & bmask : 0u;
+        const unsigned long long m = match_mask(bin, valid, nbits);
+        pos[k] = 0u;
+        if (valid) {
+            const unsigned before = hist[w][bin];
+            pos[k] = before + (unsigned)__popcll(m & lanes_below(lane));
+            if ((m & lanes_above(lane)) == 0ull) hist[w][bin] = before + (unsigned)__popcll(m);
+        }
+    }
+    __syncthreads();
+
+    unsigned c[BPT];
+    unsigned mine = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        const int b = t * BPT + q;
+        c[q] = 0u;
+        if (b < nbins) {
+#pragma unroll
+            for (int ww = 0; ww < WPB; ++ww) c[q] += hist[ww][b];
+        }
+        mine += c[q];
+    }
+    unsigned total;
+    unsigned run = block_excl_scan<WPB>(mine, wsum, &total);
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+        const int b = t * BPT + q;
+        if (b < nbins) {
+            cm[(size_t)b * ptiles + tile] = run | (c[q] << 16);
+            unsigned at = run;
+#pragma unroll
+            for (int ww = 0; ww < WPB; ++ww) {
+                const unsigned cw = hist[ww][b];
+                hist[ww][b] = at;
+                at += cw;
+            }
+        }
+        run += c[q];
+    }
+    __syncthreads();
+    unsigned woff = 0, tfirst = 0;
+#pragma unroll
+    for (int ww = 0; ww < WPB; ++ww) {
+        const unsigned x = wfirst[ww];
+        if (ww < w) woff += x;
+        tfirst += x;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (i0v[k] == kNoPid) continue;
+        const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);
+        const unsigned bin = i0v[k] & bmask;
+        staging[base + hist[w][bin] + pos[k]] = ((i0v[k] >> nbits) << 16) | local;
+        if (isf[k]) {
+            const long long i = base + local;
+            frank[i] = woff + fb[k];
+            fkey[i] = k1v[k];
+        }
+    }
+    if (t == 0 && any_prefix) tile_firsts[tile] = tfirst;
+}
+
 // At most 64 VGPRs: two 1024-thread blocks per CU. CARRY: rows come from
 // the copies k_part staged; otherwise the K lowest indices are kept in LDS
 // and the rows gathered from the cloud at the end.
@@ -1364,6 +1692,250 @@ void k_bins(
         if (kmap.p) kmap.put(key, 0u);
         kept_key[pp] = 0;
         if (C > 0) clear_compact(compact, C, kept_cslot, pp, hdr, num_voxels);
+    }
+}
+
+// One block per bin of the first-index route. Pillar slot j of bin b is the
+// cell whose first index is i0 = b + j nbins (when i0 is a first occurrence):
+// its id = (first occurrences in the tiles before i0's) + (i0's rank in its
+// tile), kept when below max_voxels. The walk over the bin's runs, the
+// ranking of arrivals within their pillar and the gather are k_bins'
+// (arrivals of pillars that are not kept are skipped). Every block clears
+// the claim state of its bin's cells; block 0 writes the status.
+constexpr int kScanTiles = 4096;                 // prefix tiles a k_bins_fb block scans, at most
+constexpr int kScanPer = kScanTiles / kBinBlock;
+
+__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8)))
+void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, int K,
+               const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
+               long long ptiles, int ptile, int tshift, int gshift, int nbits,
+               const unsigned* __restrict__ tile_firsts, int ptp,
+               unsigned long long* __restrict__ fkey, const unsigned* __restrict__ frank,
+               unsigned* __restrict__ first, unsigned long long* __restrict__ table, unsigned S,
+               int* __restrict__ slot_of, int gx, int gy, float4* __restrict__ voxels,
+               int* __restrict__ coords, int* __restrict__ num_points,
+               int* __restrict__ num_voxels, int* __restrict__ point_pillar,
+               Header* __restrict__ hdr, int nt_out) {
+    extern __shared__ unsigned lds[];
+    const int G = 1 << gshift;
+    // per-wavefront counts are 16-bit (a wavefront adds at most 64 arrivals
+    // to a slot per round, and the prefixes saturate at 65535: only ranks
+    // below K <= 64 matter); the region first holds the tile prefix
+    const int wwords = 3 * kBinWaves * G / 2 > kScanTiles ? 3 * kBinWaves * G / 2 : kScanTiles;
+    unsigned* running = lds;                     // [G] arrivals so far per pillar slot
+    unsigned* wbuf = running + G;                // [wwords] the tile prefix, then the counts
+    unsigned short* wcnt = reinterpret_cast<unsigned short*>(wbuf);  // [3][kBinWaves * G]
+    unsigned* roff = wbuf + wwords;              // [kBinBlock + 1] run offsets in the group
+    unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock] run start within its tile
+    unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
+    unsigned* pid_of = wsum + kBinWaves;         // [G] pillar id of each slot, kNoPid if none kept
+    unsigned* best = pid_of + G;                 // [G * K] the K lowest indices, in order
+
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = t / kWave;
+    const long long b = xcd_tile(blockIdx.x, gridDim.x);  // contiguous bins per XCD, as k_bins
+    const long long nbins = 1ll << nbits;
+    const int Gb = b < P ? (int)((P - b + nbins - 1) >> nbits) : 0;  // slots with i0 < P
+    // independent loads first: the first group's run words, the tile
+    // counts, and the slot this thread owns (t < Gb)
+    unsigned e = 0u;
+    if ((long long)t < ptiles) e = cm[(size_t)b * ptiles + t];
+    unsigned tc[kScanPer];
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+        const int q = t * kScanPer + u;
+        tc[u] = q < ptp ? tile_firsts[q] : 0u;
+    }
+    const long long i0 = b + ((long long)t << nbits);
+    unsigned long long fk = 0ull;
+    unsigned fr = 0u;
+    int fs = -1;
+    if (t < Gb) {
+        fk = fkey[i0];
+        fr = frank[i0];
+        if (!first) fs = slot_of[i0];
+    }
+    // the error word, read once for the whole block (another block may set
+    // it meanwhile; the status below must be block-uniform)
+    __shared__ unsigned err_sh;
+    if (t == 0) err_sh = __hip_atomic_load(&hdr->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // exclusive prefix of the prefix tiles' first-occurrence counts
+    unsigned s = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) s += tc[u];
+    unsigned distinct_u;
+    unsigned ex = block_excl_scan<kBinWaves>(s, wsum, &distinct_u);
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+        const int q = t * kScanPer + u;
+        if (q < ptp) wbuf[q] = ex;
+        ex += tc[u];
+    }
+    __syncthreads();
+    const long long distinct = distinct_u;
+    const long long V = distinct < M ? distinct : M;
+    int status = (int)V;
+    if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
+    if (err_sh != 0u) status = VOX_STATUS_DEVICE_ERROR;  // written before the scan's barriers
+    if (blockIdx.x == 0 && t == 0) {
+        hdr->status = status;
+        hdr->distinct = (int)distinct;
+        num_voxels[0] = status;
+    }
+    unsigned mypid = kNoPid;
+    if (fk != 0ull) {
+        const unsigned pid = wbuf[i0 >> tshift] + fr;
+        if ((long long)pid >= distinct) report_error(hdr, num_voxels, 4u);  // not on a clean workspace
+        else if (status > 0 && (long long)pid < V) mypid = pid;
+    }
+    if (t < G) pid_of[t] = mypid;
+    // this bin's cells are done with their claim state: return it to zero
+    if (fk != 0ull) {
+        if (first) {
+            first[fk - 1ull] = 0u;
+        } else {
+            if (fs >= 0 && (unsigned)fs < S) table[fs] = 0ull;
+            else report_error(hdr, num_voxels, 16u);
+            slot_of[i0] = 0;
+        }
+        fkey[i0] = 0ull;
+    }
+    if (status <= 0) return;  // block-uniform: nothing kept, or no decision
+    __syncthreads();          // the tile prefix in wbuf is read; pid_of is written
+
+    for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
+    for (int x = t; x < 3 * kBinWaves * G / 2; x += kBinBlock) wbuf[x] = 0u;
+    unsigned round = 0;
+    for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
+        const long long tt = tg + t;
+        if (tg > 0) {
+            e = 0u;
+            if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
+        }
+        unsigned ng;
+        const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
+        roff[t] = ro;
+        rsrc[t] = e & 0xffffu;
+        const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+        __syncthreads();
+        for (unsigned x0 = 0; x0 < ng; x0 += 4u * kBinBlock) {
+            unsigned v[4], idx[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const unsigned x = x0 + (unsigned)(u * kBinBlock + t);
+                v[u] = 0u;
+                idx[u] = 0u;
+                if (x < ng) {
+                    int lo = 0, hi = nruns;
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (roff[mid] <= x) lo = mid;
+                        else hi = mid;
+                    }
+                    const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
+                    v[u] = staging[src];
+                    idx[u] = (unsigned)((tg + lo) * ptile);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const unsigned xr = x0 + (unsigned)(u * kBinBlock);
+                if (xr >= ng) break;  // block-uniform
+                bool valid = xr + (unsigned)t < ng;
+                unsigned pl = v[u] >> 16;
+                const unsigned src = idx[u] + (v[u] & 0xffffu);  // the point's index
+                if (valid && pl >= (unsigned)Gb) {  // not on a clean workspace
+                    report_error(hdr, num_voxels, 4u);
+                    valid = false;
+                }
+                if (valid) {
+                    const unsigned pid = pid_of[pl];
+                    if (point_pillar) point_pillar[src] = pid == kNoPid ? -1 : (int)pid;
+                    valid = pid != kNoPid;  // points of pillars past the cap are dropped
+                }
+                if (!valid) pl = 0u;
+                // counts of three rounds rotate: round r writes buffer r % 3
+                // and clears (r + 1) % 3, last read two rounds ago
+                unsigned short* cur = wcnt + (round % 3u) * (kBinWaves * G);
+                unsigned* nxt = wbuf + ((round + 1u) % 3u) * (kBinWaves * G / 2);
+                for (int y = t; y < kBinWaves * G / 2; y += kBinBlock) nxt[y] = 0u;
+                const unsigned long long m = match_mask(pl, valid, gshift);
+                const unsigned rank = (unsigned)__popcll(m & lanes_below(lane));
+                if (valid && (m & lanes_above(lane)) == 0ull)
+                    cur[w * G + pl] = (unsigned short)__popcll(m);
+                __syncthreads();
+                if (t < G) {
+                    unsigned acc = running[t];
+#pragma unroll
+                    for (int h0 = 0; h0 < kBinWaves; h0 += 8) {
+                        unsigned cw[8];
+#pragma unroll
+                        for (int ww = 0; ww < 8; ++ww) cw[ww] = cur[(h0 + ww) * G + t];
+#pragma unroll
+                        for (int ww = 0; ww < 8; ++ww) {
+                            cur[(h0 + ww) * G + t] = (unsigned short)(acc < 0xffffu ? acc : 0xffffu);
+                            acc += cw[ww];
+                        }
+                    }
+                    running[t] = acc;
+                }
+                __syncthreads();
+                if (valid) {
+                    const unsigned r = (unsigned)cur[w * G + pl] + rank;
+                    if (r < (unsigned)K) best[pl * K + r] = src;
+                }
+                ++round;
+            }
+        }
+    }
+    __syncthreads();
+    // rows of the kept pillars, gathered by index (four in flight per
+    // thread), then zero padding
+    const int rows = Gb * K;
+    for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
+        float4 rw[4];
+        long long dst[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int x = x0 + u * kBinBlock + t;
+            rw[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            dst[u] = -1;
+            if (x < rows) {
+                const int p = x / K;
+                const int r = x - p * K;
+                const unsigned pid = pid_of[p];
+                if (pid != kNoPid) {
+                    dst[u] = (long long)pid * K + r;
+                    if ((unsigned)r < running[p]) {
+                        const unsigned vv = best[p * K + r];
+                        if (vv < N) rw[u] = pts[vv];
+                        else report_error(hdr, num_voxels, 8u);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (dst[u] < 0) continue;
+            float4* d = &voxels[dst[u]];
+            if (nt_out) {  // uniform
+                typedef float v4f __attribute__((ext_vector_type(4)));
+                v4f x;
+                x.x = rw[u].x;
+                x.y = rw[u].y;
+                x.z = rw[u].z;
+                x.w = rw[u].w;
+                __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(d));
+            } else {
+                *d = rw[u];
+            }
+        }
+    }
+    if (mypid != kNoPid) {  // t < Gb: this thread's own slot
+        num_points[mypid] = (int)(running[t] < (unsigned)K ? running[t] : (unsigned)K);
+        write_coords(coords, mypid, (long long)(fk - 1ull), gx, gy);
     }
 }
 
@@ -1580,10 +2152,18 @@ struct Plan {
     int part, carry, gshift, nbins, nbits, pper, pblock;
     long long ptiles;
     size_t lds;
+    // first-index route (fb = 1, single pass only): bins of 2^fshift slots,
+    // 2^fbits bins, ptp prefix tiles, fblds bytes of a k_bins_fb block;
+    // merge = lane merge before the claim atomics; first_map = 1 forbids the
+    // direct cell map
+    int fb, fbits, fshift, merge, first_map, kmap_ok;
+    long long ptp;
+    size_t fblds;
     // byte offsets into the workspace; [0, zero_bytes) is zero between calls,
     // [zero_bytes, bytes) is scratch every call writes before reading
     size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf,
-        off_compact, off_kcs, off_map, off_cm, off_stage, off_stage_pt, zero_bytes, bytes;
+        off_compact, off_kcs, off_map, off_fkey, off_cm, off_stage, off_stage_pt, off_frank,
+        off_tfirst, zero_bytes, bytes;
 };
 
 // LDS of one k_bins block for bins of G pillars (plus the selection when rows
@@ -1597,7 +2177,16 @@ inline size_t centroid_lds_bytes(int G) {
     return 16u * (size_t)kBinBlock +
            4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + 3 * G);
 }
-// Clouds of at least this many points carry rows through staging by default.
+// LDS of one k_bins_fb block for bins of G pillar slots
+inline size_t bins_fb_lds_bytes(int G, int K) {
+    const size_t ww = (size_t)3 * kBinWaves * G / 2 > (size_t)kScanTiles
+                          ? (size_t)3 * kBinWaves * G / 2 : (size_t)kScanTiles;
+    return 4u * ((size_t)G + ww + kBinBlock + 1 + kBinBlock + kBinWaves + (size_t)G +
+                 (size_t)G * K);
+}
+constexpr int kFbMaxIds = 256;     // pillar slots per k_bins_fb bin, at most
+constexpr int kFbMaxSel = 8192;    // K x slots per bin, at most (the selection's LDS)
+constexpr int kFbOneRound = 512;   // k_bins_fb blocks that fit the chip at once (2 per CU)
 
 inline bool finite_f(float v) { return isfinite(v); }
 
@@ -1626,8 +2215,14 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         if (opt->table_slots > 0) S = opt->table_slots;
         if (opt->hash < 0 || opt->hash > 2) return VOX_EINVAL;
         if (opt->compact_table < 0 || opt->compact_table > 1) return VOX_EINVAL;
-        if (opt->select_path < 0 || opt->select_path > 3) return VOX_EINVAL;
+        if (opt->select_path < 0 || opt->select_path > 4) return VOX_EINVAL;
         if (opt->kept_map < 0 || opt->kept_map > 1) return VOX_EINVAL;
+        if (opt->select_path == 4 && opt->compact_table) return VOX_EINVAL;
+        if (opt->first_map < 0 || opt->first_map > 1) return VOX_EINVAL;
+        if (opt->lane_merge < 0 || opt->lane_merge > 1) return VOX_EINVAL;
+        if (opt->bin_ids != 0 && (opt->bin_ids < 16 || opt->bin_ids > kFbMaxIds ||
+                                  (opt->bin_ids & (opt->bin_ids - 1))))
+            return VOX_EINVAL;
         hash = opt->hash;
         P = opt->prefix_points;
         if (opt->bucket_cap > 0 && K <= kSortLanes) {
@@ -1703,6 +2298,40 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
         cap = 0;  // no buckets
     }
     pl->cap = cap;
+    // First-index route: bins of pillar slots i0 = b + j * bins for i0 < P,
+    // about bin_ids slots per bin; each k_bins_fb block scans the counts of
+    // the ptp prefix tiles itself.
+    pl->fb = 0;
+    pl->fbits = 0;
+    pl->fshift = 0;
+    pl->ptp = 0;
+    pl->fblds = 0;
+    pl->merge = opt ? opt->lane_merge : 0;
+    pl->first_map = opt ? opt->first_map : 0;
+    if (pl->part && !pl->carry && (path == 0 || path == 4) && !pl->C) {
+        // default: 128 slots per bin, or 256 when 128 would need more bins
+        // than the chip runs at once and the selection still fits the LDS
+        const long long Pw = P > 0 ? P : 1;
+        long long ids = 128;
+        if (opt && opt->bin_ids) ids = opt->bin_ids;
+        else if (cdiv(Pw, 128) > kFbOneRound && 256ll * K <= kFbMaxSel) ids = 256;
+        int fbits = 0;
+        while ((1ll << fbits) < cdiv(Pw, ids) && (1 << fbits) < kMaxBins) ++fbits;
+        int fshift = 0;
+        while ((1ll << fshift) < cdiv(Pw, 1ll << fbits)) ++fshift;
+        const long long tile = (long long)pl->pblock * pl->pper;
+        const long long ptp = P > 0 ? cdiv(P, tile) : 0;  // tiles that write a count
+        const bool ok = (1 << fshift) <= kFbMaxIds && (long long)K << fshift <= kFbMaxSel &&
+                        ptp <= kScanTiles;
+        if (ok) {
+            pl->fb = 1;
+            pl->fbits = fbits;
+            pl->fshift = fshift;
+            pl->ptp = ptp;
+            pl->fblds = bins_fb_lds_bytes(1 << fshift, K);
+        }
+    }
+    if (path == 4 && !pl->fb) return VOX_EINVAL;
     size_t off = sizeof(Header);
     pl->off_table = off;
     off = align256(off + (size_t)S * sizeof(unsigned long long));
@@ -1726,18 +2355,34 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     off = align256(off + (pl->C > 0 ? (size_t)M * sizeof(int) : 0));
     // the kept-cell map: 2 S cells of 4 bytes (the table's own size), used
     // when the grid has at most that many cells
-    pl->mapn = (pl->part && pl->C == 0 && !(opt && opt->kept_map == 1)) ? 2 * S : 0;
+    // (the first-index route's direct cell map, 4 bytes per cell, shares it:
+    // each route leaves the region zero)
+    const bool kmap_ok = pl->part && pl->C == 0 && !(opt && opt->kept_map == 1);
+    const bool dmap_ok = pl->fb && !pl->first_map;
+    pl->kmap_ok = kmap_ok ? 1 : 0;
+    pl->mapn = (kmap_ok || dmap_ok) ? 2 * S : 0;
     pl->off_map = off;
     off = align256(off + (size_t)pl->mapn * sizeof(unsigned));
+    // first-index route: the cell key + 1 of each first occurrence in [0, P)
+    pl->off_fkey = off;
+    off = align256(off + (pl->fb ? (size_t)(P > 0 ? P : 1) * sizeof(unsigned long long) : 0));
     pl->zero_bytes = off;  // the scratch tail starts here
     pl->off_cm = off;
-    off = align256(off + (size_t)pl->nbins * (size_t)pl->ptiles * sizeof(unsigned));
+    const long long cm_bins = pl->fb && (1ll << pl->fbits) > pl->nbins ? (1ll << pl->fbits)
+                                                                        : pl->nbins;
+    off = align256(off + (size_t)cm_bins * (size_t)pl->ptiles * sizeof(unsigned));
     pl->off_stage = off;
     off = align256(off + (size_t)pl->ptiles * (size_t)(pl->pblock * pl->pper) * sizeof(unsigned));
     pl->off_stage_pt = off;
     off = align256(off + (pl->carry ? (size_t)pl->ptiles * (size_t)(pl->pblock * pl->pper) *
                                           sizeof(float4)
                                     : 0));
+    // first-index route: each first occurrence's rank in its tile, and each
+    // prefix tile's count of first occurrences
+    pl->off_frank = off;
+    off = align256(off + (pl->fb ? (size_t)(P > 0 ? P : 1) * sizeof(unsigned) : 0));
+    pl->off_tfirst = off;
+    off = align256(off + (pl->fb ? (size_t)pl->ptp * sizeof(unsigned) : 0));
     pl->bytes = off;
     return VOX_OK;
 }
@@ -1794,6 +2439,12 @@ struct Buffers {
     unsigned* stage;
     float4* stage_pt;
     KMap kmap;  // the kept-cell map (p null when the grid does not fit it)
+    // first-index route: the direct cell map (null: the table is used),
+    // first occurrences' keys and ranks, prefix tiles' counts
+    unsigned* first;
+    unsigned long long* fkey;
+    unsigned* frank;
+    unsigned* tfirst;
 };
 
 Buffers carve(void* ws, const Plan& pl, const Grid& g) {
@@ -1815,9 +2466,24 @@ Buffers carve(void* ws, const Plan& pl, const Grid& g) {
     x.stage_pt = reinterpret_cast<float4*>(b + pl.off_stage_pt);
     const long long cells = (long long)g.gx * g.gy * g.gz;
     // no map when the prefix holds every point: nothing would look it up
-    x.kmap.p = (pl.mapn > 0 && cells <= pl.mapn && pl.P < pl.N) ? b + pl.off_map : nullptr;
+    x.kmap.p = (pl.kmap_ok && pl.mapn > 0 && cells <= pl.mapn && pl.P < pl.N) ? b + pl.off_map
+                                                                               : nullptr;
     x.kmap.narrow = pl.M <= 65534 ? 1 : 0;
+    x.first = (pl.fb && !pl.first_map && pl.mapn > 0 && cells <= pl.mapn)
+                  ? reinterpret_cast<unsigned*>(b + pl.off_map) : nullptr;
+    x.fkey = reinterpret_cast<unsigned long long*>(b + pl.off_fkey);
+    x.frank = reinterpret_cast<unsigned*>(b + pl.off_frank);
+    x.tfirst = reinterpret_cast<unsigned*>(b + pl.off_tfirst);
     return x;
+}
+
+// Significant bits of a grid's cell keys (the lane merge matches on them).
+inline int key_bits(const Grid& g) {
+    const unsigned long long cells =
+        (unsigned long long)g.gx * (unsigned long long)g.gy * (unsigned long long)g.gz;
+    int b = 1;
+    while (b < 64 && (1ull << b) < cells) ++b;
+    return b;
 }
 
 int last_launch() {
@@ -1838,7 +2504,66 @@ int launch_insert(const float* points, long long begin, long long end, const Gri
     const unsigned blocks = (unsigned)(n > 0 ? cdiv(n, kBlock) : 1);
     hipExtLaunchKernelGGL(k_insert, dim3(blocks), dim3(kBlock), 0, st, ev_start(ev), ev_stop(ev), 0,
                        reinterpret_cast<const float4*>(points), begin, end, g, bf.table,
-                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr, count_claims);
+                       (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr, count_claims, pl.merge,
+                       key_bits(g));
+    return last_launch();
+}
+
+// First-index route, steps 1-3: the claim (direct map or table), the
+// partition, the bins.
+int launch_claim_fb(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
+                    hipStream_t st, hipEvent_t* ev) {
+    if (!bf.first) return launch_insert(points, 0, pl.P, g, pl, bf, st, 0, ev);
+    const unsigned blocks = (unsigned)(pl.P > 0 ? cdiv(pl.P, kBlock) : 1);
+    hipExtLaunchKernelGGL(k_claim, dim3(blocks), dim3(kBlock), 0, st, ev_start(ev), ev_stop(ev), 0,
+                          reinterpret_cast<const float4*>(points), pl.P, g, bf.first, pl.merge,
+                          key_bits(g));
+    return last_launch();
+}
+
+template <int PER, int BLK>
+int launch_part_fb_t(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
+                     int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
+    if (bf.first)
+        hipExtLaunchKernelGGL(k_part_fb<PER, BLK, true>, dim3((unsigned)pl.ptiles), dim3(BLK), 0, st,
+                              ev_start(ev), ev_stop(ev), 0, reinterpret_cast<const float4*>(points),
+                              pl.N, pl.P, g, bf.table, (unsigned)pl.S, pl.hash, bf.first,
+                              bf.slot_of, pl.fbits, pl.ptiles, bf.cm, bf.stage, bf.fkey, bf.frank,
+                              bf.tfirst, bf.hdr, point_pillar);
+    else
+        hipExtLaunchKernelGGL(k_part_fb<PER, BLK, false>, dim3((unsigned)pl.ptiles), dim3(BLK), 0,
+                              st, ev_start(ev), ev_stop(ev), 0,
+                              reinterpret_cast<const float4*>(points), pl.N, pl.P, g, bf.table,
+                              (unsigned)pl.S, pl.hash, bf.first, bf.slot_of, pl.fbits, pl.ptiles,
+                              bf.cm, bf.stage, bf.fkey, bf.frank, bf.tfirst, bf.hdr, point_pillar);
+    return last_launch();
+}
+
+int launch_part_fb(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
+                   int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
+    switch (pl.pper) {
+        case 2: return launch_part_fb_t<2, kBlock>(points, g, pl, bf, point_pillar, st, ev);
+        case 4: return launch_part_fb_t<4, kWideBlock>(points, g, pl, bf, point_pillar, st, ev);
+        case 8: return launch_part_fb_t<8, kWideBlock>(points, g, pl, bf, point_pillar, st, ev);
+        case 16: return launch_part_fb_t<16, kWideBlock>(points, g, pl, bf, point_pillar, st, ev);
+        default: return launch_part_fb_t<1, kBlock>(points, g, pl, bf, point_pillar, st, ev);
+    }
+}
+
+int launch_bins_fb(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
+                   float* voxels, int32_t* coords, int32_t* num_points, int32_t* num_voxels,
+                   int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
+    const int nt_out = (double)pl.M * pl.K * sizeof(float4) >= 16.0 * 1024 * 1024 ? 1 : 0;
+    const long long tile = (long long)pl.pblock * pl.pper;
+    int tshift = 0;
+    while ((1ll << tshift) < tile) ++tshift;
+    hipExtLaunchKernelGGL(k_bins_fb, dim3(1u << pl.fbits), dim3(kBinBlock), (unsigned)pl.fblds, st,
+                          ev_start(ev), ev_stop(ev), 0, reinterpret_cast<const float4*>(points),
+                          pl.N, pl.P, pl.M, pl.K, bf.cm, bf.stage, pl.ptiles, (int)tile, tshift,
+                          pl.fshift, pl.fbits, bf.tfirst, (int)pl.ptp, bf.fkey, bf.frank, bf.first,
+                          bf.table, (unsigned)pl.S, bf.slot_of, g.gx, g.gy,
+                          reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
+                          point_pillar, bf.hdr, nt_out);
     return last_launch();
 }
 
@@ -1953,6 +2678,14 @@ int run_pipeline(const float* points, const Grid& g, const Plan& pl, const Buffe
                  float* voxels, int32_t* coords, int32_t* num_points, int32_t* num_voxels,
                  int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
     int rc;
+    if (pl.fb) {  // three kernels: no rank stage (its events are left unrecorded)
+        if ((rc = launch_claim_fb(points, g, pl, bf, st, ev)) != VOX_OK) return rc;
+        if ((rc = launch_part_fb(points, g, pl, bf, point_pillar, st, ev ? ev + 4 : nullptr)) !=
+            VOX_OK)
+            return rc;
+        return launch_bins_fb(points, g, pl, bf, voxels, coords, num_points, num_voxels,
+                              point_pillar, st, ev ? ev + 6 : nullptr);
+    }
     if ((rc = launch_insert(points, 0, pl.P, g, pl, bf, st, 0, ev ? ev : nullptr)) != VOX_OK)
         return rc;
     if ((rc = launch_rank(pl.P, pl, bf, num_voxels, st, ev ? ev + 2 : nullptr)) != VOX_OK)
@@ -2053,7 +2786,7 @@ int32_t vox_select_route(int64_t n_points, int32_t max_voxels, int32_t max_point
     Plan pl;
     const int rc = make_plan(n_points, max_voxels, max_points, options, &pl);
     if (rc != VOX_OK) return rc;
-    return pl.part ? (pl.carry ? 3 : 2) : 1;
+    return pl.fb ? 4 : pl.part ? (pl.carry ? 3 : 2) : 1;
 }
 
 int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,
@@ -2116,10 +2849,20 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
                      &pl);
     if (rc != VOX_OK) return rc;
     if (n_points > 0 && point_pillar && ((uintptr_t)point_pillar & 3u)) return VOX_EINVAL;
+    if (chunked < 0 || chunked > 2) return VOX_EINVAL;
     const Buffers bf = carve(workspace, pl, g);
-    if (!chunked)
-        return run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels,
-                            point_pillar, stream, nullptr);
+    if (chunked != 1) {
+        rc = run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels,
+                          point_pillar, stream, nullptr);
+        if (rc != VOX_OK || chunked == 0) return rc;
+        // automatic: read the status; only an undecided cap takes the chunked path
+        int32_t status = 0;
+        hipError_t e = hipMemcpyAsync(&status, num_voxels, sizeof(status), hipMemcpyDeviceToHost,
+                                      stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+        if (status != VOX_STATUS_NEEDS_CHUNKED) return VOX_OK;
+    }
     long long done = 0;
     if ((rc = insert_chunked(points, g, pl, bf, stream, &done)) != VOX_OK) return rc;
     Plan p2 = pl;
@@ -2233,6 +2976,7 @@ int vox_profile_stages(const float* points, int64_t n_points, const float range[
             hipEvent_t* e = ev + (size_t)it * nev;
             for (int s = 0; s < VOX_NUM_STAGES; ++s) {
                 float ms = 0;
+                if (pl.fb && s == 1) continue;  // the first-index route has no rank kernel
                 const hipError_t he = hipEventElapsedTime(&ms, e[2 * s], e[2 * s + 1]);
                 if (he != hipSuccess) {
                     rc = hip_fail(he);

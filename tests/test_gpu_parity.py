@@ -64,7 +64,9 @@ def test_workspace_all_zero_after_calls_of_different_shapes():
     seq = [("tiny", None, {}), ("kitti_frame", 40000, {}), ("voxel3d", 60000, {}),
            ("kitti_frame", 40000, dict(select_path=1)), ("uniform_25k", None, {}),
            ("kitti_frame", 9000, {}), ("voxel3d", 3000, dict(select_path=1)),
-           ("voxel3d", 3000, {})]
+           ("voxel3d", 3000, {}), ("kitti_frame", 40000, dict(first_map=1)),
+           ("kitti_frame", 40000, dict(select_path=2)), ("tiny", None, dict(lane_merge=1)),
+           ("dense_multisweep", None, {}), ("kitti_frame", None, dict(prefix_points=1000))]
     for name, n, kw in seq:
         cfg = get_config(name)
         p = cfg.params
@@ -195,13 +197,25 @@ def test_seeded_fuzz_small_problems():
     rng = np.random.default_rng(2024)
     for t in range(120):
         pts, prm = _random_problem(rng)
-        # every select route: automatic (2 here), buckets, gathered, carried
-        # (the partitioned ones exist for K <= 64)
-        path = (0, 1, 2, 3)[t % 4]
+        # every select route: automatic (4 where it applies), buckets,
+        # pillar-id partition gathered and carried, first-index partition
+        # (the partitioned ones exist for K <= 64); the first-index route with
+        # the direct cell map and with the table, and with merged lanes
+        path = (0, 1, 2, 3, 4)[t % 5]
         if prm[3] > 64 and path >= 2:
             path = 1
-        say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]} path={path}")
-        got = gpu_vox(pts, prm, point_map=True, select_path=path)
+        kw = dict(select_path=path)
+        if path in (0, 4) and (t // 5) % 2 == 1:
+            kw["first_map"] = 1
+        if (t // 10) % 2 == 1:
+            kw["lane_merge"] = 1
+        if path == 4:
+            try:
+                vox.select_route(pts.shape[0], prm[4], prm[3], **kw)
+            except vox.VoxError:   # prefix or K past the route's limits
+                kw["select_path"] = 0
+        say(f"fuzz case {t}: N={pts.shape[0]} grid={prm[2]} K={prm[3]} M={prm[4]} {kw}")
+        got = gpu_vox(pts, prm, point_map=True, **kw)
         want = oracle.voxelize_map(pts, *prm)
         assert_bitwise(got[:3], want[:3], f"fuzz {t}")
         assert np.array_equal(got[3], want[3]), f"fuzz {t}: point map differs"
@@ -239,9 +253,39 @@ def test_result_independent_of_table_and_hash(name):
                dict(select_path=1, table_slots=3 * M, hash=2), dict(select_path=2),
                dict(select_path=3), dict(select_path=3, compact_table=1),
                dict(kept_map=1), dict(kept_map=1, select_path=3),
-               dict(table_slots=3 * M), dict(table_slots=3 * M, hash=1, kept_map=1)):
+               dict(table_slots=3 * M), dict(table_slots=3 * M, hash=1, kept_map=1),
+               dict(select_path=4), dict(first_map=1), dict(first_map=1, hash=1),
+               dict(first_map=1, table_slots=3 * M, hash=2), dict(lane_merge=1),
+               dict(lane_merge=1, first_map=1), dict(lane_merge=1, select_path=2),
+               dict(bin_ids=16), dict(bin_ids=32), dict(bin_ids=64, first_map=1),
+               dict(table_slots=3 * M, bin_ids=16)):
         say(f"invariance {name} {kw}")
         assert_bitwise(gpu_vox(pts, params_of(cfg), **kw), want, f"{name} {kw}")
+
+
+def test_two_streams_at_once():
+    """Calls on two default-priority streams, each with its own workspace,
+    run concurrently and both equal the oracle."""
+    jobs = []
+    for name in ("kitti_frame", "voxel3d"):
+        cfg = get_config(name)
+        p = cfg.params
+        pts, _ = generate(name)
+        jobs.append((name, cfg, pts, torch.from_numpy(pts).to(DEV),
+                     vox.Voxelizer(pts.shape[0], p.range_, p.cell, p.grid, p.max_points,
+                                   p.max_voxels, device=DEV)))
+    streams = [torch.cuda.Stream(device=DEV) for _ in jobs]
+    torch.cuda.synchronize()
+    say("two streams x 20 calls")
+    for _ in range(20):
+        for (name, cfg, pts, x, v), st in zip(jobs, streams):
+            with torch.cuda.stream(st):
+                v.run(x)
+    torch.cuda.synchronize()
+    for name, cfg, pts, x, v in jobs:
+        assert vox.workspace_is_clean(v.workspace, v.zero_bytes), f"{name}: workspace dirty"
+        assert_bitwise(tuple(t.cpu().numpy() for t in v.outputs()),
+                       oracle.voxelize_params(pts, cfg.params), f"{name} on its own stream")
 
 
 @pytest.mark.parametrize("name", ["kitti_frame", "tiny", "voxel3d"])
@@ -252,6 +296,7 @@ def test_small_prefix_and_chunked_path(name):
     pts, _ = generate(name)
     want = oracle.voxelize_params(pts, cfg.params)
     for kw in (dict(prefix_points=4096), dict(prefix_points=1), dict(chunked=True),
+               dict(prefix_points=4096, first_map=1), dict(prefix_points=1000, select_path=2),
                dict(chunked=True, table_slots=2 * cfg.params.max_voxels),
                dict(prefix_points=4096, compact_table=1), dict(chunked=True, compact_table=1),
                dict(chunked=True, select_path=1), dict(chunked=True, select_path=3)):

@@ -70,9 +70,11 @@ def test_workspace_bytes_bucket_cap_option():
 
 
 def test_compact_table_option():
-    # the compact table replaces the kept-cell map (which it turns off)
+    # the compact table replaces the kept-cell map (which it turns off) and
+    # the first-index route (whose direct cell map shares the map's region)
     assert vox.workspace_bytes(1000, 100, 32, compact_table=1) > \
-        vox.workspace_bytes(1000, 100, 32, kept_map=1)
+        vox.workspace_bytes(1000, 100, 32, kept_map=1, select_path=2)
+    assert vox.select_route(1000, 100, 32, compact_table=1) == 2
     assert vox.plan(1000, 100, 32)["prefix_points"] == 200   # min(N, 2 max_voxels, S/4)
     assert vox.plan(1000, 100, 32, table_slots=400)["prefix_points"] == 100   # S/4
     assert vox.plan(150, 100, 32)["prefix_points"] == 150   # N
@@ -85,8 +87,8 @@ def test_kept_map_option():
     on the partitioned routes; kept_map=1 leaves it out; the bucket route never
     has it."""
     S = vox.plan(122880, 12000, 32)["table_slots"]
-    with_map = vox.workspace_zero_bytes(122880, 12000, 32)
-    without = vox.workspace_zero_bytes(122880, 12000, 32, kept_map=1)
+    with_map = vox.workspace_zero_bytes(122880, 12000, 32, select_path=2)
+    without = vox.workspace_zero_bytes(122880, 12000, 32, select_path=2, kept_map=1)
     assert with_map - without >= 8 * S
     assert vox.workspace_zero_bytes(122880, 12000, 32, select_path=1) == \
         vox.workspace_zero_bytes(122880, 12000, 32, select_path=1, kept_map=1)
@@ -145,18 +147,39 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_select_path_option_limits():
-    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 262144)."""
+    """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 262144),
+    4 = first-index partition (K <= 64, prefix <= 262144 points, K x slots per
+    bin <= 8192)."""
     auto = vox.workspace_bytes(100000, 60000, 32)
-    assert auto == vox.workspace_bytes(100000, 60000, 32, select_path=2)
+    assert auto == vox.workspace_bytes(100000, 60000, 32, select_path=4)
+    assert vox.select_route(100000, 60000, 32) == 4
     assert auto != vox.workspace_bytes(100000, 60000, 32, select_path=1)
+    # the first-index route adds the first occurrences' keys (zero part) and
+    # ranks (scratch) to route 2's layout, which the chunked path still uses
+    assert auto > vox.workspace_bytes(100000, 60000, 32, select_path=2)
+    assert vox.select_route(100000, 60000, 32, select_path=2) == 2
+    # K = 32: bins of 256 slots hold every prefix the partition admits; K = 64
+    # allows 128, so a prefix past 262144 points (2 max_voxels) leaves route 4 out
+    assert vox.select_route(10**6, 262144, 32) == 4
+    assert vox.select_route(10**6, 140000, 64) == 2
+    with pytest.raises(vox.VoxError):
+        vox.workspace_bytes(10**6, 140000, 64, select_path=4)
+    # K = 64: 128 slots per bin x 64 = 8192 selections still fit
+    assert vox.select_route(10**6, 100000, 64) == 4
     assert vox.plan(100000, 60000, 32)["bucket_cap"] == 0          # no buckets
     assert vox.plan(100000, 60000, 32, select_path=1)["bucket_cap"] == 512
     assert vox.workspace_bytes(1000, 262144, 32, select_path=2) > 0
     # K > 64 or more than 262144 pillars: only the bucket route exists
     assert vox.plan(1000, 100, 65)["bucket_cap"] == 0
-    for bad in (dict(select_path=-1), dict(select_path=4)):
+    for bad in (dict(select_path=-1), dict(select_path=5), dict(select_path=4, compact_table=1),
+                dict(first_map=2), dict(lane_merge=2), dict(bin_ids=8), dict(bin_ids=48),
+                dict(bin_ids=512)):
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(1000, 100, 32, **bad)
+    # 256 slots x 64 rows would overflow the selection's LDS
+    with pytest.raises(vox.VoxError):
+        vox.workspace_bytes(1000, 100, 64, bin_ids=256, select_path=4)
+    assert vox.select_route(1000, 100, 32, bin_ids=256) == 4
     assert vox.workspace_bytes(1000, 262144, 64, select_path=2) > 0
     for args in ((1000, 100, 65), (1000, 262145, 32), (1000, 262145, 64)):
         assert vox.workspace_bytes(*args) > 0
@@ -188,13 +211,14 @@ def test_workspace_zero_part():
 
 
 def test_select_route_rules():
-    """Automatic route: partitioned with gathered rows, buckets for K > 64;
-    carried rows only on request."""
-    assert vox.select_route(122880, 12000, 32) == 2
-    assert vox.select_route(1 << 19, 12000, 32) == 2
-    assert vox.select_route(2097152, 60000, 32) == 2
+    """Automatic route: first-index partition with gathered rows, buckets for
+    K > 64; pillar-id partition and carried rows only on request."""
+    assert vox.select_route(122880, 12000, 32) == 4
+    assert vox.select_route(1 << 19, 12000, 32) == 4
+    assert vox.select_route(2097152, 60000, 32) == 4
+    assert vox.select_route(1048576, 40000, 5) == 4
     assert vox.select_route(1000, 100, 65) == 1
-    for p in (1, 2, 3):
+    for p in (1, 2, 3, 4):
         assert vox.select_route(122880, 12000, 32, select_path=p) == p
     # carried rows need room for them in the scratch tail
     assert vox.workspace_bytes(122880, 12000, 32, select_path=3) > \
@@ -322,3 +346,18 @@ def test_sph_reorder_rejects_on_host():
     odd[0] = ctypes.c_void_p((1 << 20) + 4)
     assert lib.sph_reorder(*odd) == vox.VOX_EINVAL
     assert "boundary table" in vox.strerror(vox.SPH_STATUS_BAD_TABLE)
+
+
+def test_voxelize_map_chunked_mode_range():
+    """voxelize_map's chunked argument: 0 single pass, 1 chunked, 2 automatic;
+    anything else is rejected on the host before any HIP call."""
+    lib = vox.library()
+    r = (ctypes.c_float * 6)(0, -1, -3, 1, 1, 1)
+    c = (ctypes.c_float * 3)(0.1, 0.1, 4)
+    g = (ctypes.c_int32 * 3)(10, 20, 1)
+    for bad in (-1, 3):
+        rc = lib.voxelize_map(ctypes.c_void_p(0x1000), 10, r, c, g, 4, 8, ctypes.c_void_p(0x2000),
+                              ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000),
+                              ctypes.c_void_p(0x5000), None, ctypes.c_void_p(0x100000),
+                              ctypes.c_size_t(1 << 30), None, None, bad)
+        assert rc == vox.VOX_EINVAL
