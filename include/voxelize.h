@@ -56,6 +56,7 @@ extern "C" {
 #define VOX_EINVAL -1      /* bad argument (null pointer, bad size, range, cell or grid) */
 #define VOX_EWORKSPACE -2  /* workspace smaller than vox_workspace_bytes() or misaligned */
 #define VOX_EHIP -4        /* a HIP call failed; vox_last_hip_error() returns its code */
+#define VOX_ESCRATCH -5    /* voxelize_static: the call needs more than its 64 MiB array */
 
 /* ---- device status written to num_voxels[0] instead of V ----------------- */
 /* The single-pass path inserts the first P points into
@@ -217,7 +218,39 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
                  size_t workspace_bytes, hipStream_t stream, const vox_options* options,
                  int32_t chunked);
 
-/* The select route a call would take (1, 2 or 3, as select_path above), or
+/*
+ * voxelize() for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same operation, arguments and outputs, with
+ * the workspace taken from an array of 64 MiB (VOX_STATIC_SCRATCH_BYTES)
+ * that the library holds on each GPU it runs on, from the first call there
+ * until the process ends. Calls no hipMalloc, hipFree or other allocating
+ * routine.
+ *   - Size limit: a call whose vox_workspace_bytes(n_points, max_voxels,
+ *     max_points, NULL) exceeds the array returns VOX_ESCRATCH before any HIP
+ *     call (with the defaults: 2,097,152 points at 60,000 pillars need about
+ *     42 MiB).
+ *   - Set-up: the first call on a device takes the array's device address and
+ *     enqueues a kernel that clears it on `stream`; keep that first call out
+ *     of graph capture. Later calls enqueue only the voxelization kernels (and,
+ *     when a larger layout reaches into scratch an earlier call left, or after
+ *     a call that returned VOX_EHIP, one clearing kernel first).
+ *   - Sharing: every call on a GPU uses that GPU's one array, which keeps the
+ *     last call's contents. Calls that overlap on one GPU (two streams or
+ *     two host threads without ordering) race on it and give wrong results:
+ *     order them. Host-side bookkeeping is guarded by a mutex.
+ *   - Status: as voxelize(); an undecided cap (VOX_STATUS_NEEDS_CHUNKED)
+ *     needs voxelize_chunked() with a workspace. After a device error the
+ *     call's last kernel clears the array's zero part itself.
+ * Asynchronous on `stream`; read num_voxels after the stream has completed.
+ */
+#define VOX_STATIC_SCRATCH_BYTES (64ll << 20)
+int voxelize_static(const float* points, int64_t n_points, const float range[6],
+                    const float cell[3], const int32_t grid[3], int32_t max_points,
+                    int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                    int32_t* num_voxels, hipStream_t stream);
+
+/* The select route a single pass would take (1 to 4, as select_path above), or
  * VOX_EINVAL. */
 int32_t vox_select_route(int64_t n_points, int32_t max_voxels, int32_t max_points,
                          const vox_options* options);

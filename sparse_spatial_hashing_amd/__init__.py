@@ -23,6 +23,7 @@ VOX_OK = 0
 VOX_EINVAL = -1
 VOX_EWORKSPACE = -2
 VOX_EHIP = -4
+VOX_ESCRATCH = -5
 VOX_STATUS_NEEDS_CHUNKED = -16
 VOX_STATUS_DEVICE_ERROR = -17
 SPH_STATUS_BAD_TABLE = -18
@@ -93,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.voxelize_map.argtypes = [vp, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp,
                                  op, i32]
     lib.voxelize_map.restype = ctypes.c_int
+    lib.voxelize_static.argtypes = [vp, i64, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.voxelize_static.restype = ctypes.c_int
     lib.vox_plan.argtypes = [i64, i32, i32, op, vp, vp, vp]
     lib.vox_plan.restype = ctypes.c_int
     lib.vox_bin_points.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp]
@@ -296,6 +299,37 @@ def voxelize(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float
     if point_map:
         return voxels[:V], coords[:V], counts[:V], pmap
     return voxels[:V], coords[:V], counts[:V]
+
+
+@torch.no_grad()
+def voxelize_static(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
+                    grid: Sequence[int], max_points: int, max_voxels: int,
+                    voxels: torch.Tensor, coords: torch.Tensor, num_points: torch.Tensor,
+                    num_voxels: torch.Tensor) -> int:
+    """The library's allocation-free entry point: one call into caller-owned
+    outputs (voxels [M,K,4] f32, coords [M,3] i32, num_points [M] i32,
+    num_voxels [1] i32, all on the points' device), with the library's own
+    per-GPU scratch array as the workspace. Enqueued on the current stream;
+    nothing is allocated and nothing synchronised. Returns the C return code
+    (VOX_OK, or VOX_ESCRATCH when the call needs more than the array)."""
+    _check_points(points)
+    dev = points.device
+    N, K, M = points.shape[0], int(max_points), int(max_voxels)
+    for t, shape, dt in ((voxels, (M, K, 4), torch.float32), (coords, (M, 3), torch.int32),
+                         (num_points, (M,), torch.int32), (num_voxels, (1,), torch.int32)):
+        if t.device != dev or tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"output must be a contiguous {dt} tensor of shape {shape} on {dev}")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        r, c, g = _host_params(range_, cell, grid)
+        rc = _lib.voxelize_static(ctypes.c_void_p(points.data_ptr()), N, r, c, g, K, M,
+                                  ctypes.c_void_p(voxels.data_ptr()),
+                                  ctypes.c_void_p(coords.data_ptr()),
+                                  ctypes.c_void_p(num_points.data_ptr()),
+                                  ctypes.c_void_p(num_voxels.data_ptr()), ctypes.c_void_p(stream))
+    if rc not in (VOX_OK, VOX_ESCRATCH):
+        _check(rc, "voxelize_static")
+    return int(rc)
 
 
 def downsample_workspace_bytes(n_points: int, max_voxels: int, **opts) -> Tuple[int, int]:

@@ -54,6 +54,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "voxelize.h"
 
 namespace {
@@ -95,7 +97,8 @@ struct alignas(256) Header {
     int status;                // V, or a VOX_STATUS_* code; written by the last rank tile
     int distinct;              // cells in the table (first occurrences in [0, P))
     unsigned int error;        // nonzero: an internal bound was exceeded (sticky)
-    unsigned int pad[59];
+    unsigned int heal;         // blocks of the last kernel that cleared their share after an error
+    unsigned int pad[58];
 };
 static_assert(sizeof(Header) == 256, "header is 256 bytes");
 
@@ -252,6 +255,41 @@ __device__ __forceinline__ unsigned long long find_word(const unsigned long long
 __device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsigned bit) {
     atomicOr(&hdr->error, bit);
     num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+}
+
+// The error word as this block sees it when it starts: read by one thread
+// and shared through LDS, so that every thread of the block takes the same
+// branch (another block may set the word meanwhile). Contains a barrier.
+__device__ __forceinline__ unsigned block_error(const Header* hdr) {
+    __shared__ unsigned err_sh;
+    if (threadIdx.x == 0)
+        err_sh = __hip_atomic_load(&hdr->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return err_sh;
+}
+
+// A call whose last kernel starts with the error word set returns the whole
+// zero part of its workspace to zero (each block clears a share, so the
+// call's outputs are void, which its status already says), and the last
+// block to get here resets the error word: after a device error the next
+// call finds the workspace ready, with no help from the caller. The final
+// kernels write only zeros into the zero part, so nothing undoes the clear.
+// A block that saw a clear word (set later by another block of this kernel)
+// does not count, so the word then stays set and the next call heals.
+__device__ __forceinline__ void heal_workspace(Header* hdr, long long zero_words, unsigned err) {
+    if (!err) return;
+    unsigned* w = reinterpret_cast<unsigned*>(hdr);
+    const long long nthreads = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)(sizeof(Header) / 4) + (long long)blockIdx.x * blockDim.x +
+                       threadIdx.x;
+         i < zero_words; i += nthreads)
+        w[i] = 0u;
+    if (threadIdx.x == 0 && atomicAdd(&hdr->heal, 1u) == gridDim.x - 1u) {
+        hdr->claims = 0u;
+        hdr->rank_ticket = 0u;
+        hdr->heal = 0u;
+        hdr->error = 0u;
+    }
 }
 
 // ----------------------------------------------------------------- insert --
@@ -761,7 +799,10 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
                                                  int* __restrict__ occ_slot,
                                                  unsigned long long* __restrict__ table, unsigned S,
                                                  unsigned long long* __restrict__ tile_state,
-                                                 long long ntiles, Header* __restrict__ hdr) {
+                                                 long long ntiles, Header* __restrict__ hdr,
+                                                 long long zero_words) {
+    const unsigned err = block_error(hdr);
+    heal_workspace(hdr, zero_words, err);
     const int status = hdr->status;
     const long long distinct = hdr->distinct;
     const long long V = status > 0 ? status : 0;
@@ -770,7 +811,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
     const long long gtid = (long long)blockIdx.x * kBlock + threadIdx.x;
     const long long nwaves = nthreads / kWave;
     const long long gwave = gtid / kWave;
-    if (gtid == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    if (gtid == 0 && err != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
 
     // 1) pillars. Nothing else touches a pillar's counter, bucket or overflow
     //    row, so they are read and cleared here.
@@ -1497,7 +1538,7 @@ void k_bins(
     int* __restrict__ coords, int* __restrict__ num_points, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
     unsigned long long* __restrict__ tile_state, long long ntiles, KMap kmap,
-    Header* __restrict__ hdr, int nt_out) {
+    Header* __restrict__ hdr, int nt_out, long long zero_words) {
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
     unsigned* running = lds;                     // [G] arrivals so far per pillar
@@ -1521,7 +1562,9 @@ void k_bins(
     const int status = hdr->status;
     const long long V = status > 0 ? status : 0;
     const long long distinct = hdr->distinct;
-    if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    const unsigned err = block_error(hdr);
+    heal_workspace(hdr, zero_words, err);
+    if (b == 0 && t == 0 && err != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
     // the release touches nothing below; its memory traffic overlaps the bins.
     // It goes by block index, not by bin: clearing in bin order measured
     // slower in the next call's inserts.
@@ -1711,11 +1754,12 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
                long long ptiles, int ptile, int tshift, int gshift, int nbits,
                const unsigned* __restrict__ tile_firsts, int ptp,
                unsigned long long* __restrict__ fkey, const unsigned* __restrict__ frank,
-               unsigned* __restrict__ first, unsigned long long* __restrict__ table, unsigned S,
+               unsigned* __restrict__ first, unsigned long long cells,
+               unsigned long long* __restrict__ table, unsigned S,
                int* __restrict__ slot_of, int gx, int gy, float4* __restrict__ voxels,
                int* __restrict__ coords, int* __restrict__ num_points,
                int* __restrict__ num_voxels, int* __restrict__ point_pillar,
-               Header* __restrict__ hdr, int nt_out) {
+               Header* __restrict__ hdr, int nt_out, long long zero_words) {
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
     // per-wavefront counts are 16-bit (a wavefront adds at most 64 arrivals
@@ -1756,10 +1800,10 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         fr = frank[i0];
         if (!first) fs = slot_of[i0];
     }
-    // the error word, read once for the whole block (another block may set
-    // it meanwhile; the status below must be block-uniform)
-    __shared__ unsigned err_sh;
-    if (t == 0) err_sh = __hip_atomic_load(&hdr->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the error word, one value for the whole block (the status below must
+    // be block-uniform)
+    const unsigned err = block_error(hdr);
+    heal_workspace(hdr, zero_words, err);
 
     // exclusive prefix of the prefix tiles' first-occurrence counts
     unsigned s = 0;
@@ -1778,7 +1822,7 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     const long long V = distinct < M ? distinct : M;
     int status = (int)V;
     if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
-    if (err_sh != 0u) status = VOX_STATUS_DEVICE_ERROR;  // written before the scan's barriers
+    if (err != 0u) status = VOX_STATUS_DEVICE_ERROR;
     if (blockIdx.x == 0 && t == 0) {
         hdr->status = status;
         hdr->distinct = (int)distinct;
@@ -1794,7 +1838,8 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     // this bin's cells are done with their claim state: return it to zero
     if (fk != 0ull) {
         if (first) {
-            first[fk - 1ull] = 0u;
+            if (fk - 1ull < cells) first[fk - 1ull] = 0u;
+            else report_error(hdr, num_voxels, 16u);  // not on a clean workspace
         } else {
             if (fs >= 0 && (unsigned)fs < S) table[fs] = 0ull;
             else report_error(hdr, num_voxels, 16u);
@@ -1960,7 +2005,7 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     int* __restrict__ coords, int* __restrict__ counts, int* __restrict__ num_voxels,
     int* __restrict__ occ_slot, unsigned long long* __restrict__ table, unsigned S,
     unsigned long long* __restrict__ tile_state, long long ntiles, KMap kmap,
-    Header* __restrict__ hdr) {
+    Header* __restrict__ hdr, long long zero_words) {
     extern __shared__ float4 lds_rows[];
     const int G = 1 << gshift;
     float4* rowbuf = lds_rows;                   // [kBinBlock] this round's rows, by voxel
@@ -1982,7 +2027,9 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     const int status = hdr->status;
     const long long V = status > 0 ? status : 0;
     const long long distinct = hdr->distinct;
-    if (b == 0 && t == 0 && hdr->error != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
+    const unsigned err = block_error(hdr);
+    heal_workspace(hdr, zero_words, err);
+    if (b == 0 && t == 0 && err != 0u) num_voxels[0] = VOX_STATUS_DEVICE_ERROR;
     release_workspace((long long)blockIdx.x * kBinBlock + t, (long long)gridDim.x * kBinBlock,
                       distinct, V, M, occ_slot, table, S, kept_key, compact, C, kept_cslot,
                       tile_state, ntiles, kmap, hdr, num_voxels);
@@ -2561,9 +2608,10 @@ int launch_bins_fb(const float* points, const Grid& g, const Plan& pl, const Buf
                           ev_start(ev), ev_stop(ev), 0, reinterpret_cast<const float4*>(points),
                           pl.N, pl.P, pl.M, pl.K, bf.cm, bf.stage, pl.ptiles, (int)tile, tshift,
                           pl.fshift, pl.fbits, bf.tfirst, (int)pl.ptp, bf.fkey, bf.frank, bf.first,
-                          bf.table, (unsigned)pl.S, bf.slot_of, g.gx, g.gy,
+                          (unsigned long long)g.gx * g.gy * g.gz, bf.table, (unsigned)pl.S,
+                          bf.slot_of, g.gx, g.gy,
                           reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
-                          point_pillar, bf.hdr, nt_out);
+                          point_pillar, bf.hdr, nt_out, (long long)(pl.zero_bytes / 4));
     return last_launch();
 }
 
@@ -2635,7 +2683,7 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                            (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                            reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
                            bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr,
-                           nt_out);
+                           nt_out, (long long)(pl.zero_bytes / 4));
         return last_launch();
     }
     // lanes per pillar: next power of two >= max(K, 8) (a whole wave if K > 64)
@@ -2655,7 +2703,8 @@ int launch_pack(const float* points, long long P, const Grid& g, const Plan& pl,
                        bf.ovf, pl.K, pl.M, seg, bf.kept, bf.compact, (unsigned)pl.C, bf.kcs,
                        g.gx, g.gy,
                        reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
-                       bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr);
+                       bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.hdr,
+                       (long long)(pl.zero_bytes / 4));
     return last_launch();
 }
 
@@ -2751,9 +2800,56 @@ int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& 
                           bf.stage_pt, pl.ptiles, pl.pblock * pl.pper, pl.gshift, pl.nbits, pl.M,
                           bf.kept, bf.compact, (unsigned)pl.C, bf.kcs, g.gx, g.gy,
                           reinterpret_cast<float4*>(centroids), coords, counts, num_voxels,
-                          bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr);
+                          bf.occ, bf.table, (unsigned)pl.S, bf.tiles, ntiles, bf.kmap, bf.hdr,
+                          (long long)(pl.zero_bytes / 4));
     return last_launch();
 }
+
+// Zeroes words [0, n) of p (grid-stride).
+__global__ __launch_bounds__(kBlock) void k_zero(unsigned* __restrict__ p, long long n) {
+    for (long long i = (long long)blockIdx.x * kBlock + threadIdx.x; i < n;
+         i += (long long)gridDim.x * kBlock)
+        p[i] = 0u;
+}
+
+int launch_zero(void* p, size_t lo, size_t hi, hipStream_t st) {
+    if (hi <= lo) return VOX_OK;
+    const long long n = (long long)((hi - lo) / 4);
+    const long long blocks = cdiv(n, kBlock) < 2048 ? cdiv(n, kBlock) : 2048;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                       reinterpret_cast<unsigned*>(static_cast<char*>(p) + lo), n);
+    return last_launch();
+}
+
+}  // namespace
+
+// ------------------------------------------------- allocation-free entry --
+//
+// voxelize_static's scratch: one array of kStaticScratchBytes per GPU, in
+// the library's own code object, which each device that loads the library
+// keeps until the process ends. In host code `scratch` only names the
+// symbol: its device address is taken once per device, with that device
+// current, by hipGetSymbolAddress, and only that address is ever passed on.
+constexpr size_t kStaticScratchBytes = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per device: the array's address, and which bytes may be nonzero. A call
+// leaves [0, its zero part) zero and may leave scratch up to its layout's
+// end, so after calls of several shapes [dlo, dhi) may be dirty; a call
+// whose zero part reaches into it clears that stretch first, as the Python
+// binding does for its cached workspaces. all_dirty: a call stopped
+// between launches (a HIP error), so the whole array is cleared next time.
+struct StaticScratch {
+    void* p;
+    size_t dlo, dhi;
+    bool all_dirty;
+};
+std::mutex g_static_mu;
+StaticScratch g_static[kMaxDevices];
 
 }  // namespace
 
@@ -3007,6 +3103,8 @@ const char* vox_strerror(int32_t code) {
         case VOX_EINVAL: return "invalid argument";
         case VOX_EWORKSPACE: return "workspace too small or not 256-byte aligned";
         case VOX_EHIP: return "HIP runtime error (see vox_last_hip_error)";
+        case VOX_ESCRATCH:
+            return "the call needs more scratch than voxelize_static's array holds";
         case VOX_STATUS_NEEDS_CHUNKED:
             return "cap not decidable in one pass: repeat with voxelize_chunked";
         case VOX_STATUS_DEVICE_ERROR: return "internal device bound exceeded";
@@ -3016,5 +3114,56 @@ const char* vox_strerror(int32_t code) {
 }
 
 int32_t vox_last_hip_error(void) { return g_last_hip_error; }
+
+int voxelize_static(const float* points, int64_t n_points, const float range[6],
+                    const float cell[3], const int32_t grid[3], int32_t max_points,
+                    int32_t max_voxels, float* voxels, int32_t* coords, int32_t* num_points,
+                    int32_t* num_voxels, hipStream_t stream) {
+    Grid g;
+    Plan pl;
+    // argument checks first: nothing touches the GPU on an argument error
+    // (the array's address stands in for the workspace pointer)
+    int rc = check_args(points, n_points, range, cell, grid, voxels, coords, num_points,
+                        num_voxels, static_cast<void*>(&g), &g);
+    if (rc != VOX_OK) return rc;
+    if ((rc = make_plan(n_points, max_voxels, max_points, nullptr, &pl)) != VOX_OK) return rc;
+    if (pl.bytes > kStaticScratchBytes) return VOX_ESCRATCH;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return VOX_EINVAL;
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    StaticScratch& st = g_static[dev];
+    if (!st.p) {
+        // set-up, once per device: the array's device address, and the
+        // whole array cleared (a kernel on the call's stream, no memset)
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        st.p = p;
+        st.all_dirty = true;
+    }
+    if (st.all_dirty) {
+        if ((rc = launch_zero(st.p, 0, kStaticScratchBytes, stream)) != VOX_OK) return rc;
+        st.all_dirty = false;
+        st.dlo = st.dhi = 0;
+    } else if (pl.zero_bytes > st.dlo && st.dhi > st.dlo) {
+        const size_t hi = pl.zero_bytes < st.dhi ? pl.zero_bytes : st.dhi;
+        if ((rc = launch_zero(st.p, st.dlo, hi, stream)) != VOX_OK) {
+            st.all_dirty = true;
+            return rc;
+        }
+    }
+    const Buffers bf = carve(st.p, pl, g);
+    rc = run_pipeline(points, g, pl, bf, voxels, coords, num_points, num_voxels, nullptr, stream,
+                      nullptr);
+    if (rc != VOX_OK) {
+        st.all_dirty = true;  // some kernels may have run without the last one
+        return rc;
+    }
+    if (st.dhi < pl.bytes) st.dhi = pl.bytes;
+    st.dlo = pl.zero_bytes;
+    return VOX_OK;
+}
 
 }  // extern "C"

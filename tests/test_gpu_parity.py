@@ -353,6 +353,35 @@ def test_default_prefix_too_short_takes_the_chunked_route():
     assert_bitwise(tuple(t.cpu().numpy() for t in got), want, "chunked retry")
 
 
+@pytest.mark.parametrize("route", [4, 2, 1])
+def test_device_error_heals_the_workspace(route):
+    """A call whose workspace holds the device error word (set from the
+    host: no valid input reaches it) reports VOX_STATUS_DEVICE_ERROR, returns
+    its zero part to zero itself (a planted nonzero word in an unused table
+    slot included), and the next call on the same workspace is exact."""
+    cfg = get_config("kitti_frame")
+    p = cfg.params
+    pts, _ = generate("kitti_frame")
+    say(f"heal route {route}")
+    v = vox.Voxelizer(pts.shape[0], p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
+                      device=DEV, select_path=route)
+    x = torch.from_numpy(pts).to(DEV)
+    ws = v.workspace
+    ws[16:20] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device=DEV)   # error word
+    # and a stray nonzero byte at the end of the zero part (every kernel
+    # bounds-checks what it reads from there, so it only has to be cleared)
+    end = v.zero_bytes - 4
+    ws[end:end + 4] = torch.tensor([0xAB, 0, 0, 0], dtype=torch.uint8, device=DEV)
+    nv = v.run(x)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == vox.VOX_STATUS_DEVICE_ERROR
+    assert vox.workspace_is_clean(v.workspace, v.zero_bytes), "the error call left it dirty"
+    v.run(x)
+    torch.cuda.synchronize()
+    assert_bitwise(tuple(t.cpu().numpy() for t in v.outputs()),
+                   oracle.voxelize_params(pts, p), f"after healing, route {route}")
+
+
 def test_repeated_calls_identical_and_workspace_zero():
     cfg = get_config("dense_multisweep")
     p = cfg.params

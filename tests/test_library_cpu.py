@@ -27,7 +27,7 @@ def test_header_declares_expected_entry_points():
     for n in ("voxelize", "voxelize_ex", "voxelize_chunked", "vox_workspace_bytes",
               "vox_bin_points", "vox_profile_stages", "vox_strerror", "vox_last_hip_error",
               "vox_stage_name", "vox_plan", "voxelize_map", "sph_table_bytes", "sph_make_table",
-              "sph_workspace_bytes", "sph_reorder", "sph_profile_stages"):
+              "sph_workspace_bytes", "sph_reorder", "sph_profile_stages", "voxelize_static"):
         assert n in names, n
 
 
@@ -361,3 +361,21 @@ def test_voxelize_map_chunked_mode_range():
                               ctypes.c_void_p(0x5000), None, ctypes.c_void_p(0x100000),
                               ctypes.c_size_t(1 << 30), None, None, bad)
         assert rc == vox.VOX_EINVAL
+
+
+def test_voxelize_static_size_limit_rejected_on_host():
+    """The allocation-free entry point refuses a call whose layout exceeds its
+    64 MiB array with VOX_ESCRATCH, and bad arguments with VOX_EINVAL, before
+    any HIP call (so this runs without a GPU)."""
+    lib = vox.library()
+    r = (ctypes.c_float * 6)(0, -40, -3, 70, 40, 1)
+    c = (ctypes.c_float * 3)(0.1, 0.1, 4)
+    g = (ctypes.c_int32 * 3)(700, 800, 1)
+    n, M, K = 20_000_000, 60000, 32
+    assert vox.workspace_bytes(n, M, K) > (64 << 20)
+    args = [ctypes.c_void_p(0x1000), n, r, c, g, K, M, ctypes.c_void_p(0x2000),
+            ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000), None]
+    assert lib.voxelize_static(*args) == vox.VOX_ESCRATCH
+    assert "scratch" in vox.strerror(vox.VOX_ESCRATCH)
+    args[7] = None  # null output
+    assert lib.voxelize_static(*args) == vox.VOX_EINVAL
