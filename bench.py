@@ -2,20 +2,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 
-A step is one complete voxelize call (insert, rank, select, pack) over one
-synthetic cloud already resident in HBM, outputs and workspace pre-allocated.
-W untimed steps, then K steps timed with HIP events on the call's stream,
-bracketed by device synchronisation (the page's protocol: mean over timed
-iterations after warm-up, inputs on the GPU). Prints one JSON line.
+A step is one complete voxelize call (claim, partition, bins on the default
+route; insert, rank, select, pack on the others) over one synthetic cloud
+already resident in HBM, outputs and workspace pre-allocated. W untimed
+steps, then K steps timed with HIP events on the call's stream, bracketed by
+device synchronisation (the page's protocol: mean over timed iterations
+after warm-up, inputs on the GPU). Prints one JSON line on stdout.
 
-* value: Mpoints/s = N / (time per call), N counting every input point.
+* value: Mpoints/s = N / (mean time per call), N counting every input point.
+* timing: mean, median, p10 and p90 of per-call HIP event times, and the
+  wall time per call including the read-back of V to the host.
 * roofline: the dominant kernel (largest mean stage time, measured live with
-  HIP events between the stages) against MI355X's 8 TB/s HBM peak, using the
-  kernel's algorithmic bytes per launch.
-* cpu_baseline: the CPU oracle (one thread) on the same cloud on this host.
-* --all: one extra JSON line per workload (to stderr) for the results table:
-  voxel-grid downsampling, spherical binning + reorder, then voxelization.
-* --spherical: only the spherical binning + reorder lines (stderr).
+  HIP events around each kernel) against MI355X's 8 TB/s HBM peak, using the
+  kernel's algorithmic bytes per launch; `bound` says what limits it.
+* cpu_baseline: the C oracle (one thread) on the same cloud on this host,
+  with the NumPy sort-then-segment brute force timed beside it, the CPU
+  model and the process affinity.
+* By default one extra JSON line per voxelization workload goes to stderr
+  (every config of the benchmark set); --all adds downsampling and the
+  spherical reorder, --spherical only the latter.
 """
 from __future__ import annotations
 
@@ -43,13 +48,18 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--all", action="store_true",
+                    help="also time downsampling and the spherical reorder (stderr)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload voxelization lines (stderr)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
     ap.add_argument("--spherical", action="store_true",
                     help="also time the spherical binning and reorder per workload (stderr)")
     ap.add_argument("--profile-iters", type=int, default=50)
+    ap.add_argument("--options", default="{}",
+                    help="voxelize options as JSON, e.g. '{\"lane_merge\": 1}' (A/B under a profiler)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run 10 plain device copies of this many MiB (counter calibration)")
     ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
@@ -106,22 +116,28 @@ def rocprof_summary(root):
     print("\n".join(out))
 
 
-def algorithmic_bytes(N, P, V, K, rows, kept, route):
+def algorithmic_bytes(N, P, V, K, rows, kept, staged, route):
     """Compulsory bytes of the whole call and of each kernel.
 
     whole call: read every point once (16 B) + write the dense output,
     V * (16 K + 16) bytes (rows incl. zero padding, 12 B coords, 4 B count).
     insert: its share of the input read, 16 B per prefix point.
-    rank:   4 B per prefix point (the slot index written by insert).
-    select: 16 B per point past the prefix + 4 B per prefix point (slot);
-            the partitioned routes (2, 3) also write one 4-byte staging word
-            per point of a kept pillar (`kept` of them), route 3 its 16-byte
+    rank:   4 B per prefix point (the slot index written by insert); route 4
+            has no rank kernel.
+    select: route 4: 16 B per point (every point is read and binned) + one
+            4-byte staging word per point of a prefix cell (`staged`);
+            otherwise 16 B per point past the prefix + 4 B per prefix point
+            (slot), and on the partitioned routes (2, 3) one 4-byte staging
+            word per point of a kept pillar (`kept`), route 3 its 16-byte
             row as well.
     pack:   the dense output + 16 B per kept row (gathered from the input, or
             on route 3 copied from the staged rows); the partitioned routes
             also read the staging words back.
     """
     out = V * (16 * K + 16)
+    if route == 4:
+        return dict(call=16 * N + out, insert=16 * P, rank=0, select=16 * N + 4 * staged,
+                    pack=out + 16 * rows + 4 * staged)
     stage = 4 * kept if route >= 2 else 0
     carried = 16 * kept if route == 3 else 0
     return dict(call=16 * N + out, insert=16 * P, rank=4 * P,
@@ -155,6 +171,41 @@ def recorded_traffic(workload, stage):
     return found if recorded == sha else None
 
 
+def call_times(vx, x, n, torch):
+    """Per-call device times (ms): one pair of HIP events around each call on
+    the call's stream, all recorded before one synchronisation."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        vx.run(x)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def wall_with_readback(vx, x, n, torch):
+    """Host wall time per call (ms) including the read-back of V, each call
+    finished (one synchronising .item()) before the next starts."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        int(vx.run(x).item())
+    return (time.perf_counter() - t0) * 1e3 / n
+
+
+def staged_points(x, prm, P, vox):
+    """Points whose cell holds a prefix point (route 4 stages exactly these),
+    counted with the library's own binning step."""
+    valid, key = vox.bin_points(x, prm.range_, prm.cell, prm.grid)
+    k = key.cpu().numpy()
+    v = valid.cpu().numpy()
+    head = np.unique(k[:P][v[:P]])
+    return int(np.isin(k[v], head).sum())
+
+
 def time_calls(vx, x, steps, warmup, torch):
     for _ in range(warmup):
         vx.run(x)
@@ -178,9 +229,21 @@ def check_parity(vx, pts, prm):
                 and np.array_equal(gv.view(np.uint32), ov.view(np.uint32)))
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(pts, prm, seconds):
     """The oracle as it stands, on one host core, repeated on the full cloud
-    until `seconds` of CPU work are spent (at least 3 repetitions)."""
+    until `seconds` of CPU work are spent (at least 3 repetitions); beside
+    it the NumPy sort-then-segment brute force of the tests (the page's naive
+    method), a few repetitions, also one thread."""
     import oracle
     oracle.load()
     reps, t0 = 0, time.perf_counter()
@@ -191,41 +254,101 @@ def cpu_baseline(pts, prm, seconds):
         if (el >= seconds and reps >= 3) or reps >= 100000:
             break
     per = el / reps
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from bruteforce import sort_then_segment
+    nreps, t1 = 0, time.perf_counter()
+    while True:
+        sort_then_segment(pts, prm.range_, prm.cell, prm.grid, prm.max_points, prm.max_voxels)
+        nreps += 1
+        nel = time.perf_counter() - t1
+        if (nel >= seconds / 4 and nreps >= 3) or nreps >= 10000:
+            break
+    nper = nel / nreps
+    try:
+        aff = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = list(range(os.cpu_count() or 1))
+    model = cpu_model()
     return {"value": round(pts.shape[0] / per / 1e6, 3), "unit": "Mpoints/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{reps} repetitions of the full {pts.shape[0]:,}-point cloud "
                       f"({el:.1f} s, {per * 1e3:.2f} ms each), single-threaded C oracle, "
-                      f"host {platform.processor() or platform.machine()} with "
-                      f"{os.cpu_count()} logical CPUs"}
+                      f"host {model}, {os.cpu_count()} logical CPUs, affinity {len(aff)} CPUs",
+            "cpu_model": model, "affinity_cpus": len(aff), "logical_cpus": os.cpu_count(),
+            "numpy_bruteforce": {"value": round(pts.shape[0] / nper / 1e6, 3),
+                                 "unit": "Mpoints/s", "cores": 1,
+                                 "sample": f"{nreps} repetitions of the sort-then-segment "
+                                           f"brute force ({nper * 1e3:.1f} ms each)"}}
 
 
-def run_workload(name, steps, warmup, profile_iters, torch, vox):
+def run_workload(name, steps, warmup, profile_iters, torch, vox, opts=None):
     from workloads import generate, get_config
     cfg = get_config(name)
     p = cfg.params
     pts, _ = generate(name)
     N = pts.shape[0]
     x = torch.from_numpy(pts).to("cuda:0")
-    vx = vox.Voxelizer(N, p.range_, p.cell, p.grid, p.max_points, p.max_voxels, device="cuda:0")
+    opts = opts or {}
+    vx = vox.Voxelizer(N, p.range_, p.cell, p.grid, p.max_points, p.max_voxels, device="cuda:0",
+                       **opts)
     ms = time_calls(vx, x, steps, warmup, torch)
+    per_call = call_times(vx, x, steps, torch)
+    wall_ms = wall_with_readback(vx, x, max(10, steps // 4), torch)
     vx.run(x)
     torch.cuda.synchronize()
     V = int(vx.num_voxels.item())
     rows = int(vx.num_points[:max(V, 0)].sum().item()) if V > 0 else 0
     parity = check_parity(vx, pts, p)
     stage_ms, total_ms = vx.profile(x, profile_iters)
-    pl = vox.plan(N, p.max_voxels, p.max_points)
+    pl = vox.plan(N, p.max_voxels, p.max_points, **opts)
     P = pl["prefix_points"]
-    route = vox.select_route(N, p.max_voxels, p.max_points)
+    route = vox.select_route(N, p.max_voxels, p.max_points, **opts)
     pmap = vox.voxelize(x, p.range_, p.cell, p.grid, p.max_points, p.max_voxels,
-                        point_map=True)[3]
+                        point_map=True, **opts)[3]
     kept = int((pmap >= 0).sum().item())
-    alg = algorithmic_bytes(N, P, V, p.max_points, rows, kept, route)
-    kernels = dict(insert="k_insert", rank="k_rank",
-                   select="k_part" if route >= 2 else "k_select",
-                   pack="k_bins" if route >= 2 else "k_pack")
+    staged = staged_points(x, p, P, vox) if route == 4 else kept
+    alg = algorithmic_bytes(N, P, V, p.max_points, rows, kept, staged, route)
+    cells = p.grid[0] * p.grid[1] * p.grid[2]
+    direct = route == 4 and cells <= 2 * pl["table_slots"] and not opts.get("first_map")
+    if route == 4:
+        kernels = dict(insert="k_claim" if direct else "k_insert", rank=None,
+                       select="k_part_fb", pack="k_bins_fb")
+    else:
+        kernels = dict(insert="k_insert", rank="k_rank",
+                       select="k_part" if route >= 2 else "k_select",
+                       pack="k_bins" if route >= 2 else "k_pack")
+    timing = {"mean_us": round(ms * 1e3, 2), "median_us": round(float(np.median(per_call)) * 1e3, 2),
+              "p10_us": round(float(np.percentile(per_call, 10)) * 1e3, 2),
+              "p90_us": round(float(np.percentile(per_call, 90)) * 1e3, 2),
+              "wall_us_incl_readback": round(wall_ms * 1e3, 2)}
     return dict(cfg=cfg, pts=pts, N=N, V=V, rows=rows, ms=ms, parity=parity, stage_ms=stage_ms,
-                total_ms=total_ms, alg=alg, P=P, kept=kept, kernels=kernels)
+                total_ms=total_ms, alg=alg, P=P, kept=kept, staged=staged, kernels=kernels,
+                route=route, timing=timing)
+
+
+# What limits the dominant kernel (the kernel sections of the design notes):
+# every voxelization kernel is a chain of dependent memory round trips over
+# scattered lines (random cell lookups, short staging runs, row gathers), far
+# below HBM bandwidth; its fraction is still stated against the HBM peak.
+BOUND = "memory-latency"
+
+
+def config_line(name, q):
+    """One stderr line per workload: time per call, throughput, whole-call
+    and dominant-kernel fractions of the HBM peak, parity."""
+    stg = {k: v for k, v in q["stage_ms"].items() if q["kernels"][k]}
+    dom = max(stg, key=stg.get)
+    dom_gbs = q["alg"][dom] / (stg[dom] * 1e-3) / 1e9
+    gbs = q["alg"]["call"] / (q["ms"] * 1e-3) / 1e9
+    return {"workload": name, "N": q["N"], "V": q["V"], "kept_rows": q["rows"],
+            "route": q["route"], **q["timing"],
+            "mpoints_s": round(q["N"] / (q["ms"] * 1e-3) / 1e6, 1),
+            "gbs_alg": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "dominant": {"kernel": q["kernels"][dom], "us": round(stg[dom] * 1e3, 2),
+                         "alg_bytes": int(q["alg"][dom]), "gbs": round(dom_gbs, 1),
+                         "frac": round(dom_gbs / HBM_PEAK_GBS, 4)},
+            "stages_us": {q["kernels"][k]: round(v * 1e3, 2) for k, v in stg.items()},
+            "parity": q["parity"]}
 
 
 def downsample_line(name, steps, warmup, torch, vox):
@@ -311,12 +434,14 @@ def main():
         sys.exit(1)
     import sparse_spatial_hashing_amd as vox
 
-    r = run_workload(args.workload, args.steps, args.warmup, args.profile_iters, torch, vox)
+    opts = json.loads(args.options)
+    r = run_workload(args.workload, args.steps, args.warmup, args.profile_iters, torch, vox, opts)
     N, ms = r["N"], r["ms"]
     value = N / (ms * 1e-3) / 1e6
     gbs = r["alg"]["call"] / (ms * 1e-3) / 1e9
-    dom = max(r["stage_ms"], key=r["stage_ms"].get)
-    dom_ms = r["stage_ms"][dom]
+    stg = {k: v for k, v in r["stage_ms"].items() if r["kernels"][k]}
+    dom = max(stg, key=stg.get)
+    dom_ms = stg[dom]
     dom_gbs = r["alg"][dom] / (dom_ms * 1e-3) / 1e9
     p = r["cfg"].params
     line = {
@@ -332,14 +457,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "n_points": N, "grid": list(p.grid),
+        "config": {"workload": args.workload, **({"options": opts} if opts else {}),
+                   "n_points": N, "grid": list(p.grid),
                    "cell_m": list(p.cell), "max_points": p.max_points,
                    "max_voxels": p.max_voxels, "pillars": r["V"], "kept_rows": r["rows"]},
         "achieved_gbs_alg": round(gbs, 1),
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "parity_vs_oracle": r["parity"],
-        "stages_ms": {k: round(v, 5) for k, v in r["stage_ms"].items()},
-        "roofline": {"bound": "hbm", "kernel": r["kernels"][dom], "stage": dom,
+        "route": r["route"],
+        "timing": r["timing"],
+        "stages_ms": {r["kernels"][k]: round(v, 5) for k, v in stg.items()},
+        "roofline": {"bound": BOUND, "ceiling": "hbm", "kernel": r["kernels"][dom], "stage": dom,
                      "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
@@ -359,16 +487,12 @@ def main():
         for name in config_names():
             print(json.dumps(downsample_line(name, args.steps, args.warmup, torch, vox)),
                   file=sys.stderr, flush=True)
+    if not args.no_configs:
+        from workloads import config_names
         for name in config_names():
-            q = run_workload(name, args.steps, args.warmup, args.profile_iters, torch, vox)
-            print(json.dumps({
-                "workload": name, "N": q["N"], "V": q["V"], "kept_rows": q["rows"],
-                "us_per_call": round(q["ms"] * 1e3, 2),
-                "mpoints_s": round(q["N"] / (q["ms"] * 1e-3) / 1e6, 1),
-                "gbs_alg": round(q["alg"]["call"] / (q["ms"] * 1e-3) / 1e9, 1),
-                "frac_hbm": round(q["alg"]["call"] / (q["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "stages_us": {k: round(v * 1e3, 2) for k, v in q["stage_ms"].items()},
-                "parity": q["parity"]}), file=sys.stderr, flush=True)
+            q = r if name == args.workload else run_workload(
+                name, args.steps, args.warmup, args.profile_iters, torch, vox)
+            print(json.dumps(config_line(name, q)), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 
