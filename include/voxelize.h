@@ -94,8 +94,8 @@ typedef struct vox_options {
                                carried through the workspace's scratch; 4 = partitioned
                                by first-index bins with no rank kernel (pillar ids from
                                per-tile counts), rows gathered; 0 = automatic: 4 when
-                               K <= 64, the prefix is at most 262,144 points and
-                               K x (its pillar slots per bin) <= 8192, else 2 when
+                               K <= 64 and the prefix is at most 524,288 points
+                               (2048 bins of 256 pillar slots), else 2 when
                                K <= 64 and max_voxels <= 262144, else 1. 2, 3 and 4
                                outside their limits: VOX_EINVAL. The chunked path
                                always takes route 2 (or 1). */
@@ -114,9 +114,8 @@ typedef struct vox_options {
     int32_t lane_merge;     /* 1 = lanes of a wavefront that fall in the same cell are
                                merged before the claim atomics (one atomic per distinct
                                cell per wavefront); 0 = one atomic per point (default) */
-    int32_t bin_ids;        /* route 4: pillar slots per bin (a power of two, 16 to 256,
-                               with max_points x bin_ids <= 8192; 0 = 128, or 256 when
-                               128 would need more than 512 bins and max_points <= 32):
+    int32_t bin_ids;        /* route 4: pillar slots per bin (a power of two, 16 to 256;
+                               0 = 128, or 256 when 128 would need more than 512 bins):
                                bins = prefix_points / bin_ids rounded up to a power of
                                two, at most 2048 */
 } vox_options;

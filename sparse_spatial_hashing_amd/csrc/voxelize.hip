@@ -1741,12 +1741,67 @@ void k_bins(
 // One block per bin of the first-index route. Pillar slot j of bin b is the
 // cell whose first index is i0 = b + j nbins (when i0 is a first occurrence):
 // its id = (first occurrences in the tiles before i0's) + (i0's rank in its
-// tile), kept when below max_voxels. The walk over the bin's runs, the
-// ranking of arrivals within their pillar and the gather are k_bins'
-// (arrivals of pillars that are not kept are skipped). Every block clears
-// the claim state of its bin's cells; block 0 writes the status.
+// tile), kept when below max_voxels. The walk over the bin's runs and the
+// ranking of arrivals within their pillar are k_bins' (arrivals of pillars
+// that are not kept are skipped). Every block clears the claim state of its
+// bin's cells; block 0 writes the status.
+//
+// Ordered for latency: the first loads (run words, tile counts, the block's
+// slots) go out together; one scan serves both the run offsets and the tile
+// prefix; the first batch of staging words is in flight while the pillar
+// ids are worked out. A bin whose arrivals fit one round (the clouds of a
+// frame or so) loads a row as soon as its rank is known to be below K and
+// stores it after the round; a bin with more rounds keeps the K lowest
+// indices in LDS and gathers the rows after the walk, all at once (a row
+// per round would put a load's round trip into every round). The padding
+// rows follow.
 constexpr int kScanTiles = 4096;                 // prefix tiles a k_bins_fb block scans, at most
 constexpr int kScanPer = kScanTiles / kBinBlock;
+constexpr int kAhead = 4;                        // rounds of arrivals loaded ahead
+
+// Arrivals x0 + u kBinBlock + t (u < kAhead) of the current group of runs: the
+// staging word and the index of its tile's first point (tile tg + lo). The
+// loads are unconditional (word 0 for lanes past the group's arrivals, whose
+// values the caller ignores): a load under a branch makes the compiler wait
+// for it where the branch joins, which would serialise the round trips this
+// is meant to overlap.
+__device__ __forceinline__ void load_arrivals(const unsigned* __restrict__ staging,
+                                              const unsigned* roff, const unsigned* rsrc,
+                                              long long tg, int nruns, int ptile, unsigned x0,
+                                              unsigned ng, unsigned v[kAhead],
+                                              unsigned idx[kAhead]) {
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+        const unsigned x = x0 + (unsigned)(u * kBinBlock + threadIdx.x);
+        size_t at = 0;
+        idx[u] = 0u;
+        if (x < ng) {
+            int lo = 0, hi = nruns;  // the last run whose offset is <= x
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (roff[mid] <= x) lo = mid;
+                else hi = mid;
+            }
+            at = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
+            idx[u] = (unsigned)((tg + lo) * ptile);
+        }
+        v[u] = staging[at];
+    }
+}
+
+__device__ __forceinline__ void store_row(float4* d, float4 r, int nt) {
+    if (nt) {  // uniform
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        v4f x;
+        x.x = r.x;
+        x.y = r.y;
+        x.z = r.z;
+        x.w = r.w;
+        __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(d));
+    } else {
+        *d = r;
+    }
+}
 
 __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8)))
 void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, int K,
@@ -1769,11 +1824,13 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     unsigned* running = lds;                     // [G] arrivals so far per pillar slot
     unsigned* wbuf = running + G;                // [wwords] the tile prefix, then the counts
     unsigned short* wcnt = reinterpret_cast<unsigned short*>(wbuf);  // [3][kBinWaves * G]
-    unsigned* roff = wbuf + wwords;              // [kBinBlock + 1] run offsets in the group
-    unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock] run start within its tile
-    unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
-    unsigned* pid_of = wsum + kBinWaves;         // [G] pillar id of each slot, kNoPid if none kept
-    unsigned* best = pid_of + G;                 // [G * K] the K lowest indices, in order
+    unsigned* roff = wbuf + wwords;              // [kBinBlock + 2] run offsets in the group
+    unsigned* rsrc = roff + kBinBlock + 2;       // [kBinBlock] run start within its tile
+    unsigned* wsum = rsrc + kBinBlock;           // [2 kBinWaves]
+    unsigned* pid_of = wsum + 2 * kBinWaves;     // [G] pillar id of each slot, kNoPid if none kept
+    // [G] cell key + 1 of each slot (8-byte aligned: every count above is even)
+    unsigned long long* key_of = reinterpret_cast<unsigned long long*>(pid_of + G);
+    unsigned* best = reinterpret_cast<unsigned*>(key_of + G);  // [G K] the K lowest, in order
 
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -1791,7 +1848,8 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         const int q = t * kScanPer + u;
         tc[u] = q < ptp ? tile_firsts[q] : 0u;
     }
-    const long long i0 = b + ((long long)t << nbits);
+    // slot indices are below P <= 2^30: 32-bit arithmetic
+    const unsigned i0 = (unsigned)b + ((unsigned)t << nbits);
     unsigned long long fk = 0ull;
     unsigned fr = 0u;
     int fs = -1;
@@ -1804,37 +1862,6 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     // be block-uniform)
     const unsigned err = block_error(hdr);
     heal_workspace(hdr, zero_words, err);
-
-    // exclusive prefix of the prefix tiles' first-occurrence counts
-    unsigned s = 0;
-#pragma unroll
-    for (int u = 0; u < kScanPer; ++u) s += tc[u];
-    unsigned distinct_u;
-    unsigned ex = block_excl_scan<kBinWaves>(s, wsum, &distinct_u);
-#pragma unroll
-    for (int u = 0; u < kScanPer; ++u) {
-        const int q = t * kScanPer + u;
-        if (q < ptp) wbuf[q] = ex;
-        ex += tc[u];
-    }
-    __syncthreads();
-    const long long distinct = distinct_u;
-    const long long V = distinct < M ? distinct : M;
-    int status = (int)V;
-    if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
-    if (err != 0u) status = VOX_STATUS_DEVICE_ERROR;
-    if (blockIdx.x == 0 && t == 0) {
-        hdr->status = status;
-        hdr->distinct = (int)distinct;
-        num_voxels[0] = status;
-    }
-    unsigned mypid = kNoPid;
-    if (fk != 0ull) {
-        const unsigned pid = wbuf[i0 >> tshift] + fr;
-        if ((long long)pid >= distinct) report_error(hdr, num_voxels, 4u);  // not on a clean workspace
-        else if (status > 0 && (long long)pid < V) mypid = pid;
-    }
-    if (t < G) pid_of[t] = mypid;
     // this bin's cells are done with their claim state: return it to zero
     if (fk != 0ull) {
         if (first) {
@@ -1847,56 +1874,92 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         }
         fkey[i0] = 0ull;
     }
+    // the slot's key and rank wait in LDS (pid_of holds the rank until the
+    // id is known), so that no register carries them past the scan
+    if (t < G) {
+        pid_of[t] = fr;
+        key_of[t] = fk;
+    }
+
+    // one scan for two prefixes: the first group's run offsets and the tile
+    // counts of first occurrences
+    unsigned s = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) s += tc[u];
+    unsigned ng, distinct_u, ex;
+    const unsigned ro = block_excl_scan2<kBinWaves>(e >> 16, s, wsum, &ng, &ex, &distinct_u);
+    roff[t] = ro;
+    rsrc[t] = e & 0xffffu;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+        const int q = t * kScanPer + u;
+        if (q < ptp) wbuf[q] = ex;
+        ex += tc[u];
+    }
+    __syncthreads();
+    const long long distinct = distinct_u;
+    const long long V = distinct < M ? distinct : M;
+    int status = (int)V;
+    if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
+    if (err != 0u) status = VOX_STATUS_DEVICE_ERROR;
+    // the first batch of staging words goes out now (unused when status <= 0)
+    int nruns = (int)(ptiles < kBinBlock ? ptiles : kBinBlock);
+    unsigned v[kAhead], idx[kAhead];
+    load_arrivals(staging, roff, rsrc, 0, nruns, ptile, 0u, status > 0 ? ng : 0u, v, idx);
+    if (blockIdx.x == 0 && t == 0) {
+        hdr->status = status;
+        hdr->distinct = (int)distinct;
+        num_voxels[0] = status;
+    }
+    if (t < G) {
+        unsigned mypid = kNoPid;
+        if (key_of[t] != 0ull) {
+            const unsigned j0 = (unsigned)b + ((unsigned)t << nbits);  // the slot's first index
+            const unsigned pid = wbuf[j0 >> tshift] + pid_of[t];
+            if ((long long)pid >= distinct) report_error(hdr, num_voxels, 4u);  // not on a clean workspace
+            else if (status > 0 && (long long)pid < V) mypid = pid;
+        }
+        pid_of[t] = mypid;
+    }
     if (status <= 0) return;  // block-uniform: nothing kept, or no decision
     __syncthreads();          // the tile prefix in wbuf is read; pid_of is written
+    const bool one_round = ptiles <= kBinBlock && ng <= (unsigned)kBinBlock;  // block-uniform
 
     for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
     for (int x = t; x < 3 * kBinWaves * G / 2; x += kBinBlock) wbuf[x] = 0u;
     unsigned round = 0;
+    bool has_row = false;     // a row loaded in the previous round, stored in this one
+    float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+    long long row_at = 0;
     for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
-        const long long tt = tg + t;
         if (tg > 0) {
+            // the next group of runs (the previous group's rounds have passed
+            // their barriers, so nobody reads roff / rsrc any more)
+            const long long tt = tg + t;
             e = 0u;
             if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
+            const unsigned r0 = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
+            roff[t] = r0;
+            rsrc[t] = e & 0xffffu;
+            nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+            __syncthreads();
         }
-        unsigned ng;
-        const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
-        roff[t] = ro;
-        rsrc[t] = e & 0xffffu;
-        const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
-        __syncthreads();
-        for (unsigned x0 = 0; x0 < ng; x0 += 4u * kBinBlock) {
-            unsigned v[4], idx[4];
+        for (unsigned x0 = 0; x0 < ng; x0 += (unsigned)(kAhead * kBinBlock)) {
+            if (tg > 0 || x0 > 0) load_arrivals(staging, roff, rsrc, tg, nruns, ptile, x0, ng, v, idx);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const unsigned x = x0 + (unsigned)(u * kBinBlock + t);
-                v[u] = 0u;
-                idx[u] = 0u;
-                if (x < ng) {
-                    int lo = 0, hi = nruns;
-                    while (hi - lo > 1) {
-                        const int mid = (lo + hi) >> 1;
-                        if (roff[mid] <= x) lo = mid;
-                        else hi = mid;
-                    }
-                    const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
-                    v[u] = staging[src];
-                    idx[u] = (unsigned)((tg + lo) * ptile);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kAhead; ++u) {
                 const unsigned xr = x0 + (unsigned)(u * kBinBlock);
                 if (xr >= ng) break;  // block-uniform
                 bool valid = xr + (unsigned)t < ng;
                 unsigned pl = v[u] >> 16;
                 const unsigned src = idx[u] + (v[u] & 0xffffu);  // the point's index
+                unsigned pid = kNoPid;
                 if (valid && pl >= (unsigned)Gb) {  // not on a clean workspace
                     report_error(hdr, num_voxels, 4u);
                     valid = false;
                 }
                 if (valid) {
-                    const unsigned pid = pid_of[pl];
+                    pid = pid_of[pl];
                     if (point_pillar) point_pillar[src] = pid == kNoPid ? -1 : (int)pid;
                     valid = pid != kNoPid;  // points of pillars past the cap are dropped
                 }
@@ -1929,58 +1992,68 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
                 __syncthreads();
                 if (valid) {
                     const unsigned r = (unsigned)cur[w * G + pl] + rank;
-                    if (r < (unsigned)K) best[pl * K + r] = src;
+                    if (r < (unsigned)K) {
+                        if (!one_round) {
+                            best[pl * K + r] = src;
+                        } else if (src < N) {
+                            row = pts[src];  // stored after the round
+                            row_at = (long long)pid * K + r;
+                            has_row = true;
+                        } else {
+                            report_error(hdr, num_voxels, 8u);
+                        }
+                    }
                 }
                 ++round;
             }
         }
     }
-    __syncthreads();
-    // rows of the kept pillars, gathered by index (four in flight per
-    // thread), then zero padding
+    if (has_row) store_row(&voxels[row_at], row, nt_out);  // the one round's row
+    __syncthreads();  // the final counts (and the selection)
     const int rows = Gb * K;
-    for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
-        float4 rw[4];
-        long long dst[4];
+    if (one_round) {
+        // zero padding: rows at or past each kept pillar's count
+        for (int x = t; x < rows; x += kBinBlock) {
+            const int p = x / K;
+            const int r = x - p * K;
+            const unsigned pid = pid_of[p];
+            if (pid != kNoPid && (unsigned)r >= running[p])
+                store_row(&voxels[(long long)pid * K + r], make_float4(0.f, 0.f, 0.f, 0.f),
+                          nt_out);
+        }
+    } else {
+        // rows gathered by index (four in flight per thread), then padding
+        for (int x0 = 0; x0 < rows; x0 += 4 * kBinBlock) {
+            float4 rw[4];
+            long long dst[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int x = x0 + u * kBinBlock + t;
-            rw[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            dst[u] = -1;
-            if (x < rows) {
-                const int p = x / K;
-                const int r = x - p * K;
-                const unsigned pid = pid_of[p];
-                if (pid != kNoPid) {
-                    dst[u] = (long long)pid * K + r;
-                    if ((unsigned)r < running[p]) {
-                        const unsigned vv = best[p * K + r];
-                        if (vv < N) rw[u] = pts[vv];
-                        else report_error(hdr, num_voxels, 8u);
+            for (int u = 0; u < 4; ++u) {
+                const int x = x0 + u * kBinBlock + t;
+                rw[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                dst[u] = -1;
+                if (x < rows) {
+                    const int p = x / K;
+                    const int r = x - p * K;
+                    const unsigned pid = pid_of[p];
+                    if (pid != kNoPid) {
+                        dst[u] = (long long)pid * K + r;
+                        if ((unsigned)r < running[p]) {
+                            const unsigned vv = best[p * K + r];
+                            if (vv < N) rw[u] = pts[vv];
+                            else report_error(hdr, num_voxels, 8u);
+                        }
                     }
                 }
             }
-        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (dst[u] < 0) continue;
-            float4* d = &voxels[dst[u]];
-            if (nt_out) {  // uniform
-                typedef float v4f __attribute__((ext_vector_type(4)));
-                v4f x;
-                x.x = rw[u].x;
-                x.y = rw[u].y;
-                x.z = rw[u].z;
-                x.w = rw[u].w;
-                __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(d));
-            } else {
-                *d = rw[u];
-            }
+            for (int u = 0; u < 4; ++u)
+                if (dst[u] >= 0) store_row(&voxels[dst[u]], rw[u], nt_out);
         }
     }
-    if (mypid != kNoPid) {  // t < Gb: this thread's own slot
-        num_points[mypid] = (int)(running[t] < (unsigned)K ? running[t] : (unsigned)K);
-        write_coords(coords, mypid, (long long)(fk - 1ull), gx, gy);
+    if (t < G && pid_of[t] != kNoPid) {  // this thread's own slot
+        const unsigned pid = pid_of[t];
+        num_points[pid] = (int)(running[t] < (unsigned)K ? running[t] : (unsigned)K);
+        write_coords(coords, pid, (long long)(key_of[t] - 1ull), gx, gy);
     }
 }
 
@@ -2228,11 +2301,11 @@ inline size_t centroid_lds_bytes(int G) {
 inline size_t bins_fb_lds_bytes(int G, int K) {
     const size_t ww = (size_t)3 * kBinWaves * G / 2 > (size_t)kScanTiles
                           ? (size_t)3 * kBinWaves * G / 2 : (size_t)kScanTiles;
-    return 4u * ((size_t)G + ww + kBinBlock + 1 + kBinBlock + kBinWaves + (size_t)G +
-                 (size_t)G * K);
+    // (the words before key_of are an even count: it is 8-byte aligned)
+    return 4u * ((size_t)G + ww + kBinBlock + 2 + kBinBlock + 2 * kBinWaves + (size_t)G) +
+           8u * (size_t)G + 4u * (size_t)G * K;
 }
 constexpr int kFbMaxIds = 256;     // pillar slots per k_bins_fb bin, at most
-constexpr int kFbMaxSel = 8192;    // K x slots per bin, at most (the selection's LDS)
 constexpr int kFbOneRound = 512;   // k_bins_fb blocks that fit the chip at once (2 per CU)
 
 inline bool finite_f(float v) { return isfinite(v); }
@@ -2357,19 +2430,18 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->first_map = opt ? opt->first_map : 0;
     if (pl->part && !pl->carry && (path == 0 || path == 4) && !pl->C) {
         // default: 128 slots per bin, or 256 when 128 would need more bins
-        // than the chip runs at once and the selection still fits the LDS
+        // than the chip runs at once
         const long long Pw = P > 0 ? P : 1;
         long long ids = 128;
         if (opt && opt->bin_ids) ids = opt->bin_ids;
-        else if (cdiv(Pw, 128) > kFbOneRound && 256ll * K <= kFbMaxSel) ids = 256;
+        else if (cdiv(Pw, 128) > kFbOneRound) ids = 256;
         int fbits = 0;
         while ((1ll << fbits) < cdiv(Pw, ids) && (1 << fbits) < kMaxBins) ++fbits;
         int fshift = 0;
         while ((1ll << fshift) < cdiv(Pw, 1ll << fbits)) ++fshift;
         const long long tile = (long long)pl->pblock * pl->pper;
         const long long ptp = P > 0 ? cdiv(P, tile) : 0;  // tiles that write a count
-        const bool ok = (1 << fshift) <= kFbMaxIds && (long long)K << fshift <= kFbMaxSel &&
-                        ptp <= kScanTiles;
+        const bool ok = (1 << fshift) <= kFbMaxIds && ptp <= kScanTiles;
         if (ok) {
             pl->fb = 1;
             pl->fbits = fbits;

@@ -50,6 +50,39 @@ __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, 
     return off + incl - v;
 }
 
+// Two exclusive prefix sums over the block at once (a and b); totals in *ta
+// and *tb, b's prefix in *eb, a's returned. wsum: 2 NW words of LDS. Two
+// barriers.
+template <int NW>
+__device__ __forceinline__ unsigned block_excl_scan2(unsigned a, unsigned b, unsigned* wsum,
+                                                     unsigned* ta, unsigned* eb, unsigned* tb) {
+    const int lane = __lane_id();
+    const int w = threadIdx.x / kWave;
+    const unsigned ia = wave_incl_scan(a, lane);
+    const unsigned ib = wave_incl_scan(b, lane);
+    if (lane == kWave - 1) {
+        wsum[w] = ia;
+        wsum[NW + w] = ib;
+    }
+    __syncthreads();
+    unsigned oa = 0, sa = 0, ob = 0, sb = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+        const unsigned xa = wsum[ww], xb = wsum[NW + ww];
+        if (ww < w) {
+            oa += xa;
+            ob += xb;
+        }
+        sa += xa;
+        sb += xb;
+    }
+    __syncthreads();
+    *ta = sa;
+    *tb = sb;
+    *eb = ob + ib - b;
+    return oa + ia - a;
+}
+
 // Block bid of a grid of n blocks -> tile: XCD x = bid % 8 takes the
 // contiguous tiles [x q + min(x, r), ...) with q = n / 8, r = n % 8 (a
 // bijection onto [0, n)).

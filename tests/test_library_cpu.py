@@ -148,8 +148,7 @@ def test_binding_refuses_cpu_tensors():
 
 def test_select_path_option_limits():
     """0 = automatic, 1 = buckets, 2 = partition (K <= 64, max_voxels <= 262144),
-    4 = first-index partition (K <= 64, prefix <= 262144 points, K x slots per
-    bin <= 8192)."""
+    4 = first-index partition (K <= 64, prefix <= 524288 points)."""
     auto = vox.workspace_bytes(100000, 60000, 32)
     assert auto == vox.workspace_bytes(100000, 60000, 32, select_path=4)
     assert vox.select_route(100000, 60000, 32) == 4
@@ -158,14 +157,13 @@ def test_select_path_option_limits():
     # ranks (scratch) to route 2's layout, which the chunked path still uses
     assert auto > vox.workspace_bytes(100000, 60000, 32, select_path=2)
     assert vox.select_route(100000, 60000, 32, select_path=2) == 2
-    # K = 32: bins of 256 slots hold every prefix the partition admits; K = 64
-    # allows 128, so a prefix past 262144 points (2 max_voxels) leaves route 4 out
+    # bins of 256 slots hold every default prefix the partition admits (at most
+    # 2 x 262144 points); a longer prefix leaves route 4 out
     assert vox.select_route(10**6, 262144, 32) == 4
-    assert vox.select_route(10**6, 140000, 64) == 2
+    assert vox.select_route(10**6, 262144, 64) == 4
+    assert vox.select_route(10**6, 200000, 32, prefix_points=600000) == 2
     with pytest.raises(vox.VoxError):
-        vox.workspace_bytes(10**6, 140000, 64, select_path=4)
-    # K = 64: 128 slots per bin x 64 = 8192 selections still fit
-    assert vox.select_route(10**6, 100000, 64) == 4
+        vox.workspace_bytes(10**6, 200000, 32, prefix_points=600000, select_path=4)
     assert vox.plan(100000, 60000, 32)["bucket_cap"] == 0          # no buckets
     assert vox.plan(100000, 60000, 32, select_path=1)["bucket_cap"] == 512
     assert vox.workspace_bytes(1000, 262144, 32, select_path=2) > 0
@@ -176,9 +174,7 @@ def test_select_path_option_limits():
                 dict(bin_ids=512)):
         with pytest.raises(vox.VoxError):
             vox.workspace_bytes(1000, 100, 32, **bad)
-    # 256 slots x 64 rows would overflow the selection's LDS
-    with pytest.raises(vox.VoxError):
-        vox.workspace_bytes(1000, 100, 64, bin_ids=256, select_path=4)
+    assert vox.select_route(1000, 100, 64, bin_ids=256, select_path=4) == 4
     assert vox.select_route(1000, 100, 32, bin_ids=256) == 4
     assert vox.workspace_bytes(1000, 262144, 64, select_path=2) > 0
     for args in ((1000, 100, 65), (1000, 262145, 32), (1000, 262145, 64)):
