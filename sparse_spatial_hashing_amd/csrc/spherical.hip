@@ -292,6 +292,11 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_pass(
     __shared__ unsigned wsum[NW];
     if (!table_ok(tab, a)) return;
     const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
+    // Tiles follow block indices. A tile waits only on lower-numbered
+    // blocks; the dispatcher starts workgroups in increasing order, so
+    // those are resident or finished, and they never wait on a higher one:
+    // every wait ends. The poll bound turns a stall that this argument
+    // rules out into an error status instead of a hang.
     const int tile = blockIdx.x;
     const int nb = 1 << dbits;
     const unsigned dmask = (unsigned)nb - 1u;
@@ -357,6 +362,7 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_pass(
         // published yet is polled again (the counts before it are final)
         unsigned excl = 0;
         unsigned polls = 0;
+        bool failed = false;
         while (true) {
             bool done = false, wait = false;
             int used = 0;
@@ -377,6 +383,7 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_pass(
             if (wait) {
                 if (++polls > kSSpinLimit) {
                     atomicOr(err, 1u);
+                    failed = true;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -385,7 +392,11 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_pass(
             for (int j = 0; j < kSLookBack; ++j)
                 sw[j] = hi - j >= 0 ? load_relaxed32(&state[(long long)(hi - j) * nb + d]) : kSIncl;
         }
-        if (tile > 0) store_relaxed32(&state[(long long)tile * nb + d], kSIncl | (excl + c));
+        // an inclusive word built on a partial prefix is never published:
+        // after a failed wait the tile's successors keep waiting on it and
+        // fail in turn, and the call reports the error
+        if (tile > 0 && !failed)
+            store_relaxed32(&state[(long long)tile * nb + d], kSIncl | (excl + c));
         lstart[d] = ls;
         gbase[d] = g0 + excl;
     }
@@ -800,7 +811,7 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     __shared__ unsigned gsum_sh, blk_err;
     __shared__ bool last_sh, failed_sh;
     const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
-    const int b = blockIdx.x;
+    const int b = blockIdx.x;  // waits only on lower blocks: see k_sph_pass
     if (tid == 0) blk_err = 0u;
     const int ntiles = a.ntiles, T = a.tile;
     const int lgT = __builtin_ctz((unsigned)T);
@@ -912,7 +923,9 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     if (b > 0)   // block-uniform: the first block has no predecessor
         excl = look_back_wide(state, nb1, b, d1 < nb1 ? d1 : 0, S, d1 >= nb1, lane, &blk_err);
     if (lead) {
-        if (b > 0) store_relaxed32(&state[(long long)b * nb1 + d1], kSIncl | (excl + c));
+        // (after a failed wait the word stays an aggregate: no inclusive
+        // word rests on a partial prefix; the error is reported)
+        if (b > 0 && !blk_err) store_relaxed32(&state[(long long)b * nb1 + d1], kSIncl | (excl + c));
         basev[d1] = g0 + excl;
     }
     if (tid == 0) gsum_sh = gall;

@@ -5,31 +5,35 @@
 // order, cap, truncation) is stated in include/voxelize.h. The page's own
 // kernel ("Claiming a pillar and packing points", "Compaction") writes each
 // pillar at its hash slot in arrival order and compacts the table with a
-// copy_if; this design makes the result a pure function of the input:
+// copy_if; this design makes the result a pure function of the input. The
+// default route (4, first-index bins) runs three kernels:
 //
-//   insert  points [0, P): bin, find-or-claim the cell in a linear-probe
-//           table of 64-bit words (key and lowest index of the cell: one CAS
-//           claims an empty slot, one 64-bit atomicMax lowers the index),
-//           remember each point's slot. The table has 16 slots per kept
-//           pillar and P = min(N, 4 max_voxels), so inserts see a load of at
-//           most 1/4 and probe chains stay short (the page sizes its table
-//           8x the pillar budget for the same reason: "A fixed table").
-//   rank    single-pass scan with decoupled look-back over points [0, P):
-//           point i is a pillar's first occurrence iff its slot's lowest
-//           index is i; its rank among first occurrences is the pillar id.
-//           The first max_voxels ids are kept (written into the slot word).
-//   select  every point of a kept pillar (prefix points through their slot,
-//           the others by a lookup-only probe) takes one arrival ticket from
-//           its pillar's counter and parks its index in the pillar's bucket;
-//           arrivals past the bucket go through an ordered atomicMax cascade
-//           that keeps their K lowest indices.
-//   pack    a lane segment per kept pillar (several pillars per wavefront)
-//           orders the pillar's candidates by rank (scalar broadcasts); a
-//           pillar with more candidates than its segment takes the whole
-//           wavefront, a bitonic network and the overflow row. The K lowest
-//           indices become rows (bit copies, 16-byte loads) with zero padding,
-//           coordinates and counts; then every workspace word the call wrote
-//           is returned to zero.
+//   claim   points [0, P), P = min(N, 2 max_voxels, S/4): bin each point and
+//           lower its cell's entry to the lowest index seen, with one
+//           non-returning atomicMax in a map indexed by cell (grids of at
+//           most 2 S cells) or, for larger grids, a CAS claim plus an
+//           atomicMax in a linear-probe table of 64-bit words (key and
+//           lowest index). The first max_voxels cells in first-occurrence
+//           order are all among these P points, or the call says it cannot
+//           decide (VOX_STATUS_NEEDS_CHUNKED).
+//   part    every point: bin, look up its cell's lowest prefix index i0 (no
+//           entry: its pillar is past the cap), and partition the tile's
+//           points by bin i0 mod nbins, keeping index order inside each bin's
+//           run; prefix tiles also count their first occurrences (i == i0)
+//           and rank them inside the tile.
+//   bins    one block per bin: every block sums the prefix tiles' counts
+//           itself, so pillar id(i0) = (first occurrences before i0's tile) +
+//           (i0's rank in it); ids below max_voxels are kept. It walks the
+//           bin's runs tile after tile, so each pillar's points arrive in
+//           index order: a point's rank is the number of earlier arrivals of
+//           its pillar, and ranks below max_points become rows (bit copies,
+//           16-byte loads) with zero padding, coordinates and counts. Then
+//           every workspace word the call dirtied is returned to zero.
+//
+// Routes 2 and 3 (the chunked path, and on request) put a rank kernel with
+// a decoupled look-back between the claim and the partition and bin by
+// pillar id; route 1 (max_points > 64) fills per-pillar buckets with one
+// atomic per point and orders them in a pack kernel.
 //
 // gfx950 notes that shape the code. Blocks are dealt round-robin to the 8
 // XCDs, each with its own L2. Device-scope read-modify-write atomics are
