@@ -1807,6 +1807,28 @@ __device__ __forceinline__ void store_row(float4* d, float4 r, int nt) {
     }
 }
 
+// Return slot i0's claim state to zero: the direct map entry or table slot
+// of its cell (fk = key + 1, 0 when i0 is not a first occurrence), its
+// slot_of entry (hashed route) and its key.
+__device__ __forceinline__ void release_slot(unsigned* __restrict__ first,
+                                             unsigned long long cells,
+                                             unsigned long long* __restrict__ fkey,
+                                             unsigned long long* __restrict__ table, unsigned S,
+                                             int* __restrict__ slot_of, unsigned i0,
+                                             unsigned long long fk, int fs, Header* hdr,
+                                             int* num_voxels) {
+    if (fk == 0ull) return;
+    if (first) {
+        if (fk - 1ull < cells) first[fk - 1ull] = 0u;
+        else report_error(hdr, num_voxels, 16u);  // not on a clean workspace
+    } else {
+        if (fs >= 0 && (unsigned)fs < S) table[fs] = 0ull;
+        else report_error(hdr, num_voxels, 16u);
+        slot_of[i0] = 0;
+    }
+    fkey[i0] = 0ull;
+}
+
 __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8)))
 void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, int K,
                const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
@@ -1834,7 +1856,9 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     unsigned* pid_of = wsum + 2 * kBinWaves;     // [G] pillar id of each slot, kNoPid if none kept
     // [G] cell key + 1 of each slot (8-byte aligned: every count above is even)
     unsigned long long* key_of = reinterpret_cast<unsigned long long*>(pid_of + G);
-    unsigned* best = reinterpret_cast<unsigned*>(key_of + G);  // [G K] the K lowest, in order
+    int* slot_at = reinterpret_cast<int*>(key_of + G);         // [G] table slot (hashed route)
+    unsigned* first_at = reinterpret_cast<unsigned*>(slot_at + G);  // [G] the slot's first index
+    unsigned* best = first_at + G;               // [G K] the K lowest, in order
 
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -1866,23 +1890,14 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     // be block-uniform)
     const unsigned err = block_error(hdr);
     heal_workspace(hdr, zero_words, err);
-    // this bin's cells are done with their claim state: return it to zero
-    if (fk != 0ull) {
-        if (first) {
-            if (fk - 1ull < cells) first[fk - 1ull] = 0u;
-            else report_error(hdr, num_voxels, 16u);  // not on a clean workspace
-        } else {
-            if (fs >= 0 && (unsigned)fs < S) table[fs] = 0ull;
-            else report_error(hdr, num_voxels, 16u);
-            slot_of[i0] = 0;
-        }
-        fkey[i0] = 0ull;
-    }
-    // the slot's key and rank wait in LDS (pid_of holds the rank until the
-    // id is known), so that no register carries them past the scan
+    // the slot's key, rank, table slot and first index wait in LDS (pid_of
+    // holds the rank until the id is known), so that no register carries
+    // them past the scan
     if (t < G) {
         pid_of[t] = fr;
         key_of[t] = fk;
+        slot_at[t] = fs;
+        first_at[t] = i0;
     }
 
     // one scan for two prefixes: the first group's run offsets and the tile
@@ -1918,13 +1933,19 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     if (t < G) {
         unsigned mypid = kNoPid;
         if (key_of[t] != 0ull) {
-            const unsigned j0 = (unsigned)b + ((unsigned)t << nbits);  // the slot's first index
-            const unsigned pid = wbuf[j0 >> tshift] + pid_of[t];
+            const unsigned pid = wbuf[first_at[t] >> tshift] + pid_of[t];
             if ((long long)pid >= distinct) report_error(hdr, num_voxels, 4u);  // not on a clean workspace
             else if (status > 0 && (long long)pid < V) mypid = pid;
         }
         pid_of[t] = mypid;
     }
+    // This bin's cells are done with their claim state: back to zero. The
+    // stores go out now, behind the first batch of staging loads: vector
+    // memory operations complete in order, so stores issued before the scan
+    // would have held up its waits, and stores at the end would add their
+    // round trip to the block's tail.
+    if (t < Gb) release_slot(first, cells, fkey, table, S, slot_of, first_at[t], key_of[t],
+                             slot_at[t], hdr, num_voxels);
     if (status <= 0) return;  // block-uniform: nothing kept, or no decision
     __syncthreads();          // the tile prefix in wbuf is read; pid_of is written
     const bool one_round = ptiles <= kBinBlock && ng <= (unsigned)kBinBlock;  // block-uniform
@@ -2307,7 +2328,7 @@ inline size_t bins_fb_lds_bytes(int G, int K) {
                           ? (size_t)3 * kBinWaves * G / 2 : (size_t)kScanTiles;
     // (the words before key_of are an even count: it is 8-byte aligned)
     return 4u * ((size_t)G + ww + kBinBlock + 2 + kBinBlock + 2 * kBinWaves + (size_t)G) +
-           8u * (size_t)G + 4u * (size_t)G * K;
+           8u * (size_t)G + 8u * (size_t)G + 4u * (size_t)G * K;
 }
 constexpr int kFbMaxIds = 256;     // pillar slots per k_bins_fb bin, at most
 constexpr int kFbOneRound = 512;   // k_bins_fb blocks that fit the chip at once (2 per CU)

@@ -20,12 +20,19 @@ __device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
     return v;
 }
 
-__device__ __forceinline__ unsigned wave_incl_scan(unsigned v, int lane) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const unsigned o = (unsigned)__shfl_up((int)v, d);
-        if (lane >= d) v += o;
-    }
+// Inclusive prefix sum over the wavefront with DPP moves (no LDS path):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in
+// from outside the row add 0), then the last lane of row 0 into row 1 and
+// of row 2 into row 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31). GFX9 DPP; every lane of the wavefront must be active
+// (the block scans below are called by every thread).
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v, int /*lane*/) {
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return v;
 }
 
