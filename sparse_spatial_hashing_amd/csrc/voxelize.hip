@@ -1188,14 +1188,17 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     __syncthreads();
 
     // bin starts within the tile, then each wavefront's start within its bin;
-    // each thread owns BPT bins
+    // each thread owns bpt consecutive bins
+    // (bpt = nbins / BLK, at least 1: with fewer bins than threads each
+    // thread takes one bin, so the bins spread over every wavefront)
+    const int bpt = nb > BLK ? nb / BLK : 1;
     unsigned c[BPT];
     unsigned mine = 0;
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-        const int b = t * BPT + q;
+        const int b = t * bpt + q;
         c[q] = 0u;
-        if (b < nb) {
+        if (q < bpt && b < nb) {
 #pragma unroll
             for (int ww = 0; ww < WPB; ++ww) c[q] += hist[ww][b];
         }
@@ -1205,8 +1208,8 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     unsigned run = block_excl_scan<WPB>(mine, wsum, &total);
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-        const int b = t * BPT + q;
-        if (b < nb) {
+        const int b = t * bpt + q;
+        if (q < bpt && b < nb) {
             cm[(size_t)b * ptiles + tile] = run | (c[q] << 16);
             unsigned at = run;
 #pragma unroll
@@ -1476,13 +1479,16 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     }
     __syncthreads();
 
+    // (bpt = nbins / BLK, at least 1: with fewer bins than threads each
+    // thread takes one bin, so the bins spread over every wavefront)
+    const int bpt = nbins > BLK ? nbins / BLK : 1;
     unsigned c[BPT];
     unsigned mine = 0;
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-        const int b = t * BPT + q;
+        const int b = t * bpt + q;
         c[q] = 0u;
-        if (b < nbins) {
+        if (q < bpt && b < nbins) {
 #pragma unroll
             for (int ww = 0; ww < WPB; ++ww) c[q] += hist[ww][b];
         }
@@ -1492,8 +1498,8 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     unsigned run = block_excl_scan<WPB>(mine, wsum, &total);
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-        const int b = t * BPT + q;
-        if (b < nbins) {
+        const int b = t * bpt + q;
+        if (q < bpt && b < nbins) {
             cm[(size_t)b * ptiles + tile] = run | (c[q] << 16);
             unsigned at = run;
 #pragma unroll
