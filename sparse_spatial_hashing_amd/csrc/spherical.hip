@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_pass(
     __shared__ unsigned hist[NW * kSMaxDigits];
     __shared__ unsigned sk[T], sv[T];
     __shared__ unsigned lstart[kSMaxDigits], gbase[kSMaxDigits];
-    __shared__ unsigned wsum[NW];
+    __shared__ unsigned wsum[kWsumWords];
     if (!table_ok(tab, a)) return;
     const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
     // Tiles follow block indices. A tile waits only on lower-numbered
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kSBlock) void k_sph_lowpart(
     constexpr int T = kSBlock * PER;
     extern __shared__ __align__(16) unsigned lds[];
     __shared__ unsigned h1[kSMaxDigits];
-    __shared__ unsigned wsum[kSWavesPart];
+    __shared__ unsigned wsum[kWsumWords];
     const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;
     const long long stride = (long long)gridDim.x * kSBlock;
     for (long long j = (long long)blockIdx.x * kSBlock + tid; j < state_words; j += stride)
@@ -807,7 +807,7 @@ __global__ __launch_bounds__(kSPassBlock) void k_sph_place(
     constexpr int CH = kSPassBlock * E;
     constexpr int RPT = kSMaxRuns / kSPassBlock;
     extern __shared__ __align__(16) unsigned lds[];
-    __shared__ unsigned wsum[NW];
+    __shared__ unsigned wsum[kWsumWords];
     __shared__ unsigned gsum_sh, blk_err;
     __shared__ bool last_sh, failed_sh;
     const int tid = threadIdx.x, lane = __lane_id(), w = tid / kWave;

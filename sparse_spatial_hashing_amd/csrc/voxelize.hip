@@ -985,7 +985,7 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     constexpr int BPT = kMaxBins / BLK;   // bins per thread in the tile's scan
     constexpr int PER_B = PER < kPartBatch ? PER : kPartBatch;
     __shared__ unsigned hist[WPB][kMaxBins];  // one histogram per wavefront
-    __shared__ unsigned wsum[WPB];
+    __shared__ unsigned wsum[kWsumWords];
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int w = t / kWave;
@@ -1343,7 +1343,7 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     constexpr int BPT = kMaxBins / BLK;
     constexpr int PER_B = PER < kPartBatch ? PER : kPartBatch;
     __shared__ unsigned hist[WPB][kMaxBins];
-    __shared__ unsigned wsum[WPB];
+    __shared__ unsigned wsum[kWsumWords];
     __shared__ unsigned wfirst[WPB];
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -1555,8 +1555,8 @@ void k_bins(
     unsigned* wbuf = running + G;                // [3][kBinWaves * G] per-wavefront counts
     unsigned* roff = wbuf + 3 * kBinWaves * G;   // [kBinBlock + 1] run offsets in the group
     unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock] run start within its tile
-    unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
-    unsigned* best = wsum + kBinWaves;           // [G * K] without CARRY: the K lowest, in order
+    unsigned* wsum = rsrc + kBinBlock;           // [kWsumWords]
+    unsigned* best = wsum + kWsumWords;          // [G * K] without CARRY: the K lowest, in order
 
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -1858,8 +1858,8 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     unsigned short* wcnt = reinterpret_cast<unsigned short*>(wbuf);  // [3][kBinWaves * G]
     unsigned* roff = wbuf + wwords;              // [kBinBlock + 2] run offsets in the group
     unsigned* rsrc = roff + kBinBlock + 2;       // [kBinBlock] run start within its tile
-    unsigned* wsum = rsrc + kBinBlock;           // [2 kBinWaves]
-    unsigned* pid_of = wsum + 2 * kBinWaves;     // [G] pillar id of each slot, kNoPid if none kept
+    unsigned* wsum = rsrc + kBinBlock;           // [kWsumWords]
+    unsigned* pid_of = wsum + kWsumWords;        // [G] pillar id of each slot, kNoPid if none kept
     // [G] cell key + 1 of each slot (8-byte aligned: every count above is even)
     unsigned long long* key_of = reinterpret_cast<unsigned long long*>(pid_of + G);
     int* slot_at = reinterpret_cast<int*>(key_of + G);         // [G] table slot (hashed route)
@@ -2117,8 +2117,8 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     unsigned* wbuf = running + G;                // [3][kBinWaves * G] per-wavefront counts
     unsigned* roff = wbuf + 3 * kBinWaves * G;   // [kBinBlock + 1]
     unsigned* rsrc = roff + kBinBlock + 1;       // [kBinBlock]
-    unsigned* wsum = rsrc + kBinBlock;           // [kBinWaves]
-    unsigned* before = wsum + kBinWaves;         // [G] arrivals before this round
+    unsigned* wsum = rsrc + kBinBlock;           // [kWsumWords]
+    unsigned* before = wsum + kWsumWords;        // [G] arrivals before this round
     unsigned* cnt_round = before + G;            // [G] arrivals in this round
     unsigned* seg = cnt_round + G;               // [G] start of the voxel's group in rowbuf
 
@@ -2320,20 +2320,20 @@ struct Plan {
 // LDS of one k_bins block for bins of G pillars (plus the selection when rows
 // are gathered rather than carried)
 inline size_t bins_lds_bytes(int G, int K, bool carry) {
-    return 4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves +
+    return 4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kWsumWords +
                          (carry ? 0 : G * K));
 }
 // LDS of one k_centroid block for bins of G voxels
 inline size_t centroid_lds_bytes(int G) {
     return 16u * (size_t)kBinBlock +
-           4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kBinWaves + 3 * G);
+           4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kWsumWords + 3 * G);
 }
 // LDS of one k_bins_fb block for bins of G pillar slots
 inline size_t bins_fb_lds_bytes(int G, int K) {
     const size_t ww = (size_t)3 * kBinWaves * G / 2 > (size_t)kScanTiles
                           ? (size_t)3 * kBinWaves * G / 2 : (size_t)kScanTiles;
     // (the words before key_of are an even count: it is 8-byte aligned)
-    return 4u * ((size_t)G + ww + kBinBlock + 2 + kBinBlock + 2 * kBinWaves + (size_t)G) +
+    return 4u * ((size_t)G + ww + kBinBlock + 2 + kBinBlock + kWsumWords + (size_t)G) +
            8u * (size_t)G + 8u * (size_t)G + 4u * (size_t)G * K;
 }
 constexpr int kFbMaxIds = 256;     // pillar slots per k_bins_fb bin, at most

@@ -36,58 +36,73 @@ __device__ __forceinline__ unsigned wave_incl_scan(unsigned v, int /*lane*/) {
     return v;
 }
 
-// Exclusive prefix sum over the block (NW wavefronts); *total gets the sum.
-// wsum is an LDS array of NW words. Contains two barriers.
+// Inclusive prefix sum within each row of 16 lanes (the first four steps
+// of wave_incl_scan). Every lane of the wavefront must be active.
+__device__ __forceinline__ unsigned row16_incl_scan(unsigned v) {
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    return v;
+}
+
+// LDS words a block scan below needs (wsum): the wavefronts' totals of up to
+// two sums in [0, 32), their exclusive prefixes in [32, 64), the block totals
+// in 64 and 65.
+constexpr int kWsumWords = 66;
+
+// Exclusive prefix sum over the block (NW <= 16 wavefronts); *total gets the
+// sum. The wavefront totals are scanned once, by wavefront 0, and every
+// wavefront reads its own prefix. Contains two barriers; wsum may be reused
+// by the next scan right away.
 template <int NW>
 __device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, unsigned* total) {
+    static_assert(NW >= 1 && NW <= 16, "one row of 16 lanes scans the wavefront totals");
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
     const unsigned incl = wave_incl_scan(v, lane);
     if (lane == kWave - 1) wsum[w] = incl;
     __syncthreads();
-    unsigned off = 0, tot = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-        const unsigned x = wsum[ww];
-        if (ww < w) off += x;
-        tot += x;
+    if (w == 0) {
+        const unsigned x = lane < NW ? wsum[lane] : 0u;
+        const unsigned xi = row16_incl_scan(x);
+        if (lane < NW) wsum[32 + lane] = xi - x;
+        if (lane == 15) wsum[64] = xi;
     }
     __syncthreads();
-    *total = tot;
-    return off + incl - v;
+    *total = wsum[64];
+    return wsum[32 + w] + incl - v;
 }
 
 // Two exclusive prefix sums over the block at once (a and b); totals in *ta
-// and *tb, b's prefix in *eb, a's returned. wsum: 2 NW words of LDS. Two
-// barriers.
+// and *tb, b's prefix in *eb, a's returned. The two sets of wavefront totals
+// are scanned side by side in rows 0 and 1 of wavefront 0. Two barriers.
 template <int NW>
 __device__ __forceinline__ unsigned block_excl_scan2(unsigned a, unsigned b, unsigned* wsum,
                                                      unsigned* ta, unsigned* eb, unsigned* tb) {
+    static_assert(NW >= 1 && NW <= 16, "one row of 16 lanes scans the wavefront totals");
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
     const unsigned ia = wave_incl_scan(a, lane);
     const unsigned ib = wave_incl_scan(b, lane);
     if (lane == kWave - 1) {
         wsum[w] = ia;
-        wsum[NW + w] = ib;
+        wsum[16 + w] = ib;
     }
     __syncthreads();
-    unsigned oa = 0, sa = 0, ob = 0, sb = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-        const unsigned xa = wsum[ww], xb = wsum[NW + ww];
-        if (ww < w) {
-            oa += xa;
-            ob += xb;
-        }
-        sa += xa;
-        sb += xb;
+    if (w == 0) {
+        const bool in = lane < 32 && (lane & 15) < NW;
+        const unsigned x = in ? wsum[lane] : 0u;
+        const unsigned xi = row16_incl_scan(x);
+        if (in) wsum[32 + lane] = xi - x;
+        if (lane == 15) wsum[64] = xi;
+        if (lane == 31) wsum[65] = xi;
     }
     __syncthreads();
-    *ta = sa;
-    *tb = sb;
-    *eb = ob + ib - b;
-    return oa + ia - a;
+    *ta = wsum[64];
+    *tb = wsum[65];
+    *eb = wsum[48 + w] + ib - b;
+    return wsum[32 + w] + ia - a;
 }
 
 // Block bid of a grid of n blocks -> tile: XCD x = bid % 8 takes the
