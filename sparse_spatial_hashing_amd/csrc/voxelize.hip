@@ -1769,32 +1769,70 @@ constexpr int kScanTiles = 4096;                 // prefix tiles a k_bins_fb blo
 constexpr int kScanPer = kScanTiles / kBinBlock;
 constexpr int kAhead = 4;                        // rounds of arrivals loaded ahead
 
-// Arrivals x0 + u kBinBlock + t (u < kAhead) of the current group of runs: the
-// staging word and the index of its tile's first point (tile tg + lo). The
-// loads are unconditional (word 0 for lanes past the group's arrivals, whose
-// values the caller ignores): a load under a branch makes the compiler wait
-// for it where the branch joins, which would serialise the round trips this
-// is meant to overlap.
-__device__ __forceinline__ void load_arrivals(const unsigned* __restrict__ staging,
-                                              const unsigned* roff, const unsigned* rsrc,
-                                              long long tg, int nruns, int ptile, unsigned x0,
-                                              unsigned ng, unsigned v[kAhead],
-                                              unsigned idx[kAhead]) {
+// The first-index bins' arrivals, found without a search. The runs of a
+// group that hold arrivals are listed in order (croff: offset of the run's
+// first arrival in the group; csrc: tile within the group << 16 | start of
+// the run in its tile's staging slice). For a window of kWin arrivals
+// [x0, x0 + kWin), bit i of `bits` is set when a listed run starts at x0 + i,
+// and wpre holds the exclusive prefix of the words' bit counts (wpre[kWinWords]
+// the window's total). Arrival x then belongs to listed run
+// base + (starts in [x0, x]) - 1, where base counts the listed runs that
+// start before x0: a rank query of a few LDS reads instead of a binary
+// search over the runs.
+constexpr int kWin = kAhead * kBinBlock;         // arrivals per window
+constexpr int kWinWords = kWin / 32;             // words of the window's start bits
+
+// Every run listed at or after `from` that starts in the window sets its bit
+// (bits must be zero). One listed run per thread.
+__device__ __forceinline__ void mark_window(const unsigned* croff, int nlist, unsigned x0,
+                                            unsigned* bits) {
+    const int k = threadIdx.x;
+    if (k < nlist) {
+        const unsigned r = croff[k];
+        if (r >= x0 && r - x0 < (unsigned)kWin)
+            atomicOr(&bits[(r - x0) >> 5], 1u << ((r - x0) & 31u));
+    }
+}
+
+// Wavefront 0: the exclusive prefix of the window's per-word start counts.
+__device__ __forceinline__ void prefix_window(const unsigned* bits, unsigned* wpre) {
+    static_assert(kWinWords == 2 * kWave, "two words per lane");
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const unsigned c0 = (unsigned)__popc(bits[2 * lane]);
+        const unsigned c1 = (unsigned)__popc(bits[2 * lane + 1]);
+        const unsigned incl = wave_incl_scan(c0 + c1, lane);
+        wpre[2 * lane] = incl - c0 - c1;
+        wpre[2 * lane + 1] = incl - c1;
+        if (lane == kWave - 1) wpre[kWinWords] = incl;
+    }
+}
+
+// Arrivals x0 + u kBinBlock + t (u < kAhead) of the current window: the
+// staging word and the index of its tile's first point. The loads are
+// unconditional (word 0 for lanes past the group's arrivals, whose values
+// the caller ignores): a load under a branch makes the compiler wait for it
+// where the branch joins, which would serialise the round trips this is meant
+// to overlap.
+__device__ __forceinline__ void load_arrivals_ranked(const unsigned* __restrict__ staging,
+                                                     const unsigned* croff, const unsigned* csrc,
+                                                     const unsigned* bits, const unsigned* wpre,
+                                                     unsigned base, long long tg, int ptile,
+                                                     unsigned x0, unsigned ng,
+                                                     unsigned v[kAhead], unsigned idx[kAhead]) {
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
-        const unsigned x = x0 + (unsigned)(u * kBinBlock + threadIdx.x);
-        size_t at = 0;
-        idx[u] = 0u;
-        if (x < ng) {
-            int lo = 0, hi = nruns;  // the last run whose offset is <= x
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (roff[mid] <= x) lo = mid;
-                else hi = mid;
-            }
-            at = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
-            idx[u] = (unsigned)((tg + lo) * ptile);
-        }
+        const unsigned i = (unsigned)(u * kBinBlock) + threadIdx.x;  // within the window
+        const unsigned x = x0 + i;
+        const bool ok = x < ng;
+        const unsigned wd = i >> 5;
+        const unsigned below = bits[wd] & (0xffffffffu >> (31u - (i & 31u)));  // bits <= i
+        int k = (int)(base + wpre[wd] + (unsigned)__popc(below)) - 1;
+        k = ok && k >= 0 ? k : 0;
+        const unsigned cs = csrc[k];
+        const long long tile = tg + (cs >> 16);
+        const size_t at = ok ? (size_t)tile * ptile + (cs & 0xffffu) + (x - croff[k]) : 0;
+        idx[u] = ok ? (unsigned)(tile * ptile) : 0u;
         v[u] = staging[at];
     }
 }
@@ -1856,9 +1894,11 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     unsigned* running = lds;                     // [G] arrivals so far per pillar slot
     unsigned* wbuf = running + G;                // [wwords] the tile prefix, then the counts
     unsigned short* wcnt = reinterpret_cast<unsigned short*>(wbuf);  // [3][kBinWaves * G]
-    unsigned* roff = wbuf + wwords;              // [kBinBlock + 2] run offsets in the group
-    unsigned* rsrc = roff + kBinBlock + 2;       // [kBinBlock] run start within its tile
-    unsigned* wsum = rsrc + kBinBlock;           // [kWsumWords]
+    unsigned* croff = wbuf + wwords;             // [kBinBlock] listed runs: first arrival
+    unsigned* csrc = croff + kBinBlock;          // [kBinBlock] listed runs: tile << 16 | start
+    unsigned* bits = csrc + kBinBlock;           // [kWinWords] run starts in the window
+    unsigned* wpre = bits + kWinWords;           // [kWinWords + 2] their prefix, and total
+    unsigned* wsum = wpre + kWinWords + 2;       // [kWsumWords]
     unsigned* pid_of = wsum + kWsumWords;        // [G] pillar id of each slot, kNoPid if none kept
     // [G] cell key + 1 of each slot (8-byte aligned: every count above is even)
     unsigned long long* key_of = reinterpret_cast<unsigned long long*>(pid_of + G);
@@ -1892,6 +1932,7 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         fr = frank[i0];
         if (!first) fs = slot_of[i0];
     }
+    if (t < kWinWords) bits[t] = 0u;
     // the error word, one value for the whole block (the status below must
     // be block-uniform)
     const unsigned err = block_error(hdr);
@@ -1906,15 +1947,23 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         first_at[t] = i0;
     }
 
-    // one scan for two prefixes: the first group's run offsets and the tile
-    // counts of first occurrences
+    // one scan for three prefixes: the first group's run offsets, its
+    // listed runs, and the tile counts of first occurrences
     unsigned s = 0;
 #pragma unroll
     for (int u = 0; u < kScanPer; ++u) s += tc[u];
-    unsigned ng, distinct_u, ex;
-    const unsigned ro = block_excl_scan2<kBinWaves>(e >> 16, s, wsum, &ng, &ex, &distinct_u);
-    roff[t] = ro;
-    rsrc[t] = e & 0xffffu;
+    const unsigned sv[3] = {e >> 16, (e >> 16) != 0u ? 1u : 0u, s};
+    unsigned sx[3], st[3];
+    block_excl_scan_n<kBinWaves, 3>(sv, wsum, sx, st);
+    unsigned ng = st[0];
+    int nlist = (int)st[1];
+    const unsigned distinct_u = st[2];
+    unsigned ex = sx[2];
+    if ((e >> 16) != 0u) {
+        croff[sx[1]] = sx[0];
+        csrc[sx[1]] = ((unsigned)t << 16) | (e & 0xffffu);
+        if (sx[0] < (unsigned)kWin) atomicOr(&bits[sx[0] >> 5], 1u << (sx[0] & 31u));
+    }
 #pragma unroll
     for (int u = 0; u < kScanPer; ++u) {
         const int q = t * kScanPer + u;
@@ -1922,15 +1971,18 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         ex += tc[u];
     }
     __syncthreads();
+    prefix_window(bits, wpre);
+    __syncthreads();
     const long long distinct = distinct_u;
     const long long V = distinct < M ? distinct : M;
     int status = (int)V;
     if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
     if (err != 0u) status = VOX_STATUS_DEVICE_ERROR;
     // the first batch of staging words goes out now (unused when status <= 0)
-    int nruns = (int)(ptiles < kBinBlock ? ptiles : kBinBlock);
     unsigned v[kAhead], idx[kAhead];
-    load_arrivals(staging, roff, rsrc, 0, nruns, ptile, 0u, status > 0 ? ng : 0u, v, idx);
+    unsigned base = 0u;  // listed runs that start before the window
+    load_arrivals_ranked(staging, croff, csrc, bits, wpre, base, 0, ptile, 0u,
+                         status > 0 ? ng : 0u, v, idx);
     if (blockIdx.x == 0 && t == 0) {
         hdr->status = status;
         hdr->distinct = (int)distinct;
@@ -1965,18 +2017,37 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
         if (tg > 0) {
             // the next group of runs (the previous group's rounds have passed
-            // their barriers, so nobody reads roff / rsrc any more)
+            // their barriers, so nobody reads the listed runs any more)
             const long long tt = tg + t;
             e = 0u;
             if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
-            const unsigned r0 = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
-            roff[t] = r0;
-            rsrc[t] = e & 0xffffu;
-            nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+            const unsigned gv[2] = {e >> 16, (e >> 16) != 0u ? 1u : 0u};
+            unsigned gx2[2], gt[2];
+            block_excl_scan_n<kBinWaves, 2>(gv, wsum, gx2, gt);
+            ng = gt[0];
+            nlist = (int)gt[1];
+            if ((e >> 16) != 0u) {
+                croff[gx2[1]] = gx2[0];
+                csrc[gx2[1]] = ((unsigned)t << 16) | (e & 0xffffu);
+            }
+            base = 0u;
             __syncthreads();
         }
-        for (unsigned x0 = 0; x0 < ng; x0 += (unsigned)(kAhead * kBinBlock)) {
-            if (tg > 0 || x0 > 0) load_arrivals(staging, roff, rsrc, tg, nruns, ptile, x0, ng, v, idx);
+        for (unsigned x0 = 0; x0 < ng; x0 += (unsigned)kWin) {
+            if (tg > 0 || x0 > 0) {
+                // the window's start bits (the previous window's readers have
+                // passed the rounds' barriers)
+                if (x0 > 0) base += wpre[kWinWords];
+                __syncthreads();  // everyone has the old total
+                if (t < kWinWords) bits[t] = 0u;
+                __syncthreads();
+                mark_window(croff, nlist, x0, bits);
+                __syncthreads();
+                prefix_window(bits, wpre);
+                __syncthreads();
+                load_arrivals_ranked(staging, croff, csrc, bits, wpre, base, tg, ptile, x0, ng, v,
+                                     idx);
+            }
 #pragma unroll
             for (int u = 0; u < kAhead; ++u) {
                 const unsigned xr = x0 + (unsigned)(u * kBinBlock);
@@ -2333,7 +2404,8 @@ inline size_t bins_fb_lds_bytes(int G, int K) {
     const size_t ww = (size_t)3 * kBinWaves * G / 2 > (size_t)kScanTiles
                           ? (size_t)3 * kBinWaves * G / 2 : (size_t)kScanTiles;
     // (the words before key_of are an even count: it is 8-byte aligned)
-    return 4u * ((size_t)G + ww + kBinBlock + 2 + kBinBlock + kWsumWords + (size_t)G) +
+    return 4u * ((size_t)G + ww + kBinBlock + kBinBlock + kWinWords + kWinWords + 2 +
+                 kWsumWords + (size_t)G) +
            8u * (size_t)G + 8u * (size_t)G + 4u * (size_t)G * K;
 }
 constexpr int kFbMaxIds = 256;     // pillar slots per k_bins_fb bin, at most

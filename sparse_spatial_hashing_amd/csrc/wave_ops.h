@@ -46,63 +46,68 @@ __device__ __forceinline__ unsigned row16_incl_scan(unsigned v) {
     return v;
 }
 
-// LDS words a block scan below needs (wsum): the wavefronts' totals of up to
-// two sums in [0, 32), their exclusive prefixes in [32, 64), the block totals
-// in 64 and 65.
-constexpr int kWsumWords = 66;
+// LDS words the block scans below need (wsum): the wavefronts' totals of up
+// to four sums (row i of 16 words each) in [0, 64), their exclusive prefixes
+// in [64, 128), the block totals in [128, 132).
+constexpr int kWsumWords = 132;
 
-// Exclusive prefix sum over the block (NW <= 16 wavefronts); *total gets the
-// sum. The wavefront totals are scanned once, by wavefront 0, and every
-// wavefront reads its own prefix. Contains two barriers; wsum may be reused
-// by the next scan right away.
-template <int NW>
-__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, unsigned* total) {
+// NV exclusive prefix sums over the block at once (NW <= 16 wavefronts,
+// NV <= 4): ex[i] gets value i's prefix, tot[i] its block total. Wavefront 0
+// scans the wavefront totals, sum i in its row i of 16 lanes, and every
+// wavefront reads its own prefixes. Contains two barriers; wsum may be
+// reused by the next scan right away.
+template <int NW, int NV>
+__device__ __forceinline__ void block_excl_scan_n(const unsigned (&v)[NV], unsigned* wsum,
+                                                  unsigned (&ex)[NV], unsigned (&tot)[NV]) {
     static_assert(NW >= 1 && NW <= 16, "one row of 16 lanes scans the wavefront totals");
+    static_assert(NV >= 1 && NV <= 4, "one row of wavefront 0 per sum");
     const int lane = __lane_id();
     const int w = threadIdx.x / kWave;
-    const unsigned incl = wave_incl_scan(v, lane);
-    if (lane == kWave - 1) wsum[w] = incl;
-    __syncthreads();
-    if (w == 0) {
-        const unsigned x = lane < NW ? wsum[lane] : 0u;
-        const unsigned xi = row16_incl_scan(x);
-        if (lane < NW) wsum[32 + lane] = xi - x;
-        if (lane == 15) wsum[64] = xi;
+    unsigned incl[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) incl[i] = wave_incl_scan(v[i], lane);
+    if (lane == kWave - 1) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) wsum[16 * i + w] = incl[i];
     }
     __syncthreads();
-    *total = wsum[64];
-    return wsum[32 + w] + incl - v;
+    if (w == 0) {
+        const bool in = lane < 16 * NV && (lane & 15) < NW;
+        const unsigned x = in ? wsum[lane] : 0u;
+        const unsigned xi = row16_incl_scan(x);
+        if (in) wsum[64 + lane] = xi - x;
+        if ((lane & 15) == 15 && lane < 16 * NV) wsum[128 + (lane >> 4)] = xi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        tot[i] = wsum[128 + i];
+        ex[i] = wsum[64 + 16 * i + w] + incl[i] - v[i];
+    }
+}
+
+// Exclusive prefix sum over the block; *total gets the sum. Two barriers.
+template <int NW>
+__device__ __forceinline__ unsigned block_excl_scan(unsigned v, unsigned* wsum, unsigned* total) {
+    const unsigned vv[1] = {v};
+    unsigned ex[1], tot[1];
+    block_excl_scan_n<NW, 1>(vv, wsum, ex, tot);
+    *total = tot[0];
+    return ex[0];
 }
 
 // Two exclusive prefix sums over the block at once (a and b); totals in *ta
-// and *tb, b's prefix in *eb, a's returned. The two sets of wavefront totals
-// are scanned side by side in rows 0 and 1 of wavefront 0. Two barriers.
+// and *tb, b's prefix in *eb, a's returned. Two barriers.
 template <int NW>
 __device__ __forceinline__ unsigned block_excl_scan2(unsigned a, unsigned b, unsigned* wsum,
                                                      unsigned* ta, unsigned* eb, unsigned* tb) {
-    static_assert(NW >= 1 && NW <= 16, "one row of 16 lanes scans the wavefront totals");
-    const int lane = __lane_id();
-    const int w = threadIdx.x / kWave;
-    const unsigned ia = wave_incl_scan(a, lane);
-    const unsigned ib = wave_incl_scan(b, lane);
-    if (lane == kWave - 1) {
-        wsum[w] = ia;
-        wsum[16 + w] = ib;
-    }
-    __syncthreads();
-    if (w == 0) {
-        const bool in = lane < 32 && (lane & 15) < NW;
-        const unsigned x = in ? wsum[lane] : 0u;
-        const unsigned xi = row16_incl_scan(x);
-        if (in) wsum[32 + lane] = xi - x;
-        if (lane == 15) wsum[64] = xi;
-        if (lane == 31) wsum[65] = xi;
-    }
-    __syncthreads();
-    *ta = wsum[64];
-    *tb = wsum[65];
-    *eb = wsum[48 + w] + ib - b;
-    return wsum[32 + w] + ia - a;
+    const unsigned vv[2] = {a, b};
+    unsigned ex[2], tot[2];
+    block_excl_scan_n<NW, 2>(vv, wsum, ex, tot);
+    *ta = tot[0];
+    *tb = tot[1];
+    *eb = ex[1];
+    return ex[0];
 }
 
 // Block bid of a grid of n blocks -> tile: XCD x = bid % 8 takes the
