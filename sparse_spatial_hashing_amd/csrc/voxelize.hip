@@ -2011,7 +2011,7 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
     for (int x = t; x < 3 * kBinWaves * G / 2; x += kBinBlock) wbuf[x] = 0u;
     unsigned round = 0;
-    bool has_row = false;     // a row loaded in the previous round, stored in this one
+    bool has_row = false;     // one-round bins: this thread's row is kept
     float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
     long long row_at = 0;
     for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
@@ -2066,6 +2066,10 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
                     valid = pid != kNoPid;  // points of pillars past the cap are dropped
                 }
                 if (!valid) pl = 0u;
+                // a one-round bin loads every kept arrival's row now, before
+                // its rank is known, so that the load overlaps the ranking;
+                // rows ranked past max_points are not stored
+                if (one_round) row = pts[valid && src < N ? src : 0u];
                 // counts of three rounds rotate: round r writes buffer r % 3
                 // and clears (r + 1) % 3, last read two rounds ago
                 unsigned short* cur = wcnt + (round % 3u) * (kBinWaves * G);
@@ -2098,8 +2102,7 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
                         if (!one_round) {
                             best[pl * K + r] = src;
                         } else if (src < N) {
-                            row = pts[src];  // stored after the round
-                            row_at = (long long)pid * K + r;
+                            row_at = (long long)pid * K + r;  // the row is stored after the round
                             has_row = true;
                         } else {
                             report_error(hdr, num_voxels, 8u);
