@@ -1970,19 +1970,19 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         if (q < ptp) wbuf[q] = ex;
         ex += tc[u];
     }
-    __syncthreads();
-    prefix_window(bits, wpre);
+    // This bin's cells are done with their claim state: back to zero. The
+    // stores go out after the last use of a loaded value and before the
+    // staging loads: nothing waits on memory until the walk, whose first
+    // wait they long precede, and the compiler's wait counts for the
+    // staging loads are not blurred by stores issued after them.
+    if (t < Gb) release_slot(first, cells, fkey, table, S, slot_of, i0, fk, fs, hdr, num_voxels);
     __syncthreads();
     const long long distinct = distinct_u;
     const long long V = distinct < M ? distinct : M;
     int status = (int)V;
     if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
     if (err != 0u) status = VOX_STATUS_DEVICE_ERROR;
-    // the first batch of staging words goes out now (unused when status <= 0)
-    unsigned v[kAhead], idx[kAhead];
-    unsigned base = 0u;  // listed runs that start before the window
-    load_arrivals_ranked(staging, croff, csrc, bits, wpre, base, 0, ptile, 0u,
-                         status > 0 ? ng : 0u, v, idx);
+    prefix_window(bits, wpre);
     if (blockIdx.x == 0 && t == 0) {
         hdr->status = status;
         hdr->distinct = (int)distinct;
@@ -1997,19 +1997,23 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
         }
         pid_of[t] = mypid;
     }
-    // This bin's cells are done with their claim state: back to zero. The
-    // stores go out now, behind the first batch of staging loads: vector
-    // memory operations complete in order, so stores issued before the scan
-    // would have held up its waits, and stores at the end would add their
-    // round trip to the block's tail.
-    if (t < Gb) release_slot(first, cells, fkey, table, S, slot_of, first_at[t], key_of[t],
-                             slot_at[t], hdr, num_voxels);
+    __syncthreads();  // the window prefix, pid_of written; the tile prefix in wbuf read
+    // the first batch of staging words goes out now (unused when status <= 0)
+    unsigned v[kAhead], idx[kAhead];
+    unsigned base = 0u;  // listed runs that start before the window
+    load_arrivals_ranked(staging, croff, csrc, bits, wpre, base, 0, ptile, 0u,
+                         status > 0 ? ng : 0u, v, idx);
     if (status <= 0) return;  // block-uniform: nothing kept, or no decision
-    __syncthreads();          // the tile prefix in wbuf is read; pid_of is written
     const bool one_round = ptiles <= kBinBlock && ng <= (unsigned)kBinBlock;  // block-uniform
 
+    // each wavefront clears its own counts in the three rotating buffers (in
+    // a round only wavefront w writes entries w G to w G + G - 1), so no
+    // barrier is needed before the first round writes them
     for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
-    for (int x = t; x < 3 * kBinWaves * G / 2; x += kBinBlock) wbuf[x] = 0u;
+    for (int x = lane; x < G; x += kWave) {
+#pragma unroll
+        for (int r3 = 0; r3 < 3; ++r3) wcnt[r3 * (kBinWaves * G) + w * G + x] = 0u;
+    }
     unsigned round = 0;
     bool has_row = false;     // one-round bins: this thread's row is kept
     float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
