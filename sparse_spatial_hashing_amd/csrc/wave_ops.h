@@ -61,7 +61,11 @@ __device__ __forceinline__ void block_excl_scan_n(const unsigned (&v)[NV], unsig
                                                   unsigned (&ex)[NV], unsigned (&tot)[NV]) {
     static_assert(NW >= 1 && NW <= 16, "one row of 16 lanes scans the wavefront totals");
     static_assert(NV >= 1 && NV <= 4, "one row of wavefront 0 per sum");
-    const int lane = __lane_id();
+    int lane = __lane_id();
+    // an empty asm that "changes" the lane id: the LDS addresses derived
+    // from it are then computed here, not hoisted out of a caller's loop to
+    // be held (or spilled) across it
+    asm volatile("" : "+v"(lane));
     const int w = threadIdx.x / kWave;
     unsigned incl[NV];
 #pragma unroll
