@@ -1017,11 +1017,9 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     const int nbins = 1 << nbits;
     const unsigned bmask = (unsigned)nbins - 1u;
     const int nb = status > 0 ? nbins : 0;
-    for (int b = t; b < nb; b += BLK) {
-#pragma unroll
-        for (int ww = 0; ww < WPB; ++ww) hist[ww][b] = 0u;
-    }
-    __syncthreads();
+    // each wavefront clears its own histogram (only it writes it before the
+    // barrier that follows the ranking), so no barrier is needed here
+    for (int b = lane; b < nb; b += kWave) hist[w][b] = 0u;
 
     // lookups go to the kept-cell table when there is one (found = kept)
     const unsigned long long* __restrict__ look = C > 0 ? compact : table;
@@ -1355,10 +1353,9 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     const bool any_rest = base + TILE > P && base < N;     // block-uniform
     const int nbins = 1 << nbits;
     const unsigned bmask = (unsigned)nbins - 1u;
-    for (int b = t; b < nbins; b += BLK) {
-#pragma unroll
-        for (int ww = 0; ww < WPB; ++ww) hist[ww][b] = 0u;
-    }
+    // each wavefront clears its own histogram (only it writes it before the
+    // barrier that follows the ranking)
+    for (int b = lane; b < nbins; b += kWave) hist[w][b] = 0u;
 
     unsigned i0v[PER];             // the point's pillar as its first index, or kNoPid
     bool isf[PER];                 // a first occurrence (i0 == i)
@@ -1460,8 +1457,7 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
         fb[k] = wf + (unsigned)__popcll(bb & lanes_below(lane));
         wf += (unsigned)__popcll(bb);
     }
-    if (lane == 0) wfirst[w] = wf;
-    __syncthreads();  // histograms cleared, wavefront counts in
+    if (lane == 0) wfirst[w] = wf;  // read after the ranking's barrier
 
     // rank among equal bins inside this wavefront's stretch (as k_part)
     unsigned pos[PER];
