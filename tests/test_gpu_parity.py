@@ -517,6 +517,19 @@ def test_largest_partition_tiles(name):
     assert_bitwise(gpu_vox(pts, params_of(cfg), select_path=3), want, f"{name} carried")
 
 
+@pytest.mark.parametrize("name", ["kitti_frame", "voxel3d"])
+def test_more_than_one_group_of_runs(name):
+    """Past 2^23 points the partition has more tiles (runs per bin) than one
+    bins block takes at once (1,024): the first-index bins walk a second
+    group of runs, listed and rank-queried anew. 2^23 + 12,345 points give
+    1,026 tiles, the last one ragged."""
+    cfg = get_config(name)
+    pts, _ = generate(name, n=(1 << 23) + 12345)
+    say(f"two groups of runs {name} N={pts.shape[0]}")
+    want = oracle.voxelize_params(pts, cfg.params)
+    assert_bitwise(gpu_vox(pts, params_of(cfg)), want, f"{name} route 4")
+
+
 @pytest.mark.parametrize("per_cell,K", [(70, 64), (200, 32), (40, 5)])
 def test_bin_spanning_several_chunks(per_cell, K):
     """64 cells that share one pillar-id bin, with more candidates than one
