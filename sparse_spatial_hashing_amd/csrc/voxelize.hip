@@ -178,6 +178,16 @@ __device__ __forceinline__ unsigned home_slot(long long key, unsigned S, int has
     return __umulhi(h, S);
 }
 
+// First-index route on the table: a byte filter of 2^(32 - shift) entries,
+// one byte per hash of a prefix cell, set (to 1) by the claim. A lookup past
+// the prefix whose byte is 0 has no prefix point in its cell and skips the
+// table; the others probe it. Plain byte stores of the same value need no
+// atomics, and the bins kernel clears each first occurrence's byte.
+__device__ __forceinline__ unsigned filt_index(long long key, int shift) {
+    const unsigned h = ((unsigned)key ^ (unsigned)((unsigned long long)key >> 32)) * 0x85EBCA77u;
+    return h >> shift;
+}
+
 // Lookups read the aligned slot pair holding the home slot first (16 bytes);
 // when that does not settle it, they probe a cache line at a time: the 16
 // slots (128 bytes) of the line come in with eight independent 16-byte loads,
@@ -318,7 +328,8 @@ __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pt
                                                    unsigned S, int hash,
                                                    int* __restrict__ slot_of,
                                                    Header* __restrict__ hdr, int count_claims,
-                                                   int merge, int kbits) {
+                                                   int merge, int kbits,
+                                                   unsigned char* __restrict__ filt, int fshift) {
     const long long i = begin + (long long)blockIdx.x * kBlock + threadIdx.x;
     const int lane = __lane_id();
     bool claimed = false;
@@ -365,6 +376,7 @@ __global__ __launch_bounds__(kBlock) void k_insert(const float4* __restrict__ pt
         const int ls = __shfl(out, leader);
         if (key >= 0) out = ls;
     }
+    if (filt && key >= 0) filt[filt_index(key, fshift)] = 1u;
     if (i < end) slot_of[i] = out;
     if (count_claims) {
         // only the chunked path reads the number of cells; one atomic per wave
@@ -1335,7 +1347,7 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     unsigned* __restrict__ cm, unsigned* __restrict__ staging,
     unsigned long long* __restrict__ fkey, unsigned* __restrict__ frank,
     unsigned* __restrict__ tile_firsts, Header* __restrict__ hdr,
-    int* __restrict__ point_pillar) {
+    int* __restrict__ point_pillar, const unsigned char* __restrict__ filt, int fltshift) {
     constexpr int TILE = BLK * PER;
     constexpr int WPB = BLK / kWave;
     constexpr int BPT = kMaxBins / BLK;
@@ -1411,6 +1423,15 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
 #pragma unroll
                 for (int k = 0; k < PER_B; ++k)
                     rk[k] = (ii[k] >= P && ii[k] < N) ? bin_key(row[k], g) : -1;
+                if (filt) {  // uniform: cells whose filter byte is 0 skip the table
+                    unsigned char fv[PER_B];
+#pragma unroll
+                    for (int k = 0; k < PER_B; ++k)
+                        fv[k] = filt[rk[k] >= 0 ? filt_index(rk[k], fltshift) : 0u];
+#pragma unroll
+                    for (int k = 0; k < PER_B; ++k)
+                        if (fv[k] == 0u) rk[k] = -1;
+                }
                 unsigned long long rw[PER_B];
                 probe_batch<PER_B>(table, S, hash, rk, rw, hdr);
 #pragma unroll
@@ -1856,7 +1877,8 @@ __device__ __forceinline__ void release_slot(unsigned* __restrict__ first,
                                              unsigned long long* __restrict__ table, unsigned S,
                                              int* __restrict__ slot_of, unsigned i0,
                                              unsigned long long fk, int fs, Header* hdr,
-                                             int* num_voxels) {
+                                             int* num_voxels, unsigned char* __restrict__ filt,
+                                             int fltshift) {
     if (fk == 0ull) return;
     if (first) {
         if (fk - 1ull < cells) first[fk - 1ull] = 0u;
@@ -1865,6 +1887,7 @@ __device__ __forceinline__ void release_slot(unsigned* __restrict__ first,
         if (fs >= 0 && (unsigned)fs < S) table[fs] = 0ull;
         else report_error(hdr, num_voxels, 16u);
         slot_of[i0] = 0;
+        if (filt) filt[filt_index((long long)(fk - 1ull), fltshift)] = 0u;
     }
     fkey[i0] = 0ull;
 }
@@ -1880,7 +1903,8 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
                int* __restrict__ slot_of, int gx, int gy, float4* __restrict__ voxels,
                int* __restrict__ coords, int* __restrict__ num_points,
                int* __restrict__ num_voxels, int* __restrict__ point_pillar,
-               Header* __restrict__ hdr, int nt_out, long long zero_words) {
+               Header* __restrict__ hdr, int nt_out, long long zero_words,
+               unsigned char* __restrict__ filt, int fltshift) {
     extern __shared__ unsigned lds[];
     const int G = 1 << gshift;
     // per-wavefront counts are 16-bit (a wavefront adds at most 64 arrivals
@@ -1971,7 +1995,9 @@ void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, 
     // staging loads: nothing waits on memory until the walk, whose first
     // wait they long precede, and the compiler's wait counts for the
     // staging loads are not blurred by stores issued after them.
-    if (t < Gb) release_slot(first, cells, fkey, table, S, slot_of, i0, fk, fs, hdr, num_voxels);
+    if (t < Gb)
+        release_slot(first, cells, fkey, table, S, slot_of, i0, fk, fs, hdr, num_voxels, filt,
+                     fltshift);
     __syncthreads();
     const long long distinct = distinct_u;
     const long long V = distinct < M ? distinct : M;
@@ -2382,12 +2408,13 @@ struct Plan {
     // merge = lane merge before the claim atomics; first_map = 1 forbids the
     // direct cell map
     int fb, fbits, fshift, merge, first_map, kmap_ok;
+    int fltshift;  // first-index route on the table: 32 - log2(filter bytes)
     long long ptp;
     size_t fblds;
     // byte offsets into the workspace; [0, zero_bytes) is zero between calls,
     // [zero_bytes, bytes) is scratch every call writes before reading
     size_t off_table, off_slot, off_tiles, off_occ, off_kept, off_cnt, off_bucket, off_ovf,
-        off_compact, off_kcs, off_map, off_fkey, off_cm, off_stage, off_stage_pt, off_frank,
+        off_compact, off_kcs, off_map, off_fkey, off_filt, off_cm, off_stage, off_stage_pt, off_frank,
         off_tfirst, zero_bytes, bytes;
 };
 
@@ -2591,6 +2618,17 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     // first-index route: the cell key + 1 of each first occurrence in [0, P)
     pl->off_fkey = off;
     off = align256(off + (pl->fb ? (size_t)(P > 0 ? P : 1) * sizeof(unsigned long long) : 0));
+    // first-index route: the claim's byte filter (used when the claim fills
+    // the table), about 8 bytes per prefix point, a power of two from 64 KiB
+    // to 4 MiB
+    pl->fltshift = 0;
+    pl->off_filt = off;
+    if (pl->fb) {
+        int lb = 16;
+        while (lb < 22 && (1ll << lb) < 8 * (P > 0 ? P : 1)) ++lb;
+        pl->fltshift = 32 - lb;
+        off = align256(off + ((size_t)1 << lb));
+    }
     pl->zero_bytes = off;  // the scratch tail starts here
     pl->off_cm = off;
     const long long cm_bins = pl->fb && (1ll << pl->fbits) > pl->nbins ? (1ll << pl->fbits)
@@ -2670,6 +2708,7 @@ struct Buffers {
     unsigned long long* fkey;
     unsigned* frank;
     unsigned* tfirst;
+    unsigned char* filt;  // the claim's byte filter (first-index route on the table), or null
 };
 
 Buffers carve(void* ws, const Plan& pl, const Grid& g) {
@@ -2697,6 +2736,7 @@ Buffers carve(void* ws, const Plan& pl, const Grid& g) {
     x.first = (pl.fb && !pl.first_map && pl.mapn > 0 && cells <= pl.mapn)
                   ? reinterpret_cast<unsigned*>(b + pl.off_map) : nullptr;
     x.fkey = reinterpret_cast<unsigned long long*>(b + pl.off_fkey);
+    x.filt = (pl.fb && !x.first) ? reinterpret_cast<unsigned char*>(b + pl.off_filt) : nullptr;
     x.frank = reinterpret_cast<unsigned*>(b + pl.off_frank);
     x.tfirst = reinterpret_cast<unsigned*>(b + pl.off_tfirst);
     return x;
@@ -2730,7 +2770,7 @@ int launch_insert(const float* points, long long begin, long long end, const Gri
     hipExtLaunchKernelGGL(k_insert, dim3(blocks), dim3(kBlock), 0, st, ev_start(ev), ev_stop(ev), 0,
                        reinterpret_cast<const float4*>(points), begin, end, g, bf.table,
                        (unsigned)pl.S, pl.hash, bf.slot_of, bf.hdr, count_claims, pl.merge,
-                       key_bits(g));
+                       key_bits(g), bf.filt, pl.fltshift);
     return last_launch();
 }
 
@@ -2754,13 +2794,14 @@ int launch_part_fb_t(const float* points, const Grid& g, const Plan& pl, const B
                               ev_start(ev), ev_stop(ev), 0, reinterpret_cast<const float4*>(points),
                               pl.N, pl.P, g, bf.table, (unsigned)pl.S, pl.hash, bf.first,
                               bf.slot_of, pl.fbits, pl.ptiles, bf.cm, bf.stage, bf.fkey, bf.frank,
-                              bf.tfirst, bf.hdr, point_pillar);
+                              bf.tfirst, bf.hdr, point_pillar, bf.filt, pl.fltshift);
     else
         hipExtLaunchKernelGGL(k_part_fb<PER, BLK, false>, dim3((unsigned)pl.ptiles), dim3(BLK), 0,
                               st, ev_start(ev), ev_stop(ev), 0,
                               reinterpret_cast<const float4*>(points), pl.N, pl.P, g, bf.table,
                               (unsigned)pl.S, pl.hash, bf.first, bf.slot_of, pl.fbits, pl.ptiles,
-                              bf.cm, bf.stage, bf.fkey, bf.frank, bf.tfirst, bf.hdr, point_pillar);
+                              bf.cm, bf.stage, bf.fkey, bf.frank, bf.tfirst, bf.hdr, point_pillar,
+                              bf.filt, pl.fltshift);
     return last_launch();
 }
 
@@ -2789,7 +2830,8 @@ int launch_bins_fb(const float* points, const Grid& g, const Plan& pl, const Buf
                           (unsigned long long)g.gx * g.gy * g.gz, bf.table, (unsigned)pl.S,
                           bf.slot_of, g.gx, g.gy,
                           reinterpret_cast<float4*>(voxels), coords, num_points, num_voxels,
-                          point_pillar, bf.hdr, nt_out, (long long)(pl.zero_bytes / 4));
+                          point_pillar, bf.hdr, nt_out, (long long)(pl.zero_bytes / 4), bf.filt,
+                          pl.fltshift);
     return last_launch();
 }
 
@@ -2934,10 +2976,14 @@ int insert_chunked(const float* points, const Grid& g, const Plan& pl, const Buf
     long long have = 0;
     const long long half = pl.S / 2;
     int rc;
+    // the rank, select and pack kernels that follow never clear the
+    // first-index route's key filter, so the chunks leave it untouched
+    Buffers nb = bf;
+    nb.filt = nullptr;
     while (done < pl.N && have < pl.M) {
         long long chunk = half - have;
         if (chunk > pl.N - done) chunk = pl.N - done;
-        if ((rc = launch_insert(points, done, done + chunk, g, pl, bf, stream, 1, nullptr)) !=
+        if ((rc = launch_insert(points, done, done + chunk, g, pl, nb, stream, 1, nullptr)) !=
             VOX_OK)
             return rc;
         done += chunk;
