@@ -228,7 +228,7 @@ int voxelize_map(const float* points, int64_t n_points, const float range[6],
  *   - Size limit: a call whose vox_workspace_bytes(n_points, max_voxels,
  *     max_points, NULL) exceeds the array returns VOX_ESCRATCH before any HIP
  *     call (with the defaults: 2,097,152 points at 60,000 pillars need about
- *     42 MiB).
+ *     43 MiB).
  *   - Set-up: the first call on a device takes the array's device address and
  *     enqueues a kernel that clears it on `stream`; keep that first call out
  *     of graph capture. Later calls enqueue only the voxelization kernels (and,
@@ -265,8 +265,8 @@ int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,
              int32_t* bucket_cap);
 
 /*
- * Voxel-grid downsampling (NEXT row f3; the voxel_downsample operation, section
- * 4.4 "operation 1", of the GPU K-D tree ICP page, which truncates the cell
+ * Voxel-grid downsampling (the voxel_downsample operation, section 4.4
+ * "operation 1", of the GPU K-D tree ICP page, which truncates the cell
  * index and averages with float atomics). One mean point per kept voxel:
  *   - binning, voxel numbering in first-occurrence order and the max_voxels
  *     cap are voxelize()'s (floorf cell index, same reject rules);

@@ -13,11 +13,13 @@
 //           non-returning atomicMax in a map indexed by cell (grids of at
 //           most 2 S cells) or, for larger grids, a CAS claim plus an
 //           atomicMax in a linear-probe table of 64-bit words (key and
-//           lowest index). The first max_voxels cells in first-occurrence
+//           lowest index), with a plain byte store into a filter indexed by
+//           a hash of the cell. The first max_voxels cells in first-occurrence
 //           order are all among these P points, or the call says it cannot
 //           decide (VOX_STATUS_NEEDS_CHUNKED).
 //   part    every point: bin, look up its cell's lowest prefix index i0 (no
-//           entry: its pillar is past the cap), and partition the tile's
+//           entry: its pillar is past the cap; on the table, a zero filter
+//           byte settles that without a probe), and partition the tile's
 //           points by bin i0 mod nbins, keeping index order inside each bin's
 //           run; prefix tiles also count their first occurrences (i == i0)
 //           and rank them inside the tile.
