@@ -1894,7 +1894,13 @@ __device__ __forceinline__ void release_slot(unsigned* __restrict__ first,
     fkey[i0] = 0ull;
 }
 
-__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8)))
+// WPE: wavefronts per SIMD the kernel is compiled for. 8 (at most 64 VGPRs)
+// lets two blocks share a CU, which plans of more bins than CUs need; with 4
+// a block has the CU to itself, and the extra SGPRs keep the kernel's
+// arguments out of VGPR lanes (at 8 the compiler spills several dozen and
+// reloads them with v_readlane inside the walk).
+template <int WPE>
+__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(WPE)))
 void k_bins_fb(const float4* __restrict__ pts, long long N, long long P, int M, int K,
                const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
                long long ptiles, int ptile, int tshift, int gshift, int nbits,
@@ -2442,6 +2448,7 @@ inline size_t bins_fb_lds_bytes(int G, int K) {
 }
 constexpr int kFbMaxIds = 256;     // pillar slots per k_bins_fb bin, at most
 constexpr int kFbOneRound = 512;   // k_bins_fb blocks that fit the chip at once (2 per CU)
+constexpr int kFbOneBlockPerCu = 256;  // bins that get one k_bins_fb block per CU (256 CUs)
 
 inline bool finite_f(float v) { return isfinite(v); }
 
@@ -2825,7 +2832,9 @@ int launch_bins_fb(const float* points, const Grid& g, const Plan& pl, const Buf
     const long long tile = (long long)pl.pblock * pl.pper;
     int tshift = 0;
     while ((1ll << tshift) < tile) ++tshift;
-    hipExtLaunchKernelGGL(k_bins_fb, dim3(1u << pl.fbits), dim3(kBinBlock), (unsigned)pl.fblds, st,
+    // up to one bin per CU: the kernel built for one block per CU
+    hipExtLaunchKernelGGL((1 << pl.fbits) <= kFbOneBlockPerCu ? &k_bins_fb<4> : &k_bins_fb<8>,
+                          dim3(1u << pl.fbits), dim3(kBinBlock), (unsigned)pl.fblds, st,
                           ev_start(ev), ev_stop(ev), 0, reinterpret_cast<const float4*>(points),
                           pl.N, pl.P, pl.M, pl.K, bf.cm, bf.stage, pl.ptiles, (int)tile, tshift,
                           pl.fshift, pl.fbits, bf.tfirst, (int)pl.ptp, bf.fkey, bf.frank, bf.first,
