@@ -276,10 +276,13 @@ __device__ __forceinline__ void report_error(Header* hdr, int* num_voxels, unsig
 // The error word as this block sees it when it starts: read by one thread
 // and shared through LDS, so that every thread of the block takes the same
 // branch (another block may set the word meanwhile). Contains a barrier.
+// A plain load: earlier kernels' writes are visible at this kernel's start,
+// and a block that misses a word set meanwhile by another block of this
+// kernel is a case the heal already allows for; a relaxed agent-scope load
+// would go past the L2 on every block, and the whole block waits for it.
 __device__ __forceinline__ unsigned block_error(const Header* hdr) {
     __shared__ unsigned err_sh;
-    if (threadIdx.x == 0)
-        err_sh = __hip_atomic_load(&hdr->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) err_sh = hdr->error;
     __syncthreads();
     return err_sh;
 }
