@@ -279,8 +279,12 @@ int vox_plan(int64_t n_points, int32_t max_voxels, int32_t max_points,
  * f32, 16-byte aligned; coords [max_voxels,3] i32; counts [max_voxels] i32;
  * num_voxels [1] i32 receives V or a VOX_STATUS_* code, as for voxelize().
  * Rows [0, V) are written, rows past V untouched. options: table_slots,
- * prefix_points, hash and compact_table apply; select_path must be 0 or 3
- * (the route with rows carried is the only one); max_voxels <= 262144.
+ * prefix_points, hash, compact_table, kept_map, first_map, lane_merge and
+ * bin_ids apply; select_path 0 (automatic: route 4 with rows carried where
+ * it applies, as for voxelize(), else 3), 3 (rows carried through route 2's
+ * partition) or 4 (VOX_EINVAL where it does not apply); others VOX_EINVAL;
+ * max_voxels <= 262144. Route 4's workspace also holds route 3's layout,
+ * which the chunked path takes.
  * chunked = 1 inserts chunk by chunk with a host sync between chunks (needed
  * when the status is VOX_STATUS_NEEDS_CHUNKED). The workspace follows the
  * rules of vox_workspace_bytes() with the two sizes below. Asynchronous on

@@ -346,16 +346,19 @@ def downsample_workspace_bytes(n_points: int, max_voxels: int, **opts) -> Tuple[
 def downsample(points: torch.Tensor, range_: Sequence[float], cell: Sequence[float],
                grid: Sequence[int], max_voxels: int, *, table_slots: int = 0,
                prefix_points: int = 0, hash: int = 0, compact_table: int = 0, kept_map: int = 0,
+               select_path: int = 0, first_map: int = 0, lane_merge: int = 0, bin_ids: int = 0,
                chunked: bool = False):
     """Voxel-grid downsampling: (centroids [V,4] f32 (x, y, z, intensity means),
     coords [V,3] i32 (z, y, x), counts [V] i32) for the first max_voxels voxels
-    in first-occurrence order. The chunked route is taken when the single pass
-    reports that the cap could not be decided."""
+    in first-occurrence order. select_path 0 (automatic: the first-index
+    route where it applies, else 3), 3 or 4. The chunked route is taken when
+    the single pass reports that the cap could not be decided."""
     _check_points(points)
     dev = points.device
     N, M = points.shape[0], int(max_voxels)
     kw = dict(table_slots=table_slots, prefix_points=prefix_points, hash=hash,
-              compact_table=compact_table, kept_map=kept_map)
+              compact_table=compact_table, kept_map=kept_map, select_path=select_path,
+              first_map=first_map, lane_merge=lane_merge, bin_ids=bin_ids)
     opts = _options(**kw)
     nbytes, zbytes = downsample_workspace_bytes(N, M, **kw)
     with torch.cuda.device(dev):

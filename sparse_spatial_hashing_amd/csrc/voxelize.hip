@@ -1343,8 +1343,9 @@ __device__ __forceinline__ void probe_batch(const unsigned long long* __restrict
 // DIRECT: the cell's entry in the direct map `first` (grids of at most
 // 2 S cells); otherwise prefix points read their word through slot_of and
 // later points probe the table. Block layout, ranking by bin, the count
-// table and the staging words are k_part's.
-template <int PER, int BLK, bool DIRECT>
+// table and the staging words are k_part's. CARRY (downsampling): each
+// staged point's row is also copied to stage_pt next to its staging word.
+template <int PER, int BLK, bool DIRECT, bool CARRY = false>
 __global__ __launch_bounds__(BLK) void k_part_fb(
     const float4* __restrict__ pts, long long N, long long P, Grid g,
     const unsigned long long* __restrict__ table, unsigned S, int hash,
@@ -1352,7 +1353,8 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     unsigned* __restrict__ cm, unsigned* __restrict__ staging,
     unsigned long long* __restrict__ fkey, unsigned* __restrict__ frank,
     unsigned* __restrict__ tile_firsts, Header* __restrict__ hdr,
-    int* __restrict__ point_pillar, const unsigned char* __restrict__ filt, int fltshift) {
+    int* __restrict__ point_pillar, const unsigned char* __restrict__ filt, int fltshift,
+    float4* __restrict__ stage_pt) {
     constexpr int TILE = BLK * PER;
     constexpr int WPB = BLK / kWave;
     constexpr int BPT = kMaxBins / BLK;
@@ -1377,6 +1379,7 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     unsigned i0v[PER];             // the point's pillar as its first index, or kNoPid
     bool isf[PER];                 // a first occurrence (i0 == i)
     unsigned long long k1v[PER];   // cell key + 1 (first occurrences)
+    float4 rowk[CARRY ? PER : 1];  // CARRY: each point's row, kept to the staging stores
 #pragma unroll
     for (int k0 = 0; k0 < PER; k0 += PER_B) {
         long long ii[PER_B];
@@ -1403,7 +1406,17 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
             }
 #pragma unroll
             for (int k = 0; k < PER_B; ++k) wd[k] = f[k];
+            if (CARRY) {
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k) rowk[k0 + k] = row[k];
+            }
         } else {
+            if (CARRY) {  // prefix points' rows too (the lookups below load only the rest)
+#pragma unroll
+                for (int k = 0; k < PER_B; ++k)
+                    rowk[k0 + k] = base < N ? pts[ii[k] < N ? ii[k] : N - 1]
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
             if (any_prefix) {
                 int sl[PER_B];
                 unsigned long long tw[PER_B];
@@ -1546,7 +1559,9 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
         if (i0v[k] == kNoPid) continue;
         const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);
         const unsigned bin = i0v[k] & bmask;
-        staging[base + hist[w][bin] + pos[k]] = ((i0v[k] >> nbits) << 16) | local;
+        const unsigned at = hist[w][bin] + pos[k];
+        staging[base + at] = ((i0v[k] >> nbits) << 16) | local;
+        if (CARRY) stage_pt[base + at] = rowk[k];  // the row, bit for bit
         if (isf[k]) {
             const long long i = base + local;
             frank[i] = woff + fb[k];
@@ -2368,6 +2383,226 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
     }
 }
 
+// Downsampling on the first-index route: the bins of k_bins_fb (slot j of
+// bin b is the cell whose lowest prefix index is i0 = b + j nbins; its id
+// comes from the prefix tiles' counts, ids below max_voxels are kept) with
+// k_centroid's sums. The rows arrive carried (stage_pt), bin after bin in
+// index order; each round's arrivals are grouped by slot in LDS in arrival
+// order and four threads per slot add its group's x, y, z and intensity into
+// double sums in that order. The set-up returns the bin's claim state to
+// zero, as k_bins_fb does.
+__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) void k_centroid_fb(
+    const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
+    const float4* __restrict__ stage_pt, long long N, long long P, int M, long long ptiles,
+    int ptile, int tshift, int gshift, int nbits, const unsigned* __restrict__ tile_firsts,
+    int ptp, unsigned long long* __restrict__ fkey, const unsigned* __restrict__ frank,
+    unsigned* __restrict__ first, unsigned long long cells,
+    unsigned long long* __restrict__ table, unsigned S, int* __restrict__ slot_of,
+    unsigned char* __restrict__ filt, int fltshift, int gx, int gy,
+    float4* __restrict__ centroids, int* __restrict__ coords, int* __restrict__ counts,
+    int* __restrict__ num_voxels, Header* __restrict__ hdr, long long zero_words) {
+    extern __shared__ float4 lds_rows[];
+    const int G = 1 << gshift;
+    // per-wavefront counts are 16-bit offsets within the round (at most
+    // kBinBlock); the region first holds the tile prefix
+    const int wwords = 3 * kBinWaves * G / 2 > kScanTiles ? 3 * kBinWaves * G / 2 : kScanTiles;
+    float4* rowbuf = lds_rows;                   // [kBinBlock] this round's rows, by slot
+    unsigned* running = reinterpret_cast<unsigned*>(rowbuf + kBinBlock);  // [G] arrivals so far
+    unsigned* wbuf = running + G;                // [wwords] the tile prefix, then the counts
+    unsigned short* wcnt = reinterpret_cast<unsigned short*>(wbuf);  // [3][kBinWaves * G]
+    unsigned* roff = wbuf + wwords;              // [kBinBlock + 2] run offsets in the group
+    unsigned* rsrc = roff + kBinBlock + 2;       // [kBinBlock] run start within its tile
+    unsigned* wsum = rsrc + kBinBlock;           // [kWsumWords]
+    unsigned* cnt_round = wsum + kWsumWords;     // [G] arrivals of the slot in this round
+    unsigned* seg = cnt_round + G;               // [G] start of the slot's group in rowbuf
+    unsigned* pid_of = seg + G;                  // [G] voxel id of each slot, kNoPid if none kept
+    // [G] cell key + 1 of each slot (8-byte aligned: every count above is even)
+    unsigned long long* key_of = reinterpret_cast<unsigned long long*>(pid_of + G);
+
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int w = t / kWave;
+    const long long b = xcd_tile(blockIdx.x, gridDim.x);  // contiguous bins per XCD
+    const long long nbins = 1ll << nbits;
+    const int Gb = b < P ? (int)((P - b + nbins - 1) >> nbits) : 0;  // slots with i0 < P
+    unsigned e = 0u;
+    if ((long long)t < ptiles) e = cm[(size_t)b * ptiles + t];
+    unsigned tc[kScanPer];
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+        const int q = t * kScanPer + u;
+        tc[u] = q < ptp ? tile_firsts[q] : 0u;
+    }
+    const unsigned i0 = (unsigned)b + ((unsigned)t << nbits);  // this thread's slot
+    unsigned long long fk = 0ull;
+    unsigned fr = 0u;
+    int fs = -1;
+    if (t < Gb) {
+        fk = fkey[i0];
+        fr = frank[i0];
+        if (!first) fs = slot_of[i0];
+    }
+    const unsigned err = block_error(hdr);
+    heal_workspace(hdr, zero_words, err);
+    if (t < G) {
+        pid_of[t] = fr;  // the rank until the id is known
+        key_of[t] = fk;
+    }
+    // one scan: the first group's run offsets and the tile counts
+    unsigned s = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) s += tc[u];
+    const unsigned sv[2] = {e >> 16, s};
+    unsigned sx[2], st[2];
+    block_excl_scan_n<kBinWaves, 2>(sv, wsum, sx, st);
+    unsigned ng = st[0];
+    const unsigned distinct_u = st[1];
+    roff[t] = sx[0];
+    rsrc[t] = e & 0xffffu;
+    unsigned ex = sx[1];
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+        const int q = t * kScanPer + u;
+        if (q < ptp) wbuf[q] = ex;
+        ex += tc[u];
+    }
+    if (t < Gb)
+        release_slot(first, cells, fkey, table, S, slot_of, i0, fk, fs, hdr, num_voxels, filt,
+                     fltshift);
+    __syncthreads();
+    const long long distinct = distinct_u;
+    const long long V = distinct < M ? distinct : M;
+    int status = (int)V;
+    if (N > P && distinct < M) status = VOX_STATUS_NEEDS_CHUNKED;
+    if (err != 0u) status = VOX_STATUS_DEVICE_ERROR;
+    if (blockIdx.x == 0 && t == 0) {
+        hdr->status = status;
+        hdr->distinct = (int)distinct;
+        num_voxels[0] = status;
+    }
+    if (t < G) {
+        unsigned mypid = kNoPid;
+        if (key_of[t] != 0ull) {
+            const unsigned pid = wbuf[i0 >> tshift] + pid_of[t];
+            if ((long long)pid >= distinct) report_error(hdr, num_voxels, 4u);  // not on a clean workspace
+            else if (status > 0 && (long long)pid < V) mypid = pid;
+        }
+        pid_of[t] = mypid;
+    }
+    __syncthreads();  // pid_of written, the tile prefix read
+    if (status <= 0) return;  // block-uniform
+    for (int x = t; x < G; x += kBinBlock) running[x] = 0u;
+    for (int x = t; x < 3 * kBinWaves * G / 2; x += kBinBlock) wbuf[x] = 0u;
+    __syncthreads();
+
+    // thread t < 4 Gb: component t % 4 (x, y, z, intensity) of slot t / 4
+    double sum = 0.0;
+    unsigned round = 0;
+    for (long long tg = 0; tg < ptiles; tg += kBinBlock) {
+        if (tg > 0) {
+            const long long tt = tg + t;
+            e = 0u;
+            if (tt < ptiles) e = cm[(size_t)b * ptiles + tt];
+            const unsigned ro = block_excl_scan<kBinWaves>(e >> 16, wsum, &ng);
+            roff[t] = ro;
+            rsrc[t] = e & 0xffffu;
+            __syncthreads();
+        }
+        const int nruns = (int)(ptiles - tg < kBinBlock ? ptiles - tg : kBinBlock);
+        for (unsigned x0 = 0; x0 < ng; x0 += kBinBlock) {
+            const unsigned x = x0 + (unsigned)t;
+            bool valid = x < ng;
+            unsigned pl = 0u;
+            float4 row = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (valid) {
+                int lo = 0, hi = nruns;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (roff[mid] <= x) lo = mid;
+                    else hi = mid;
+                }
+                const size_t src = (size_t)(tg + lo) * ptile + rsrc[lo] + (x - roff[lo]);
+                pl = staging[src] >> 16;
+                row = stage_pt[src];
+                if (pl >= (unsigned)Gb) {  // not on a clean workspace
+                    report_error(hdr, num_voxels, 4u);
+                    valid = false;
+                } else {
+                    valid = pid_of[pl] != kNoPid;  // points of voxels past the cap are dropped
+                }
+                if (!valid) pl = 0u;
+            }
+            // counts of three rounds rotate: round r writes buffer r % 3 and
+            // clears (r + 1) % 3, last read two rounds ago
+            unsigned short* cur = wcnt + (round % 3u) * (kBinWaves * G);
+            unsigned* nxt = wbuf + ((round + 1u) % 3u) * (kBinWaves * G / 2);
+            for (int y = t; y < kBinWaves * G / 2; y += kBinBlock) nxt[y] = 0u;
+            const unsigned long long m = match_mask(pl, valid, gshift);
+            const unsigned rank = (unsigned)__popcll(m & lanes_below(lane));
+            if (valid && (m & lanes_above(lane)) == 0ull)
+                cur[w * G + pl] = (unsigned short)__popcll(m);
+            __syncthreads();
+            // thread p < G, slot p: the wavefronts' offsets within the round
+            // (eight reads in flight, then eight writes) and the round's count
+            unsigned cnt = 0u;
+            if (t < G) {
+                unsigned acc = 0u;
+#pragma unroll
+                for (int h0 = 0; h0 < kBinWaves; h0 += 8) {
+                    unsigned cw[8];
+#pragma unroll
+                    for (int ww = 0; ww < 8; ++ww) cw[ww] = cur[(h0 + ww) * G + t];
+#pragma unroll
+                    for (int ww = 0; ww < 8; ++ww) {
+                        cur[(h0 + ww) * G + t] = (unsigned short)acc;
+                        acc += cw[ww];
+                    }
+                }
+                cnt = acc;
+                cnt_round[t] = cnt;
+                running[t] += cnt;
+            }
+            unsigned round_total;
+            const unsigned sg = block_excl_scan<kBinWaves>(cnt, wsum, &round_total);
+            if (t < G) seg[t] = sg;
+            __syncthreads();
+            if (valid) rowbuf[seg[pl] + (unsigned)cur[w * G + pl] + rank] = row;
+            __syncthreads();
+            if (t < 4 * Gb) {
+                // one component of this slot's rows of the round, added in
+                // input order; the LDS reads go four at a time ahead of the
+                // additions
+                const unsigned s0 = seg[t >> 2], n = cnt_round[t >> 2];
+                const float* col = reinterpret_cast<const float*>(rowbuf + s0) + (t & 3);
+                unsigned k = 0;
+                for (; k + 4u <= n; k += 4u) {
+                    float f[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) f[j] = col[4 * (k + j)];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sum += (double)f[j];
+                }
+                for (; k < n; ++k) sum += (double)col[4 * k];
+            }
+            __syncthreads();  // rowbuf and the per-slot words are reused
+            ++round;
+        }
+    }
+    // the four sums of slot p meet in LDS (rowbuf is free now)
+    double* dsum = reinterpret_cast<double*>(rowbuf);
+    if (t < 4 * Gb) dsum[t] = sum;
+    __syncthreads();
+    if (t < Gb && pid_of[t] != kNoPid) {
+        const unsigned pid = pid_of[t];
+        const unsigned n = running[t];
+        const double dn = (double)n;
+        centroids[pid] = make_float4((float)(dsum[4 * t] / dn), (float)(dsum[4 * t + 1] / dn),
+                                     (float)(dsum[4 * t + 2] / dn), (float)(dsum[4 * t + 3] / dn));
+        counts[pid] = (int)n;
+        write_coords(coords, pid, (long long)(key_of[t] - 1ull), gx, gy);
+    }
+}
+
 // -------------------------------------------------------------- bin only --
 
 __global__ __launch_bounds__(kBlock) void k_bin(const float4* __restrict__ pts, long long N,
@@ -2440,6 +2675,15 @@ inline size_t centroid_lds_bytes(int G) {
     return 16u * (size_t)kBinBlock +
            4u * (size_t)(G + 3 * kBinWaves * G + kBinBlock + 1 + kBinBlock + kWsumWords + 3 * G);
 }
+// LDS of one k_centroid_fb block for bins of G slots (16-bit counts; the
+// words before key_of are an even count: it is 8-byte aligned)
+inline size_t centroid_fb_lds_bytes(int G) {
+    const size_t ww = (size_t)3 * kBinWaves * G / 2 > (size_t)kScanTiles
+                          ? (size_t)3 * kBinWaves * G / 2 : (size_t)kScanTiles;
+    return 16u * (size_t)kBinBlock +
+           4u * ((size_t)G + ww + kBinBlock + 2 + kBinBlock + kWsumWords + 3 * (size_t)G) +
+           8u * (size_t)G;
+}
 // LDS of one k_bins_fb block for bins of G pillar slots
 inline size_t bins_fb_lds_bytes(int G, int K) {
     const size_t ww = (size_t)3 * kBinWaves * G / 2 > (size_t)kScanTiles
@@ -2461,7 +2705,10 @@ inline int default_cap(int K) {
     return (int)cdiv(16ll * K, kWave) * kWave;
 }
 
-int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
+// fb_carry (downsampling): the first-index route with rows carried, beside
+// route 3's layout (which the chunked path then takes).
+int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl,
+              bool fb_carry = false) {
     if (N < 0 || N > kMaxPoints) return VOX_EINVAL;
     if (M < 1 || K < 1) return VOX_EINVAL;
     if ((long long)M > (1ll << 27)) return VOX_EINVAL;
@@ -2573,7 +2820,7 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl) {
     pl->fblds = 0;
     pl->merge = opt ? opt->lane_merge : 0;
     pl->first_map = opt ? opt->first_map : 0;
-    if (pl->part && !pl->carry && (path == 0 || path == 4) && !pl->C) {
+    if (pl->part && (fb_carry || (!pl->carry && (path == 0 || path == 4))) && !pl->C) {
         // default: 128 slots per bin, or 256 when 128 would need more bins
         // than the chip runs at once
         const long long Pw = P > 0 ? P : 1;
@@ -2800,31 +3047,53 @@ int launch_claim_fb(const float* points, const Grid& g, const Plan& pl, const Bu
 
 template <int PER, int BLK>
 int launch_part_fb_t(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
-                     int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
+                     int32_t* point_pillar, hipStream_t st, hipEvent_t* ev, bool carry) {
+    if (carry) {  // downsampling: rows carried, no inverse map
+        if (bf.first)
+            hipExtLaunchKernelGGL(k_part_fb<PER, BLK, true, true>, dim3((unsigned)pl.ptiles),
+                                  dim3(BLK), 0, st, ev_start(ev), ev_stop(ev), 0,
+                                  reinterpret_cast<const float4*>(points), pl.N, pl.P, g, bf.table,
+                                  (unsigned)pl.S, pl.hash, bf.first, bf.slot_of, pl.fbits,
+                                  pl.ptiles, bf.cm, bf.stage, bf.fkey, bf.frank, bf.tfirst, bf.hdr,
+                                  nullptr, bf.filt, pl.fltshift, bf.stage_pt);
+        else
+            hipExtLaunchKernelGGL(k_part_fb<PER, BLK, false, true>, dim3((unsigned)pl.ptiles),
+                                  dim3(BLK), 0, st, ev_start(ev), ev_stop(ev), 0,
+                                  reinterpret_cast<const float4*>(points), pl.N, pl.P, g, bf.table,
+                                  (unsigned)pl.S, pl.hash, bf.first, bf.slot_of, pl.fbits,
+                                  pl.ptiles, bf.cm, bf.stage, bf.fkey, bf.frank, bf.tfirst, bf.hdr,
+                                  nullptr, bf.filt, pl.fltshift, bf.stage_pt);
+        return last_launch();
+    }
     if (bf.first)
         hipExtLaunchKernelGGL(k_part_fb<PER, BLK, true>, dim3((unsigned)pl.ptiles), dim3(BLK), 0, st,
                               ev_start(ev), ev_stop(ev), 0, reinterpret_cast<const float4*>(points),
                               pl.N, pl.P, g, bf.table, (unsigned)pl.S, pl.hash, bf.first,
                               bf.slot_of, pl.fbits, pl.ptiles, bf.cm, bf.stage, bf.fkey, bf.frank,
-                              bf.tfirst, bf.hdr, point_pillar, bf.filt, pl.fltshift);
+                              bf.tfirst, bf.hdr, point_pillar, bf.filt, pl.fltshift,
+                              static_cast<float4*>(nullptr));
     else
         hipExtLaunchKernelGGL(k_part_fb<PER, BLK, false>, dim3((unsigned)pl.ptiles), dim3(BLK), 0,
                               st, ev_start(ev), ev_stop(ev), 0,
                               reinterpret_cast<const float4*>(points), pl.N, pl.P, g, bf.table,
                               (unsigned)pl.S, pl.hash, bf.first, bf.slot_of, pl.fbits, pl.ptiles,
                               bf.cm, bf.stage, bf.fkey, bf.frank, bf.tfirst, bf.hdr, point_pillar,
-                              bf.filt, pl.fltshift);
+                              bf.filt, pl.fltshift, static_cast<float4*>(nullptr));
     return last_launch();
 }
 
 int launch_part_fb(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
-                   int32_t* point_pillar, hipStream_t st, hipEvent_t* ev) {
+                   int32_t* point_pillar, hipStream_t st, hipEvent_t* ev, bool carry = false) {
     switch (pl.pper) {
-        case 2: return launch_part_fb_t<2, kBlock>(points, g, pl, bf, point_pillar, st, ev);
-        case 4: return launch_part_fb_t<4, kWideBlock>(points, g, pl, bf, point_pillar, st, ev);
-        case 8: return launch_part_fb_t<8, kWideBlock>(points, g, pl, bf, point_pillar, st, ev);
-        case 16: return launch_part_fb_t<16, kWideBlock>(points, g, pl, bf, point_pillar, st, ev);
-        default: return launch_part_fb_t<1, kBlock>(points, g, pl, bf, point_pillar, st, ev);
+        case 2: return launch_part_fb_t<2, kBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
+        case 4:
+            return launch_part_fb_t<4, kWideBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
+        case 8:
+            return launch_part_fb_t<8, kWideBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
+        case 16:
+            return launch_part_fb_t<16, kWideBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
+        default:
+            return launch_part_fb_t<1, kBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
     }
 }
 
@@ -3012,21 +3281,42 @@ int insert_chunked(const float* points, const Grid& g, const Plan& pl, const Buf
     return VOX_OK;
 }
 
-// Downsampling runs the partitioned route with rows carried and no max_points
-// (the plan takes K = 1); options may set select_path to 0 or 3 only.
+// Downsampling carries the rows through the partition and has no
+// max_points (the plan takes K = 1). select_path 0: the first-index route
+// where it applies (route 3's layout beside it, for the chunked path), else
+// route 3; 3: route 3; 4: the first-index route or VOX_EINVAL.
 int downsample_plan(long long N, int M, const vox_options* options, Plan* pl) {
     vox_options o;
     if (options) {
         o = *options;
-        if (o.select_path != 0 && o.select_path != 3) return VOX_EINVAL;
+        if (o.select_path != 0 && o.select_path != 3 && o.select_path != 4) return VOX_EINVAL;
     } else {
         memset(&o, 0, sizeof(o));
     }
+    const int want = o.select_path;
     o.select_path = 3;
-    const int rc = make_plan(N, M, 1, &o, pl);
+    const int rc = make_plan(N, M, 1, &o, pl, want != 3);
     if (rc != VOX_OK) return rc;
+    if (want == 4 && !pl->fb) return VOX_EINVAL;
     pl->lds = centroid_lds_bytes(1 << pl->gshift);
+    if (pl->fb) pl->fblds = centroid_fb_lds_bytes(1 << pl->fshift);
     return VOX_OK;
+}
+
+int launch_centroid_fb(const Plan& pl, const Buffers& bf, const Grid& g, float* centroids,
+                       int32_t* coords, int32_t* counts, int32_t* num_voxels, hipStream_t st) {
+    const long long tile = (long long)pl.pblock * pl.pper;
+    int tshift = 0;
+    while ((1ll << tshift) < tile) ++tshift;
+    hipExtLaunchKernelGGL(k_centroid_fb, dim3(1u << pl.fbits), dim3(kBinBlock),
+                          (unsigned)pl.fblds, st, nullptr, nullptr, 0, bf.cm, bf.stage,
+                          bf.stage_pt, pl.N, pl.P, pl.M, pl.ptiles, (int)tile, tshift, pl.fshift,
+                          pl.fbits, bf.tfirst, (int)pl.ptp, bf.fkey, bf.frank, bf.first,
+                          (unsigned long long)g.gx * g.gy * g.gz, bf.table, (unsigned)pl.S,
+                          bf.slot_of, bf.filt, pl.fltshift, g.gx, g.gy,
+                          reinterpret_cast<float4*>(centroids), coords, counts, num_voxels,
+                          bf.hdr, (long long)(pl.zero_bytes / 4));
+    return last_launch();
 }
 
 int launch_centroid(const Plan& pl, long long P, const Buffers& bf, const Grid& g,
@@ -3257,6 +3547,13 @@ int vox_downsample(const float* points, int64_t n_points, const float range[6],
     if ((rc = downsample_plan(n_points, max_voxels, options, &pl)) != VOX_OK) return rc;
     if (((uintptr_t)workspace & 255u) || workspace_bytes < pl.bytes) return VOX_EWORKSPACE;
     const Buffers bf = carve(workspace, pl, g);
+    if (!chunked && pl.fb) {
+        // first-index route: claim, partition with rows carried, centroids
+        if ((rc = launch_claim_fb(points, g, pl, bf, stream, nullptr)) != VOX_OK) return rc;
+        if ((rc = launch_part_fb(points, g, pl, bf, nullptr, stream, nullptr, true)) != VOX_OK)
+            return rc;
+        return launch_centroid_fb(pl, bf, g, centroids, coords, counts, num_voxels, stream);
+    }
     long long P = pl.P;
     if (chunked) {
         if ((rc = insert_chunked(points, g, pl, bf, stream, &P)) != VOX_OK) return rc;

@@ -78,8 +78,15 @@ def test_downsample_options_and_chunked(name):
     pts, _ = generate(name)
     want = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
     M = p.max_voxels
+    # route 4 (the default here) with the claim in the table and its key
+    # filter, and route 3; a prefix too short for the cap falls back to the
+    # chunked route 3 on the workspace route 4 left
     for kw in (dict(hash=1), dict(hash=2), dict(compact_table=1), dict(table_slots=3 * M),
-               dict(prefix_points=4096), dict(chunked=True)):
+               dict(prefix_points=4096), dict(chunked=True), dict(select_path=3),
+               dict(select_path=4), dict(select_path=4, first_map=1),
+               dict(select_path=4, first_map=1, hash=2), dict(select_path=4, lane_merge=1),
+               dict(select_path=4, bin_ids=32), dict(select_path=3, prefix_points=4096),
+               dict(select_path=4, prefix_points=4096), dict(kept_map=1)):
         say(f"downsample {name} {kw}")
         check(gpu_ds(pts, p.range_, p.cell, p.grid, M, **kw), want, f"{name} {kw}")
 
@@ -102,9 +109,11 @@ def test_downsample_fuzz():
         pts[rng.random(n) < 0.02, 3] = np.nan
         M = int(rng.choice([1, 3, 50, 1000, 100000]))
         r = (x0, y0, z0, x0 + gx * vx, y0 + gy * vy, z1)
-        say(f"downsample fuzz {t}: N={n} grid=({gx},{gy},{gz}) M={M}")
+        # routes 4 (automatic), 3, and 4 on the table
+        kw = (dict(), dict(select_path=3), dict(first_map=1))[t % 3]
+        say(f"downsample fuzz {t}: N={n} grid=({gx},{gy},{gz}) M={M} {kw}")
         want = oracle.downsample(pts, r, (vx, vy, vz), (gx, gy, gz), M)
-        check(gpu_ds(pts, r, (vx, vy, vz), (gx, gy, gz), M), want, f"fuzz {t}")
+        check(gpu_ds(pts, r, (vx, vy, vz), (gx, gy, gz), M, **kw), want, f"fuzz {t}")
 
 
 def test_downsample_heavy_voxel_and_edge_cases():

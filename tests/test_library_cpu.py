@@ -230,11 +230,18 @@ def test_downsample_workspace_and_limits():
     for bad in (dict(max_voxels=262145), dict(max_voxels=0)):
         with pytest.raises(vox.VoxError):
             vox.downsample_workspace_bytes(1000, **bad)
-    # only the carried-rows route exists for downsampling
+    # only the carried-rows routes exist for downsampling: 3, and 4 where it
+    # applies (its layout holds route 3's too, for the chunked path)
     for path in (1, 2):
         with pytest.raises(vox.VoxError):
             vox.downsample_workspace_bytes(1000, 100, select_path=path)
-    assert vox.downsample_workspace_bytes(1000, 100, select_path=3)[0] > 0
+    n3 = vox.downsample_workspace_bytes(1000, 100, select_path=3)[0]
+    n4 = vox.downsample_workspace_bytes(1000, 100, select_path=4)[0]
+    assert 0 < n3 < n4 == vox.downsample_workspace_bytes(1000, 100)[0]
+    with pytest.raises(vox.VoxError):   # route 4 has no kept-cell table
+        vox.downsample_workspace_bytes(1000, 100, select_path=4, compact_table=1)
+    # the kept-cell table selects route 3 automatically
+    assert vox.downsample_workspace_bytes(1000, 100, compact_table=1)[0] > 0
 
 
 # ------------------------------------------------------ spherical binning --
