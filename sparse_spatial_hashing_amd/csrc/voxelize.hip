@@ -1554,6 +1554,13 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
         if (ww < w) woff += x;
         tfirst += x;
     }
+    // CARRY with a tile's rows fitting the histograms' LDS (PER <= 8 at 512
+    // threads): the rows are placed there in staging order after the
+    // positions are read, and written out as one contiguous run
+    constexpr bool kRowsViaLds = CARRY && BLK * PER * sizeof(float4) <= sizeof(hist);
+    unsigned lat[kRowsViaLds ? PER : 1];  // each row's position in the tile's slice
+#pragma unroll
+    for (int k = 0; k < (kRowsViaLds ? PER : 1); ++k) lat[k] = 0u;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         if (i0v[k] == kNoPid) continue;
@@ -1561,7 +1568,10 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
         const unsigned bin = i0v[k] & bmask;
         const unsigned at = hist[w][bin] + pos[k];
         staging[base + at] = ((i0v[k] >> nbits) << 16) | local;
-        if (CARRY) stage_pt[base + at] = rowk[k];  // the row, bit for bit
+        if (CARRY) {
+            if (kRowsViaLds) lat[k] = at;
+            else stage_pt[base + at] = rowk[k];  // the row, bit for bit
+        }
         if (isf[k]) {
             const long long i = base + local;
             frank[i] = woff + fb[k];
@@ -1569,6 +1579,15 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
         }
     }
     if (t == 0 && any_prefix) tile_firsts[tile] = tfirst;
+    if (kRowsViaLds) {
+        float4* trow = reinterpret_cast<float4*>(&hist[0][0]);
+        __syncthreads();  // every position has been read from hist
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (i0v[k] != kNoPid) trow[lat[k]] = rowk[k];
+        __syncthreads();
+        for (unsigned q = t; q < total; q += BLK) stage_pt[base + q] = trow[q];
+    }
 }
 
 // At most 64 VGPRs: two 1024-thread blocks per CU. CARRY: rows come from
