@@ -1558,20 +1558,19 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
     // threads): the rows are placed there in staging order after the
     // positions are read, and written out as one contiguous run
     constexpr bool kRowsViaLds = CARRY && BLK * PER * sizeof(float4) <= sizeof(hist);
-    unsigned lat[kRowsViaLds ? PER : 1];  // each row's position in the tile's slice
-#pragma unroll
-    for (int k = 0; k < (kRowsViaLds ? PER : 1); ++k) lat[k] = 0u;
+    // The staging words go through the same LDS: placed in staging order once
+    // every position has been read, then written out as one contiguous run
+    // (the tile's slice of at most BLK PER words fits the histograms).
+    static_assert(BLK * PER * sizeof(unsigned) <= sizeof(hist), "a tile's words fit the histograms");
+    unsigned lat[PER];  // each staged point's position in the tile's slice
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
+        lat[k] = 0u;
         if (i0v[k] == kNoPid) continue;
         const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);
         const unsigned bin = i0v[k] & bmask;
-        const unsigned at = hist[w][bin] + pos[k];
-        staging[base + at] = ((i0v[k] >> nbits) << 16) | local;
-        if (CARRY) {
-            if (kRowsViaLds) lat[k] = at;
-            else stage_pt[base + at] = rowk[k];  // the row, bit for bit
-        }
+        lat[k] = hist[w][bin] + pos[k];
+        if (CARRY && !kRowsViaLds) stage_pt[base + lat[k]] = rowk[k];  // the row, bit for bit
         if (isf[k]) {
             const long long i = base + local;
             frank[i] = woff + fb[k];
@@ -1579,9 +1578,19 @@ __global__ __launch_bounds__(BLK) void k_part_fb(
         }
     }
     if (t == 0 && any_prefix) tile_firsts[tile] = tfirst;
+    unsigned* tword = &hist[0][0];
+    __syncthreads();  // every position has been read from hist
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (i0v[k] == kNoPid) continue;
+        const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);
+        tword[lat[k]] = ((i0v[k] >> nbits) << 16) | local;
+    }
+    __syncthreads();
+    for (unsigned q = t; q < total; q += BLK) staging[base + q] = tword[q];
     if (kRowsViaLds) {
         float4* trow = reinterpret_cast<float4*>(&hist[0][0]);
-        __syncthreads();  // every position has been read from hist
+        __syncthreads();  // every word has been read from LDS
 #pragma unroll
         for (int k = 0; k < PER; ++k)
             if (i0v[k] != kNoPid) trow[lat[k]] = rowk[k];
