@@ -152,3 +152,29 @@ def test_downsample_then_voxelize_share_one_workspace():
         got = vox.voxelize(x, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
         wv = oracle.voxelize(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
         assert np.array_equal(got[1].cpu().numpy(), wv[1])
+
+
+@pytest.mark.parametrize("route", [4, 3])
+def test_downsample_device_error_heals_the_workspace(route):
+    """As for voxelization: the error word set from the host (no valid input
+    reaches it) makes the call report VOX_STATUS_DEVICE_ERROR and return its
+    zero part to zero (a planted stray byte included); the next call on the
+    same workspace is exact."""
+    p = get_config("kitti_frame").params
+    pts, _ = generate("kitti_frame")
+    say(f"downsample heal route {route}")
+    ds = vox.Downsampler(pts.shape[0], p.range_, p.cell, p.grid, p.max_voxels, device=DEV,
+                         select_path=route)
+    x = torch.from_numpy(pts).to(DEV)
+    ds.workspace[16:20] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device=DEV)
+    end = ds.zero_bytes - 4
+    ds.workspace[end:end + 4] = torch.tensor([0xAB, 0, 0, 0], dtype=torch.uint8, device=DEV)
+    nv = ds.run(x)
+    torch.cuda.synchronize()
+    assert int(nv.item()) == vox.VOX_STATUS_DEVICE_ERROR
+    assert vox.workspace_is_clean(ds.workspace, ds.zero_bytes), "the error call left it dirty"
+    ds.run(x)
+    torch.cuda.synchronize()
+    got = tuple(t.cpu().numpy() for t in ds.outputs())
+    check(got, oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels),
+          f"after healing, route {route}")
