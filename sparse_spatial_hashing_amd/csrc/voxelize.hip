@@ -1241,21 +1241,31 @@ __global__ __launch_bounds__(BLK) void k_part(const float4* __restrict__ pts, lo
     // the rows are placed there in staging order and written out in one
     // contiguous run; otherwise each row goes straight to its position.
     constexpr bool kRowsViaLds = CARRY && BLK * PER * sizeof(float4) <= sizeof(hist);
+    // The staging words go through the histograms' LDS too: placed in
+    // staging order once every position is read, then written as one
+    // contiguous run per tile instead of one scattered 4-byte store each.
+    static_assert(BLK * PER * sizeof(unsigned) <= sizeof(hist), "a tile's words fit the histograms");
     unsigned lat[PER];  // position within the tile's staging slice
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         lat[k] = 0u;
         if (pid[k] == kNoPid) continue;
-        const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);  // in the tile
-        const unsigned bin = pid[k] & bmask;
-        const unsigned id = pid[k] >> nbits;  // id within the bin
-        lat[k] = hist[w][bin] + pos[k];
-        staging[base + lat[k]] = (id << 16) | local;
+        lat[k] = hist[w][pid[k] & bmask] + pos[k];
         if (CARRY && !kRowsViaLds) stage_pt[base + lat[k]] = row[k];  // the row, bit for bit
     }
+    unsigned* tword = &hist[0][0];
+    __syncthreads();   // every position is read from hist
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if (pid[k] == kNoPid) continue;
+        const unsigned local = (unsigned)(w * (kWave * PER) + k * kWave + lane);  // in the tile
+        tword[lat[k]] = ((pid[k] >> nbits) << 16) | local;  // id within the bin, index in tile
+    }
+    __syncthreads();
+    for (unsigned q = t; q < total; q += BLK) staging[base + q] = tword[q];
     if (kRowsViaLds) {
         float4* trow = reinterpret_cast<float4*>(&hist[0][0]);
-        __syncthreads();   // every position is read from hist
+        __syncthreads();   // every word is read from LDS
 #pragma unroll
         for (int k = 0; k < PER; ++k)
             if (pid[k] != kNoPid) trow[lat[k]] = row[k];
@@ -2418,8 +2428,9 @@ __global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) 
 // index order; each round's arrivals are grouped by slot in LDS in arrival
 // order and four threads per slot add its group's x, y, z and intensity into
 // double sums in that order. The set-up returns the bin's claim state to
-// zero, as k_bins_fb does.
-__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(8))) void k_centroid_fb(
+// zero, as k_bins_fb does. WPE as for k_bins_fb.
+template <int WPE>
+__global__ __launch_bounds__(kBinBlock) __attribute__((amdgpu_waves_per_eu(WPE))) void k_centroid_fb(
     const unsigned* __restrict__ cm, const unsigned* __restrict__ staging,
     const float4* __restrict__ stage_pt, long long N, long long P, int M, long long ptiles,
     int ptile, int tshift, int gshift, int nbits, const unsigned* __restrict__ tile_firsts,
@@ -3336,7 +3347,8 @@ int launch_centroid_fb(const Plan& pl, const Buffers& bf, const Grid& g, float* 
     const long long tile = (long long)pl.pblock * pl.pper;
     int tshift = 0;
     while ((1ll << tshift) < tile) ++tshift;
-    hipExtLaunchKernelGGL(k_centroid_fb, dim3(1u << pl.fbits), dim3(kBinBlock),
+    hipExtLaunchKernelGGL((1 << pl.fbits) <= kFbOneBlockPerCu ? &k_centroid_fb<4> : &k_centroid_fb<8>,
+                          dim3(1u << pl.fbits), dim3(kBinBlock),
                           (unsigned)pl.fblds, st, nullptr, nullptr, 0, bf.cm, bf.stage,
                           bf.stage_pt, pl.N, pl.P, pl.M, pl.ptiles, (int)tile, tshift, pl.fshift,
                           pl.fbits, bf.tfirst, (int)pl.ptp, bf.fkey, bf.frank, bf.first,
