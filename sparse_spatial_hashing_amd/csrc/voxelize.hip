@@ -969,6 +969,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float4* __restrict__ pts,
 constexpr int kPartMaxPer = 16;                // points per k_part thread, at most
 constexpr int kPartBatch = 4;                  // lookups in flight per thread
 constexpr int kWideBlock = 2 * kBlock;         // k_part threads from 4 points per thread
+constexpr long long kWideTilesMin = 192;       // 512-thread tiles below 4 points per thread from here
 constexpr int kMaxBins = 2048;                 // bins per call (k_part: one LDS histogram per wavefront)
 constexpr int kBinBlock = 1024;                // k_bins threads (16 wavefronts)
 constexpr int kBinWaves = kBinBlock / kWave;
@@ -2843,8 +2844,13 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl,
         pl->pper = per;
         // from 4 points per thread the tiles take 512 threads: as many threads
         // per CU (two blocks instead of four), half the tiles, so every bin's
-        // run in a tile, which k_bins reads, is twice as long
-        pl->pblock = per >= 4 ? kWideBlock : kBlock;
+        // run in a tile, which k_bins reads, is twice as long; with fewer
+        // points per thread too, as long as that leaves kWideTilesMin tiles
+        // (a frame of 122,880 points: 240 tiles, and bins kernels that walk
+        // half as many runs; smaller clouds keep 256-thread tiles, which
+        // spread them over more CUs)
+        pl->pblock = (per >= 4 || cdiv(Nw, (long long)kWideBlock * per) >= kWideTilesMin)
+                         ? kWideBlock : kBlock;
         pl->ptiles = cdiv(Nw, (long long)pl->pblock * per);
         cap = 0;  // no buckets
     }
@@ -3123,8 +3129,12 @@ int launch_part_fb_t(const float* points, const Grid& g, const Plan& pl, const B
 
 int launch_part_fb(const float* points, const Grid& g, const Plan& pl, const Buffers& bf,
                    int32_t* point_pillar, hipStream_t st, hipEvent_t* ev, bool carry = false) {
+    const bool wide = pl.pblock == kWideBlock;
     switch (pl.pper) {
-        case 2: return launch_part_fb_t<2, kBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
+        case 2:
+            return wide ? launch_part_fb_t<2, kWideBlock>(points, g, pl, bf, point_pillar, st, ev,
+                                                          carry)
+                        : launch_part_fb_t<2, kBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
         case 4:
             return launch_part_fb_t<4, kWideBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
         case 8:
@@ -3132,7 +3142,9 @@ int launch_part_fb(const float* points, const Grid& g, const Plan& pl, const Buf
         case 16:
             return launch_part_fb_t<16, kWideBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
         default:
-            return launch_part_fb_t<1, kBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
+            return wide ? launch_part_fb_t<1, kWideBlock>(points, g, pl, bf, point_pillar, st, ev,
+                                                          carry)
+                        : launch_part_fb_t<1, kBlock>(points, g, pl, bf, point_pillar, st, ev, carry);
     }
 }
 
@@ -3173,11 +3185,17 @@ int launch_select(const float* points, long long P, const Grid& g, const Plan& p
                   const Buffers& bf, int32_t* num_voxels, int32_t* point_pillar,
                   hipStream_t st, hipEvent_t* ev) {
     if (pl.part) {
-        // 256-thread tiles below 4 points per thread, 512-thread tiles from 4
+        // the plan's tile: 256 or 512 threads below 4 points per thread,
+        // 512 from 4
+        const bool wide = pl.pblock == kWideBlock;
         decltype(&k_part<1, false, kBlock>) kern =
-            pl.carry ? &k_part<1, true, kBlock> : &k_part<1, false, kBlock>;
+            wide ? (pl.carry ? &k_part<1, true, kWideBlock> : &k_part<1, false, kWideBlock>)
+                 : (pl.carry ? &k_part<1, true, kBlock> : &k_part<1, false, kBlock>);
         switch (pl.pper) {
-            case 2: kern = pl.carry ? &k_part<2, true, kBlock> : &k_part<2, false, kBlock>; break;
+            case 2:
+                kern = wide ? (pl.carry ? &k_part<2, true, kWideBlock> : &k_part<2, false, kWideBlock>)
+                            : (pl.carry ? &k_part<2, true, kBlock> : &k_part<2, false, kBlock>);
+                break;
             case 4:
                 kern = pl.carry ? &k_part<4, true, kWideBlock> : &k_part<4, false, kWideBlock>;
                 break;
