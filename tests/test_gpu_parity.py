@@ -530,6 +530,34 @@ def test_more_than_one_group_of_runs(name):
     assert_bitwise(gpu_vox(pts, params_of(cfg)), want, f"{name} route 4")
 
 
+@pytest.mark.parametrize("n", [98303, 98304, 98304 + 511])
+def test_partition_tile_size_boundary(n):
+    """At one point per thread the partition takes 512-thread tiles from
+    98,304 points (192 tiles) and 256-thread tiles below: both sides of the
+    switch, and a ragged last wide tile, on routes 4 and 2 and the inverse map,
+    and downsampling on routes 4 and 3."""
+    from bruteforce import same_f32
+    orc = oracle
+    cfg = get_config("kitti_frame")
+    p = cfg.params
+    pts, _ = generate("kitti_frame", n=n)
+    say(f"tile size boundary N={n}")
+    want = orc.voxelize_params(pts, p)
+    assert_bitwise(gpu_vox(pts, params_of(cfg)), want, f"N={n} route 4")
+    assert_bitwise(gpu_vox(pts, params_of(cfg), select_path=2), want, f"N={n} route 2")
+    got = gpu_vox(pts, params_of(cfg), point_map=True)
+    wmap = orc.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+    assert np.array_equal(got[3], wmap[3]), f"N={n}: point map differs"
+    wds = orc.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    for route in (4, 3):
+        out = vox.downsample(torch.from_numpy(pts).to(DEV), p.range_, p.cell, p.grid,
+                             p.max_voxels, select_path=route)
+        torch.cuda.synchronize()
+        c, k, m = (t.cpu().numpy() for t in out)
+        assert np.array_equal(k, wds[1]) and np.array_equal(m, wds[2]), f"N={n} ds {route}"
+        assert same_f32(c, wds[0]), f"N={n} downsample route {route}"
+
+
 @pytest.mark.parametrize("per_cell,K", [(70, 64), (200, 32), (40, 5)])
 def test_bin_spanning_several_chunks(per_cell, K):
     """64 cells that share one pillar-id bin, with more candidates than one
