@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline leg")
+    ap.add_argument("--downsample", action="store_true",
+                    help="also time voxel-grid downsampling of --workload (stderr line)")
     ap.add_argument("--spherical", action="store_true",
                     help="also time the spherical binning and reorder per workload (stderr)")
     ap.add_argument("--profile-iters", type=int, default=50)
@@ -487,6 +489,9 @@ def main():
         for name in config_names():
             print(json.dumps(downsample_line(name, args.steps, args.warmup, torch, vox)),
                   file=sys.stderr, flush=True)
+    elif args.downsample:
+        print(json.dumps(downsample_line(args.workload, args.steps, args.warmup, torch, vox)),
+              file=sys.stderr, flush=True)
     if not args.no_configs:
         from workloads import config_names
         for name in config_names():
