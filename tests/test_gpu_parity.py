@@ -558,6 +558,34 @@ def test_partition_tile_size_boundary(n):
         assert same_f32(c, wds[0]), f"N={n} downsample route {route}"
 
 
+@pytest.mark.parametrize("name,n,kw", [
+    ("kitti_frame", 700001, dict(lane_merge=1)),     # 2 points per thread, wide tiles
+    ("uniform_130k", 524289, dict()),                # just past 1 point per thread
+    ("kitti_frame", 98311, dict(bin_ids=32)),        # small bins on wide tiles
+    ("voxel3d", 200003, dict(select_path=2)),        # route 2 on the table
+])
+def test_odd_sizes_and_options(name, n, kw):
+    """Cloud sizes between the configs' and option mixes they do not take:
+    all three tensors and the inverse map, and downsampling, bit-exact."""
+    from bruteforce import same_f32
+    cfg = get_config(name)
+    p = cfg.params
+    pts, _ = generate(name, n=n)
+    say(f"odd size {name} N={n} {kw}")
+    got = gpu_vox(pts, params_of(cfg), point_map=True, **kw)
+    want = oracle.voxelize_map(pts, p.range_, p.cell, p.grid, p.max_points, p.max_voxels)
+    assert_bitwise(got[:3], want[:3], f"{name} N={n} {kw}")
+    assert np.array_equal(got[3], want[3]), f"{name} N={n}: point map differs"
+    dkw = {k: v for k, v in kw.items() if k != "select_path"}
+    out = vox.downsample(torch.from_numpy(pts).to(DEV), p.range_, p.cell, p.grid, p.max_voxels,
+                         **dkw)
+    torch.cuda.synchronize()
+    c, k, m = (t.cpu().numpy() for t in out)
+    wd = oracle.downsample(pts, p.range_, p.cell, p.grid, p.max_voxels)
+    assert np.array_equal(k, wd[1]) and np.array_equal(m, wd[2]), f"{name} N={n}: downsample"
+    assert same_f32(c, wd[0]), f"{name} N={n}: centroids differ"
+
+
 @pytest.mark.parametrize("per_cell,K", [(70, 64), (200, 32), (40, 5)])
 def test_bin_spanning_several_chunks(per_cell, K):
     """64 cells that share one pillar-id bin, with more candidates than one
