@@ -970,6 +970,7 @@ constexpr int kPartMaxPer = 16;                // points per k_part thread, at m
 constexpr int kPartBatch = 4;                  // lookups in flight per thread
 constexpr int kWideBlock = 2 * kBlock;         // k_part threads from 4 points per thread
 constexpr long long kWideTilesMin = 192;       // 512-thread tiles below 4 points per thread from here
+constexpr long long kWideTilesMax = 640;       // partition tiles of 512 threads, at most (about 512)
 constexpr int kMaxBins = 2048;                 // bins per call (k_part: one LDS histogram per wavefront)
 constexpr int kBinBlock = 1024;                // k_bins threads (16 wavefronts)
 constexpr int kBinWaves = kBinBlock / kWave;
@@ -2837,10 +2838,13 @@ int make_plan(long long N, int M, int K, const vox_options* opt, Plan* pl,
         const long long per_bin = cdiv(M, pl->nbins);
         while ((1ll << pl->gshift) < per_bin) ++pl->gshift;
         pl->lds = bins_lds_bytes(1 << pl->gshift, K, pl->carry);  // <= 66 KB
-        // points per k_part thread: the largest power of two up to 16 that
-        // still gives about 1024 tiles (small clouds spread over every CU)
+        // points per k_part thread: the smallest power of two up to 16 that
+        // leaves at most kWideTilesMax 512-thread tiles. About 512 tiles
+        // keeps both kernels busy: every bins block walks one run per tile,
+        // so more tiles cost the bins kernel, and fewer leave CUs idle in
+        // the partition.
         int per = 1;
-        while (per < kPartMaxPer && Nw >= (long long)per * 2 * kBlock * 1024) per *= 2;
+        while (per < kPartMaxPer && cdiv(Nw, (long long)kWideBlock * per) > kWideTilesMax) per *= 2;
         pl->pper = per;
         // from 4 points per thread the tiles take 512 threads: as many threads
         // per CU (two blocks instead of four), half the tiles, so every bin's

@@ -530,12 +530,13 @@ def test_more_than_one_group_of_runs(name):
     assert_bitwise(gpu_vox(pts, params_of(cfg)), want, f"{name} route 4")
 
 
-@pytest.mark.parametrize("n", [98303, 98304, 98304 + 511])
+@pytest.mark.parametrize("n", [97792, 97793, 327680, 327681])
 def test_partition_tile_size_boundary(n):
-    """At one point per thread the partition takes 512-thread tiles from
-    98,304 points (192 tiles) and 256-thread tiles below: both sides of the
-    switch, and a ragged last wide tile, on routes 4 and 2 and the inverse map,
-    and downsampling on routes 4 and 3."""
+    """The partition's tiles: 256 threads at one point per thread up to
+    97,792 points (191 tiles of 512 would be too few), 512 threads from
+    97,793 (192 tiles, the last one ragged); two points per thread past
+    327,680 points (more than 640 tiles of 512). Both sides of each switch,
+    on routes 4 and 2 and the inverse map, and downsampling on routes 4 and 3."""
     from bruteforce import same_f32
     orc = oracle
     cfg = get_config("kitti_frame")
